@@ -1,0 +1,137 @@
+/*
+ * specverify.h -- C ABI of the batched speculative-sampling verify step
+ * (hand-written HIP kernels for gfx950 / MI355X).
+ *
+ * Pages cited (all about speculative decoding):
+ *   [WR] wrblog.cn, "推测解码：草稿模型、接受率、正确性与加速边界"
+ *   [RL] rainlin-net.pages.dev, "投机解码" (notes)
+ *   [BS] baisen.site, "投机采样 / 投机解码（Speculative Decoding）"
+ *   [MN] magicnetworld.com, "投机解码到底能加速多少：把接受率、草稿成本与墙钟收益算清楚"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees or retains caller memory and keeps no
+ *   state between calls.  All scratch lives in the caller's `workspace`
+ *   (device memory of at least spec_verify_workspace_size() bytes, 256-byte
+ *   aligned, contents need not be initialised).
+ * - Layout is contiguous row-major.  `target_logits` is [B, gamma+1, V]
+ *   (float32 or bfloat16, see sv_dtype); `draft_probs` (q) is [B, gamma, V]
+ *   float32; `draft_ids` is [B, gamma] int32.  The logits and q base pointers
+ *   must be 16-byte aligned.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  The returned status reports only synchronous host-side
+ *   validation and launch errors; outputs are valid once the stream reaches
+ *   the end of the call.  Calls that share a workspace must not overlap.
+ * - Argument errors return a status and launch nothing.  Data faults never
+ *   abort: they raise per-request bits in `out_row_flags` (SV_ROW_*).
+ * - Inputs are read-only.  Every output element is written on every call.
+ * - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or parameter */
+  SV_ERR_UNSUPPORTED = 2, /* a size the kernels do not handle (e.g. V >= 2^31) */
+  SV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  SV_ERR_HIP = 4          /* a kernel launch failed                           */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Decoding rules that turn target logits into the processed distribution p
+ * ([WR] §2.3: p is the distribution after the production decoding rules;
+ * [WR] §7.2 temperature, §7.3 top-k / top-p).  Order: temperature, top-k on
+ * the logits (every token tied with the k-th largest logit is kept), top-p on
+ * the renormalised top-k distribution (the smallest most-probable prefix whose
+ * mass reaches top_p, plus tokens tied with its last one), renormalise.
+ *   temperature : finite, > 0
+ *   top_k       : 0 or >= V disables; otherwise 1 <= top_k < V
+ *   top_p       : in (0, 1]; 1 disables                                     */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} sv_sampling_params;
+
+/* Per-request status bits in out_row_flags. */
+#define SV_ROW_BAD_ID 1u       /* a draft id outside [0, V) was rejected        */
+#define SV_ROW_Q_ZERO 2u       /* q(d)=0 at an evaluated position: accepted iff p(d)>0 */
+#define SV_ROW_Z_DEGENERATE 4u /* rejected with an empty residual; token drawn from p */
+#define SV_ROW_NONFINITE 8u    /* NaN/+Inf logits (or an all -Inf row), or q(d) NaN,
+                                  negative or +Inf: no token emitted              */
+
+/* Bytes of workspace that spec_verify_sample, spec_verify_greedy and
+ * spec_accept_stats need for these sizes (the maximum over the three).
+ * Returns 0 when the sizes are invalid. */
+size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt,
+                                  sv_sampling_params prm);
+
+/* Sampling verify ([WR] §6 multi-token verification; [RL] §1 steps 3-4;
+ * [BS] §四 rules (1)-(2)).
+ * For each request b, position j = 0..gamma-1 in order:
+ *   accept d_j iff u_accept[b,j] < p_j(d_j) / q_j(d_j)   ([WR] §4.1)
+ *   (q_j(d_j) = 0: accept iff p_j(d_j) > 0, SV_ROW_Q_ZERO);
+ * stop at the first rejection j*: emit d_0..d_{j*-1}, then a token drawn from
+ * the residual (p_{j*} - q_{j*})_+ ([WR] §5; [RL] §2); if every draft passes,
+ * emit all gamma drafts and a bonus token drawn from p_gamma ([WR] §6).
+ * A draw takes the first token id (ascending) whose running sum of weights
+ * exceeds u_resample[b, n_accepted] * (sum of weights).
+ *   target_logits  [B, gamma+1, V]  dt
+ *   draft_probs    [B, gamma, V]    float32, the draft's processed q (not
+ *                                   renormalised by the library)
+ *   draft_ids      [B, gamma]       int32
+ *   u_accept       [B, gamma]       float32 in [0, 1)
+ *   u_resample     [B, gamma+1]     float32 in [0, 1); only index n_accepted is used
+ *   out_tokens       [B, gamma+1]   int32: emitted tokens, -1 padded
+ *   out_num_accepted [B]            int32 in [0, gamma]; emitted = n + 1 ([WR] §10)
+ *   out_row_flags    [B]            uint32 SV_ROW_* bits, or NULL
+ * gamma = 0 is plain sampling from p_0.  B = 0 is a no-op. */
+sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                             const int32_t* draft_ids, const float* u_accept,
+                             const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                             sv_sampling_params prm, int32_t* out_tokens,
+                             int32_t* out_num_accepted, uint32_t* out_row_flags,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy verify ([WR] §7.1; [RL] §2 last paragraph; [BS] §二 example):
+ * g_j = argmax of row j (lowest id on ties), j = 0..gamma;
+ * n = first j < gamma with d_j != g_j (else gamma); emit d_0..d_{n-1}, g_n.
+ * A request whose logits hold NaN emits nothing (SV_ROW_NONFINITE). */
+sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,
+                             int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                             int32_t* out_num_accepted, uint32_t* out_row_flags,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Acceptance statistics of positions j = 0..gamma-1 (rows j of the same
+ * [B, gamma+1, V] logits; the bonus row is not read):
+ *   out_alpha       = sum_x min(p_j, q_j)          ([WR] §4.2; [MN] §三)
+ *   out_z_pq        = sum_x (p_j - q_j)_+  (residual mass Z)     ([RL] §2)
+ *   out_z_qp        = sum_x (q_j - p_j)_+                        ([BS] §五)
+ *   out_accept_prob = min(1, p_j(d_j) / q_j(d_j))  ([WR] §6)
+ * each [B, gamma] float32.  q is used as given.  q_j(d_j) = 0 gives
+ * accept_prob 1 if p_j(d_j) > 0 else 0; an id outside [0, V) gives NaN; a
+ * non-finite logits row gives NaN in all four outputs of that position. */
+sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                            const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V,
+                            sv_sampling_params prm, float* out_alpha, float* out_z_pq,
+                            float* out_z_qp, float* out_accept_prob, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* spec_status_string(sv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

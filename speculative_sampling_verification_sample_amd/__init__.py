@@ -1,0 +1,18 @@
+"""Batched speculative-sampling verify step for MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/specverify.h`` (``libspecverify.so``); this package is its thin
+Python binding.
+"""
+
+from ._lib import LIB_PATH, load_library, status_string  # noqa: F401
+from .api import (  # noqa: F401
+    FLAG_BAD_ID,
+    FLAG_NONFINITE,
+    FLAG_Q_ZERO,
+    FLAG_Z_DEGENERATE,
+    accept_stats,
+    verify_greedy,
+    verify_sample,
+    workspace_size,
+)

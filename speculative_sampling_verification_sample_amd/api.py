@@ -1,0 +1,151 @@
+"""Python binding of the verify step: torch tensors in, torch tensors out.
+
+Marshalling only -- shapes and dtypes are checked, outputs and the workspace
+are allocated with torch on the tensors' device, and the C ABI is called on
+torch's current stream.  Every step of the computation runs in the HIP
+kernels of libspecverify.so.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._lib import SV_BF16, SV_F32, SV_OK, SamplingParamsC, load_library, status_string
+
+FLAG_BAD_ID = 1
+FLAG_Q_ZERO = 2
+FLAG_Z_DEGENERATE = 4
+FLAG_NONFINITE = 8
+
+_DT = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
+
+
+def _params(temperature: float, top_k: int, top_p: float) -> SamplingParamsC:
+    return SamplingParamsC(float(temperature), int(top_k), float(top_p))
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(code: int, what: str) -> None:
+    if code != SV_OK:
+        raise RuntimeError(f"{what}: {status_string(code)} (status {code})")
+
+
+def workspace_size(B: int, gamma: int, V: int, dtype=torch.bfloat16, temperature=1.0, top_k=0, top_p=1.0) -> int:
+    n = load_library().spec_verify_workspace_size(B, gamma, V, _DT[dtype], _params(temperature, top_k, top_p))
+    if n == 0:
+        raise ValueError("invalid sizes or sampling parameters")
+    return int(n)
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def verify_sample(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0,
+                  workspace: Optional[torch.Tensor] = None, out=None):
+    """Sampling verify step; returns (tokens [B, gamma+1] int32, n_accepted [B] int32, flags [B] int32)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    if G > 0:
+        _check(q, "q", torch.float32, (B, G, V))
+        _check(ids, "ids", torch.int32, (B, G))
+        _check(u_accept, "u_accept", torch.float32, (B, G))
+    _check(u_resample, "u_resample", torch.float32, (B, G1))
+    if out is None:
+        out = (torch.empty((B, G1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    tokens, nacc, flags = out
+    need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    lib = load_library()
+    code = lib.spec_verify_sample(
+        logits.data_ptr(), _DT[logits.dtype],
+        q.data_ptr() if G > 0 else None, ids.data_ptr() if G > 0 else None,
+        u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample")
+    return tokens, nacc, flags
+
+
+def verify_greedy(logits, ids, workspace: Optional[torch.Tensor] = None, out=None):
+    """Greedy verify step; returns (tokens, n_accepted, flags)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    if G > 0:
+        _check(ids, "ids", torch.int32, (B, G))
+    if out is None:
+        out = (torch.empty((B, G1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    tokens, nacc, flags = out
+    need = workspace_size(B, G, V, logits.dtype)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_greedy(
+        logits.data_ptr(), _DT[logits.dtype], ids.data_ptr() if G > 0 else None, B, G, V,
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_greedy")
+    return tokens, nacc, flags
+
+
+def accept_stats(logits, q, ids, temperature=1.0, top_k=0, top_p=1.0,
+                 workspace: Optional[torch.Tensor] = None, out=None):
+    """Per-position (alpha, Z, Z', accept_prob), each [B, gamma] float32."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    _check(q, "q", torch.float32, (B, G, V))
+    _check(ids, "ids", torch.int32, (B, G))
+    if out is None:
+        out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
+    alpha, zpq, zqp, acc = out
+    need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_accept_stats(
+        logits.data_ptr(), _DT[logits.dtype], q.data_ptr(), ids.data_ptr(), B, G, V,
+        _params(temperature, top_k, top_p), alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_accept_stats")
+    return alpha, zpq, zqp, acc

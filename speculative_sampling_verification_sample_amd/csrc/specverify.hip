@@ -1,0 +1,403 @@
+// C ABI of the verify step: argument validation, workspace layout and the
+// launch sequence of the kernels on the caller's stream.
+//
+//   sample : K1 row pass -> K2 row finalisation -> (truncation) exact
+//            fallback -> K3 acceptance + list draws -> K4 full-row draws
+//   greedy : K1 row pass (argmax) -> greedy scan
+//   stats  : K1 -> K2 -> (fallback) -> per-chunk sums -> per-row finish
+//
+// Nothing here allocates or frees device memory: every scratch buffer is a
+// slice of the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "specverify.h"
+#include "sv_device.h"
+#include "sv_rowfinal.h"
+#include "sv_rowpass.h"
+#include "sv_verify.h"
+
+namespace {
+
+using namespace sv;
+
+constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 per CU)
+constexpr int kKMax = 2048;       // longest kept set stored as a list
+constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
+constexpr int kNwTopP = 128;      // entries each wave keeps for top-p candidates
+constexpr int kNoutTopP = 1024;   // candidates a chunk hands over for top-p
+constexpr int kTieSlack = 256;    // room for ties at a chunk's cut
+constexpr int64_t kCh4 = 16384;   // chunk of the full-row sampler (multiple of kTile)
+constexpr int kTruncBS = 512;
+
+enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS };
+
+struct Plan {
+  int64_t rows = 0;
+  int rows_per_req = 0;
+  int mode = M_SOFTMAX;
+  bool trunc = false, need_s = false, fast = true;
+  int nchunks = 1;
+  int64_t chunk = 8;
+  int nw = 0, nout = 0, cap_out = 0, um = 0;
+  int nch4 = 1;
+  int scale_bits = 40;
+  size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_cnt = 0, off_part = 0;
+  size_t total = 0;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_params prm) {
+  Plan p;
+  const bool topk = prm.top_k > 0 && (int64_t)prm.top_k < V;
+  const bool topp = prm.top_p < 1.0f;
+  p.rows_per_req = (kind == CALL_STATS) ? gamma : gamma + 1;
+  p.rows = (int64_t)B * p.rows_per_req;
+  p.trunc = (kind != CALL_GREEDY) && (topk || topp);
+  p.mode = (kind == CALL_GREEDY) ? M_ARGMAX : (p.trunc ? M_TRUNC : M_SOFTMAX);
+  p.need_s = p.trunc && topp && !topk;
+  p.fast = !topk || prm.top_k <= kFastTopK;
+  if (p.trunc) {
+    if (topk) {
+      p.nw = std::min<int>(prm.top_k, kFastTopK);
+      p.nout = p.nw;
+    } else {
+      p.nw = kNwTopP;
+      p.nout = kNoutTopP;
+    }
+    p.cap_out = p.nout + kTieSlack;
+  }
+  const int64_t minchunk = p.trunc ? 16384 : 4096;
+  const int64_t maxchunks = p.trunc ? 4 : (1 << 20);
+  const int64_t want = p.rows > 0 ? (kTargetWG + p.rows - 1) / p.rows : 1;
+  const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
+  int64_t nch = std::max<int64_t>(1, std::min(std::min(want, lim), maxchunks));
+  int64_t chunk = (V + nch - 1) / nch;
+  chunk = (chunk + 7) / 8 * 8;
+  nch = (V + chunk - 1) / chunk;
+  p.nchunks = (int)nch;
+  p.chunk = chunk;
+  if (p.trunc) {
+    int64_t u = nch * p.cap_out;
+    int um = 1;
+    while (um < u) um <<= 1;
+    p.um = um;
+  }
+  p.nch4 = (int)((V + kCh4 - 1) / kCh4);
+  int lg = 0;
+  while (((int64_t)1 << lg) < V) ++lg;
+  p.scale_bits = std::min(40, 62 - lg);
+
+  const size_t rows = (size_t)p.rows;
+  size_t off = 0;
+  p.off_cout = off;
+  off = align_up(off + rows * nch * sizeof(ChunkOut), 256);
+  p.off_cand = off;
+  if (p.trunc) off = align_up(off + rows * nch * (size_t)p.cap_out * sizeof(Cand), 256);
+  p.off_info = off;
+  if (kind != CALL_GREEDY) off = align_up(off + rows * sizeof(RowInfo), 256);
+  p.off_kept = off;
+  if (p.trunc) off = align_up(off + rows * (size_t)kKMax * sizeof(Cand), 256);
+  p.off_jobs = off;
+  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * sizeof(BigJob), 256);
+  p.off_cnt = off;
+  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+  p.off_part = off;
+  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * p.nch4 * sizeof(double), 256);
+  if (kind == CALL_STATS) off = align_up(off + rows * nch * 4 * sizeof(double), 256);
+  p.total = std::max<size_t>(off, 256);
+  return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+sv_status check_sizes(int32_t B, int32_t gamma, int32_t V, sv_dtype dt) {
+  if (B < 0 || gamma < 0 || V < 1) return SV_ERR_INVALID_ARG;
+  if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (gamma > 4096) return SV_ERR_UNSUPPORTED;
+  // element offsets are 64-bit; rows are addressed with 32-bit indices
+  if ((int64_t)B * (gamma + 1) > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
+  return SV_OK;
+}
+
+sv_status check_params(sv_sampling_params prm, float* c_out) {
+  const float T = prm.temperature;
+  if (!(T > 0.0f) || !std::isfinite(T)) return SV_ERR_INVALID_ARG;
+  if (prm.top_k < 0) return SV_ERR_INVALID_ARG;
+  if (!(prm.top_p > 0.0f && prm.top_p <= 1.0f)) return SV_ERR_INVALID_ARG;
+  const double c = 1.4426950408889634 / (double)T;
+  if (!std::isfinite(c) || c > 1e30) return SV_ERR_INVALID_ARG;
+  *c_out = (float)c;
+  return SV_OK;
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+sv_status launched() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
+
+template <int MODE, bool BF16, bool NEED_S, int BS>
+void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
+  size_t dyn = (MODE == M_TRUNC) ? (size_t)(BS / kWave) * (kCapW * sizeof(Cand) + 256 * sizeof(uint32_t)) : 0;
+  dim3 grid((unsigned)(p.nchunks * p.rows));
+  hipLaunchKernelGGL((rowpass_kernel<MODE, BF16, NEED_S, BS>), grid, dim3(BS), dyn, st, a);
+}
+
+template <bool BF16>
+sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st) {
+  RowPassArgs a;
+  a.logits = logits;
+  a.V = V;
+  a.chunk = p.chunk;
+  a.rows_per_req = p.rows_per_req;
+  a.G1 = G1;
+  a.nchunks = p.nchunks;
+  a.c = c;
+  a.nw = p.nw;
+  a.nout = p.nout;
+  a.cap_out = p.cap_out;
+  a.out = ws_at<ChunkOut>(ws, p.off_cout);
+  a.cand = p.trunc ? ws_at<Cand>(ws, p.off_cand) : nullptr;
+  if (p.mode == M_SOFTMAX) launch_rowpass<M_SOFTMAX, BF16, false, 256>(p, a, st);
+  else if (p.mode == M_ARGMAX) launch_rowpass<M_ARGMAX, BF16, false, 256>(p, a, st);
+  else if (p.need_s) launch_rowpass<M_TRUNC, BF16, true, kTruncBS>(p, a, st);
+  else launch_rowpass<M_TRUNC, BF16, false, kTruncBS>(p, a, st);
+  return launched();
+}
+
+std::once_flag g_attr_once;
+
+void set_kernel_attrs() {
+  std::call_once(g_attr_once, [] {
+    const int kMaxDyn = 160 * 1024;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rowfinal_kernel<true>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDyn);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rowfinal_kernel<false>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDyn);
+    (void)hipGetLastError();
+  });
+}
+
+template <bool BF16>
+sv_status run_rowfinal(const Plan& p, const void* logits, const float* q, const int32_t* ids, int64_t V, int G1,
+                       int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st) {
+  RowFinalArgs a;
+  a.logits = logits;
+  a.q = q;
+  a.ids = ids;
+  a.V = V;
+  a.rows_per_req = p.rows_per_req;
+  a.G1 = G1;
+  a.gamma = gamma;
+  a.nchunks = p.nchunks;
+  a.cap_out = p.cap_out;
+  a.trunc = p.trunc ? 1 : 0;
+  a.fast = p.fast ? 1 : 0;
+  a.top_k = prm.top_k;
+  a.top_p = prm.top_p;
+  a.c = c;
+  a.um = p.um;
+  a.kmax = kKMax;
+  a.scale_bits = p.scale_bits;
+  a.cout = ws_at<ChunkOut>(ws, p.off_cout);
+  a.cand = p.trunc ? ws_at<Cand>(ws, p.off_cand) : nullptr;
+  a.info = ws_at<RowInfo>(ws, p.off_info);
+  a.kept = p.trunc ? ws_at<Cand>(ws, p.off_kept) : nullptr;
+  set_kernel_attrs();
+  size_t dyn = p.trunc ? (size_t)p.um * (sizeof(uint64_t) + sizeof(double)) : 0;
+  hipLaunchKernelGGL((rowfinal_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), dyn, st, a);
+  sv_status s = launched();
+  if (s != SV_OK) return s;
+  if (p.trunc) {
+    hipLaunchKernelGGL((rowslow_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), 0, st, a);
+    s = launched();
+  }
+  return s;
+}
+
+sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamma, int32_t V) {
+  sv_status s = check_sizes(B, gamma, V, dt);
+  if (s != SV_OK) return s;
+  if (B > 0 && (logits == nullptr || !aligned16(logits))) return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
+  float c;
+  if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
+  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, prm).total;
+  size_t g = make_plan(CALL_GREEDY, B, gamma, V, prm).total;
+  size_t s = make_plan(CALL_STATS, B, gamma, V, prm).total;
+  return std::max(a, std::max(g, s));
+}
+
+sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                             const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                             int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, int32_t* out_tokens,
+                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int G1 = gamma + 1;
+  const bool bf = dt == SV_BF16;
+
+  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
+         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  if (s != SV_OK) return s;
+  s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
+         : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
+  if (s != SV_OK) return s;
+
+  AcceptArgs ac;
+  ac.info = ws_at<RowInfo>(workspace, p.off_info);
+  ac.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
+  ac.kmax = kKMax;
+  ac.q = draft_probs;
+  ac.ids = draft_ids;
+  ac.ua = u_accept;
+  ac.ur = u_resample;
+  ac.B = B;
+  ac.gamma = gamma;
+  ac.V = V;
+  ac.out_tokens = out_tokens;
+  ac.out_nacc = out_num_accepted;
+  ac.out_flags = out_row_flags;
+  ac.jobs = ws_at<BigJob>(workspace, p.off_jobs);
+  ac.counters = ws_at<uint32_t>(workspace, p.off_cnt);
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, ac);
+  s = launched();
+  if (s != SV_OK) return s;
+
+  BigArgs bg;
+  bg.logits = target_logits;
+  bg.q = draft_probs;
+  bg.V = V;
+  bg.G1 = G1;
+  bg.nch4 = p.nch4;
+  bg.ch4 = kCh4;
+  bg.c = c;
+  bg.jobs = ac.jobs;
+  bg.counters = ac.counters;
+  bg.partials = ws_at<double>(workspace, p.off_part);
+  bg.out_tokens = out_tokens;
+  bg.out_flags = out_row_flags;
+  dim3 grid((unsigned)((int64_t)p.nch4 * B));
+  if (bf) hipLaunchKernelGGL((big_kernel<true>), grid, dim3(256), 0, st, bg);
+  else hipLaunchKernelGGL((big_kernel<false>), grid, dim3(256), 0, st, bg);
+  return launched();
+}
+
+sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32_t* draft_ids, int32_t B,
+                             int32_t gamma, int32_t V, int32_t* out_tokens, int32_t* out_num_accepted,
+                             uint32_t* out_row_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && draft_ids == nullptr) return SV_ERR_INVALID_ARG;
+  sv_sampling_params prm = {1.0f, 0, 1.0f};
+  const Plan p = make_plan(CALL_GREEDY, B, gamma, V, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = dt == SV_BF16;
+  s = bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, 1.0f, workspace, st)
+         : run_rowpass<false>(p, target_logits, V, gamma + 1, 1.0f, workspace, st);
+  if (s != SV_OK) return s;
+  GreedyArgs g;
+  g.cout = ws_at<ChunkOut>(workspace, p.off_cout);
+  g.nchunks = p.nchunks;
+  g.ids = draft_ids;
+  g.B = B;
+  g.gamma = gamma;
+  g.V = V;
+  g.out_tokens = out_tokens;
+  g.out_nacc = out_num_accepted;
+  g.out_flags = out_row_flags;
+  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, g);
+  return launched();
+}
+
+sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                            const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V,
+                            sv_sampling_params prm, float* out_alpha, float* out_z_pq, float* out_z_qp,
+                            float* out_accept_prob, void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0 || gamma == 0) return SV_OK;
+  if (draft_probs == nullptr || draft_ids == nullptr || !aligned16(draft_probs) || out_alpha == nullptr ||
+      out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr)
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_STATS, B, gamma, V, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = dt == SV_BF16;
+  const int G1 = gamma + 1;
+  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
+         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  if (s != SV_OK) return s;
+  s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
+         : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
+  if (s != SV_OK) return s;
+  StatsArgs a;
+  a.logits = target_logits;
+  a.q = draft_probs;
+  a.ids = draft_ids;
+  a.V = V;
+  a.gamma = gamma;
+  a.nchunks = p.nchunks;
+  a.chunk = p.chunk;
+  a.c = c;
+  a.info = ws_at<RowInfo>(workspace, p.off_info);
+  a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
+  a.kmax = kKMax;
+  a.partials = ws_at<double>(workspace, p.off_part);
+  a.out_alpha = out_alpha;
+  a.out_zpq = out_z_pq;
+  a.out_zqp = out_z_qp;
+  a.out_acc = out_accept_prob;
+  a.rows = p.rows;
+  dim3 grid((unsigned)(p.rows * p.nchunks));
+  if (bf) hipLaunchKernelGGL((stats_chunk_kernel<true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
+  s = launched();
+  if (s != SV_OK) return s;
+  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
+  return launched();
+}
+
+const char* spec_status_string(sv_status status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported size";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

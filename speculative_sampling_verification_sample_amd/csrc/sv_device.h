@@ -1,0 +1,218 @@
+// Device-side building blocks of the verify-step kernels (gfx950, wave64).
+//
+// Arithmetic shared by every kernel (so that a value computed in two kernels
+// is bit-identical):
+//   c      = log2(e) / T                     (float, computed once on the host)
+//   R      = ceilf(xmax * c)                 (integral float, per row)
+//   e(x)   = exp2(fma(x, c, -R))             (float; p(x) = e(x) / S)
+//   S      = sum of e over the kept set      (double)
+// p(x) = exp((x - xmax) / T) / sum(...) is the temperature softmax of
+// [WR] §7.2; any reference R >= max(x * c) gives the same p, and an integral R
+// lets partial sums taken against different references be merged exactly
+// with ldexp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
+constexpr float kLowest = -3.40282346638528859812e+38f;  // -FLT_MAX
+
+// ---- chunk / row flags (internal) ----------------------------------------
+constexpr uint32_t CF_NAN = 1u;       // a NaN logit was seen
+constexpr uint32_t CF_POSINF = 2u;    // a +Inf logit was seen
+constexpr uint32_t CF_OVERFLOW = 4u;  // candidate buffer could not hold the ties
+
+constexpr uint32_t RF_NONFINITE = 1u;  // row unusable (NaN / +Inf / all -Inf)
+constexpr uint32_t RF_SLOW = 2u;       // truncation needs the exact multi-pass kernel
+constexpr uint32_t RF_BIG = 4u;        // kept set not stored as a list: full-row passes
+
+// Per (row, chunk) result of the streaming pass.
+struct alignas(16) ChunkOut {
+  float xmax;      // max over the chunk (NaN ignored); -inf if none
+  int32_t argmax;  // first index (within the row) holding xmax
+  float thr;       // every finite chunk element >= thr is in the candidate list
+  int32_t ncand;   // candidates written for this chunk
+  double s;        // sum over the chunk of exp2(x * c - Rs)
+  float Rs;        // integral reference of s; -inf when nothing finite was seen
+  uint32_t flags;  // CF_*
+};
+
+struct alignas(8) Cand {
+  float v;
+  int32_t idx;
+};
+
+// Per row result of the finalisation (kept set and draft gather).
+struct alignas(16) RowInfo {
+  double S;        // normaliser of p over the kept set, reference R
+  float R;         // integral reference
+  float tau;       // kept set = {x : z(x) >= tau}; kLowest keeps every finite x
+  int32_t nkept;   // length of the stored kept list, -1 for RF_BIG rows
+  uint32_t flags;  // RF_*
+  float ed;        // e(d) of this row's draft (0 if not kept / bad id / no draft)
+  float qd;        // q(d) of this row's draft
+  int32_t d;       // draft id; -1 for the bonus row; -2 for an id outside [0, V)
+  int32_t pad;
+};
+
+// A request whose token must be drawn by the full-row sampler.
+struct alignas(16) BigJob {
+  double S;
+  float R;
+  float tau;
+  float u;
+  int32_t row;       // tensor row (b * (gamma + 1) + j)
+  int32_t qrow;      // q row (b * gamma + j) when residual, else -1
+  int32_t slot;      // output slot (= n_accepted)
+  int32_t active;
+  int32_t pad;
+};
+
+// ---- scalar helpers ---------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// e(x) relative to the integral reference R.
+__device__ __forceinline__ float e_of(float x, float c, float R) { return ex2(__builtin_fmaf(x, c, -R)); }
+
+// Order-preserving key of a float (-0 folded onto +0, so keys of equal
+// values are equal).
+__device__ __forceinline__ uint32_t f2key(float f) {
+  uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Orders LDS traffic of one wave without a workgroup barrier.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- wave reductions / scans (fixed butterfly order: deterministic) -------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum across lanes (lane 0 first).
+__device__ __forceinline__ double wave_incl_scan_d(double v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+// (value, index) argmax: larger value wins, equal values keep the lower index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, kWave);
+    int i2 = __shfl_xor(i, o, kWave);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+// Exact merge of (s, R) pairs: s * 2^R summed onto the larger reference.
+__device__ __forceinline__ void sr_merge(double& s, float& R, double s2, float R2) {
+  if (R2 == kNegInf) return;
+  if (R == kNegInf) {
+    s = s2;
+    R = R2;
+    return;
+  }
+  if (R2 > R) {
+    s = ldexp(s, (int)(R - R2)) + s2;
+    R = R2;
+  } else {
+    s = s + ldexp(s2, (int)(R2 - R));
+  }
+}
+
+// Find the radix digit holding the element of rank `need` (1-based, counted
+// from the largest) in a 256-bin histogram; executed by one whole wave.
+// Returns the digit; `need` becomes the rank inside that digit's bin.
+__device__ __forceinline__ int wave_find_digit(const uint32_t* hist, int& need) {
+  const int l = lane_id();
+  // lane l holds bins 255-4l .. 252-4l (descending)
+  uint32_t c0 = hist[255 - 4 * l], c1 = hist[254 - 4 * l], c2 = hist[253 - 4 * l], c3 = hist[252 - 4 * l];
+  int lsum = (int)(c0 + c1 + c2 + c3);
+  int incl = wave_incl_scan_i(lsum);
+  int excl = incl - lsum;
+  uint64_t hit = ballot(incl >= need);
+  int src = hit ? (int)__builtin_ctzll(hit) : 63;
+  int digit = 0, newneed = need;
+  if (l == src) {
+    int run = excl;
+    int cs[4] = {(int)c0, (int)c1, (int)c2, (int)c3};
+    int k = 0;
+    for (; k < 3; ++k) {
+      if (run + cs[k] >= need) break;
+      run += cs[k];
+    }
+    digit = 255 - 4 * l - k;
+    newneed = need - run;
+  }
+  digit = __shfl(digit, src, kWave);
+  need = __shfl(newneed, src, kWave);
+  return digit;
+}
+
+}  // namespace sv

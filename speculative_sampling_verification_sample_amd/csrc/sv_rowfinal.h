@@ -1,0 +1,507 @@
+// K2 -- per-row finalisation of the processed target distribution p, and
+// the exact multi-pass fallback for rows the fast path cannot certify.
+//
+// K2 merges the chunk results of a row: the row max gives the integral
+// reference R, the chunk sums give the full-row mass S (temperature softmax,
+// [WR] §7.2).  With truncation ([WR] §7.3) it gathers the candidate union
+// (every element >= the highest chunk threshold is in it), sorts it by
+// logit, and applies
+//   top-k : keep every token whose logit >= the k-th largest logit;
+//   top-p : keep the most probable tokens until their mass reaches
+//           top_p * S (on the top-k set when both are active), plus ties.
+// The kept set is stored as a list sorted by token id (for the inverse CDF)
+// together with S over it.  Finally it reads this row's draft logit and
+// q(d) so the acceptance test needs no further pass ([WR] §6).
+#pragma once
+
+#include "sv_device.h"
+
+namespace sv {
+
+struct RowFinalArgs {
+  const void* logits;
+  const float* q;       // [B, gamma, V]
+  const int32_t* ids;   // [B, gamma]
+  int64_t V;
+  int32_t rows_per_req;
+  int32_t G1;
+  int32_t gamma;
+  int32_t nchunks;
+  int32_t cap_out;
+  int32_t trunc;        // 0: untruncated rows, 1: top-k and/or top-p
+  int32_t fast;         // 0: every truncated row takes the exact multi-pass path
+  int32_t top_k;        // active when 0 < top_k < V
+  float top_p;          // active when < 1
+  float c;
+  int32_t um;           // LDS capacity (power of two) for the candidate union
+  int32_t kmax;         // capacity of a stored kept list
+  int32_t scale_bits;   // fixed-point bits of the exact path's mass histogram
+  const ChunkOut* cout;
+  const Cand* cand;
+  RowInfo* info;        // [rows]
+  Cand* kept;           // [rows][kmax]  (v = e(x), idx = token id), id order
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_logit(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    uint32_t h = reinterpret_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(h << 16);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// Draft gather for a row whose kept set and normaliser are final.
+template <bool BF16>
+__device__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
+  ri.ed = 0.0f;
+  ri.qd = 0.0f;
+  ri.d = -1;
+  if (j >= a.gamma) return;  // bonus row: no draft
+  int d = a.ids[(int64_t)b * a.gamma + j];
+  if (d < 0 || (int64_t)d >= a.V) {
+    ri.d = -2;
+    return;
+  }
+  ri.d = d;
+  float z = load_logit<BF16>(a.logits, rowoff + d);
+  ri.ed = (z >= ri.tau) ? e_of(z, a.c, ri.R) : 0.0f;
+  ri.qd = a.q[((int64_t)b * a.gamma + j) * a.V + d];
+}
+
+// Block-wide inclusive scan of n doubles in place (256 threads, fixed order).
+__device__ void block_incl_scan_d(double* v, int n, double* s_tmp /*[4]*/) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int per = (n + 255) / 256;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  double run = 0.0;
+  for (int i = lo; i < hi; ++i) run += v[i];
+  double incl = wave_incl_scan_d(run);
+  if (lane == 63) s_tmp[wid] = incl;
+  __syncthreads();
+  double off = 0.0;
+  for (int w = 0; w < wid; ++w) off += s_tmp[w];
+  double pre = off + (incl - run);
+  for (int i = lo; i < hi; ++i) {
+    pre += v[i];
+    v[i] = pre;
+  }
+  __syncthreads();
+}
+
+// Bitonic sort (ascending) of n = power-of-two 64-bit keys in LDS.
+__device__ void block_bitonic_u64(uint64_t* k, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        int ixj = i ^ stride;
+        if (ixj > i) {
+          uint64_t x = k[i], y = k[ixj];
+          bool up = (i & size) == 0;
+          if (up ? (x > y) : (x < y)) {
+            k[i] = y;
+            k[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t desc_key(float v, int idx) {
+  // ascending order of ~key == descending value, then ascending index
+  return ~(((uint64_t)f2key(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx));
+}
+__device__ __forceinline__ float desc_val(uint64_t k) { return key2f((uint32_t)(~k >> 32)); }
+__device__ __forceinline__ int desc_idx(uint64_t k) { return (int)(0xffffffffu - (uint32_t)(~k)); }
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
+  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
+
+  __shared__ float s_xm, s_th, s_R;
+  __shared__ double s_S, s_tmp[4];
+  __shared__ uint32_t s_fl;
+  __shared__ int s_n, s_i;
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(s_dyn);
+  double* cum = reinterpret_cast<double*>(s_dyn + (size_t)a.um * sizeof(uint64_t));
+
+  if (tid == 0) {
+    const ChunkOut* co = a.cout + r * a.nchunks;
+    float xm = kNegInf, th = kLowest;
+    uint32_t fl = 0;
+    double s = 0.0;
+    float Rs = kNegInf;
+    for (int c = 0; c < a.nchunks; ++c) {
+      ChunkOut o = co[c];
+      xm = fmaxf(xm, o.xmax);
+      th = fmaxf(th, o.thr);
+      fl |= o.flags;
+      sr_merge(s, Rs, o.s, o.Rs);
+    }
+    s_xm = xm;
+    s_th = th;
+    s_fl = fl;
+    float R = ceilf(xm * a.c);
+    s_R = R;
+    s_S = (Rs == kNegInf) ? 0.0 : ldexp(s, (int)(Rs - R));
+    s_n = 0;
+  }
+  __syncthreads();
+  RowInfo ri;
+  ri.S = s_S;
+  ri.R = s_R;
+  ri.tau = kLowest;
+  ri.nkept = -1;
+  ri.flags = 0;
+  ri.ed = 0.0f;
+  ri.qd = 0.0f;
+  ri.d = -1;
+  ri.pad = 0;
+  const uint32_t fl = s_fl;
+  if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf)) {
+    if (tid == 0) {
+      ri.flags = RF_NONFINITE;
+      a.info[r] = ri;
+    }
+    return;
+  }
+  if (!a.trunc) {
+    if (tid == 0) {
+      ri.flags = RF_BIG;
+      gather_draft<BF16>(a, b, j, rowoff, ri);
+      a.info[r] = ri;
+    }
+    return;
+  }
+  if ((fl & CF_OVERFLOW) || !a.fast) {
+    if (tid == 0) {
+      ri.flags = RF_SLOW;
+      a.info[r] = ri;
+    }
+    return;
+  }
+
+  // ---- candidate union (entries >= the highest chunk threshold) ----
+  const float theta = s_th;
+  const Cand* cd = a.cand + r * a.nchunks * (int64_t)a.cap_out;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const int nc = a.cout[r * a.nchunks + c].ncand;
+    for (int i = tid; i < nc; i += 256) {
+      Cand e = cd[(int64_t)c * a.cap_out + i];
+      if (e.v >= theta) {
+        int pos = atomicAdd(&s_n, 1);
+        if (pos < a.um) keys[pos] = desc_key(e.v, e.idx);
+      }
+    }
+  }
+  __syncthreads();
+  const int nu = s_n;
+  if (nu > a.um) {
+    if (tid == 0) {
+      ri.flags = RF_SLOW;
+      a.info[r] = ri;
+    }
+    return;
+  }
+  int np2 = 1;
+  while (np2 < nu) np2 <<= 1;
+  for (int i = nu + tid; i < np2; i += 256) keys[i] = ~0ull;
+  __syncthreads();
+  block_bitonic_u64(keys, np2);
+
+  // ---- thresholds ----
+  const float R = s_R;
+  const bool topk = a.top_k > 0 && (int64_t)a.top_k < a.V;
+  const bool topp = a.top_p < 1.0f;
+  for (int i = tid; i < nu; i += 256) cum[i] = (double)e_of(desc_val(keys[i]), a.c, R);
+  __syncthreads();
+  block_incl_scan_d(cum, nu, s_tmp);
+  int nK = nu;
+  float tau = kLowest;
+  if (topk) {
+    if (nu >= a.top_k) {
+      tau = desc_val(keys[a.top_k - 1]);
+      if (tid == 0) s_i = nu;
+      __syncthreads();
+      for (int i = tid; i < nu; i += 256)
+        if (desc_val(keys[i]) < tau) atomicMin(&s_i, i);
+      __syncthreads();
+      nK = s_i;
+    }
+  }
+  int nkept = nK;
+  double Sfin = nK > 0 ? cum[nK - 1] : 0.0;
+  bool slow = false;
+  if (topp) {
+    const double Sref = topk ? Sfin : s_S;
+    const double target = (double)a.top_p * Sref;
+    if (tid == 0) s_i = 0x7fffffff;
+    __syncthreads();
+    for (int i = tid; i < nK; i += 256)
+      if (cum[i] >= target) atomicMin(&s_i, i);
+    __syncthreads();
+    int istar = s_i;
+    if (istar == 0x7fffffff) {
+      if (topk || theta == kLowest) istar = nK - 1;  // rounding: keep everything
+      else slow = true;                                // crossing below the certified region
+    }
+    if (!slow) {
+      tau = desc_val(keys[istar]);
+      if (tid == 0) s_i = nK;
+      __syncthreads();
+      for (int i = tid; i < nK; i += 256)
+        if (desc_val(keys[i]) < tau) atomicMin(&s_i, i);
+      __syncthreads();
+      nkept = s_i;
+      Sfin = cum[nkept - 1];
+    }
+  }
+  if (slow) {
+    if (tid == 0) {
+      ri.flags = RF_SLOW;
+      a.info[r] = ri;
+    }
+    return;
+  }
+  ri.tau = tau;
+  ri.S = Sfin;
+  if (nkept > a.kmax) {
+    if (tid == 0) {
+      ri.flags = RF_BIG;
+      ri.nkept = -1;
+      gather_draft<BF16>(a, b, j, rowoff, ri);
+      a.info[r] = ri;
+    }
+    return;
+  }
+  // kept list sorted by token id: reuse the key array (index-major keys)
+  __syncthreads();
+  int kp2 = 1;
+  while (kp2 < nkept) kp2 <<= 1;
+  for (int i = tid; i < kp2; i += 256) {
+    uint64_t k = ~0ull;
+    if (i < nkept) {
+      uint64_t dk = keys[i];
+      k = ((uint64_t)(uint32_t)desc_idx(dk) << 32) | (uint64_t)__float_as_uint(desc_val(dk));
+    }
+    __syncthreads();
+    keys[i] = k;
+  }
+  __syncthreads();
+  block_bitonic_u64(keys, kp2);
+  Cand* out = a.kept + r * (int64_t)a.kmax;
+  for (int i = tid; i < nkept; i += 256) {
+    Cand e;
+    e.idx = (int32_t)(keys[i] >> 32);
+    e.v = e_of(__uint_as_float((uint32_t)keys[i]), a.c, R);
+    out[i] = e;
+  }
+  if (tid == 0) {
+    ri.nkept = nkept;
+    gather_draft<BF16>(a, b, j, rowoff, ri);
+    a.info[r] = ri;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact multi-pass path (rows flagged RF_SLOW): radix selection over the row
+// in global memory.  top-k selects by count over order-preserving keys;
+// top-p selects by mass with a fixed-point histogram (integer atomics, so the
+// result does not depend on the order of the additions).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ double block_sum_d(double v, double* s_tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum_d(v);
+  __syncthreads();
+  if (lane == 0) s_tmp[wid] = v;
+  __syncthreads();
+  double t = ((s_tmp[0] + s_tmp[1]) + (s_tmp[2] + s_tmp[3]));
+  __syncthreads();
+  return t;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) rowslow_kernel(RowFinalArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t r = blockIdx.x;
+  if (!(a.info[r].flags & RF_SLOW)) return;
+  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
+  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
+  const int64_t V = a.V;
+  const float c = a.c;
+  RowInfo ri = a.info[r];
+  const float R = ri.R;
+
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long mhist[256];
+  __shared__ double s_tmp[4];
+  __shared__ int s_digit, s_need, s_cnt[4];
+  __shared__ unsigned long long s_above;
+  constexpr int kLow = BF16 ? 16 : 0;
+
+  // ---- top-k threshold (count) ----
+  float tau = kLowest;
+  const bool topk = a.top_k > 0 && (int64_t)a.top_k < V;
+  if (topk) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = a.top_k;
+    int64_t nfinite = 0;
+    for (int shift = 24; shift >= kLow; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int64_t x = tid; x < V; x += 256) {
+        float z = load_logit<BF16>(a.logits, rowoff + x);
+        if (!(z > kNegInf)) continue;
+        uint32_t key = f2key(z);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (shift == 24) {
+        int64_t tot = 0;
+        for (int k = 0; k < 256; ++k) tot += hist[k];
+        nfinite = tot;
+        if (nfinite < need) break;
+      }
+      if (wid == 0) {
+        int d = wave_find_digit(hist, need);
+        if (lane == 0) {
+          s_digit = d;
+          s_need = need;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      pmask |= 255u << shift;
+      need = s_need;
+      __syncthreads();
+    }
+    if (nfinite >= a.top_k) tau = key2f(prefix);
+  }
+  // ---- mass of the top-k set ----
+  double part = 0.0;
+  for (int64_t x = tid; x < V; x += 256) {
+    float z = load_logit<BF16>(a.logits, rowoff + x);
+    if (z >= tau) part += (double)e_of(z, c, R);
+  }
+  double S = block_sum_d<BF16>(part, s_tmp);
+  // ---- top-p threshold (mass) ----
+  if (a.top_p < 1.0f) {
+    const double sc = ldexp(1.0, a.scale_bits);
+    const double target = (double)a.top_p * S * sc;
+    uint32_t prefix = 0, pmask = 0;
+    if (tid == 0) s_above = 0ull;
+    bool found_all = true;
+    for (int shift = 24; shift >= kLow; shift -= 8) {
+      mhist[tid] = 0ull;
+      __syncthreads();
+      for (int64_t x = tid; x < V; x += 256) {
+        float z = load_logit<BF16>(a.logits, rowoff + x);
+        if (!(z >= tau)) continue;
+        uint32_t key = f2key(z);
+        if ((key & pmask) == prefix) {
+          unsigned long long m = (unsigned long long)rint((double)e_of(z, c, R) * sc);
+          atomicAdd(&mhist[(key >> shift) & 255u], m);
+        }
+      }
+      __syncthreads();
+      if (wid == 0) {
+        // lane l holds bins 255-4l .. 252-4l
+        unsigned long long c0 = mhist[255 - 4 * lane], c1 = mhist[254 - 4 * lane], c2 = mhist[253 - 4 * lane],
+                           c3 = mhist[252 - 4 * lane];
+        unsigned long long ls = c0 + c1 + c2 + c3;
+        unsigned long long incl = ls;
+        for (int o = 1; o < 64; o <<= 1) {
+          unsigned long long t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        unsigned long long above = s_above;
+        uint64_t hit = ballot((double)(above + incl) >= target);
+        int src = hit ? (int)__builtin_ctzll(hit) : -1;
+        if (src < 0) {
+          if (lane == 0) s_digit = -1;
+        } else if (lane == src) {
+          unsigned long long run = above + (incl - ls);
+          unsigned long long cs[4] = {c0, c1, c2, c3};
+          int k = 0;
+          for (; k < 3; ++k) {
+            if ((double)(run + cs[k]) >= target) break;
+            run += cs[k];
+          }
+          s_digit = 255 - 4 * lane - k;
+          s_above = run;
+        }
+      }
+      __syncthreads();
+      int d = s_digit;
+      __syncthreads();
+      if (d < 0) {
+        found_all = false;
+        break;
+      }
+      prefix |= (uint32_t)d << shift;
+      pmask |= 255u << shift;
+    }
+    if (found_all) tau = fmaxf(tau, key2f(prefix));
+    // mass of the final kept set
+    part = 0.0;
+    for (int64_t x = tid; x < V; x += 256) {
+      float z = load_logit<BF16>(a.logits, rowoff + x);
+      if (z >= tau) part += (double)e_of(z, c, R);
+    }
+    S = block_sum_d<BF16>(part, s_tmp);
+  }
+  // ---- kept count and (if small) the id-ordered list ----
+  int cntp = 0;
+  for (int64_t x = tid; x < V; x += 256) {
+    float z = load_logit<BF16>(a.logits, rowoff + x);
+    cntp += (z >= tau) ? 1 : 0;
+  }
+  cntp = wave_sum_i(cntp);
+  if (lane == 0) s_cnt[wid] = cntp;
+  __syncthreads();
+  const int nkept = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  __syncthreads();
+  ri.tau = tau;
+  ri.S = S;
+  ri.flags = 0;
+  if (nkept > a.kmax) {
+    ri.flags = RF_BIG;
+    ri.nkept = -1;
+  } else {
+    Cand* out = a.kept + r * (int64_t)a.kmax;
+    int basepos = 0;
+    for (int64_t x0 = 0; x0 < V; x0 += 256) {
+      int64_t x = x0 + tid;
+      float z = x < V ? load_logit<BF16>(a.logits, rowoff + x) : kNegInf;
+      bool k = x < V && z >= tau;
+      uint64_t m = ballot(k);
+      if (lane == 0) s_cnt[wid] = (int)__popcll(m);
+      __syncthreads();
+      int off = basepos;
+      for (int w = 0; w < wid; ++w) off += s_cnt[w];
+      if (k) {
+        Cand e;
+        e.idx = (int32_t)x;
+        e.v = e_of(z, c, R);
+        out[off + lanes_below(m)] = e;
+      }
+      basepos += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      __syncthreads();
+    }
+    ri.nkept = nkept;
+  }
+  if (tid == 0) {
+    gather_draft<BF16>(a, b, j, rowoff, ri);
+    a.info[r] = ri;
+  }
+}
+
+}  // namespace sv

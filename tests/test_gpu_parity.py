@@ -1,0 +1,268 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Sampling: token ids, accepted lengths and flags must match exactly for every
+request outside the boundary band (a uniform within 1e-6 of an acceptance or
+CDF boundary, or a top-p cut within 1e-6 of top_p, as the oracle reports);
+boundary rows are counted and printed.  Greedy: bit-exact for every request.
+Statistics: within 1e-5 relative (plus 2e-7 absolute, the float32 resolution
+of the per-token probabilities).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import compare_greedy, compare_sample, compare_stats, gpu_sample, widen
+from workloads import generate
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+# ---- the five workloads at sizes the oracle finishes in seconds -------------
+
+def test_c2_small_untruncated_fp32():
+    w = generate("c2", DEV, B=8)
+    compare_sample(w, label="c2 B=8")
+
+
+def test_c2_ragged_vocab():
+    w = generate("c2", DEV, B=6, gamma=3, V=10007)
+    compare_sample(w, label="c2 V=10007")
+
+
+def test_c3_small_topk():
+    w = generate("c3", DEV, B=6)
+    compare_sample(w, label="c3 B=6")
+
+
+def test_c3_ragged_topk():
+    w = generate("c3", DEV, B=5, gamma=2, V=40003)
+    compare_sample(w, label="c3 V=40003")
+
+
+def test_c5_small_topp():
+    w = generate("c5", DEV, B=4)
+    compare_sample(w, label="c5 B=4")
+
+
+def test_c5_ragged_topp():
+    w = generate("c5", DEV, B=3, gamma=3, V=70001)
+    compare_sample(w, label="c5 V=70001")
+
+
+def test_c4_small_greedy():
+    w = generate("c4", DEV, B=8)
+    compare_greedy(w, label="c4 B=8")
+
+
+def test_c4_ragged_greedy():
+    w = generate("c4", DEV, B=7, gamma=5, V=9999)
+    compare_greedy(w, label="c4 V=9999")
+
+
+def test_toy_parity():
+    w = generate("toy", DEV, B=20000)
+    compare_sample(w, label="toy 2e4")
+
+
+def test_toy_chi_square_on_gpu_outputs():
+    """1e6 rounds on the GPU: every emitted slot follows its p_j, and tokens
+    per round match E[N] = 1 + sum_i prod_{k<=i} alpha_k ([WR] §10)."""
+    from scipy import stats
+
+    w = generate("toy", DEV, B=1_000_000)
+    tok, nacc, fl = gpu_sample(w)
+    assert (fl == 0).all()
+    z = w.logits[0].double().cpu().numpy()
+    q = w.q[0].double().cpu().numpy()
+    G = w.cfg.gamma
+    p_rows = [oracle.process_row(z[j], 1.0).p for j in range(G + 1)]
+    pv = []
+    for j in range(G + 1):
+        reached = nacc >= j
+        counts = np.bincount(tok[reached, j], minlength=5)
+        pv.append(stats.chisquare(counts, p_rows[j] * reached.sum()).pvalue)
+    print("chi-square p-values per slot:", [f"{x:.3g}" for x in pv], flush=True)
+    assert min(pv) > 1e-4
+    alpha = [np.minimum(p_rows[j], q[j]).sum() for j in range(G)]
+    EN = 1 + sum(np.prod(alpha[: i + 1]) for i in range(G))
+    N = nacc + 1
+    assert abs(N.mean() - EN) < 4 * N.std() / np.sqrt(len(N))
+
+
+# ---- edge cases ----------------------------------------------------------------
+
+@pytest.mark.parametrize("gamma", [0, 1, 8])
+def test_gamma_values(gamma):
+    w = generate("c2", DEV, B=5, gamma=gamma, V=3001)
+    compare_sample(w, label=f"gamma={gamma}")
+    w = generate("c5", DEV, B=3, gamma=gamma, V=5000)
+    compare_sample(w, label=f"gamma={gamma} top-p")
+
+
+def test_single_request():
+    compare_sample(generate("c3", DEV, B=1, V=20000), label="B=1 top-k")
+    compare_greedy(generate("c4", DEV, B=1, V=20000), label="B=1 greedy")
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 15])
+def test_tiny_vocab(V):
+    for kw in (dict(), dict(top_k=2), dict(top_p=0.6), dict(top_k=3, top_p=0.8)):
+        w = generate("c2", DEV, B=64, gamma=3, V=V, **kw)
+        compare_sample(w, label=f"V={V} {kw}")
+    compare_greedy(generate("c4", DEV, B=64, gamma=3, V=V), label=f"V={V} greedy")
+
+
+def _integer_logits(w, lo=-3, hi=4, seed=7):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    z = torch.randint(lo, hi, w.logits.shape, generator=g, device=DEV).to(w.logits.dtype)
+    w.logits = z.contiguous()
+    return w
+
+
+def test_ties_at_the_cuts():
+    """Integer logits: many ties at the k-th value, the top-p cut and argmax."""
+    for kw in (dict(top_k=50), dict(top_p=0.5, top_k=0), dict(top_k=5, top_p=0.7)):
+        w = _integer_logits(generate("c3", DEV, B=6, V=3000, **kw))
+        compare_sample(w, label=f"ties {kw}")
+    w = _integer_logits(generate("c4", DEV, B=16, V=3000))
+    compare_greedy(w, label="ties greedy")
+
+
+def test_flat_rows_take_the_exact_path():
+    """All-equal logits: the nucleus is the whole row (a kept set too long to
+    store as a list) -- exercised for bf16 and fp32."""
+    for dt in (torch.bfloat16, torch.float32):
+        w = generate("c5", DEV, B=3, gamma=2, V=5000)
+        w.logits = torch.zeros_like(w.logits, dtype=dt)
+        compare_sample(w, label=f"flat {dt}")
+        w = generate("c5", DEV, B=3, gamma=2, V=1500)
+        w.logits = torch.zeros_like(w.logits, dtype=dt)
+        compare_sample(w, label=f"flat short {dt}")
+
+
+def test_large_top_k_exact_path():
+    w = generate("c3", DEV, B=4, gamma=2, V=6000, top_k=300)
+    compare_sample(w, label="top-k 300")
+    w = generate("c3", DEV, B=4, gamma=2, V=6000, top_k=3000)
+    compare_sample(w, label="top-k 3000")
+
+
+def test_wide_nucleus_exact_path():
+    """Flat-ish rows whose nucleus exceeds the fast path's candidate set."""
+    w = generate("c5", DEV, B=3, gamma=2, V=30000, temperature=50.0, top_p=0.9)
+    compare_sample(w, label="wide nucleus")
+
+
+def test_flags():
+    w = generate("c2", DEV, B=8, gamma=2, V=300)
+    lg = w.logits.clone()
+    q = w.q.clone()
+    ids = w.ids.clone()
+    ua = w.u_accept.clone()
+    lg[0, 1, 17] = float("nan")
+    lg[1, 2, 5] = float("inf")
+    lg[2, 0, :] = float("-inf")
+    lg[3, 1, :100] = float("-inf")  # partial -inf row is fine
+    ids[4, 0] = 300 + 5               # bad id
+    ids[5, 1] = -1                    # bad id at position 1
+    d = int(ids[6, 0])
+    q[6, 0, d] = 0.0                  # q(d) = 0, p(d) > 0: accepted
+    # unnormalised q = 2 p at position 0 of request 7: rejection leaves no residual
+    p0 = torch.softmax(lg[7, 0].double(), -1)
+    q[7, 0] = (2.0 * p0).float()
+    ua[7, 0] = 0.99
+    w.logits, w.q, w.ids, w.u_accept = lg.contiguous(), q.contiguous(), ids.contiguous(), ua.contiguous()
+    o, _ = compare_sample(w, label="flags")
+    fl = o["flags"]
+    assert fl[0] == oracle.FLAG_NONFINITE and fl[1] == oracle.FLAG_NONFINITE and fl[2] == oracle.FLAG_NONFINITE
+    assert fl[3] == 0 and fl[4] == oracle.FLAG_BAD_ID
+    assert fl[6] & oracle.FLAG_Q_ZERO and fl[7] == oracle.FLAG_Z_DEGENERATE
+    # NaN q(d)
+    w2 = generate("c2", DEV, B=2, gamma=2, V=300)
+    q2 = w2.q.clone()
+    q2[1, 1, int(w2.ids[1, 1])] = float("nan")
+    w2.q = q2.contiguous()
+    o2, _ = compare_sample(w2, label="nan q")
+    assert o2["flags"][1] == oracle.FLAG_NONFINITE
+    # greedy with NaN
+    w3 = generate("c4", DEV, B=3, gamma=2, V=500)
+    lg3 = w3.logits.clone()
+    lg3[1, 2, 7] = float("nan")
+    w3.logits = lg3.contiguous()
+    compare_greedy(w3, label="greedy nan")
+
+
+def test_determinism():
+    for name, kw in (("c5", dict(B=4)), ("c2", dict(B=8)), ("c3", dict(B=6))):
+        w = generate(name, DEV, **kw)
+        a = gpu_sample(w)
+        b = gpu_sample(w)
+        for x, y in zip(a, b):
+            assert (x == y).all()
+
+
+# ---- statistics ------------------------------------------------------------
+
+def test_stats_small():
+    compare_stats(generate("c5", DEV, B=4), label="stats c5 B=4")
+    compare_stats(generate("c2", DEV, B=6), label="stats c2 B=6")
+    compare_stats(generate("c3", DEV, B=4), label="stats c3 B=4")
+    compare_stats(generate("c2", DEV, B=4, gamma=3, V=4001), label="stats c2 V=4001")
+
+
+def test_stats_flags_and_flat():
+    w = generate("c5", DEV, B=3, gamma=2, V=5000)
+    w.logits = torch.zeros_like(w.logits)
+    compare_stats(w, label="stats flat")
+    w = generate("c2", DEV, B=3, gamma=2, V=300)
+    lg = w.logits.clone()
+    lg[0, 1, 3] = float("nan")
+    ids = w.ids.clone()
+    ids[1, 0] = 1000
+    w.logits, w.ids = lg.contiguous(), ids.contiguous()
+    compare_stats(w, label="stats flags")
+
+
+# ---- full sizes, sampled requests -------------------------------------------
+
+def _sampled(B, n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(B, size=min(n, B), replace=False))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_full_size_sample(name):
+    w = generate(name, DEV)
+    gpu = gpu_sample(w)
+    compare_sample(w, requests=_sampled(w.cfg.B), label=f"{name} full", gpu=gpu)
+    # properties that hold for every request
+    tok, nacc, fl = gpu
+    G1 = w.cfg.gamma + 1
+    assert ((nacc >= 0) & (nacc <= w.cfg.gamma)).all()
+    pos = np.arange(G1)[None, :]
+    emitted = tok >= 0
+    assert (emitted == (pos <= nacc[:, None])).all()
+    assert (tok < w.cfg.V).all()
+    ids = w.ids.cpu().numpy()
+    assert all((tok[b, : nacc[b]] == ids[b, : nacc[b]]).all() for b in range(w.cfg.B))
+
+
+def test_full_size_greedy():
+    w = generate("c4", DEV)
+    compare_greedy(w, requests=_sampled(w.cfg.B), label="c4 full")
+
+
+def test_full_size_stats():
+    w = generate("c5", DEV)
+    compare_stats(w, requests=_sampled(w.cfg.B, 8), label="c5 full stats")
