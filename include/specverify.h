@@ -12,7 +12,8 @@
  * ---------------------------------------
  * - Every tensor argument is a DEVICE pointer owned by the caller.  The
  *   library never allocates, frees or retains caller memory and keeps no
- *   state between calls.  All scratch lives in the caller's `workspace`
+ *   state between calls (apart from the optional profiling hook
+ *   spec_set_rowpass_timer).  All scratch lives in the caller's `workspace`
  *   (device memory of at least spec_verify_workspace_size() bytes, 256-byte
  *   aligned, contents need not be initialised).
  * - Layout is contiguous row-major.  `target_logits` is [B, gamma+1, V]
@@ -126,6 +127,15 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
                             sv_sampling_params prm, float* out_alpha, float* out_z_pq,
                             float* out_z_qp, float* out_accept_prob, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
+ * arguments are non-NULL, every later spec_verify_sample /
+ * spec_verify_greedy / spec_accept_stats call records `start_event` just
+ * before and `stop_event` just after its streaming row-pass kernel (the
+ * HBM-bound pass over the logits) on the call's stream.  Both are hipEvent_t
+ * handles owned by the caller.  Passing NULL for either turns it off.  Event
+ * records are plain stream operations; nothing else changes. */
+sv_status spec_set_rowpass_timer(void* start_event, void* stop_event);
 
 /* Static description of a status code. */
 const char* spec_status_string(sv_status status);

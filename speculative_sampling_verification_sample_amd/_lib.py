@@ -40,6 +40,7 @@ SIGNATURES = {
          _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "spec_set_rowpass_timer": (ctypes.c_int, [_ptr, _ptr]),
 }
 
 _LIB = None

@@ -143,11 +143,16 @@ T* ws_at(void* ws, size_t off) {
 
 sv_status launched() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;  // profiling hook
+
 template <int MODE, bool BF16, bool NEED_S, int BS>
 void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
   size_t dyn = (MODE == M_TRUNC) ? (size_t)(BS / kWave) * (kCapW * sizeof(Cand) + 256 * sizeof(uint32_t)) : 0;
   dim3 grid((unsigned)(p.nchunks * p.rows));
+  hipEvent_t e0 = g_timer_start, e1 = g_timer_stop;
+  if (e0 && e1) (void)hipEventRecord(e0, st);
   hipLaunchKernelGGL((rowpass_kernel<MODE, BF16, NEED_S, BS>), grid, dim3(BS), dyn, st, a);
+  if (e0 && e1) (void)hipEventRecord(e1, st);
 }
 
 template <bool BF16>
@@ -387,6 +392,17 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   if (s != SV_OK) return s;
   hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
   return launched();
+}
+
+sv_status spec_set_rowpass_timer(void* start_event, void* stop_event) {
+  if (start_event == nullptr || stop_event == nullptr) {
+    g_timer_start = nullptr;
+    g_timer_stop = nullptr;
+  } else {
+    g_timer_start = reinterpret_cast<hipEvent_t>(start_event);
+    g_timer_stop = reinterpret_cast<hipEvent_t>(stop_event);
+  }
+  return SV_OK;
 }
 
 const char* spec_status_string(sv_status status) {

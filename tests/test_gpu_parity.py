@@ -266,3 +266,48 @@ def test_full_size_greedy():
 def test_full_size_stats():
     w = generate("c5", DEV)
     compare_stats(w, requests=_sampled(w.cfg.B, 8), label="c5 full stats")
+
+
+# ---- graph capture (the benchmark replays captured steps) ---------------------
+
+@pytest.mark.parametrize("name,kw", [("c2", dict(B=8)), ("c5", dict(B=4)), ("c3", dict(B=4)), ("c4", dict(B=8))])
+def test_graph_replay_matches_eager(name, kw):
+    import speculative_sampling_verification_sample_amd as sv
+
+    w = generate(name, DEV, **kw)
+    c = w.cfg
+    B, G1, V = w.logits.shape
+    ws = torch.empty(sv.workspace_size(B, G1 - 1, V, w.logits.dtype, c.temperature, c.top_k, c.top_p),
+                     dtype=torch.uint8, device=DEV)
+    outs = (torch.empty((B, G1), dtype=torch.int32, device=DEV), torch.empty((B,), dtype=torch.int32, device=DEV),
+            torch.empty((B,), dtype=torch.int32, device=DEV))
+
+    def call():
+        if c.mode == "greedy":
+            sv.verify_greedy(w.logits, w.ids, workspace=ws, out=outs)
+        else:
+            sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature, c.top_k, c.top_p,
+                             workspace=ws, out=outs)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
