@@ -1,8 +1,9 @@
 // C ABI of the verify step: argument validation, workspace layout and the
 // launch sequence of the kernels on the caller's stream.
 //
-//   sample : K1 row pass -> K2 row finalisation -> (truncation) exact
-//            fallback -> K3 acceptance + list draws -> K4 full-row draws
+//   sample : K1 row pass -> [truncation: K2 row finalisation -> exact
+//            fallback] -> K3 acceptance + list draws -> K4 full-row draws
+//            (chunk totals, then the per-request search)
 //   greedy : K1 row pass (argmax) -> greedy scan
 //   stats  : K1 -> K2 -> (fallback) -> per-chunk sums -> per-row finish
 //
@@ -31,8 +32,11 @@ constexpr int kFastTopK = 256;    // top-k above this always takes the exact pat
 constexpr int kNwTopP = 128;      // entries each wave keeps for top-p candidates
 constexpr int kNoutTopP = 1024;   // candidates a chunk hands over for top-p
 constexpr int kTieSlack = 256;    // room for ties at a chunk's cut
-constexpr int64_t kCh4 = 16384;   // chunk of the full-row sampler (multiple of kTile)
 constexpr int kTruncBS = 512;
+// Below this many requests the sampled rows are weighed by many workgroups
+// per request (two launches); above it one workgroup per request already
+// fills the GPU and the single launch wins.
+constexpr int kOneLaunchMinB = 256;
 
 enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS };
 
@@ -46,7 +50,7 @@ struct Plan {
   int nw = 0, nout = 0, cap_out = 0, um = 0;
   int nch4 = 1;
   int scale_bits = 40;
-  size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_cnt = 0, off_part = 0;
+  size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
   size_t total = 0;
 };
 
@@ -88,7 +92,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_p
     while (um < u) um <<= 1;
     p.um = um;
   }
-  p.nch4 = (int)((V + kCh4 - 1) / kCh4);
+  p.nch4 = (int)((V + kChunk4 - 1) / kChunk4);
   int lg = 0;
   while (((int64_t)1 << lg) < V) ++lg;
   p.scale_bits = std::min(40, 62 - lg);
@@ -105,8 +109,8 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_p
   if (p.trunc) off = align_up(off + rows * (size_t)kKMax * sizeof(Cand), 256);
   p.off_jobs = off;
   if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * sizeof(BigJob), 256);
-  p.off_cnt = off;
-  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+  p.off_gath = off;
+  if (kind == CALL_SAMPLE) off = align_up(off + rows * sizeof(float2), 256);
   p.off_part = off;
   if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * p.nch4 * sizeof(double), 256);
   if (kind == CALL_STATS) off = align_up(off + rows * nch * 4 * sizeof(double), 256);
@@ -156,8 +160,13 @@ void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
 }
 
 template <bool BF16>
-sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st) {
+sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st,
+                      const int32_t* ids = nullptr, const float* q = nullptr, int gamma = 0, float2* gath = nullptr) {
   RowPassArgs a;
+  a.ids = ids;
+  a.q = q;
+  a.gamma = gamma;
+  a.gath = gath;
   a.logits = logits;
   a.V = V;
   a.chunk = p.chunk;
@@ -267,15 +276,24 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
-  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
-         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  // untruncated rows: the row pass also gathers each draft's logit and q(d)
+  float2* gath = p.trunc ? nullptr : ws_at<float2>(workspace, p.off_gath);
+  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, draft_probs, gamma, gath)
+         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, draft_probs, gamma, gath);
   if (s != SV_OK) return s;
-  s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
-         : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
-  if (s != SV_OK) return s;
+  if (p.trunc) {
+    s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
+           : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
+    if (s != SV_OK) return s;
+  }
 
   AcceptArgs ac;
   ac.info = ws_at<RowInfo>(workspace, p.off_info);
+  ac.cout = ws_at<ChunkOut>(workspace, p.off_cout);
+  ac.nchunks = p.nchunks;
+  ac.logits = target_logits;
+  ac.c = c;
+  ac.gath = gath;
   ac.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
   ac.kmax = kKMax;
   ac.q = draft_probs;
@@ -289,10 +307,13 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   ac.out_nacc = out_num_accepted;
   ac.out_flags = out_row_flags;
   ac.jobs = ws_at<BigJob>(workspace, p.off_jobs);
-  ac.counters = ws_at<uint32_t>(workspace, p.off_cnt);
-  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, ac);
-  s = launched();
-  if (s != SV_OK) return s;
+  const dim3 agrid((unsigned)((B + 3) / 4));
+  if (p.trunc) {
+    // kept lists (and the rare oversized kept set) are drawn inside K3
+    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), 0, st, ac);
+    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), 0, st, ac);
+    return launched();
+  }
 
   BigArgs bg;
   bg.logits = target_logits;
@@ -300,16 +321,40 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   bg.V = V;
   bg.G1 = G1;
   bg.nch4 = p.nch4;
-  bg.ch4 = kCh4;
   bg.c = c;
   bg.jobs = ac.jobs;
-  bg.counters = ac.counters;
   bg.partials = ws_at<double>(workspace, p.off_part);
   bg.out_tokens = out_tokens;
   bg.out_flags = out_row_flags;
+  const int64_t tiles_big = (V + 1024 * kSeg - 1) / (1024 * kSeg);  // tiles of the 1024-thread sampler
+  if (G1 <= kWave && tiles_big <= kMaxTiles && B >= kOneLaunchMinB) {
+    // one workgroup per request: decision, row weights and the draw
+    if (V >= 16384) {
+      if (bf) hipLaunchKernelGGL((sample_full_kernel<true, 1024>), dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
+      else hipLaunchKernelGGL((sample_full_kernel<false, 1024>), dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
+    } else {
+      if (bf) hipLaunchKernelGGL((sample_full_kernel<true, 256>), dim3((unsigned)B), dim3(256), 0, st, bg, ac);
+      else hipLaunchKernelGGL((sample_full_kernel<false, 256>), dim3((unsigned)B), dim3(256), 0, st, bg, ac);
+    }
+    return launched();
+  }
   dim3 grid((unsigned)((int64_t)p.nch4 * B));
-  if (bf) hipLaunchKernelGGL((big_kernel<true>), grid, dim3(256), 0, st, bg);
-  else hipLaunchKernelGGL((big_kernel<false>), grid, dim3(256), 0, st, bg);
+  if (G1 <= kWave) {
+    // acceptance fused into the chunk weighing
+    if (bf) hipLaunchKernelGGL((big_partial_kernel<true, true>), grid, dim3(256), 0, st, bg, ac);
+    else hipLaunchKernelGGL((big_partial_kernel<false, true>), grid, dim3(256), 0, st, bg, ac);
+  } else {
+    if (bf) hipLaunchKernelGGL((accept_kernel<true, true>), agrid, dim3(256), 0, st, ac);
+    else hipLaunchKernelGGL((accept_kernel<false, true>), agrid, dim3(256), 0, st, ac);
+    s = launched();
+    if (s != SV_OK) return s;
+    if (bf) hipLaunchKernelGGL((big_partial_kernel<true, false>), grid, dim3(256), 0, st, bg, ac);
+    else hipLaunchKernelGGL((big_partial_kernel<false, false>), grid, dim3(256), 0, st, bg, ac);
+  }
+  s = launched();
+  if (s != SV_OK) return s;
+  if (bf) hipLaunchKernelGGL((big_finish_kernel<true>), dim3((unsigned)B), dim3(256), 0, st, bg);
+  else hipLaunchKernelGGL((big_finish_kernel<false>), dim3((unsigned)B), dim3(256), 0, st, bg);
   return launched();
 }
 

@@ -77,6 +77,17 @@ struct alignas(16) BigJob {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+template <bool BF16>
+__device__ __forceinline__ void widen(const uint4& w, float* x) {
+  if constexpr (BF16) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+}
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // e(x) relative to the integral reference R.

@@ -52,22 +52,103 @@ __device__ __forceinline__ float load_logit(const void* p, int64_t i) {
   }
 }
 
-// Draft gather for a row whose kept set and normaliser are final.
+// Draft gather for a row whose kept set and normaliser are final: the
+// draft's logit and q(d) (acceptance needs e(d), q(d) and S only).
 template <bool BF16>
-__device__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
+__device__ void gather_draft_at(const void* logits, const float* q, const int32_t* ids, int64_t V, int gamma,
+                                float c, int b, int j, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
-  if (j >= a.gamma) return;  // bonus row: no draft
-  int d = a.ids[(int64_t)b * a.gamma + j];
-  if (d < 0 || (int64_t)d >= a.V) {
+  if (j >= gamma) return;  // bonus row: no draft
+  int d = ids[(int64_t)b * gamma + j];
+  if (d < 0 || (int64_t)d >= V) {
     ri.d = -2;
     return;
   }
   ri.d = d;
-  float z = load_logit<BF16>(a.logits, rowoff + d);
-  ri.ed = (z >= ri.tau) ? e_of(z, a.c, ri.R) : 0.0f;
-  ri.qd = a.q[((int64_t)b * a.gamma + j) * a.V + d];
+  float z = load_logit<BF16>(logits, rowoff + d);
+  ri.ed = (z >= ri.tau) ? e_of(z, c, ri.R) : 0.0f;
+  ri.qd = q[((int64_t)b * gamma + j) * V + d];
+}
+
+template <bool BF16>
+__device__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
+  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.gamma, a.c, b, j, rowoff, ri);
+}
+
+// Merge the chunk results of one row in chunk order (one thread).
+struct RowMerge {
+  float xmax, thr, R;
+  uint32_t flags;
+  double S;  // full-row mass against R (0 when the pass kept no sums)
+};
+__device__ inline RowMerge merge_chunks(const ChunkOut* co, int nchunks, float c) {
+  RowMerge m;
+  m.xmax = kNegInf;
+  m.thr = kLowest;
+  m.flags = 0;
+  double s = 0.0;
+  float Rs = kNegInf;
+  for (int k0 = 0; k0 < nchunks; k0 += 8) {
+    ChunkOut o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i < nchunks) o[i] = co[k0 + i];  // loads issued together
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (k0 + i >= nchunks) break;
+      m.xmax = fmaxf(m.xmax, o[i].xmax);
+      m.thr = fmaxf(m.thr, o[i].thr);
+      m.flags |= o[i].flags;
+      sr_merge(s, Rs, o[i].s, o[i].Rs);
+    }
+  }
+  m.R = ceilf(m.xmax * c);
+  m.S = (Rs == kNegInf) ? 0.0 : ldexp(s, (int)(Rs - m.R));
+  return m;
+}
+__device__ inline bool merge_nonfinite(const RowMerge& m) {
+  return (m.flags & (CF_NAN | CF_POSINF)) || !(m.xmax > kNegInf) || !(fabsf(m.R) < kPosInf);
+}
+
+// Row info of an untruncated row straight from its chunk results; the
+// draft's logit and q(d) come from the row pass's gather when `gath` is set.
+template <bool BF16>
+__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const float* q,
+                                    const int32_t* ids, int64_t V, int gamma, int b, int j, int64_t rowoff,
+                                    const float2* gath = nullptr) {
+  RowMerge m = merge_chunks(co, nchunks, c);
+  RowInfo ri;
+  ri.S = m.S;
+  ri.R = m.R;
+  ri.tau = kLowest;
+  ri.nkept = -1;
+  ri.flags = RF_BIG;
+  ri.ed = 0.0f;
+  ri.qd = 0.0f;
+  ri.d = -1;
+  ri.pad = 0;
+  if (merge_nonfinite(m)) {
+    ri.flags = RF_NONFINITE;
+    return ri;
+  }
+  if (gath != nullptr) {
+    if (j < gamma) {
+      const int d = ids[(int64_t)b * gamma + j];
+      if (d < 0 || (int64_t)d >= V) {
+        ri.d = -2;
+      } else {
+        const float2 g = gath[rowoff / V];
+        ri.d = d;
+        ri.ed = (g.x >= ri.tau) ? e_of(g.x, c, ri.R) : 0.0f;
+        ri.qd = g.y;
+      }
+    }
+    return ri;
+  }
+  gather_draft_at<BF16>(logits, q, ids, V, gamma, c, b, j, rowoff, ri);
+  return ri;
 }
 
 // Block-wide inclusive scan of n doubles in place (256 threads, fixed order).
@@ -133,24 +214,12 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   double* cum = reinterpret_cast<double*>(s_dyn + (size_t)a.um * sizeof(uint64_t));
 
   if (tid == 0) {
-    const ChunkOut* co = a.cout + r * a.nchunks;
-    float xm = kNegInf, th = kLowest;
-    uint32_t fl = 0;
-    double s = 0.0;
-    float Rs = kNegInf;
-    for (int c = 0; c < a.nchunks; ++c) {
-      ChunkOut o = co[c];
-      xm = fmaxf(xm, o.xmax);
-      th = fmaxf(th, o.thr);
-      fl |= o.flags;
-      sr_merge(s, Rs, o.s, o.Rs);
-    }
-    s_xm = xm;
-    s_th = th;
-    s_fl = fl;
-    float R = ceilf(xm * a.c);
-    s_R = R;
-    s_S = (Rs == kNegInf) ? 0.0 : ldexp(s, (int)(Rs - R));
+    RowMerge m = merge_chunks(a.cout + r * a.nchunks, a.nchunks, a.c);
+    s_xm = m.xmax;
+    s_th = m.thr;
+    s_fl = m.flags;
+    s_R = m.R;
+    s_S = m.S;
     s_n = 0;
   }
   __syncthreads();

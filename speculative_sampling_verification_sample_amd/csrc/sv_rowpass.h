@@ -36,20 +36,15 @@ struct RowPassArgs {
   int32_t cap_out;
   ChunkOut* out;  // [rows][nchunks]
   Cand* cand;     // [rows][nchunks][cap_out]
+  // Optional draft gather (untruncated sampling): the workgroup whose chunk
+  // holds d_j stores (z(d_j), q_j(d_j)) in gath[row].
+  const int32_t* ids;
+  const float* q;
+  int32_t gamma;
+  float2* gath;
 };
 
 constexpr int kCapW = 512;  // candidate slots per wave
-
-template <bool BF16>
-__device__ __forceinline__ void widen(const uint4& w, float* x) {
-  if constexpr (BF16) {
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  } else {
-    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
-    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
-  }
-}
 
 // Radix select inside one wave: the key of the `need`-th largest entry.
 template <bool BF16>
@@ -130,6 +125,15 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     whist = reinterpret_cast<uint32_t*>(s_dyn + (size_t)NWV * kCapW * sizeof(Cand)) + wid * 256;
     if (tid == 0) s_thr = f2key(kLowest);
     __syncthreads();
+  }
+
+  if (a.gath != nullptr && tid == 0 && j < a.gamma) {
+    const int d = a.ids[(int64_t)b * a.gamma + j];
+    if ((int64_t)d >= e0 && (int64_t)d < e1) {
+      float zd = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.logits)[rowoff + d] << 16)
+                      : reinterpret_cast<const float*>(a.logits)[rowoff + d];
+      a.gath[r] = make_float2(zd, a.q[((int64_t)b * a.gamma + j) * a.V + d]);
+    }
   }
 
   float xmax = kNegInf;

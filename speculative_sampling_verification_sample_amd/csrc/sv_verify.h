@@ -9,7 +9,7 @@
 // token from p_gamma ([WR] §6): when the kept set of that row is a short
 // list the wave draws it at once (inverse CDF, fp64 wave scans); otherwise
 // it leaves a BigJob for K4, which sums the weights of a whole row in chunks
-// and lets the last chunk to finish locate the token.
+// (one launch) and locates the token from the chunk totals (a second launch).
 #pragma once
 
 #include "sv_device.h"
@@ -18,7 +18,12 @@
 namespace sv {
 
 struct AcceptArgs {
-  const RowInfo* info;  // [B * (gamma+1)]
+  RowInfo* info;        // [B * (gamma+1)]
+  const float2* gath;   // draft gather of the row pass (untruncated rows) or null
+  const ChunkOut* cout; // chunk results, read when rows are untruncated (no K2)
+  int32_t nchunks;
+  const void* logits;
+  float c;
   const Cand* kept;     // [rows][kmax]
   int32_t kmax;
   const float* q;
@@ -32,7 +37,6 @@ struct AcceptArgs {
   int32_t* out_nacc;
   uint32_t* out_flags;  // may be null
   BigJob* jobs;
-  uint32_t* counters;
 };
 
 // Draw from the kept list of one row (called by a whole wave).
@@ -83,14 +87,239 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const float* qrow,
   return token >= 0 ? token : lastpos;
 }
 
+// Full-row draw by one wave (oversized kept sets of truncated rows, which
+// are rare): two passes over the row, weights as in the chunked sampler.
+template <bool BF16>
+__device__ int draw_full_row_wave(const void* logits, const float* q, int64_t V, float c, int64_t row, int64_t qrow,
+                                  double S, float R, float tau, float u, bool& residual, uint32_t& fl) {
+  const int lane = lane_id();
+  auto weight = [&](int64_t x, bool res) -> double {
+    if (x >= V) return 0.0;
+    float z = load_logit<BF16>(logits, row * V + x);
+    if (!(z >= tau)) return 0.0;
+    double e = (double)e_of(z, c, R);
+    if (!res) return e;
+    double d = e - (double)q[qrow * V + x] * S;
+    return d > 0.0 ? d : 0.0;
+  };
+  auto total = [&](bool res) -> double {
+    double carry = 0.0;
+    for (int64_t x0 = 0; x0 < V; x0 += kWave) {
+      double incl = wave_incl_scan_d(weight(x0 + lane, res));
+      carry = carry + __shfl(incl, kWave - 1, kWave);
+    }
+    return carry;
+  };
+  double W = total(residual);
+  if (residual && !(W > 0.0)) {
+    fl |= 4u;  // SV_ROW_Z_DEGENERATE
+    residual = false;
+    W = total(false);
+  }
+  const double t = (double)u * W;
+  double carry = 0.0;
+  int64_t lastpos = -1;
+  for (int64_t x0 = 0; x0 < V; x0 += kWave) {
+    const int64_t x = x0 + lane;
+    const double w = weight(x, residual);
+    const double incl = wave_incl_scan_d(w);
+    uint64_t hit = ballot(x < V && carry + incl > t);
+    if (hit) return (int)(x0 + (int)__builtin_ctzll(hit));
+    uint64_t pos = ballot(x < V && w > 0.0);
+    if (pos) lastpos = x0 + 63 - (int)__builtin_clzll(pos);
+    carry = carry + __shfl(incl, kWave - 1, kWave);
+  }
+  return (int)lastpos;
+}
+
+// Block-wide "first token whose running weight exceeds t, else the last
+// token of positive weight" when thread segments are in token order: the
+// first hit lives in the lowest wave and lane holding one, the last positive
+// token in the highest.  Ballots and one LDS slot per wave, no atomics.
+template <int NW>
+__device__ int block_first_or_last(int found, int lp, int* s_f, int* s_l) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t hm = ballot(found != 0x7fffffff);
+  const int ff = hm ? __shfl(found, (int)__builtin_ctzll(hm), kWave) : 0x7fffffff;
+  const uint64_t lm = ballot(lp >= 0);
+  const int ll = lm ? __shfl(lp, 63 - (int)__builtin_clzll(lm), kWave) : -1;
+  if (lane == 0) {
+    s_f[wid] = ff;
+    s_l[wid] = ll;
+  }
+  __syncthreads();
+  int tok = -1;
+  for (int k = 0; k < NW; ++k)
+    if (s_f[k] != 0x7fffffff) {
+      tok = s_f[k];
+      break;
+    }
+  if (tok < 0)
+    for (int k = NW - 1; k >= 0; --k)
+      if (s_l[k] >= 0) {
+        tok = s_l[k];
+        break;
+      }
+  return tok;
+}
+
+// Shuffle a RowInfo from lane `src`.
+__device__ __forceinline__ RowInfo shfl_info(const RowInfo& r, int src) {
+  RowInfo o;
+  o.S = __shfl(r.S, src, kWave);
+  o.R = __shfl(r.R, src, kWave);
+  o.tau = __shfl(r.tau, src, kWave);
+  o.nkept = __shfl(r.nkept, src, kWave);
+  o.flags = __shfl(r.flags, src, kWave);
+  o.ed = __shfl(r.ed, src, kWave);
+  o.qd = __shfl(r.qd, src, kWave);
+  o.d = __shfl(r.d, src, kWave);
+  o.pad = 0;
+  return o;
+}
+
+// Emit the outputs of one request once n_accepted is known (whole wave).
+template <bool BF16, bool BIG_INWAVE>
+__device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl, const RowInfo& rs,
+                               int32_t* out) {
+  const int lane = lane_id();
+  const int G = a.gamma, G1 = G + 1;
+  for (int jj = lane; jj < G1; jj += kWave)
+    if (jj != nacc) out[jj] = jj < nacc ? a.ids[(int64_t)b * G + jj] : -1;
+  bool residual = nacc < G;
+  const float u = a.ur[(int64_t)b * G1 + nacc];
+  const int64_t trow = (int64_t)b * G1 + nacc;
+  const int64_t qrow = residual ? (int64_t)b * G + nacc : -1;
+  if ((rs.flags & RF_BIG) && BIG_INWAVE) {
+    int token = draw_full_row_wave<BF16>(a.logits, a.q, a.V, a.c, trow, qrow, rs.S, rs.R, rs.tau, u, residual, fl);
+    if (lane == 0) {
+      out[nacc] = token;
+      a.out_nacc[b] = nacc;
+      if (a.out_flags) a.out_flags[b] = fl;
+    }
+    return;
+  }
+  if (rs.flags & RF_BIG) {
+    if (lane == 0) {
+      BigJob jb;
+      jb.S = rs.S;
+      jb.R = rs.R;
+      jb.tau = rs.tau;
+      jb.u = u;
+      jb.row = (int32_t)trow;
+      jb.qrow = (int32_t)qrow;
+      jb.slot = nacc;
+      jb.active = 1;
+      jb.pad = 0;
+      a.jobs[b] = jb;
+      out[nacc] = -1;  // written by the full-row sampler
+      a.out_nacc[b] = nacc;
+      if (a.out_flags) a.out_flags[b] = fl;
+    }
+    return;
+  }
+  const float* qr = residual ? a.q + qrow * a.V : nullptr;
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
+  if (lane == 0) {
+    out[nacc] = token;
+    a.out_nacc[b] = nacc;
+    if (a.out_flags) a.out_flags[b] = fl;
+    a.jobs[b].active = 0;
+  }
+}
+
+__device__ void nonfinite_request(const AcceptArgs& a, int b, int32_t* out) {
+  const int lane = lane_id();
+  for (int jj = lane; jj < a.gamma + 1; jj += kWave) out[jj] = -1;
+  if (lane == 0) {
+    a.out_nacc[b] = 0;
+    if (a.out_flags) a.out_flags[b] = 8u;  // SV_ROW_NONFINITE
+    a.jobs[b].active = 0;
+  }
+}
+
+// Acceptance decision of one request with gamma + 1 <= 64 (whole wave, one
+// lane per position, all in registers).
+struct Decision {
+  int nacc;
+  uint32_t fl;
+  bool bad;
+  RowInfo rs;  // info of row n_accepted (the row the token is drawn from)
+};
+
+template <bool BF16, bool FROM_CHUNKS>
+__device__ Decision decide_short(const AcceptArgs& a, int b) {
+  const int lane = lane_id();
+  const int G = a.gamma, G1 = G + 1;
+  RowInfo ri;
+  ri.flags = 0;
+  ri.d = -1;
+  ri.qd = 0.0f;
+  ri.ed = 0.0f;
+  ri.S = 1.0;
+  ri.R = 0.0f;
+  ri.tau = kLowest;
+  ri.nkept = -1;
+  ri.pad = 0;
+  float ua = 0.0f;
+  if (lane < G) ua = a.ua[(int64_t)b * G + lane];
+  if (lane <= G) {
+    const int64_t row = (int64_t)b * G1 + lane;
+    if constexpr (FROM_CHUNKS)
+      ri = untrunc_row_info<BF16>(a.cout + row * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, G, b, lane,
+                                  row * a.V, a.gath);
+    else
+      ri = a.info[row];
+  }
+  Decision dc;
+  bool bad = (lane <= G) && ((ri.flags & RF_NONFINITE) ||
+                              (lane < G && ri.d >= 0 && !(ri.qd >= 0.0f && ri.qd < kPosInf)));
+  dc.bad = ballot(bad) != 0;
+  bool acc = true;
+  if (lane < G) {
+    if (ri.d < 0) acc = false;
+    else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
+    else acc = (double)ua * (double)ri.qd * ri.S < (double)ri.ed;
+  }
+  uint64_t rej = ballot(!acc);
+  dc.nacc = rej ? (int)__builtin_ctzll(rej) : G;
+  dc.fl = 0;
+  if (ballot(lane < G && lane <= dc.nacc && ri.d >= 0 && ri.qd == 0.0f) != 0) dc.fl |= 2u;  // SV_ROW_Q_ZERO
+  dc.rs = shfl_info(ri, dc.nacc);
+  if (dc.nacc < G && dc.rs.d == -2) dc.fl |= 1u;  // SV_ROW_BAD_ID
+  return dc;
+}
+
+template <bool BF16, bool FROM_CHUNKS>
 __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wid;
   if (b >= a.B) return;
   const int G = a.gamma, G1 = G + 1;
-  const RowInfo* inf = a.info + (int64_t)b * G1;
+  RowInfo* inf = a.info + (int64_t)b * G1;
   int32_t* out = a.out_tokens + (int64_t)b * G1;
+  constexpr bool kInwave = !FROM_CHUNKS;  // truncated rows draw oversized kept sets in the wave
 
+  if (G1 <= kWave) {
+    Decision dc = decide_short<BF16, FROM_CHUNKS>(a, b);
+    if (dc.bad) {
+      nonfinite_request(a, b, out);
+      return;
+    }
+    finish_request<BF16, kInwave>(a, b, dc.nacc, dc.fl, dc.rs, out);
+    return;
+  }
+
+  // Long drafts: rows go through the workspace copy of the row infos.
+  if constexpr (FROM_CHUNKS) {
+    for (int jj = lane; jj <= G; jj += kWave) {
+      const int64_t row = (int64_t)b * G1 + jj;
+      inf[jj] = untrunc_row_info<BF16>(a.cout + row * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, G, b,
+                                       jj, row * a.V);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wave_sync();
+  }
   bool bad = false;
   for (int jj = lane; jj <= G; jj += kWave) {
     RowInfo ri = inf[jj];
@@ -98,15 +327,9 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
     if (jj < G && ri.d >= 0 && !(ri.qd >= 0.0f && ri.qd < kPosInf)) bad = true;
   }
   if (ballot(bad) != 0) {
-    for (int jj = lane; jj < G1; jj += kWave) out[jj] = -1;
-    if (lane == 0) {
-      a.out_nacc[b] = 0;
-      if (a.out_flags) a.out_flags[b] = 8u;  // SV_ROW_NONFINITE
-      a.jobs[b].active = 0;
-    }
+    nonfinite_request(a, b, out);
     return;
   }
-  // acceptance scan
   int nacc = G;
   for (int j0 = 0; j0 < G; j0 += kWave) {
     const int jj = j0 + lane;
@@ -130,54 +353,23 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
     if (ri.d >= 0 && ri.qd == 0.0f) qz = true;
   }
   if (ballot(qz) != 0) fl |= 2u;  // SV_ROW_Q_ZERO
-  if (nacc < G && inf[nacc].d == -2) fl |= 1u;  // SV_ROW_BAD_ID
-  for (int jj = lane; jj < G1; jj += kWave)
-    if (jj != nacc) out[jj] = jj < nacc ? a.ids[(int64_t)b * G + jj] : -1;
-
   const RowInfo rs = inf[nacc];
-  bool residual = nacc < G;
-  const float u = a.ur[(int64_t)b * G1 + nacc];
-  const int64_t trow = (int64_t)b * G1 + nacc;
-  const int64_t qrow = residual ? (int64_t)b * G + nacc : -1;
-  if (rs.flags & RF_BIG) {
-    if (lane == 0) {
-      BigJob jb;
-      jb.S = rs.S;
-      jb.R = rs.R;
-      jb.tau = rs.tau;
-      jb.u = u;
-      jb.row = (int32_t)trow;
-      jb.qrow = (int32_t)qrow;
-      jb.slot = nacc;
-      jb.active = 1;
-      jb.pad = 0;
-      a.jobs[b] = jb;
-      a.counters[b] = 0u;
-      out[nacc] = -1;  // written by the full-row sampler
-      a.out_nacc[b] = nacc;
-      if (a.out_flags) a.out_flags[b] = fl;
-    }
-    return;
-  }
-  const float* qr = residual ? a.q + qrow * a.V : nullptr;
-  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
-  if (lane == 0) {
-    out[nacc] = token;
-    a.out_nacc[b] = nacc;
-    if (a.out_flags) a.out_flags[b] = fl;
-    a.jobs[b].active = 0;
-  }
+  if (nacc < G && rs.d == -2) fl |= 1u;  // SV_ROW_BAD_ID
+  finish_request<BF16, kInwave>(a, b, nacc, fl, rs, out);
 }
 
 // ---------------------------------------------------------------------------
-// K4: full-row draw.  Grid (nch4 * B); a workgroup sums the weights of one
-// chunk of the sampled row in tiles (thread t owns `kSeg` consecutive
-// elements of a tile), the last workgroup of a request to finish walks the
-// chunk totals and rescans the chunk holding the token with the same
-// arithmetic.
+// K4: full-row draw, two launches.  big_partial_kernel (grid nch4 * B):
+// workgroup ci of request b weighs the 2048 tokens [2048 ci, 2048 ci + 2048)
+// of the sampled row (thread t owns 8 consecutive tokens, read with 16-byte
+// loads) and writes their total, reduced in a fixed order.
+// big_finish_kernel (grid B) walks the chunk totals, picks the chunk where
+// the running total first exceeds t = u * W, and recomputes that chunk with
+// the same arithmetic to find the token.  Workgroups never wait on or signal
+// each other inside a launch.
 // ---------------------------------------------------------------------------
-constexpr int kSeg = 16;
-constexpr int kTile = 256 * kSeg;
+constexpr int kSeg = 8;
+constexpr int kChunk4 = 256 * kSeg;
 
 struct BigArgs {
   const void* logits;
@@ -185,185 +377,476 @@ struct BigArgs {
   int64_t V;
   int32_t G1;
   int32_t nch4;
-  int64_t ch4;  // multiple of kTile
   float c;
   const BigJob* jobs;
-  uint32_t* counters;
   double* partials;  // [B][nch4]
   int32_t* out_tokens;
   uint32_t* out_flags;
 };
 
+// Weights of tokens x0 .. x0+7 of the job's row (0 past the end).
 template <bool BF16>
-__device__ __forceinline__ double big_weight(const BigArgs& a, const BigJob& jb, bool residual, int64_t x) {
-  float z = load_logit<BF16>(a.logits, (int64_t)jb.row * a.V + x);
-  if (!(z >= jb.tau)) return 0.0;
-  double e = (double)e_of(z, a.c, jb.R);
-  if (!residual) return e;
-  double d = e - (double)a.q[(int64_t)jb.qrow * a.V + x] * jb.S;
-  return d > 0.0 ? d : 0.0;
+__device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0,
+                                            double* w) {
+  const int64_t V = a.V;
+  const int64_t zo = (int64_t)jb.row * V + x0;
+  const bool full = x0 + kSeg <= V;
+  float z[kSeg];
+  if constexpr (BF16) {
+    if (full && (zo & 7) == 0) {
+      widen<true>(reinterpret_cast<const uint4*>(a.logits)[zo >> 3], z);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<true>(a.logits, zo + k) : kNegInf;
+    }
+  } else {
+    if (full && (zo & 3) == 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.logits) + (zo >> 2);
+      widen<false>(p[0], z);
+      widen<false>(p[1], z + 4);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
+    }
+  }
+  float qv[kSeg];
+  if (residual) {
+    const int64_t qo = (int64_t)jb.qrow * V + x0;
+    if (full && (qo & 3) == 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.q) + (qo >> 2);
+      widen<false>(p[0], qv);
+      widen<false>(p[1], qv + 4);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q[qo + k] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) {
+    double wk = 0.0;
+    if (z[k] >= jb.tau) {
+      double e = (double)e_of(z[k], a.c, jb.R);
+      if (residual) {
+        double d = e - (double)qv[k] * jb.S;
+        wk = d > 0.0 ? d : 0.0;
+      } else {
+        wk = e;
+      }
+    }
+    w[k] = wk;
+  }
 }
 
-// Weight total of tile [x0, x0 + kTile) ∩ [.., x1): per-thread segment sums
-// and their exclusive scan (fixed order).  Returns the tile total.
-template <bool BF16>
-__device__ double tile_scan(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0, int64_t x1,
-                            double& seg, double& excl, double* s_w) {
+// Chunk total (thread segments summed left to right, then a fixed-order
+// block reduction); also returns this thread's exclusive prefix.
+__device__ __forceinline__ double chunk_reduce(double seg, double& excl, double* s_w) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int64_t s0 = x0 + (int64_t)tid * kSeg;
-  double acc = 0.0;
-  for (int k = 0; k < kSeg; ++k) {
-    int64_t x = s0 + k;
-    if (x < x1) acc += big_weight<BF16>(a, jb, residual, x);
-  }
-  seg = acc;
-  double incl = wave_incl_scan_d(acc);
+  double incl = wave_incl_scan_d(seg);
+  double ex = __shfl_up(incl, 1, kWave);
+  if (lane == 0) ex = 0.0;
   __syncthreads();
   if (lane == 63) s_w[wid] = incl;
   __syncthreads();
   double off = 0.0;
-  for (int w = 0; w < wid; ++w) off += s_w[w];
-  excl = off + (incl - acc);
-  double tot = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
-  return tot;
+  for (int k = 0; k < wid; ++k) off += s_w[k];
+  excl = off + ex;
+  return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
 }
 
 template <bool BF16>
-__device__ double chunk_total(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0, int64_t x1,
-                              double* s_w) {
-  double tot = 0.0;
-  for (int64_t t0 = x0; t0 < x1; t0 += kTile) {
-    double seg, excl;
-    tot = tot + tile_scan<BF16>(a, jb, residual, t0, x1, seg, excl, s_w);
-  }
-  return tot;
+__device__ __forceinline__ double chunk_weights(const BigArgs& a, const BigJob& jb, bool residual, int ci,
+                                                double* w, double& seg, double& excl, double* s_w) {
+  const int64_t x0 = (int64_t)ci * kChunk4 + (int64_t)threadIdx.x * kSeg;
+  seg_weights<BF16>(a, jb, residual, x0, w);
+  seg = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) seg += w[k];
+  return chunk_reduce(seg, excl, s_w);
 }
 
-// Token in chunk [x0, x1) whose running weight (starting at `carry`) first
-// exceeds t; the last positive-weight token of the chunk when rounding
-// leaves none.
-template <bool BF16>
-__device__ int chunk_find(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0, int64_t x1, double carry,
-                          double t, double* s_w, int* s_best) {
-  const int tid = threadIdx.x;
-  int lastpos = -1;
-  for (int64_t t0 = x0; t0 < x1; t0 += kTile) {
-    double seg, excl;
-    double tot = tile_scan<BF16>(a, jb, residual, t0, x1, seg, excl, s_w);
-    if (tid == 0) {
-      s_best[0] = 0x7fffffff;
-      s_best[1] = -1;
-    }
-    __syncthreads();
-    const int64_t s0 = t0 + (int64_t)tid * kSeg;
-    double run = carry + excl;
-    const bool here = carry + tot > t;
-    int found = 0x7fffffff, lp = -1;
-    for (int k = 0; k < kSeg; ++k) {
-      int64_t x = s0 + k;
-      if (x >= x1) break;
-      double w = big_weight<BF16>(a, jb, residual, x);
-      run = run + w;
-      if (w > 0.0) lp = (int)x;
-      if (here && run > t && found == 0x7fffffff) found = (int)x;
-    }
-    if (found != 0x7fffffff) atomicMin(&s_best[0], found);
-    if (lp >= 0) atomicMax(&s_best[1], lp);
-    __syncthreads();
-    int f = s_best[0];
-    if (s_best[1] >= 0) lastpos = s_best[1];
-    __syncthreads();
-    if (here) return f != 0x7fffffff ? f : lastpos;
-    carry = carry + tot;
-  }
-  return lastpos;
-}
-
-template <bool BF16>
-__global__ void __launch_bounds__(256) big_kernel(BigArgs a) {
-  const int tid = threadIdx.x;
+// FUSED (untruncated rows, gamma + 1 <= 64): every workgroup of request b
+// first takes the acceptance decision itself (wave 0; it is a few hundred
+// bytes of reads, so repeating it per chunk is cheaper than a launch), chunk
+// 0 writes the request's outputs and the job, then all weigh their chunk.
+template <bool BF16, bool FUSED>
+__global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs ac) {
   const int64_t blk = blockIdx.x;
   const int b = (int)(blk / a.nch4), ci = (int)(blk - (int64_t)b * a.nch4);
+  __shared__ double s_w[4];
+  __shared__ BigJob s_job;
+  BigJob jb;
+  if constexpr (FUSED) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < kWave) {
+      Decision dc = decide_short<BF16, true>(ac, b);
+      const int G = ac.gamma, G1 = G + 1;
+      int32_t* out = ac.out_tokens + (int64_t)b * G1;
+      if (dc.bad) {
+        if (ci == 0) nonfinite_request(ac, b, out);
+        if (lane == 0) s_job.active = 0;
+      } else {
+        const bool residual = dc.nacc < G;
+        if (lane == 0) {
+          BigJob j;
+          j.S = dc.rs.S;
+          j.R = dc.rs.R;
+          j.tau = dc.rs.tau;
+          j.u = ac.ur[(int64_t)b * G1 + dc.nacc];
+          j.row = (int32_t)((int64_t)b * G1 + dc.nacc);
+          j.qrow = residual ? (int32_t)((int64_t)b * G + dc.nacc) : -1;
+          j.slot = dc.nacc;
+          j.active = 1;
+          j.pad = 0;
+          s_job = j;
+        }
+        if (ci == 0) {
+          for (int jj = lane; jj < G1; jj += kWave)
+            if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)b * G + jj] : -1;
+          if (lane == 0) {
+            ac.out_nacc[b] = dc.nacc;
+            if (ac.out_flags) ac.out_flags[b] = dc.fl;
+            ac.jobs[b] = s_job;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    jb = s_job;
+  } else {
+    jb = a.jobs[b];
+  }
+  if (!jb.active) return;
+  double w[kSeg], seg, excl;
+  double W = chunk_weights<BF16>(a, jb, jb.qrow >= 0, ci, w, seg, excl, s_w);
+  if (threadIdx.x == 0) a.partials[(int64_t)b * a.nch4 + ci] = W;
+}
+
+// One workgroup per request: walk the chunk totals (written by the previous
+// launch) and rescan the chunk that holds the token.
+template <bool BF16>
+__global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x;
   const BigJob jb = a.jobs[b];
   if (!jb.active) return;
   __shared__ double s_w[4];
-  __shared__ int s_best[2];
-  __shared__ int s_last;
-  __shared__ int s_cstar;
-  __shared__ double s_carry;
-  bool residual = jb.qrow >= 0;
-  const int64_t x0 = (int64_t)ci * a.ch4, x1 = min(x0 + a.ch4, a.V);
-  double W = chunk_total<BF16>(a, jb, residual, x0, x1, s_w);
+  __shared__ int s_cstar, s_wf[4], s_wl[4];
+  __shared__ double s_carry, s_t;
   double* P = a.partials + (int64_t)b * a.nch4;
-  if (tid == 0) {
-    P[ci] = W;
-    __threadfence();
-    unsigned old = atomicAdd(&a.counters[b], 1u);
-    s_last = (old == (unsigned)(a.nch4 - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  bool residual = jb.qrow >= 0;
+  double w[kSeg], seg, excl;
   uint32_t extra = 0;
-  // total and chunk search (sequential, fixed order)
-  auto locate = [&](double& tot_out) {
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int k = 0; k < a.nch4; ++k) tot = tot + __builtin_nontemporal_load(&P[k]);
-      tot_out = tot;
-      s_carry = tot;
+  // Walk the chunk totals with wave scans (fixed order: identical sums in
+  // both walks).  Wave 0 decides; the result goes through LDS.
+  auto walk_total = [&]() {
+    if (wid == 0) {
+      double carry = 0.0;
+      for (int k0 = 0; k0 < a.nch4; k0 += kWave) {
+        const int k = k0 + lane;
+        double pk = k < a.nch4 ? P[k] : 0.0;
+        double incl = wave_incl_scan_d(pk);
+        carry = carry + __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) s_carry = carry;
     }
     __syncthreads();
-    tot_out = s_carry;
+    double tot = s_carry;
     __syncthreads();
+    return tot;
   };
-  double tot;
-  locate(tot);
+  double tot = walk_total();
   if (residual && !(tot > 0.0)) {
     extra |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
     residual = false;
     for (int k = 0; k < a.nch4; ++k) {
-      const int64_t y0 = (int64_t)k * a.ch4, y1 = min(y0 + a.ch4, a.V);
-      double wk = chunk_total<BF16>(a, jb, false, y0, y1, s_w);
+      double wk = chunk_weights<BF16>(a, jb, false, k, w, seg, excl, s_w);
       if (tid == 0) P[k] = wk;
+      __syncthreads();
     }
-    __threadfence();
-    __syncthreads();
-    locate(tot);
+    tot = walk_total();
   }
-  const double t = (double)jb.u * tot;
-  if (tid == 0) {
+  if (wid == 0) {
+    const double t = (double)jb.u * tot;
     double carry = 0.0;
     int cstar = -1, lastc = -1;
-    for (int k = 0; k < a.nch4; ++k) {
-      double pk = __builtin_nontemporal_load(&P[k]);
-      if (pk > 0.0) lastc = k;
-      if (carry + pk > t) {
-        cstar = k;
+    double cex = 0.0;
+    for (int k0 = 0; k0 < a.nch4; k0 += kWave) {
+      const int k = k0 + lane;
+      double pk = k < a.nch4 ? P[k] : 0.0;
+      double incl = wave_incl_scan_d(pk);
+      double C = carry + incl;
+      double ex = __shfl_up(C, 1, kWave);
+      if (lane == 0) ex = carry;
+      uint64_t pos = ballot(k < a.nch4 && pk > 0.0);
+      if (pos) lastc = k0 + 63 - (int)__builtin_clzll(pos);
+      uint64_t hit = ballot(k < a.nch4 && C > t);
+      if (hit) {
+        int src = (int)__builtin_ctzll(hit);
+        cstar = k0 + src;
+        cex = __shfl(ex, src, kWave);
         break;
       }
-      carry = carry + pk;
+      carry = carry + __shfl(incl, kWave - 1, kWave);
     }
     if (cstar < 0) {
-      // rounding left no chunk: the last positive token of the last
-      // positive chunk (carry chosen so that nothing exceeds t)
+      // rounding left no chunk above t: the last positive token of the last
+      // positive chunk
       cstar = lastc;
-      carry = -1.0 / 0.0;
+      cex = -1.0 / 0.0;
     }
-    s_cstar = cstar;
-    s_carry = carry;
+    if (lane == 0) {
+      s_cstar = cstar;
+      s_carry = cex;
+      s_t = t;
+    }
   }
   __syncthreads();
   const int cstar = s_cstar;
-  const double carry = s_carry;
   int token = -1;
   if (cstar >= 0) {
-    const int64_t y0 = (int64_t)cstar * a.ch4, y1 = min(y0 + a.ch4, a.V);
-    token = chunk_find<BF16>(a, jb, residual, y0, y1, carry, t, s_w, s_best);
+    const double t = s_t;
+    chunk_weights<BF16>(a, jb, residual, cstar, w, seg, excl, s_w);
+    const int64_t x0 = (int64_t)cstar * kChunk4 + (int64_t)tid * kSeg;
+    double run = s_carry + excl;
+    int found = 0x7fffffff, lp = -1;
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      run = run + w[k];
+      if (w[k] > 0.0) lp = (int)(x0 + k);
+      if (run > t && found == 0x7fffffff) found = (int)(x0 + k);
+    }
+    token = block_first_or_last<4>(found, lp, s_wf, s_wl);
   }
   if (tid == 0) {
     a.out_tokens[(int64_t)b * a.G1 + jb.slot] = token;
     if (extra && a.out_flags) a.out_flags[b] |= extra;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Untruncated requests with gamma + 1 <= 64, in one launch: one workgroup
+// of BS threads per request takes the acceptance decision (wave 0), weighs
+// the sampled row in tiles of BS * 8 tokens (each thread 8 consecutive
+// tokens, 16-byte loads; tile totals reduced in a fixed order and kept in
+// LDS), then re-weighs only the tile holding t = u * W (now in L2) to find
+// the token.
+// ---------------------------------------------------------------------------
+constexpr int kMaxTiles = 256;  // rows up to 256 * 8192 tokens (BS = 1024)
+
+template <int BS>
+__device__ __forceinline__ double block_excl_scan(double v, double& total, double* s_wt) {
+  constexpr int NW = BS / kWave;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  double incl = wave_incl_scan_d(v);
+  double ex = __shfl_up(incl, 1, kWave);
+  if (lane == 0) ex = 0.0;
+  __syncthreads();
+  if (lane == 63) s_wt[wid] = incl;
+  __syncthreads();
+  double off = 0.0;
+  for (int k = 0; k < wid; ++k) off += s_wt[k];
+  double tot = 0.0;
+  for (int k = 0; k < NW; ++k) tot += s_wt[k];
+  total = tot;
+  return off + ex;
+}
+
+// Raw logits / q of tokens x0 .. x0+7 (16-byte loads when aligned).
+template <bool BF16>
+__device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0, float* z,
+                                         float* qv) {
+  const int64_t V = a.V;
+  const int64_t zo = (int64_t)jb.row * V + x0;
+  const bool full = x0 + kSeg <= V;
+  if constexpr (BF16) {
+    if (full && (zo & 7) == 0) {
+      widen<true>(reinterpret_cast<const uint4*>(a.logits)[zo >> 3], z);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<true>(a.logits, zo + k) : kNegInf;
+    }
+  } else {
+    if (full && (zo & 3) == 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.logits) + (zo >> 2);
+      widen<false>(p[0], z);
+      widen<false>(p[1], z + 4);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
+    }
+  }
+  if (residual) {
+    const int64_t qo = (int64_t)jb.qrow * V + x0;
+    if (full && (qo & 3) == 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.q) + (qo >> 2);
+      widen<false>(p[0], qv);
+      widen<false>(p[1], qv + 4);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q[qo + k] : 0.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ void seg_weigh(const BigJob& jb, float c, bool residual, const float* z, const float* qv,
+                                          double* w) {
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) {
+    double wk = 0.0;
+    if (z[k] >= jb.tau) {
+      double e = (double)e_of(z[k], c, jb.R);
+      if (residual) {
+        double d = e - (double)qv[k] * jb.S;
+        wk = d > 0.0 ? d : 0.0;
+      } else {
+        wk = e;
+      }
+    }
+    w[k] = wk;
+  }
+}
+
+template <bool BF16, int BS>
+__global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs ac) {
+  constexpr int NW = BS / kWave;
+  constexpr int kU = 4;  // tiles whose loads are in flight together
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x;
+  __shared__ BigJob s_job;
+  __shared__ double s_wt[NW];
+  __shared__ double s_part[kMaxTiles * NW];  // per-wave tile partial sums
+  __shared__ double s_tile[kMaxTiles];
+  __shared__ int s_kstar, s_wf[NW], s_wl[NW];
+  __shared__ double s_cex, s_t, s_W;
+  const int G = ac.gamma, G1 = G + 1;
+  int32_t* out = ac.out_tokens + (int64_t)b * G1;
+  if (tid < kWave) {
+    Decision dc = decide_short<BF16, true>(ac, b);
+    if (dc.bad) {
+      nonfinite_request(ac, b, out);
+      if (lane == 0) s_job.active = 0;
+    } else {
+      const bool residual = dc.nacc < G;
+      for (int jj = lane; jj < G1; jj += kWave)
+        if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)b * G + jj] : -1;
+      if (lane == 0) {
+        BigJob j;
+        j.S = dc.rs.S;
+        j.R = dc.rs.R;
+        j.tau = dc.rs.tau;
+        j.u = ac.ur[(int64_t)b * G1 + dc.nacc];
+        j.row = (int32_t)((int64_t)b * G1 + dc.nacc);
+        j.qrow = residual ? (int32_t)((int64_t)b * G + dc.nacc) : -1;
+        j.slot = dc.nacc;
+        j.active = 1;
+        j.pad = (int32_t)dc.fl;
+        s_job = j;
+        ac.out_nacc[b] = dc.nacc;
+      }
+    }
+  }
+  __syncthreads();
+  const BigJob jb = s_job;
+  if (!jb.active) return;
+  uint32_t fl = (uint32_t)jb.pad;
+  bool residual = jb.qrow >= 0;
+  constexpr int64_t kTileN = (int64_t)BS * kSeg;
+  const int ntiles = (int)((a.V + kTileN - 1) / kTileN);
+
+  // Pass 1: tile totals.  Loads of kU tiles are issued together; each wave
+  // reduces its share of a tile and parks it in LDS (no barrier in the loop).
+  auto weigh_row = [&](bool res) {
+    for (int k0 = 0; k0 < ntiles; k0 += kU) {
+      float z[kU][kSeg], qv[kU][kSeg];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (k0 + u < ntiles) seg_load<BF16>(a, jb, res, (int64_t)(k0 + u) * kTileN + (int64_t)tid * kSeg, z[u], qv[u]);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (k0 + u >= ntiles) break;
+        double w[kSeg];
+        seg_weigh(jb, a.c, res, z[u], qv[u], w);
+        double seg = 0.0;
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i) seg += w[i];
+        double ws = wave_sum_d(seg);
+        if (lane == 0) s_part[(k0 + u) * NW + wid] = ws;
+      }
+    }
+    __syncthreads();
+    for (int k = tid; k < ntiles; k += BS) {
+      double t = 0.0;
+      for (int w2 = 0; w2 < NW; ++w2) t += s_part[k * NW + w2];
+      s_tile[k] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double W = 0.0;
+      for (int k = 0; k < ntiles; ++k) W = W + s_tile[k];
+      s_W = W;
+    }
+    __syncthreads();
+    double W = s_W;
+    __syncthreads();
+    return W;
+  };
+  double W = weigh_row(residual);
+  if (residual && !(W > 0.0)) {
+    fl |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
+    residual = false;
+    W = weigh_row(false);
+  }
+  if (tid == 0) {
+    const double t = (double)jb.u * W;
+    double carry = 0.0;
+    int kstar = -1, lastk = -1;
+    for (int k = 0; k < ntiles; ++k) {
+      const double tk = s_tile[k];
+      if (tk > 0.0) lastk = k;
+      if (carry + tk > t) {
+        kstar = k;
+        break;
+      }
+      carry = carry + tk;
+    }
+    if (kstar < 0) {
+      // rounding left no tile above t: the last positive token of the last
+      // positive tile
+      kstar = lastk;
+      carry = -1.0 / 0.0;
+    }
+    s_kstar = kstar;
+    s_cex = carry;
+    s_t = t;
+  }
+  __syncthreads();
+  const int kstar = s_kstar;
+  int token = -1;
+  if (kstar >= 0) {
+    const int64_t x0 = (int64_t)kstar * kTileN + (int64_t)tid * kSeg;
+    float z[kSeg], qv[kSeg];
+    double w[kSeg];
+    seg_load<BF16>(a, jb, residual, x0, z, qv);
+    seg_weigh(jb, a.c, residual, z, qv, w);
+    double seg = 0.0;
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) seg += w[i];
+    double tot;
+    const double ex = block_excl_scan<BS>(seg, tot, s_wt);
+    const double t = s_t;
+    double run = s_cex + ex;
+    int found = 0x7fffffff, lp = -1;
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      run = run + w[i];
+      if (w[i] > 0.0) lp = (int)(x0 + i);
+      if (run > t && found == 0x7fffffff) found = (int)(x0 + i);
+    }
+    token = block_first_or_last<NW>(found, lp, s_wf, s_wl);
+  }
+  if (tid == 0) {
+    out[jb.slot] = token;
+    if (ac.out_flags) ac.out_flags[b] = fl;
   }
 }
 

@@ -101,7 +101,7 @@ def test_toy_chi_square_on_gpu_outputs():
 
 # ---- edge cases ----------------------------------------------------------------
 
-@pytest.mark.parametrize("gamma", [0, 1, 8])
+@pytest.mark.parametrize("gamma", [0, 1, 8, 70])
 def test_gamma_values(gamma):
     w = generate("c2", DEV, B=5, gamma=gamma, V=3001)
     compare_sample(w, label=f"gamma={gamma}")
@@ -311,3 +311,18 @@ def test_graph_replay_matches_eager(name, kw):
         torch.cuda.synchronize()
         for a, b in zip(outs, ref):
             assert torch.equal(a, b)
+
+
+def test_very_long_rows():
+    """Rows longer than the one-workgroup sampler's tile table (V > 2048 * 8192):
+    the chunked two-launch sampler takes over."""
+    w = generate("c2", DEV, B=2, gamma=1, V=17_000_000)
+    compare_sample(w, label="V=17M")
+
+
+def test_many_requests_one_launch_sampler():
+    """B >= 256 untruncated: one workgroup per request decides and draws."""
+    w = generate("c2", DEV, B=260, gamma=3, V=20000)
+    compare_sample(w, label="c2 B=260")
+    w = generate("c2", DEV, B=300, gamma=2, V=999)
+    compare_sample(w, label="c2 B=300 V=999")
