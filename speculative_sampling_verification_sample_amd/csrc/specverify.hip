@@ -76,9 +76,12 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_p
     }
     p.cap_out = p.nout + kTieSlack;
   }
+  // Short workgroups in several waves of residency keep the launch tail
+  // short; truncated rows keep few chunks (their candidate lists merge in K2).
   const int64_t minchunk = p.trunc ? 16384 : 4096;
   const int64_t maxchunks = p.trunc ? 4 : (1 << 20);
-  const int64_t want = p.rows > 0 ? (kTargetWG + p.rows - 1) / p.rows : 1;
+  const int64_t target = p.trunc ? kTargetWG : kTargetWG * 4;
+  const int64_t want = p.rows > 0 ? (target + p.rows - 1) / p.rows : 1;
   const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
   int64_t nch = std::max<int64_t>(1, std::min(std::min(want, lim), maxchunks));
   int64_t chunk = (V + nch - 1) / nch;
@@ -225,7 +228,7 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const float* q, const 
   a.info = ws_at<RowInfo>(ws, p.off_info);
   a.kept = p.trunc ? ws_at<Cand>(ws, p.off_kept) : nullptr;
   set_kernel_attrs();
-  size_t dyn = p.trunc ? (size_t)p.um * (sizeof(uint64_t) + sizeof(double)) : 0;
+  size_t dyn = p.trunc ? (size_t)p.um * 16 : 0;  // key, id, fixed-point mass per entry
   hipLaunchKernelGGL((rowfinal_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), dyn, st, a);
   sv_status s = launched();
   if (s != SV_OK) return s;
@@ -309,9 +312,11 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   ac.jobs = ws_at<BigJob>(workspace, p.off_jobs);
   const dim3 agrid((unsigned)((B + 3) / 4));
   if (p.trunc) {
-    // kept lists (and the rare oversized kept set) are drawn inside K3
-    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), 0, st, ac);
-    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), 0, st, ac);
+    // kept lists (and the rare oversized kept set) are drawn inside K3; each
+    // wave sorts its list by token id in LDS first
+    const size_t dyn = 4 * (size_t)kKMax * sizeof(Cand);
+    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), dyn, st, ac);
+    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), dyn, st, ac);
     return launched();
   }
 
@@ -435,7 +440,8 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
   s = launched();
   if (s != SV_OK) return s;
-  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
+  const size_t sdyn = p.trunc ? 4 * (size_t)kKMax * sizeof(Cand) : 0;
+  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), sdyn, st, a);
   return launched();
 }
 

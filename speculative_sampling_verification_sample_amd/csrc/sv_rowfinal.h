@@ -109,7 +109,8 @@ __device__ inline RowMerge merge_chunks(const ChunkOut* co, int nchunks, float c
   return m;
 }
 __device__ inline bool merge_nonfinite(const RowMerge& m) {
-  return (m.flags & (CF_NAN | CF_POSINF)) || !(m.xmax > kNegInf) || !(fabsf(m.R) < kPosInf);
+  // a NaN logit poisons the exp sums of the modes that keep them (S != S)
+  return (m.flags & (CF_NAN | CF_POSINF)) || !(m.xmax > kNegInf) || !(fabsf(m.R) < kPosInf) || (m.S != m.S);
 }
 
 // Row info of an untruncated row straight from its chunk results; the
@@ -151,52 +152,122 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
   return ri;
 }
 
-// Block-wide inclusive scan of n doubles in place (256 threads, fixed order).
-__device__ void block_incl_scan_d(double* v, int n, double* s_tmp /*[4]*/) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int per = (n + 255) / 256;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  double run = 0.0;
-  for (int i = lo; i < hi; ++i) run += v[i];
-  double incl = wave_incl_scan_d(run);
-  if (lane == 63) s_tmp[wid] = incl;
-  __syncthreads();
-  double off = 0.0;
-  for (int w = 0; w < wid; ++w) off += s_tmp[w];
-  double pre = off + (incl - run);
-  for (int i = lo; i < hi; ++i) {
-    pre += v[i];
-    v[i] = pre;
-  }
-  __syncthreads();
+// ---- block-level selection over an LDS candidate array (256 threads) ----
+// Fixed-point masses (e * 2^40, e <= ~1) make every sum an integer sum, so
+// results do not depend on the order of the additions.
+constexpr int kMassBits = 40;
+
+__device__ __forceinline__ unsigned long long to_fixed(float e) {
+  return (unsigned long long)rint((double)e * 1099511627776.0);  // 2^40
 }
 
-// Bitonic sort (ascending) of n = power-of-two 64-bit keys in LDS.
-__device__ void block_bitonic_u64(uint64_t* k, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        int ixj = i ^ stride;
-        if (ixj > i) {
-          uint64_t x = k[i], y = k[ixj];
-          bool up = (i & size) == 0;
-          if (up ? (x > y) : (x < y)) {
-            k[i] = y;
-            k[ixj] = x;
+__device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s_tmp /*[4]*/) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  __syncthreads();
+  if (lane == 0) s_tmp[wid] = v;
+  __syncthreads();
+  unsigned long long t = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  __syncthreads();
+  return t;
+}
+
+// Key of the `need`-th largest entry (count), entries with key >= floor only.
+template <bool BF16>
+__device__ uint32_t block_select_count(const uint32_t* keys, int n, int need, uint32_t* hist, int* s_dn) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int kLow = BF16 ? 16 : 0;
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= kLow; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      uint32_t k = keys[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      int d = wave_find_digit(hist, need);
+      if (lane == 0) {
+        s_dn[0] = d;
+        s_dn[1] = need;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_dn[0] << shift;
+    pmask |= 255u << shift;
+    need = s_dn[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Largest key v with mass(entries with key >= v, key >= floor) >= target.
+// Returns false when the whole mass stays below target.
+template <bool BF16>
+__device__ bool block_select_mass(const uint32_t* keys, const unsigned long long* mass, int n, uint32_t floor_key,
+                                  double target, unsigned long long* mh, int* s_dn, unsigned long long* s_above,
+                                  uint32_t& out_key) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int kLow = BF16 ? 16 : 0;
+  uint32_t prefix = 0, pmask = 0;
+  if (tid == 0) *s_above = 0ull;
+  for (int shift = 24; shift >= kLow; shift -= 8) {
+    mh[tid] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      uint32_t k = keys[i];
+      if (k >= floor_key && (k & pmask) == prefix) atomicAdd(&mh[(k >> shift) & 255u], mass[i]);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      unsigned long long c0 = mh[255 - 4 * lane], c1 = mh[254 - 4 * lane], c2 = mh[253 - 4 * lane],
+                         c3 = mh[252 - 4 * lane];
+      unsigned long long ls = c0 + c1 + c2 + c3, incl = ls;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        unsigned long long t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const unsigned long long above = *s_above;
+      uint64_t hit = ballot((double)(above + incl) >= target);
+      if (!hit) {
+        if (lane == 0) s_dn[0] = -1;
+      } else {
+        const int src = (int)__builtin_ctzll(hit);
+        if (lane == src) {
+          unsigned long long run = above + (incl - ls);
+          unsigned long long cs[4] = {c0, c1, c2, c3};
+          int k = 0;
+          for (; k < 3; ++k) {
+            if ((double)(run + cs[k]) >= target) break;
+            run += cs[k];
           }
+          s_dn[0] = 255 - 4 * lane - k;
+          *s_above = run;
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
+    const int d = s_dn[0];
+    __syncthreads();
+    if (d < 0) return false;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
   }
+  out_key = prefix;
+  return true;
 }
 
-__device__ __forceinline__ uint64_t desc_key(float v, int idx) {
-  // ascending order of ~key == descending value, then ascending index
-  return ~(((uint64_t)f2key(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx));
+// Append entries to an LDS list with one atomic per wave (order arbitrary).
+__device__ __forceinline__ int wave_append_slot(bool keep, int* counter) {
+  const uint64_t m = ballot(keep);
+  int base = 0;
+  if (lane_id() == 0 && m) base = atomicAdd(counter, (int)__popcll(m));
+  base = __shfl(base, 0, kWave);
+  return base + lanes_below(m);
 }
-__device__ __forceinline__ float desc_val(uint64_t k) { return key2f((uint32_t)(~k >> 32)); }
-__device__ __forceinline__ int desc_idx(uint64_t k) { return (int)(0xffffffffu - (uint32_t)(~k)); }
 
 template <bool BF16>
 __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
@@ -206,12 +277,16 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
 
   __shared__ float s_xm, s_th, s_R;
-  __shared__ double s_S, s_tmp[4];
+  __shared__ double s_S;
   __shared__ uint32_t s_fl;
-  __shared__ int s_n, s_i;
+  __shared__ int s_n, s_dn[2];
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long mh[256], s_u64[4], s_above;
   extern __shared__ __align__(16) unsigned char s_dyn[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(s_dyn);
-  double* cum = reinterpret_cast<double*>(s_dyn + (size_t)a.um * sizeof(uint64_t));
+  // union entries: keys, token ids, fixed-point masses
+  uint32_t* keys = reinterpret_cast<uint32_t*>(s_dyn);
+  int32_t* idxs = reinterpret_cast<int32_t*>(s_dyn + (size_t)a.um * 4);
+  unsigned long long* mass = reinterpret_cast<unsigned long long*>(s_dyn + (size_t)a.um * 8);
 
   if (tid == 0) {
     RowMerge m = merge_chunks(a.cout + r * a.nchunks, a.nchunks, a.c);
@@ -234,7 +309,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   ri.d = -1;
   ri.pad = 0;
   const uint32_t fl = s_fl;
-  if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf)) {
+  if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf) || (s_S != s_S)) {
     if (tid == 0) {
       ri.flags = RF_NONFINITE;
       a.info[r] = ri;
@@ -259,14 +334,22 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
 
   // ---- candidate union (entries >= the highest chunk threshold) ----
   const float theta = s_th;
+  const float R = s_R;
   const Cand* cd = a.cand + r * a.nchunks * (int64_t)a.cap_out;
   for (int c = 0; c < a.nchunks; ++c) {
     const int nc = a.cout[r * a.nchunks + c].ncand;
-    for (int i = tid; i < nc; i += 256) {
-      Cand e = cd[(int64_t)c * a.cap_out + i];
-      if (e.v >= theta) {
-        int pos = atomicAdd(&s_n, 1);
-        if (pos < a.um) keys[pos] = desc_key(e.v, e.idx);
+    for (int i0 = 0; i0 < nc; i0 += 256) {
+      const int i = i0 + tid;
+      Cand e;
+      e.v = kNegInf;
+      e.idx = 0;
+      if (i < nc) e = cd[(int64_t)c * a.cap_out + i];
+      const bool keep = i < nc && e.v >= theta;
+      const int pos = wave_append_slot(keep, &s_n);
+      if (keep && pos < a.um) {
+        keys[pos] = f2key(e.v);
+        idxs[pos] = e.idx;
+        mass[pos] = to_fixed(e_of(e.v, a.c, R));
       }
     }
   }
@@ -279,101 +362,63 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     }
     return;
   }
-  int np2 = 1;
-  while (np2 < nu) np2 <<= 1;
-  for (int i = nu + tid; i < np2; i += 256) keys[i] = ~0ull;
-  __syncthreads();
-  block_bitonic_u64(keys, np2);
 
   // ---- thresholds ----
-  const float R = s_R;
   const bool topk = a.top_k > 0 && (int64_t)a.top_k < a.V;
   const bool topp = a.top_p < 1.0f;
-  for (int i = tid; i < nu; i += 256) cum[i] = (double)e_of(desc_val(keys[i]), a.c, R);
-  __syncthreads();
-  block_incl_scan_d(cum, nu, s_tmp);
-  int nK = nu;
-  float tau = kLowest;
-  if (topk) {
-    if (nu >= a.top_k) {
-      tau = desc_val(keys[a.top_k - 1]);
-      if (tid == 0) s_i = nu;
-      __syncthreads();
-      for (int i = tid; i < nu; i += 256)
-        if (desc_val(keys[i]) < tau) atomicMin(&s_i, i);
-      __syncthreads();
-      nK = s_i;
-    }
-  }
-  int nkept = nK;
-  double Sfin = nK > 0 ? cum[nK - 1] : 0.0;
-  bool slow = false;
+  uint32_t kfloor = 0;  // keys below this are outside the top-k set
+  if (topk && nu >= a.top_k) kfloor = block_select_count<BF16>(keys, nu, a.top_k, hist, s_dn);
+  auto mass_from = [&](uint32_t kf) -> unsigned long long {
+    unsigned long long part = 0ull;
+    for (int i = tid; i < nu; i += 256)
+      if (keys[i] >= kf) part += mass[i];
+    return block_sum_u64(part, s_u64);
+  };
+  uint32_t kfinal = kfloor;
+  const double scale = 1099511627776.0;  // 2^40
   if (topp) {
-    const double Sref = topk ? Sfin : s_S;
+    const double Sref = topk ? (double)mass_from(kfloor) : s_S * scale;
     const double target = (double)a.top_p * Sref;
-    if (tid == 0) s_i = 0x7fffffff;
-    __syncthreads();
-    for (int i = tid; i < nK; i += 256)
-      if (cum[i] >= target) atomicMin(&s_i, i);
-    __syncthreads();
-    int istar = s_i;
-    if (istar == 0x7fffffff) {
-      if (topk || theta == kLowest) istar = nK - 1;  // rounding: keep everything
-      else slow = true;                                // crossing below the certified region
-    }
-    if (!slow) {
-      tau = desc_val(keys[istar]);
-      if (tid == 0) s_i = nK;
-      __syncthreads();
-      for (int i = tid; i < nK; i += 256)
-        if (desc_val(keys[i]) < tau) atomicMin(&s_i, i);
-      __syncthreads();
-      nkept = s_i;
-      Sfin = cum[nkept - 1];
+    uint32_t kp;
+    if (block_select_mass<BF16>(keys, mass, nu, kfloor, target, mh, s_dn, &s_above, kp)) {
+      kfinal = kp;
+    } else if (!(topk || theta == kLowest)) {
+      // the crossing lies below the certified candidates: exact path
+      if (tid == 0) {
+        ri.flags = RF_SLOW;
+        a.info[r] = ri;
+      }
+      return;
+    }  // else rounding: keep the whole base set
+  }
+  const unsigned long long Sfx = mass_from(kfinal);
+  ri.S = (double)Sfx / scale;
+  ri.tau = key2f(kfinal);
+  if (kfinal == 0) ri.tau = kLowest;
+  // ---- kept list (token order is restored by the sampler when needed) ----
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  Cand* out = a.kept + r * (int64_t)a.kmax;
+  for (int i0 = 0; i0 < nu; i0 += 256) {
+    const int i = i0 + tid;
+    const bool keep = i < nu && keys[i] >= kfinal;
+    const int pos = wave_append_slot(keep, &s_n);
+    if (keep && pos < a.kmax) {
+      Cand e;
+      e.idx = idxs[i];
+      e.v = e_of(key2f(keys[i]), a.c, R);
+      out[pos] = e;
     }
   }
-  if (slow) {
-    if (tid == 0) {
-      ri.flags = RF_SLOW;
-      a.info[r] = ri;
-    }
-    return;
-  }
-  ri.tau = tau;
-  ri.S = Sfin;
-  if (nkept > a.kmax) {
-    if (tid == 0) {
+  __syncthreads();
+  const int nkept = s_n;
+  if (tid == 0) {
+    if (nkept > a.kmax) {
       ri.flags = RF_BIG;
       ri.nkept = -1;
-      gather_draft<BF16>(a, b, j, rowoff, ri);
-      a.info[r] = ri;
+    } else {
+      ri.nkept = nkept;
     }
-    return;
-  }
-  // kept list sorted by token id: reuse the key array (index-major keys)
-  __syncthreads();
-  int kp2 = 1;
-  while (kp2 < nkept) kp2 <<= 1;
-  for (int i = tid; i < kp2; i += 256) {
-    uint64_t k = ~0ull;
-    if (i < nkept) {
-      uint64_t dk = keys[i];
-      k = ((uint64_t)(uint32_t)desc_idx(dk) << 32) | (uint64_t)__float_as_uint(desc_val(dk));
-    }
-    __syncthreads();
-    keys[i] = k;
-  }
-  __syncthreads();
-  block_bitonic_u64(keys, kp2);
-  Cand* out = a.kept + r * (int64_t)a.kmax;
-  for (int i = tid; i < nkept; i += 256) {
-    Cand e;
-    e.idx = (int32_t)(keys[i] >> 32);
-    e.v = e_of(__uint_as_float((uint32_t)keys[i]), a.c, R);
-    out[i] = e;
-  }
-  if (tid == 0) {
-    ri.nkept = nkept;
     gather_draft<BF16>(a, b, j, rowoff, ri);
     a.info[r] = ri;
   }

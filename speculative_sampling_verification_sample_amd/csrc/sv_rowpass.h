@@ -168,7 +168,8 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
         if (f < F0 || f >= F1) x[i] = kNegInf;
         else if (x[i] != x[i]) flags |= CF_NAN;
       }
-    } else {
+    } else if constexpr (!DO_S) {
+      // no exp sums in this mode: NaN needs its own test (|bits| above +Inf)
       if constexpr (BF16) {
         uint32_t m0 = w.x & 0x7fff7fffu, m1 = w.y & 0x7fff7fffu, m2 = w.z & 0x7fff7fffu, m3 = w.w & 0x7fff7fffu;
         uint32_t lo = max(max(m0 & 0xffffu, m1 & 0xffffu), max(m2 & 0xffffu, m3 & 0xffffu));
@@ -198,6 +199,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
         R = Rn;
       }
       if (R != kNegInf) {
+        // a NaN logit turns s into NaN, which the row merge reports
         float ev[EPV];
 #pragma unroll
         for (int i = 0; i < EPV; ++i) ev[i] = e_of(x[i], c, R);
@@ -205,6 +207,11 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
         if constexpr (EPV == 8) t = ((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7]));
         else t = (ev[0] + ev[1]) + (ev[2] + ev[3]);
         s += (double)t;
+      } else {
+        // nothing finite seen yet by this thread: test this unit directly
+#pragma unroll
+        for (int i = 0; i < EPV; ++i)
+          if (x[i] != x[i]) flags |= CF_NAN;
       }
     }
     if constexpr (MODE == M_TRUNC) {
@@ -235,34 +242,27 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   // Block-uniform steps: step k gives thread tid the unit U0 + k*BS + tid.
   // Every thread runs every step (lanes past the end see an all -inf unit),
   // so the wave-wide ballots and LDS selections of M_TRUNC see whole waves.
+  // Up to kUnroll units' loads are issued before any is processed.
+  constexpr int kUnroll = 8;
   const bool aligned = (F0 % EPV == 0) && (F1 % EPV == 0);
   const int64_t nunits = U1 - U0;
-  const int64_t nfull = nunits / BS;
-  int64_t k = 0;
-  if (aligned) {
-    for (; k + 4 <= nfull; k += 4) {
-      const int64_t u = U0 + k * BS + tid;
-      uint4 w0 = base[u], w1 = base[u + BS], w2 = base[u + 2 * BS], w3 = base[u + 3 * BS];
-      process(u, w0, NoEdge{});
-      process(u + BS, w1, NoEdge{});
-      process(u + 2 * BS, w2, NoEdge{});
-      process(u + 3 * BS, w3, NoEdge{});
+  const int64_t nsteps = (nunits + BS - 1) / BS;
+  const int64_t nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
+  for (int64_t k0 = 0; k0 < nsteps; k0 += kUnroll) {
+    uint4 wv[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t u = U0 + (k0 + i) * BS + tid;
+      wv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (k0 + i < nsteps && u < U1) wv[i] = base[u];
     }
-    for (; k < nfull; ++k) {
-      const int64_t u = U0 + k * BS + tid;
-      process(u, base[u], NoEdge{});
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      if (k0 + i >= nsteps) break;
+      const int64_t u = U0 + (k0 + i) * BS + tid;
+      if (k0 + i < nfull) process(u, wv[i], NoEdge{});
+      else process(u, wv[i], Edge{});
     }
-  } else {
-    for (; k < nfull; ++k) {
-      const int64_t u = U0 + k * BS + tid;
-      process(u, base[u], Edge{});
-    }
-  }
-  if (nfull * BS < nunits) {
-    const int64_t u = U0 + nfull * BS + tid;
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (u < U1) w = base[u];
-    process(u, w, Edge{});
   }
 
   // NaN / +Inf detection
