@@ -29,10 +29,11 @@ using namespace sv;
 constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 per CU)
 constexpr int kKMax = 2048;       // longest kept set stored as a list
 constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
-constexpr int kNwTopP = 128;      // entries each wave keeps for top-p candidates
-constexpr int kNoutTopP = 1024;   // candidates a chunk hands over for top-p
+constexpr int kNwTopP = 128;      // chunk elements a top-p candidate threshold certifies
+constexpr int kNoutTrunc = 1024;  // entries an oversized chunk list is trimmed to
 constexpr int kTieSlack = 256;    // room for ties at a chunk's cut
-constexpr int kTruncBS = 512;
+constexpr int kTruncMinWG = 2048; // truncated pass: shorter chunks until this many workgroups
+constexpr int kUnionMax = 2048;   // LDS entries of the row finisher's candidate union
 // Below this many requests the sampled rows are weighed by many workgroups
 // per request (two launches); above it one workgroup per request already
 // fills the GPU and the single launch wins.
@@ -48,6 +49,7 @@ struct Plan {
   int nchunks = 1;
   int64_t chunk = 8;
   int nw = 0, nout = 0, cap_out = 0, um = 0;
+  int nu = 16;  // truncated pass: 16-byte units per thread
   int nch4 = 1;
   int scale_bits = 40;
   size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
@@ -56,7 +58,7 @@ struct Plan {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_params prm) {
+Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, sv_sampling_params prm) {
   Plan p;
   const bool topk = prm.top_k > 0 && (int64_t)prm.top_k < V;
   const bool topp = prm.top_p < 1.0f;
@@ -67,24 +69,31 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_p
   p.need_s = p.trunc && topp && !topk;
   p.fast = !topk || prm.top_k <= kFastTopK;
   if (p.trunc) {
-    if (topk) {
-      p.nw = std::min<int>(prm.top_k, kFastTopK);
-      p.nout = p.nw;
-    } else {
-      p.nw = kNwTopP;
-      p.nout = kNoutTopP;
-    }
+    p.nw = topk ? std::min<int>(prm.top_k, kFastTopK) : kNwTopP;
+    p.nout = kNoutTrunc;
     p.cap_out = p.nout + kTieSlack;
   }
-  // Short workgroups in several waves of residency keep the launch tail
-  // short; truncated rows keep few chunks (their candidate lists merge in K2).
-  const int64_t minchunk = p.trunc ? 16384 : 4096;
-  const int64_t maxchunks = p.trunc ? 4 : (1 << 20);
-  const int64_t target = p.trunc ? kTargetWG : kTargetWG * 4;
-  const int64_t want = p.rows > 0 ? (target + p.rows - 1) / p.rows : 1;
-  const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
-  int64_t nch = std::max<int64_t>(1, std::min(std::min(want, lim), maxchunks));
-  int64_t chunk = (V + nch - 1) / nch;
+  int64_t nch, chunk;
+  if (p.trunc) {
+    // A chunk is held in registers: at most nu * kTruncBS units of 16 bytes,
+    // two of them possibly straddling the chunk ends.  Shorter chunks (fewer
+    // units per thread) only when the rows alone do not fill the GPU.
+    const int64_t epv = (dt == SV_BF16) ? 8 : 4;
+    int64_t cap = 0;
+    for (p.nu = 16;; p.nu /= 2) {
+      cap = ((int64_t)p.nu * kTruncBS - 2) * epv / 8 * 8;
+      nch = (V + cap - 1) / cap;
+      if (p.nu == 4 || p.rows * nch >= kTruncMinWG) break;
+    }
+  } else {
+    // Short workgroups in several waves of residency keep the launch tail short.
+    const int64_t minchunk = 4096;
+    const int64_t target = kTargetWG * 4;
+    const int64_t want = p.rows > 0 ? (target + p.rows - 1) / p.rows : 1;
+    const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
+    nch = std::max<int64_t>(1, std::min(want, lim));
+  }
+  chunk = (V + nch - 1) / nch;
   chunk = (chunk + 7) / 8 * 8;
   nch = (V + chunk - 1) / chunk;
   p.nchunks = (int)nch;
@@ -92,7 +101,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_sampling_p
   if (p.trunc) {
     int64_t u = nch * p.cap_out;
     int um = 1;
-    while (um < u) um <<= 1;
+    while (um < u && um < kUnionMax) um <<= 1;
     p.um = um;
   }
   p.nch4 = (int)((V + kChunk4 - 1) / kChunk4);
@@ -152,14 +161,27 @@ sv_status launched() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_H
 
 hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;  // profiling hook
 
-template <int MODE, bool BF16, bool NEED_S, int BS>
+void record_timer(hipEvent_t e, hipStream_t st) {
+  if (g_timer_start && g_timer_stop) (void)hipEventRecord(e, st);
+}
+
+template <int MODE, bool BF16>
 void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
-  size_t dyn = (MODE == M_TRUNC) ? (size_t)(BS / kWave) * (kCapW * sizeof(Cand) + 256 * sizeof(uint32_t)) : 0;
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  hipEvent_t e0 = g_timer_start, e1 = g_timer_stop;
-  if (e0 && e1) (void)hipEventRecord(e0, st);
-  hipLaunchKernelGGL((rowpass_kernel<MODE, BF16, NEED_S, BS>), grid, dim3(BS), dyn, st, a);
-  if (e0 && e1) (void)hipEventRecord(e1, st);
+  record_timer(g_timer_start, st);
+  hipLaunchKernelGGL((rowpass_kernel<MODE, BF16, 256>), grid, dim3(256), 0, st, a);
+  record_timer(g_timer_stop, st);
+}
+
+template <bool BF16, bool NEED_S>
+void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(p.nchunks * p.rows));
+  const size_t dyn = (size_t)kStageCap * sizeof(Cand);
+  record_timer(g_timer_start, st);
+  if (p.nu == 16) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 16>), grid, dim3(kTruncBS), dyn, st, a);
+  else if (p.nu == 8) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 8>), grid, dim3(kTruncBS), dyn, st, a);
+  else hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 4>), grid, dim3(kTruncBS), dyn, st, a);
+  record_timer(g_timer_stop, st);
 }
 
 template <bool BF16>
@@ -182,10 +204,17 @@ sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, floa
   a.cap_out = p.cap_out;
   a.out = ws_at<ChunkOut>(ws, p.off_cout);
   a.cand = p.trunc ? ws_at<Cand>(ws, p.off_cand) : nullptr;
-  if (p.mode == M_SOFTMAX) launch_rowpass<M_SOFTMAX, BF16, false, 256>(p, a, st);
-  else if (p.mode == M_ARGMAX) launch_rowpass<M_ARGMAX, BF16, false, 256>(p, a, st);
-  else if (p.need_s) launch_rowpass<M_TRUNC, BF16, true, kTruncBS>(p, a, st);
-  else launch_rowpass<M_TRUNC, BF16, false, kTruncBS>(p, a, st);
+  if (p.mode == M_TRUNC) {
+    // every chunk's units must fit the registers of one workgroup
+    const int64_t epv = BF16 ? 8 : 4;
+    if (p.chunk / epv + 2 > (int64_t)p.nu * kTruncBS) return SV_ERR_UNSUPPORTED;
+    if (p.need_s) launch_trunc<BF16, true>(p, a, st);
+    else launch_trunc<BF16, false>(p, a, st);
+  } else if (p.mode == M_SOFTMAX) {
+    launch_rowpass<M_SOFTMAX, BF16>(p, a, st);
+  } else {
+    launch_rowpass<M_ARGMAX, BF16>(p, a, st);
+  }
   return launched();
 }
 
@@ -253,9 +282,9 @@ extern "C" {
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
   float c;
   if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
-  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, prm).total;
-  size_t g = make_plan(CALL_GREEDY, B, gamma, V, prm).total;
-  size_t s = make_plan(CALL_STATS, B, gamma, V, prm).total;
+  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm).total;
+  size_t g = make_plan(CALL_GREEDY, B, gamma, V, dt, prm).total;
+  size_t s = make_plan(CALL_STATS, B, gamma, V, dt, prm).total;
   return std::max(a, std::max(g, s));
 }
 
@@ -273,7 +302,7 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
   if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
     return SV_ERR_INVALID_ARG;
-  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, prm);
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int G1 = gamma + 1;
@@ -372,7 +401,7 @@ sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32
   if (out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
   if (gamma > 0 && draft_ids == nullptr) return SV_ERR_INVALID_ARG;
   sv_sampling_params prm = {1.0f, 0, 1.0f};
-  const Plan p = make_plan(CALL_GREEDY, B, gamma, V, prm);
+  const Plan p = make_plan(CALL_GREEDY, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool bf = dt == SV_BF16;
@@ -406,7 +435,7 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   if (draft_probs == nullptr || draft_ids == nullptr || !aligned16(draft_probs) || out_alpha == nullptr ||
       out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr)
     return SV_ERR_INVALID_ARG;
-  const Plan p = make_plan(CALL_STATS, B, gamma, V, prm);
+  const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool bf = dt == SV_BF16;

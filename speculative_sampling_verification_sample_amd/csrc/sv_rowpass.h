@@ -1,18 +1,30 @@
 // K1 -- the streaming pass over the logits (the HBM-bound hot loop).
 //
-// Grid nchunks * rows (chunk fastest); each workgroup reads one chunk of one logits row with
-// 16-byte loads (8 bf16 or 4 fp32 per load, 64 consecutive loads per wave)
-// and produces a ChunkOut:
+// Every workgroup reads one chunk of one logits row with 16-byte loads
+// (8 bf16 or 4 fp32 per load, 64 consecutive loads per wave) and writes a
+// ChunkOut.  The grid is linear, nchunks * rows, chunk index fastest.
+//
+// rowpass_kernel, untruncated rows:
 //   M_SOFTMAX : max and s = sum exp2(x*c - R)   (temperature softmax, [WR] §7.2)
 //   M_ARGMAX  : max and the first index holding it    (greedy, [WR] §7.1)
-//   M_TRUNC   : max, optional s (top-p needs the full-row mass), and a list of
-//               candidates that certainly contains every chunk element >= thr
-//               (top-k / top-p, [WR] §7.3).  Candidates are kept in per-wave
-//               LDS buffers; a wave whose buffer fills up runs an LDS radix
-//               select and keeps its `nw` largest; waves share the highest
-//               threshold seen (any wave's nw-th largest is a valid filter for
-//               the whole chunk).  At the end the workgroup keeps its `nout`
-//               largest (ties included) and writes them out.
+//
+// trunc_pass_kernel, rows under top-k / top-p ([WR] §7.3): max, optional s
+// (top-p needs the full-row mass) and a candidate list holding every chunk
+// element >= a threshold t0 that at least `nw` chunk elements reach.  Each
+// thread keeps the max of every unit it streams, so t0 is chosen after the
+// whole chunk is seen, and only the few units that reach it are read again:
+//   - each thread's maximum over its units is one element of the chunk;
+//   - each wave takes the ceil(nw/8)-th largest of its 64 thread maxima
+//     (distinct threads hold distinct elements, so that many elements of
+//     the wave reach it);
+//   - t0 is the lowest of the 8 wave values, which therefore at least
+//     8*ceil(nw/8) >= nw chunk elements reach.
+// Any chunk's nw-th largest is <= the row's nw-th largest, so the merged
+// lists contain every token of the row's top-k set (nw = k), and for top-p
+// the row finisher certifies that the mass above the highest chunk
+// threshold covers the nucleus.  A list longer than cap_out is trimmed to
+// the chunk's nout largest (plus ties) through LDS; one that does not fit
+// there is flagged CF_OVERFLOW and the row takes the exact path.
 #pragma once
 
 #include <type_traits>
@@ -31,9 +43,9 @@ struct RowPassArgs {
   int32_t G1;
   int32_t nchunks;
   float c;
-  int32_t nw;
-  int32_t nout;
-  int32_t cap_out;
+  int32_t nw;          // chunk elements the candidate threshold must certify
+  int32_t nout;        // entries an oversized list is trimmed to
+  int32_t cap_out;     // capacity of one chunk's list
   ChunkOut* out;  // [rows][nchunks]
   Cand* cand;     // [rows][nchunks][cap_out]
   // Optional draft gather (untruncated sampling): the workgroup whose chunk
@@ -44,157 +56,77 @@ struct RowPassArgs {
   float2* gath;
 };
 
-constexpr int kCapW = 512;  // candidate slots per wave
+constexpr int kTruncBS = 512;    // threads of the truncated-row pass
+constexpr int kStageCap = 4096;  // LDS entries for trimming an oversized list
 
-// Radix select inside one wave: the key of the `need`-th largest entry.
-template <bool BF16>
-__device__ uint32_t wave_select(const Cand* buf, int cnt, int need, uint32_t* hist) {
-  const int lane = lane_id();
-  uint32_t prefix = 0, pmask = 0;
-  constexpr int kLow = BF16 ? 16 : 0;
-  for (int shift = 24; shift >= kLow; shift -= 8) {
-    for (int k = lane; k < 256; k += kWave) hist[k] = 0;
-    wave_sync();
-    for (int i = lane; i < cnt; i += kWave) {
-      uint32_t key = f2key(buf[i].v);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    wave_sync();
-    int digit = wave_find_digit(hist, need);
-    prefix |= (uint32_t)digit << shift;
-    pmask |= 255u << shift;
-    wave_sync();
-  }
-  return prefix;
+// Geometry of the chunk a workgroup owns: flat element range [F0, F1) and
+// 16-byte unit range [U0, U1) (a unit may straddle the range ends).
+struct ChunkGeom {
+  int r, ci, b, j;
+  int64_t rowoff, e0, e1, F0, F1, U0, U1;
+};
+
+template <int EPV>
+__device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
+  ChunkGeom g;
+  const int64_t blk = blockIdx.x;
+  g.r = (int)(blk / a.nchunks);
+  g.ci = (int)(blk - (int64_t)g.r * a.nchunks);
+  g.b = g.r / a.rows_per_req;
+  g.j = g.r - g.b * a.rows_per_req;
+  g.rowoff = ((int64_t)g.b * a.G1 + g.j) * a.V;
+  g.e0 = (int64_t)g.ci * a.chunk;
+  g.e1 = min(g.e0 + a.chunk, a.V);
+  g.F0 = g.rowoff + g.e0;
+  g.F1 = g.rowoff + g.e1;
+  g.U0 = g.F0 / EPV;
+  g.U1 = (g.F1 + EPV - 1) / EPV;
+  return g;
 }
 
-// Keep entries with key >= K (in place, order preserved); returns the count.
-__device__ int wave_filter(Cand* buf, int cnt, uint32_t K) {
-  const int lane = lane_id();
-  int newcnt = 0;
-  for (int base = 0; base < cnt; base += kWave) {
-    int i = base + lane;
-    bool valid = i < cnt;
-    Cand e;
-    e.v = kNegInf;
-    e.idx = 0;
-    if (valid) e = buf[i];
-    bool keep = valid && f2key(e.v) >= K;
-    uint64_t m = ballot(keep);
-    wave_sync();
-    if (keep) buf[newcnt + lanes_below(m)] = e;
-    newcnt += (int)__popcll(m);
-    wave_sync();
-  }
-  return newcnt;
-}
-
-template <int MODE, bool BF16, bool NEED_S, int BS>
-__global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
-  constexpr int EPV = BF16 ? 8 : 4;
-  constexpr int NWV = BS / kWave;
-  constexpr bool DO_S = (MODE == M_SOFTMAX) || NEED_S;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int64_t blk = blockIdx.x;  // linear grid, chunk index fastest
-  const int r = (int)(blk / a.nchunks), ci = (int)(blk - (int64_t)r * a.nchunks);
-  const int b = r / a.rows_per_req, j = r - b * a.rows_per_req;
-  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
-  const int64_t e0 = (int64_t)ci * a.chunk;
-  const int64_t e1 = min(e0 + a.chunk, a.V);
-  const int64_t F0 = rowoff + e0, F1 = rowoff + e1;
-  const int64_t U0 = F0 / EPV, U1 = (F1 + EPV - 1) / EPV;
-  const uint4* __restrict__ base = reinterpret_cast<const uint4*>(a.logits);
-  const float c = a.c;
-
-  __shared__ uint32_t s_thr;  // shared candidate threshold (key), monotone
-  __shared__ int s_cnt[NWV];
-  __shared__ float s_xm[NWV];
-  __shared__ int s_ai[NWV];
-  __shared__ double s_s[NWV];
-  __shared__ float s_R[NWV];
-  __shared__ uint32_t s_fl[NWV];
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_digit, s_need, s_out;
-  extern __shared__ __align__(16) unsigned char s_dyn[];
-
-  Cand* wbuf = nullptr;
-  uint32_t* whist = nullptr;
-  if constexpr (MODE == M_TRUNC) {
-    wbuf = reinterpret_cast<Cand*>(s_dyn) + wid * kCapW;
-    whist = reinterpret_cast<uint32_t*>(s_dyn + (size_t)NWV * kCapW * sizeof(Cand)) + wid * 256;
-    if (tid == 0) s_thr = f2key(kLowest);
-    __syncthreads();
-  }
-
-  if (a.gath != nullptr && tid == 0 && j < a.gamma) {
-    const int d = a.ids[(int64_t)b * a.gamma + j];
-    if ((int64_t)d >= e0 && (int64_t)d < e1) {
-      float zd = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.logits)[rowoff + d] << 16)
-                      : reinterpret_cast<const float*>(a.logits)[rowoff + d];
-      a.gath[r] = make_float2(zd, a.q[((int64_t)b * a.gamma + j) * a.V + d]);
-    }
-  }
-
+// Per-thread running statistics of the units it has seen: max, the online
+// exponential sum (s, R) and NaN evidence.
+template <bool BF16, bool DO_S>
+struct UnitAcc {
+  static constexpr int EPV = BF16 ? 8 : 4;
   float xmax = kNegInf;
-  int64_t bestu = -1;
   double s = 0.0;
   float R = kNegInf;
-  uint32_t nan_words = 0;  // max of |bits| over full units (per 16-bit half for bf16)
+  uint32_t nan_words = 0;  // max of |bits| over whole units (per 16-bit half for bf16)
   uint32_t flags = 0;
-  // TRUNC state (wave-uniform)
-  int cnt = 0;
-  float thr = kLowest;
-  bool dead = false;
 
-  auto compact = [&]() {
-    uint32_t K = wave_select<BF16>(wbuf, cnt, a.nw, whist);
-    cnt = wave_filter(wbuf, cnt, K);
-    if (lane == 0) atomicMax(&s_thr, K);
-    wave_sync();
-    uint32_t Ks = max(K, __atomic_load_n(&s_thr, __ATOMIC_RELAXED));
-    thr = key2f(Ks);
-    if (cnt > kCapW - kWave) dead = true;  // ties alone fill the buffer
-  };
-
-  auto process = [&](int64_t u, const uint4& w, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    float x[EPV];
+  // Widens a unit into x and returns its max.  rel is the chunk-relative
+  // index of the unit's first element; with EDGE, elements outside [0, n)
+  // become -inf.
+  template <bool EDGE>
+  __device__ __forceinline__ float add(const uint4& w, int rel, int n, float c, float (&x)[EPV]) {
     widen<BF16>(w, x);
     if constexpr (EDGE) {
 #pragma unroll
       for (int i = 0; i < EPV; ++i) {
-        int64_t f = u * EPV + i;
-        if (f < F0 || f >= F1) x[i] = kNegInf;
+        if ((unsigned)(rel + i) >= (unsigned)n) x[i] = kNegInf;
         else if (x[i] != x[i]) flags |= CF_NAN;
       }
     } else if constexpr (!DO_S) {
       // no exp sums in this mode: NaN needs its own test (|bits| above +Inf)
       if constexpr (BF16) {
-        uint32_t m0 = w.x & 0x7fff7fffu, m1 = w.y & 0x7fff7fffu, m2 = w.z & 0x7fff7fffu, m3 = w.w & 0x7fff7fffu;
-        uint32_t lo = max(max(m0 & 0xffffu, m1 & 0xffffu), max(m2 & 0xffffu, m3 & 0xffffu));
-        uint32_t hi = max(max(m0 >> 16, m1 >> 16), max(m2 >> 16, m3 >> 16));
+        const uint32_t m0 = w.x & 0x7fff7fffu, m1 = w.y & 0x7fff7fffu, m2 = w.z & 0x7fff7fffu, m3 = w.w & 0x7fff7fffu;
+        const uint32_t lo = max(max(m0 & 0xffffu, m1 & 0xffffu), max(m2 & 0xffffu, m3 & 0xffffu));
+        const uint32_t hi = max(max(m0 >> 16, m1 >> 16), max(m2 >> 16, m3 >> 16));
         nan_words = max(nan_words, max(lo, hi));
       } else {
-        uint32_t m = max(max(w.x & 0x7fffffffu, w.y & 0x7fffffffu), max(w.z & 0x7fffffffu, w.w & 0x7fffffffu));
+        const uint32_t m = max(max(w.x & 0x7fffffffu, w.y & 0x7fffffffu), max(w.z & 0x7fffffffu, w.w & 0x7fffffffu));
         nan_words = max(nan_words, m);
       }
     }
     float vm = x[0];
 #pragma unroll
     for (int i = 1; i < EPV; ++i) vm = fmaxf(vm, x[i]);
-    if constexpr (MODE == M_ARGMAX) {
-      if (vm > xmax) {
-        xmax = vm;
-        bestu = u;
-      }
-    } else {
-      xmax = fmaxf(xmax, vm);
-    }
+    xmax = fmaxf(xmax, vm);
     if constexpr (DO_S) {
-      float vc = vm * c;
+      const float vc = vm * c;
       if (vc > R && vm < kPosInf) {
-        float Rn = ceilf(vc);
+        const float Rn = ceilf(vc);
         if (R != kNegInf) s = ldexp(s, (int)(R - Rn));
         R = Rn;
       }
@@ -214,24 +146,67 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
           if (x[i] != x[i]) flags |= CF_NAN;
       }
     }
-    if constexpr (MODE == M_TRUNC) {
-      if (ballot(vm >= thr) != 0 && !dead) {
+    return vm;
+  }
+
+  __device__ __forceinline__ void finish_flags() {
+    if constexpr (BF16) {
+      if (nan_words > 0x7f80u) flags |= CF_NAN;
+    } else {
+      if (nan_words > 0x7f800000u) flags |= CF_NAN;
+    }
+    if (xmax == kPosInf) flags |= CF_POSINF;
+  }
+};
+
+// Wave-wide merge of the (s, R) pairs in a fixed butterfly order.
+__device__ __forceinline__ void wave_sr_merge(double& s, float& R) {
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-          if (cnt > kCapW - kWave) {
-            compact();
-            if (dead) break;
-          }
-          bool p = x[i] >= thr;
-          uint64_t m = ballot(p);
-          if (p) {
-            Cand e;
-            e.v = x[i];
-            e.idx = (int32_t)(u * EPV + i - rowoff);
-            wbuf[cnt + lanes_below(m)] = e;
-          }
-          cnt += (int)__popcll(m);
-        }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double s2 = __shfl_xor(s, o, kWave);
+    const float R2 = __shfl_xor(R, o, kWave);
+    sr_merge(s, R, s2, R2);
+  }
+}
+
+template <int MODE, bool BF16, int BS>
+__global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NWV = BS / kWave;
+  constexpr bool DO_S = (MODE == M_SOFTMAX);
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const ChunkGeom g = chunk_geom<EPV>(a);
+  const uint4* __restrict__ base = reinterpret_cast<const uint4*>(a.logits);
+  const float c = a.c;
+
+  __shared__ float s_xm[NWV];
+  __shared__ int s_ai[NWV];
+  __shared__ double s_s[NWV];
+  __shared__ float s_R[NWV];
+  __shared__ uint32_t s_fl[NWV];
+
+  if (a.gath != nullptr && tid == 0 && g.j < a.gamma) {
+    const int d = a.ids[(int64_t)g.b * a.gamma + g.j];
+    if ((int64_t)d >= g.e0 && (int64_t)d < g.e1) {
+      const float zd = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.logits)[g.rowoff + d] << 16)
+                            : reinterpret_cast<const float*>(a.logits)[g.rowoff + d];
+      a.gath[g.r] = make_float2(zd, a.q[((int64_t)g.b * a.gamma + g.j) * a.V + d]);
+    }
+  }
+
+  UnitAcc<BF16, DO_S> acc;
+  int64_t bestu = -1;
+  float bestv = kNegInf;
+
+  auto process = [&](int64_t u, const uint4& w, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    float x[EPV];
+    const float vm = acc.template add<EDGE>(w, (int)(u * EPV - g.F0), (int)(g.F1 - g.F0), c, x);
+    if constexpr (MODE == M_ARGMAX) {
+      if (vm > bestv) {
+        bestv = vm;
+        bestu = u;
       }
     }
   };
@@ -239,72 +214,54 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   using Edge = std::true_type;
   using NoEdge = std::false_type;
 
-  // Block-uniform steps: step k gives thread tid the unit U0 + k*BS + tid.
-  // Every thread runs every step (lanes past the end see an all -inf unit),
-  // so the wave-wide ballots and LDS selections of M_TRUNC see whole waves.
-  // Up to kUnroll units' loads are issued before any is processed.
+  // Step k gives thread tid the unit U0 + k*BS + tid; up to kUnroll units'
+  // loads are issued before any is processed.
   constexpr int kUnroll = 8;
-  const bool aligned = (F0 % EPV == 0) && (F1 % EPV == 0);
-  const int64_t nunits = U1 - U0;
+  const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
+  const int64_t nunits = g.U1 - g.U0;
   const int64_t nsteps = (nunits + BS - 1) / BS;
   const int64_t nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
   for (int64_t k0 = 0; k0 < nsteps; k0 += kUnroll) {
     uint4 wv[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t u = U0 + (k0 + i) * BS + tid;
+      const int64_t u = g.U0 + (k0 + i) * BS + tid;
       wv[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (k0 + i < nsteps && u < U1) wv[i] = base[u];
+      if (k0 + i < nsteps && u < g.U1) wv[i] = base[u];
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       if (k0 + i >= nsteps) break;
-      const int64_t u = U0 + (k0 + i) * BS + tid;
+      const int64_t u = g.U0 + (k0 + i) * BS + tid;
       if (k0 + i < nfull) process(u, wv[i], NoEdge{});
-      else process(u, wv[i], Edge{});
+      else if (u < g.U1) process(u, wv[i], Edge{});
     }
   }
-
-  // NaN / +Inf detection
-  if constexpr (BF16) {
-    if (nan_words > 0x7f80u) flags |= CF_NAN;
-  } else {
-    if (nan_words > 0x7f800000u) flags |= CF_NAN;
-  }
-  if (xmax == kPosInf) flags |= CF_POSINF;
+  acc.finish_flags();
 
   // ---- argmax index inside the best unit ----
   int aidx = 0x7fffffff;
   if constexpr (MODE == M_ARGMAX) {
     if (bestu >= 0) {
-      uint4 w = base[bestu];
       float x[EPV];
-      widen<BF16>(w, x);
+      widen<BF16>(base[bestu], x);
 #pragma unroll
       for (int i = EPV - 1; i >= 0; --i) {
-        int64_t f = bestu * EPV + i;
-        if (f >= F0 && f < F1 && x[i] == xmax) aidx = (int)(f - rowoff);
+        const int64_t f = bestu * EPV + i;
+        if (f >= g.F0 && f < g.F1 && x[i] == bestv) aidx = (int)(f - g.rowoff);
       }
     }
   }
 
   // ---- workgroup reductions (fixed order) ----
-  float wxm = xmax;
+  float wxm = acc.xmax;
   int wai = aidx;
   if constexpr (MODE == M_ARGMAX) wave_argmax(wxm, wai);
   else wxm = wave_max(wxm);
-  if (MODE == M_TRUNC && dead) flags |= CF_OVERFLOW;
-  uint32_t wfl = wave_or(flags);
-  double ws = s;
-  float wR = R;
-  if constexpr (DO_S) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      double s2 = __shfl_xor(ws, o, kWave);
-      float R2 = __shfl_xor(wR, o, kWave);
-      sr_merge(ws, wR, s2, R2);
-    }
-  }
+  const uint32_t wfl = wave_or(acc.flags);
+  double ws = acc.s;
+  float wR = acc.R;
+  if constexpr (DO_S) wave_sr_merge(ws, wR);
   if (lane == 0) {
     s_xm[wid] = wxm;
     s_ai[wid] = wai;
@@ -312,31 +269,223 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     s_R[wid] = wR;
     s_fl[wid] = wfl;
   }
+  __syncthreads();
+  if (tid == 0) {
+    float xm = s_xm[0];
+    int ai = s_ai[0];
+    uint32_t fl = s_fl[0];
+    double ss = s_s[0];
+    float RR = s_R[0];
+    for (int k = 1; k < NWV; ++k) {
+      if constexpr (MODE == M_ARGMAX) argmax_merge(xm, ai, s_xm[k], s_ai[k]);
+      else xm = fmaxf(xm, s_xm[k]);
+      fl |= s_fl[k];
+      if constexpr (DO_S) sr_merge(ss, RR, s_s[k], s_R[k]);
+    }
+    if (MODE == M_ARGMAX && xm == kNegInf) ai = (int)g.e0;  // all -inf: first element
+    ChunkOut o;
+    o.xmax = xm;
+    o.argmax = (MODE == M_ARGMAX) ? ai : -1;
+    o.thr = kLowest;
+    o.ncand = 0;
+    o.s = DO_S ? ss : 0.0;
+    o.Rs = DO_S ? RR : kNegInf;
+    o.flags = fl;
+    a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
+  }
+}
 
-  if constexpr (MODE == M_TRUNC) {
-    // Final candidate set of the chunk.
+// Truncated rows: a streaming pass that keeps only the max of each of the
+// thread's NU units (the chunk has at most NU * kTruncBS units, checked by
+// the host).  Once t0 is known, the units whose max reaches it (a few per
+// cent) are listed in LDS and read again -- from cache, moments after the
+// first read -- to cut the candidates.
+template <bool BF16, bool NEED_S, int NU>
+__global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
+  constexpr int BS = kTruncBS;
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NWV = BS / kWave;
+  constexpr int kUnroll = NU < 8 ? NU : 8;
+  constexpr int kListCap = 2 * BS;  // listed units: each thread re-reads at most two
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const ChunkGeom g = chunk_geom<EPV>(a);
+  const uint4* __restrict__ base = reinterpret_cast<const uint4*>(a.logits);
+  const float c = a.c;
+
+  __shared__ float s_xm[NWV];
+  __shared__ double s_s[NWV];
+  __shared__ float s_R[NWV];
+  __shared__ uint32_t s_fl[NWV], s_kw[NWV];
+  __shared__ int s_tot[NWV];
+  __shared__ int s_list[kListCap];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_nl, s_digit, s_need, s_out;
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  Cand* stage = reinterpret_cast<Cand*>(s_dyn);  // kStageCap entries
+
+  if (tid == 0) s_nl = 0;
+
+  // ---- streaming pass: statistics and per-unit maxima ----
+  // Unit k of this thread is unit k*BS + tid of the chunk; its first
+  // element has the chunk-relative index rel0 + k*BS*EPV (the chunk holds
+  // elements [0, n); rel0 >= -(EPV-1)).
+  const int n = (int)(g.F1 - g.F0);
+  const int nunits = (int)(g.U1 - g.U0);
+  const int relu = (int)(g.U0 * EPV - g.F0);  // relative index of unit 0's first element
+  const int rel0 = relu + tid * EPV;
+  const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
+  const int nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
+  UnitAcc<BF16, NEED_S> acc;
+  float um[NU];
+#pragma unroll
+  for (int k0 = 0; k0 < NU; k0 += kUnroll) {
+    uint4 wv[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) wv[i] = base[g.U0 + min((k0 + i) * BS + tid, nunits - 1)];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int k = k0 + i;
+      const int ul = k * BS + tid;
+      const int rel = rel0 + k * BS * EPV;
+      float x[EPV];
+      um[k] = kNegInf;
+      if (k < nfull) {
+        um[k] = acc.template add<false>(wv[i], rel, n, c, x);
+      } else if (ul < nunits) {
+        if (aligned || (ul > 0 && ul + 1 < nunits)) um[k] = acc.template add<false>(wv[i], rel, n, c, x);
+        else um[k] = acc.template add<true>(wv[i], rel, n, c, x);
+      }
+    }
+  }
+  acc.finish_flags();
+
+  // ---- this wave's ceil(nw/NWV)-th largest thread maximum (bitwise
+  //      search on order-preserving keys) ----
+  const int kw = (a.nw + NWV - 1) / NWV;
+  const uint32_t tkey = f2key(acc.xmax);
+  uint32_t K = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = K | (1u << bit);
+    if ((int)__popcll(ballot(tkey >= cand)) >= kw) K = cand;
+  }
+
+  const float wxm = wave_max(acc.xmax);
+  const uint32_t wfl = wave_or(acc.flags);
+  double ws = acc.s;
+  float wR = acc.R;
+  if constexpr (NEED_S) wave_sr_merge(ws, wR);
+  if (lane == 0) {
+    s_xm[wid] = wxm;
+    s_s[wid] = ws;
+    s_R[wid] = wR;
+    s_fl[wid] = wfl;
+    s_kw[wid] = K;
+  }
+  __syncthreads();
+  uint32_t t0key = s_kw[0];
+  for (int k = 1; k < NWV; ++k) t0key = min(t0key, s_kw[k]);
+  t0key = max(t0key, f2key(kLowest));  // -inf logits never become candidates
+  const float t0 = key2f(t0key);
+
+  // ---- list the units whose max reaches t0 (units past the chunk have
+  //      um = -inf < t0) ----
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const bool p = um[k] >= t0;
+    const uint64_t m = ballot(p);
+    if (m != 0) {
+      int bp = 0;
+      if (lane == 0) bp = atomicAdd(&s_nl, (int)__popcll(m));
+      bp = __shfl(bp, 0, kWave);
+      const int slot = bp + lanes_below(m);
+      if (p && slot < kListCap) s_list[slot] = k * BS + tid;
+    }
+  }
+  __syncthreads();
+  const int nl = s_nl;
+
+  Cand* dst = a.cand + ((int64_t)g.r * a.nchunks + g.ci) * a.cap_out;
+  uint32_t Kc = t0key;
+  int nout_written = 0;
+  uint32_t extra = 0;
+  if (nl > kListCap) {
+    extra = CF_OVERFLOW;  // ties fill too many units: exact path
+  } else {
+    // ---- re-read the listed units, count, place and emit ----
+    uint4 lw[2];
+    int lrel[2];
+    int nc = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = r * BS + tid;
+      lrel[r] = 0;
+      lw[r] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < nl) {
+        const int ul = s_list[i];
+        lw[r] = base[g.U0 + ul];
+        lrel[r] = relu + ul * EPV;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r * BS + tid < nl) {
+        float x[EPV];
+        widen<BF16>(lw[r], x);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) nc += (x[e] >= t0 && (unsigned)(lrel[r] + e) < (unsigned)n) ? 1 : 0;
+      }
+    }
+    const int incl = wave_incl_scan_i(nc);
+    if (lane == kWave - 1) s_tot[wid] = incl;
     __syncthreads();
-    uint32_t Ks = s_thr;
-    cnt = wave_filter(wbuf, cnt, Ks);
-    if (lane == 0) s_cnt[wid] = cnt;
-    __syncthreads();
-    int total = 0;
-    for (int k = 0; k < NWV; ++k) total += s_cnt[k];
-    uint32_t Kc = Ks;
-    if (total > a.nout) {
+    int pos = incl - nc, total = 0;
+    for (int k = 0; k < NWV; ++k) {
+      const int t = s_tot[k];
+      if (k < wid) pos += t;
+      total += t;
+    }
+
+    const bool direct = total <= a.cap_out;
+    if (direct || total <= kStageCap) {
+      // straight into the chunk's list, or into LDS for trimming
+      Cand* to = direct ? dst : stage;
+      const int id0 = (int)g.e0;  // token id of chunk element 0
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (r * BS + tid < nl) {
+          float x[EPV];
+          widen<BF16>(lw[r], x);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            if (x[e] >= t0 && (unsigned)(lrel[r] + e) < (unsigned)n) {
+              Cand ce;
+              ce.v = x[e];
+              ce.idx = id0 + lrel[r] + e;
+              to[pos++] = ce;
+            }
+          }
+        }
+      }
+    }
+    if (direct) {
+      nout_written = total;
+    } else if (total <= kStageCap) {
+      // trim to the nout largest (ties at the cut kept)
+      __syncthreads();
       uint32_t prefix = 0, pmask = 0;
       int need = a.nout;
       constexpr int kLow = BF16 ? 16 : 0;
       for (int shift = 24; shift >= kLow; shift -= 8) {
         if (tid < 256) s_hist[tid] = 0;
         __syncthreads();
-        for (int i = lane; i < cnt; i += kWave) {
-          uint32_t key = f2key(wbuf[i].v);
+        for (int i = tid; i < total; i += BS) {
+          const uint32_t key = f2key(stage[i].v);
           if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
         if (wid == 0) {
-          int d = wave_find_digit(s_hist, need);
+          const int d = wave_find_digit(s_hist, need);
           if (lane == 0) {
             s_digit = d;
             s_need = need;
@@ -349,71 +498,48 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
         __syncthreads();
       }
       Kc = prefix;
-    }
-    if (tid == 0) s_out = 0;
-    __syncthreads();
-    Cand* dst = a.cand + ((int64_t)r * a.nchunks + ci) * a.cap_out;
-    for (int bse = 0; bse < cnt; bse += kWave) {
-      int i = bse + lane;
-      bool keep = i < cnt && f2key(wbuf[i].v) >= Kc;
-      uint64_t m = ballot(keep);
-      int basepos = 0;
-      if (lane == 0 && m) basepos = atomicAdd(&s_out, (int)__popcll(m));
-      basepos = __shfl(basepos, 0, kWave);
-      int pos = basepos + lanes_below(m);
-      if (keep && pos < a.cap_out) dst[pos] = wbuf[i];
-    }
-    __syncthreads();
-    if (tid == 0) {
-      ChunkOut o;
-      float xm = s_xm[0];
-      uint32_t fl = s_fl[0];
-      double ss = s_s[0];
-      float RR = s_R[0];
-      for (int k = 1; k < NWV; ++k) {
-        xm = fmaxf(xm, s_xm[k]);
-        fl |= s_fl[k];
-        if constexpr (NEED_S) sr_merge(ss, RR, s_s[k], s_R[k]);
+      if (tid == 0) s_out = 0;
+      __syncthreads();
+      for (int bse = 0; bse < total; bse += BS) {
+        const int i = bse + tid;
+        const bool keep = i < total && f2key(stage[i].v) >= Kc;
+        const uint64_t m = ballot(keep);
+        int bp = 0;
+        if (lane == 0 && m) bp = atomicAdd(&s_out, (int)__popcll(m));
+        bp = __shfl(bp, 0, kWave);
+        const int p = bp + lanes_below(m);
+        if (keep && p < a.cap_out) dst[p] = stage[i];
       }
-      int no = s_out;
-      if (no > a.cap_out) {
-        fl |= CF_OVERFLOW;
-        no = a.cap_out;
+      __syncthreads();
+      nout_written = s_out;
+      if (nout_written > a.cap_out) {
+        extra = CF_OVERFLOW;
+        nout_written = a.cap_out;
       }
-      o.xmax = xm;
-      o.argmax = -1;
-      o.thr = key2f(Kc);
-      o.ncand = no;
-      o.s = NEED_S ? ss : 0.0;
-      o.Rs = NEED_S ? RR : kNegInf;
-      o.flags = fl;
-      a.out[(int64_t)r * a.nchunks + ci] = o;
+    } else {
+      extra = CF_OVERFLOW;  // ties alone exceed the staging room
     }
-  } else {
-    __syncthreads();
-    if (tid == 0) {
-      float xm = s_xm[0];
-      int ai = s_ai[0];
-      uint32_t fl = s_fl[0];
-      double ss = s_s[0];
-      float RR = s_R[0];
-      for (int k = 1; k < NWV; ++k) {
-        if constexpr (MODE == M_ARGMAX) argmax_merge(xm, ai, s_xm[k], s_ai[k]);
-        else xm = fmaxf(xm, s_xm[k]);
-        fl |= s_fl[k];
-        if constexpr (DO_S) sr_merge(ss, RR, s_s[k], s_R[k]);
-      }
-      if (MODE == M_ARGMAX && xm == kNegInf) ai = (int)e0;  // all -inf: first element
-      ChunkOut o;
-      o.xmax = xm;
-      o.argmax = (MODE == M_ARGMAX) ? ai : -1;
-      o.thr = kLowest;
-      o.ncand = 0;
-      o.s = DO_S ? ss : 0.0;
-      o.Rs = DO_S ? RR : kNegInf;
-      o.flags = fl;
-      a.out[(int64_t)r * a.nchunks + ci] = o;
+  }
+
+  if (tid == 0) {
+    float xm = s_xm[0];
+    uint32_t fl = s_fl[0] | extra;
+    double ss = s_s[0];
+    float RR = s_R[0];
+    for (int k = 1; k < NWV; ++k) {
+      xm = fmaxf(xm, s_xm[k]);
+      fl |= s_fl[k];
+      if constexpr (NEED_S) sr_merge(ss, RR, s_s[k], s_R[k]);
     }
+    ChunkOut o;
+    o.xmax = xm;
+    o.argmax = -1;
+    o.thr = key2f(Kc);
+    o.ncand = nout_written;
+    o.s = NEED_S ? ss : 0.0;
+    o.Rs = NEED_S ? RR : kNegInf;
+    o.flags = fl;
+    a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
   }
 }
 

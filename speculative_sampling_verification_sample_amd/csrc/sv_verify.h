@@ -1008,17 +1008,53 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   if (!(ri.flags & RF_NONFINITE)) {
     const bool big = (ri.flags & RF_BIG) != 0;
     const double invS = 1.0 / ri.S;
-    for (int64_t x = x0 + tid; x < x1; x += 256) {
-      double qv = (double)a.q[qrowo + x];
-      if (big) {
-        float z = load_logit<BF16>(a.logits, lrow + x);
-        double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
-        double d = p - qv;
-        mn += fmin(p, qv);
-        if (d > 0.0) pq += d;
-        if (d < 0.0) qp -= d;
-      } else {
-        sq += qv;
+    // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
+    const bool vec = (a.V & 7) == 0;
+    constexpr int kU = 4;
+    const int64_t ngroups = (x1 - x0 + 7) / 8;
+    for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kU * 256) {
+      float qv[kU][8], zv[kU][8];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
+        if (vec && x + 8 <= x1) {
+          const uint4* qp4 = reinterpret_cast<const uint4*>(a.q + qrowo + x);
+          widen<false>(qp4[0], qv[u]);
+          widen<false>(qp4[1], qv[u] + 4);
+          if (big) {
+            if constexpr (BF16) {
+              widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
+            } else {
+              const uint4* zp4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + x);
+              widen<false>(zp4[0], zv[u]);
+              widen<false>(zp4[1], zv[u] + 4);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const bool in = x + k < x1;
+            qv[u][k] = in ? a.q[qrowo + x + k] : 0.0f;
+            zv[u][k] = (in && big) ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const double qd = (double)qv[u][k];
+          if (big) {
+            const float z = zv[u][k];
+            const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
+            const double d = p - qd;
+            mn += fmin(p, qd);
+            if (d > 0.0) pq += d;
+            if (d < 0.0) qp -= d;
+          } else {
+            sq += qd;
+          }
+        }
       }
     }
   }
