@@ -196,17 +196,23 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   }
 
   UnitAcc<BF16, DO_S> acc;
-  int64_t bestu = -1;
   float bestv = kNegInf;
+  int aidx = 0x7fffffff;  // row index of this thread's first maximum
 
   auto process = [&](int64_t u, const uint4& w, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     float x[EPV];
     const float vm = acc.template add<EDGE>(w, (int)(u * EPV - g.F0), (int)(g.F1 - g.F0), c, x);
     if constexpr (MODE == M_ARGMAX) {
+      // units arrive in increasing order, so a strictly larger max is the
+      // only case that moves the first maximum; rare after the first units
       if (vm > bestv) {
         bestv = vm;
-        bestu = u;
+        int first = 0;
+#pragma unroll
+        for (int i = EPV - 1; i >= 0; --i)
+          if (x[i] == vm) first = i;
+        aidx = (int)(u * EPV + first - g.rowoff);
       }
     }
   };
@@ -238,20 +244,6 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     }
   }
   acc.finish_flags();
-
-  // ---- argmax index inside the best unit ----
-  int aidx = 0x7fffffff;
-  if constexpr (MODE == M_ARGMAX) {
-    if (bestu >= 0) {
-      float x[EPV];
-      widen<BF16>(base[bestu], x);
-#pragma unroll
-      for (int i = EPV - 1; i >= 0; --i) {
-        const int64_t f = bestu * EPV + i;
-        if (f >= g.F0 && f < g.F1 && x[i] == bestv) aidx = (int)(f - g.rowoff);
-      }
-    }
-  }
 
   // ---- workgroup reductions (fixed order) ----
   float wxm = acc.xmax;
@@ -295,13 +287,13 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   }
 }
 
-// Truncated rows: a streaming pass that keeps only the max of each of the
-// thread's NU units (the chunk has at most NU * kTruncBS units, checked by
-// the host).  Once t0 is known, the units whose max reaches it (a few per
-// cent) are listed in LDS and read again -- from cache, moments after the
-// first read -- to cut the candidates.
+// Truncated rows: a streaming pass that keeps the max of each of the
+// thread's NU units and the data of its best unit (the chunk has at most
+// NU * kTruncBS units, checked by the host).  Once t0 is known, the best
+// units cut their candidates from registers; the other units whose max
+// reaches t0 (a fraction of a per cent) are listed in LDS and read again.
 template <bool BF16, bool NEED_S, int NU>
-__global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
+__global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) {
   constexpr int BS = kTruncBS;
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NWV = BS / kWave;
@@ -338,6 +330,11 @@ __global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
   const int nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
   UnitAcc<BF16, NEED_S> acc;
   float um[NU];
+  // The thread's best unit stays in registers: most units that reach t0
+  // are their thread's best, so few need a second read.
+  uint4 bw = make_uint4(0u, 0u, 0u, 0u);
+  float bestv = kNegInf;
+  int bestk = -1;
 #pragma unroll
   for (int k0 = 0; k0 < NU; k0 += kUnroll) {
     uint4 wv[kUnroll];
@@ -355,6 +352,11 @@ __global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
       } else if (ul < nunits) {
         if (aligned || (ul > 0 && ul + 1 < nunits)) um[k] = acc.template add<false>(wv[i], rel, n, c, x);
         else um[k] = acc.template add<true>(wv[i], rel, n, c, x);
+      }
+      if (um[k] > bestv) {
+        bestv = um[k];
+        bestk = k;
+        bw = wv[i];
       }
     }
   }
@@ -388,11 +390,11 @@ __global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
   t0key = max(t0key, f2key(kLowest));  // -inf logits never become candidates
   const float t0 = key2f(t0key);
 
-  // ---- list the units whose max reaches t0 (units past the chunk have
-  //      um = -inf < t0) ----
+  // ---- list the other units whose max reaches t0 (units past the chunk
+  //      have um = -inf < t0) ----
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const bool p = um[k] >= t0;
+    const bool p = um[k] >= t0 && k != bestk;
     const uint64_t m = ballot(p);
     if (m != 0) {
       int bp = 0;
@@ -412,24 +414,30 @@ __global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
   if (nl > kListCap) {
     extra = CF_OVERFLOW;  // ties fill too many units: exact path
   } else {
-    // ---- re-read the listed units, count, place and emit ----
-    uint4 lw[2];
-    int lrel[2];
+    // ---- the best unit (slot 0) and up to two re-read listed units,
+    //      counted, placed and emitted ----
+    uint4 lw[3];
+    int lrel[3];
+    bool lon[3];
     int nc = 0;
+    lw[0] = bw;
+    lrel[0] = rel0 + bestk * BS * EPV;
+    lon[0] = bestk >= 0 && bestv >= t0;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = r * BS + tid;
+    for (int r = 1; r < 3; ++r) {
+      const int i = (r - 1) * BS + tid;
       lrel[r] = 0;
       lw[r] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < nl) {
+      lon[r] = i < nl;
+      if (lon[r]) {
         const int ul = s_list[i];
         lw[r] = base[g.U0 + ul];
         lrel[r] = relu + ul * EPV;
       }
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if (r * BS + tid < nl) {
+    for (int r = 0; r < 3; ++r) {
+      if (lon[r]) {
         float x[EPV];
         widen<BF16>(lw[r], x);
 #pragma unroll
@@ -452,8 +460,8 @@ __global__ void __launch_bounds__(kTruncBS) trunc_pass_kernel(RowPassArgs a) {
       Cand* to = direct ? dst : stage;
       const int id0 = (int)g.e0;  // token id of chunk element 0
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        if (r * BS + tid < nl) {
+      for (int r = 0; r < 3; ++r) {
+        if (lon[r]) {
           float x[EPV];
           widen<BF16>(lw[r], x);
 #pragma unroll
