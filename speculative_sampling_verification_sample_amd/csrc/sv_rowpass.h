@@ -85,13 +85,20 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
 }
 
 // Per-thread running statistics of the units it has seen: max, the online
-// exponential sum (s, R) and NaN evidence.
+// exponential sum (s, R) and NaN evidence.  Unit sums collect in a float
+// partial `sb` (at most 64 elements, each <= 1, between flushes) that is
+// folded into the double `s` by flush() and before every rescale.
 template <bool BF16, bool DO_S>
 struct UnitAcc {
   static constexpr int EPV = BF16 ? 8 : 4;
   float xmax = kNegInf;
   double s = 0.0;
-  float R = kNegInf;
+  float sb = 0.0f;
+  float R = kNegInf;  // integral reference; -inf until a finite value is seen
+  // Reference the exponentials use: R once it exists, before that a huge
+  // finite value, so finite logits add exactly 0 while NaN still reaches s
+  // (and +Inf, which the row flags anyway, makes s infinite).
+  float Re = 0x1p126f;
   uint32_t nan_words = 0;  // max of |bits| over whole units (per 16-bit half for bf16)
   uint32_t flags = 0;
 
@@ -127,29 +134,38 @@ struct UnitAcc {
       const float vc = vm * c;
       if (vc > R && vm < kPosInf) {
         const float Rn = ceilf(vc);
+        s += (double)sb;
         if (R != kNegInf) s = ldexp(s, (int)(R - Rn));
+        sb = 0.0f;
         R = Rn;
+        Re = Rn;
       }
-      if (R != kNegInf) {
-        // a NaN logit turns s into NaN, which the row merge reports
-        float ev[EPV];
+      // a NaN logit turns s into NaN, which the row merge reports
+      float ev[EPV];
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) ev[i] = e_of(x[i], c, R);
-        float t;
-        if constexpr (EPV == 8) t = ((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7]));
-        else t = (ev[0] + ev[1]) + (ev[2] + ev[3]);
-        s += (double)t;
-      } else {
-        // nothing finite seen yet by this thread: test this unit directly
-#pragma unroll
-        for (int i = 0; i < EPV; ++i)
-          if (x[i] != x[i]) flags |= CF_NAN;
-      }
+      for (int i = 0; i < EPV; ++i) ev[i] = e_of(x[i], c, Re);
+      float t;
+      if constexpr (EPV == 8) t = ((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7]));
+      else t = (ev[0] + ev[1]) + (ev[2] + ev[3]);
+      sb += t;
     }
     return vm;
   }
 
+  __device__ __forceinline__ void flush() {
+    if constexpr (DO_S) {
+      s += (double)sb;
+      sb = 0.0f;
+    }
+  }
+
+  // After the last flush().
   __device__ __forceinline__ void finish_flags() {
+    // merges drop sums without a reference: keep the evidence they carry
+    // (only NaN or +Inf logits make such a sum nonzero)
+    if constexpr (DO_S) {
+      if (R == kNegInf && s != 0.0) flags |= CF_NAN;
+    }
     if constexpr (BF16) {
       if (nan_words > 0x7f80u) flags |= CF_NAN;
     } else {
@@ -159,14 +175,15 @@ struct UnitAcc {
   }
 };
 
-// Wave-wide merge of the (s, R) pairs in a fixed butterfly order.
+// Wave-wide merge of the (s, R) pairs: every lane's s is moved to the
+// wave's largest reference by an exact power-of-two scaling, then summed in
+// a fixed butterfly order.
 __device__ __forceinline__ void wave_sr_merge(double& s, float& R) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double s2 = __shfl_xor(s, o, kWave);
-    const float R2 = __shfl_xor(R, o, kWave);
-    sr_merge(s, R, s2, R2);
-  }
+  const float Rm = wave_max(R);
+  double sl = 0.0;
+  if (R != kNegInf) sl = ldexp(s, (int)(R - Rm));
+  s = wave_sum_d(sl);
+  R = Rm;
 }
 
 template <int MODE, bool BF16, int BS>
@@ -242,6 +259,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
       if (k0 + i < nfull) process(u, wv[i], NoEdge{});
       else if (u < g.U1) process(u, wv[i], Edge{});
     }
+    acc.flush();
   }
   acc.finish_flags();
 
@@ -359,6 +377,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
         bw = wv[i];
       }
     }
+    acc.flush();
   }
   acc.finish_flags();
 

@@ -203,6 +203,31 @@ def test_flags():
     compare_greedy(w3, label="greedy nan")
 
 
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_nonfinite_rows(name):
+    """NaN where no finite value precedes it in a thread's share of the row
+    (whole row, long prefix), NaN as the last element, and an all -inf row
+    holding one NaN: every such request is flagged in all three row-pass
+    variants (fp32 untruncated, bf16 top-k, bf16 top-p) and in the
+    statistics."""
+    w = generate(name, DEV, B=6, gamma=2, V=20000)
+    lg = w.logits.clone()
+    nan, ninf = float("nan"), float("-inf")
+    lg[0, 0, :] = nan             # whole row
+    lg[1, 1, :9000] = nan         # long prefix, finite afterwards
+    lg[2, 2, -1] = nan            # last element of the bonus row
+    lg[3, 0, :] = ninf
+    lg[3, 0, 12345] = nan         # NaN among -inf only
+    lg[4, 1, 4096:4104] = nan     # one whole 16-byte unit (bf16) / two (fp32)
+    w.logits = lg.contiguous()
+    o, _ = compare_sample(w, label=f"nonfinite {name}")
+    fl = o["flags"]
+    for b in range(5):
+        assert fl[b] == oracle.FLAG_NONFINITE, (b, fl[b])
+    assert fl[5] & oracle.FLAG_NONFINITE == 0
+    compare_stats(w, label=f"stats nonfinite {name}")
+
+
 def test_determinism():
     for name, kw in (("c5", dict(B=4)), ("c2", dict(B=8)), ("c3", dict(B=6))):
         w = generate(name, DEV, **kw)
