@@ -1,11 +1,11 @@
 // C ABI of the verify step: argument validation, workspace layout and the
 // launch sequence of the kernels on the caller's stream.
 //
-//   sample : K1 row pass -> [truncation: K2 row finalisation -> exact
-//            fallback] -> K3 acceptance + list draws -> K4 full-row draws
-//            (chunk totals, then the per-request search)
+//   sample : K1 row pass -> [truncation: K2 row finalisation, with the
+//            exact path inside] -> K3 acceptance + list draws -> K4
+//            full-row draws (chunk totals, then the per-request search)
 //   greedy : K1 row pass (argmax) -> greedy scan
-//   stats  : K1 -> K2 -> (fallback) -> per-chunk sums -> per-row finish
+//   stats  : K1 -> K2 -> per-chunk sums -> per-row finish
 //
 // Nothing here allocates or frees device memory: every scratch buffer is a
 // slice of the caller's workspace.
@@ -259,13 +259,7 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const float* q, const 
   set_kernel_attrs();
   size_t dyn = p.trunc ? (size_t)p.um * 16 : 0;  // key, id, fixed-point mass per entry
   hipLaunchKernelGGL((rowfinal_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), dyn, st, a);
-  sv_status s = launched();
-  if (s != SV_OK) return s;
-  if (p.trunc) {
-    hipLaunchKernelGGL((rowslow_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), 0, st, a);
-    s = launched();
-  }
-  return s;
+  return launched();
 }
 
 sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamma, int32_t V) {
@@ -341,11 +335,10 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   ac.jobs = ws_at<BigJob>(workspace, p.off_jobs);
   const dim3 agrid((unsigned)((B + 3) / 4));
   if (p.trunc) {
-    // kept lists (and the rare oversized kept set) are drawn inside K3; each
-    // wave sorts its list by token id in LDS first
-    const size_t dyn = 4 * (size_t)kKMax * sizeof(Cand);
-    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), dyn, st, ac);
-    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), dyn, st, ac);
+    // kept lists (stored in token-id order) and the rare oversized kept set
+    // are drawn inside K3
+    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), 0, st, ac);
+    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), 0, st, ac);
     return launched();
   }
 
@@ -469,8 +462,7 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
   s = launched();
   if (s != SV_OK) return s;
-  const size_t sdyn = p.trunc ? 4 * (size_t)kKMax * sizeof(Cand) : 0;
-  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), sdyn, st, a);
+  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
   return launched();
 }
 

@@ -28,7 +28,6 @@ constexpr uint32_t CF_POSINF = 2u;    // a +Inf logit was seen
 constexpr uint32_t CF_OVERFLOW = 4u;  // candidate buffer could not hold the ties
 
 constexpr uint32_t RF_NONFINITE = 1u;  // row unusable (NaN / +Inf / all -Inf)
-constexpr uint32_t RF_SLOW = 2u;       // truncation needs the exact multi-pass kernel
 constexpr uint32_t RF_BIG = 4u;        // kept set not stored as a list: full-row passes
 
 // Per (row, chunk) result of the streaming pass.

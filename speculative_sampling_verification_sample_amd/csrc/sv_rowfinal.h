@@ -269,164 +269,10 @@ __device__ __forceinline__ int wave_append_slot(bool keep, int* counter) {
   return base + lanes_below(m);
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
-  const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
-  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
-  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
-
-  __shared__ float s_xm, s_th, s_R;
-  __shared__ double s_S;
-  __shared__ uint32_t s_fl;
-  __shared__ int s_n, s_dn[2];
-  __shared__ uint32_t hist[256];
-  __shared__ unsigned long long mh[256], s_u64[4], s_above;
-  extern __shared__ __align__(16) unsigned char s_dyn[];
-  // union entries: keys, token ids, fixed-point masses
-  uint32_t* keys = reinterpret_cast<uint32_t*>(s_dyn);
-  int32_t* idxs = reinterpret_cast<int32_t*>(s_dyn + (size_t)a.um * 4);
-  unsigned long long* mass = reinterpret_cast<unsigned long long*>(s_dyn + (size_t)a.um * 8);
-
-  if (tid == 0) {
-    RowMerge m = merge_chunks(a.cout + r * a.nchunks, a.nchunks, a.c);
-    s_xm = m.xmax;
-    s_th = m.thr;
-    s_fl = m.flags;
-    s_R = m.R;
-    s_S = m.S;
-    s_n = 0;
-  }
-  __syncthreads();
-  RowInfo ri;
-  ri.S = s_S;
-  ri.R = s_R;
-  ri.tau = kLowest;
-  ri.nkept = -1;
-  ri.flags = 0;
-  ri.ed = 0.0f;
-  ri.qd = 0.0f;
-  ri.d = -1;
-  ri.pad = 0;
-  const uint32_t fl = s_fl;
-  if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf) || (s_S != s_S)) {
-    if (tid == 0) {
-      ri.flags = RF_NONFINITE;
-      a.info[r] = ri;
-    }
-    return;
-  }
-  if (!a.trunc) {
-    if (tid == 0) {
-      ri.flags = RF_BIG;
-      gather_draft<BF16>(a, b, j, rowoff, ri);
-      a.info[r] = ri;
-    }
-    return;
-  }
-  if ((fl & CF_OVERFLOW) || !a.fast) {
-    if (tid == 0) {
-      ri.flags = RF_SLOW;
-      a.info[r] = ri;
-    }
-    return;
-  }
-
-  // ---- candidate union (entries >= the highest chunk threshold) ----
-  const float theta = s_th;
-  const float R = s_R;
-  const Cand* cd = a.cand + r * a.nchunks * (int64_t)a.cap_out;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const int nc = a.cout[r * a.nchunks + c].ncand;
-    for (int i0 = 0; i0 < nc; i0 += 256) {
-      const int i = i0 + tid;
-      Cand e;
-      e.v = kNegInf;
-      e.idx = 0;
-      if (i < nc) e = cd[(int64_t)c * a.cap_out + i];
-      const bool keep = i < nc && e.v >= theta;
-      const int pos = wave_append_slot(keep, &s_n);
-      if (keep && pos < a.um) {
-        keys[pos] = f2key(e.v);
-        idxs[pos] = e.idx;
-        mass[pos] = to_fixed(e_of(e.v, a.c, R));
-      }
-    }
-  }
-  __syncthreads();
-  const int nu = s_n;
-  if (nu > a.um) {
-    if (tid == 0) {
-      ri.flags = RF_SLOW;
-      a.info[r] = ri;
-    }
-    return;
-  }
-
-  // ---- thresholds ----
-  const bool topk = a.top_k > 0 && (int64_t)a.top_k < a.V;
-  const bool topp = a.top_p < 1.0f;
-  uint32_t kfloor = 0;  // keys below this are outside the top-k set
-  if (topk && nu >= a.top_k) kfloor = block_select_count<BF16>(keys, nu, a.top_k, hist, s_dn);
-  auto mass_from = [&](uint32_t kf) -> unsigned long long {
-    unsigned long long part = 0ull;
-    for (int i = tid; i < nu; i += 256)
-      if (keys[i] >= kf) part += mass[i];
-    return block_sum_u64(part, s_u64);
-  };
-  uint32_t kfinal = kfloor;
-  const double scale = 1099511627776.0;  // 2^40
-  if (topp) {
-    const double Sref = topk ? (double)mass_from(kfloor) : s_S * scale;
-    const double target = (double)a.top_p * Sref;
-    uint32_t kp;
-    if (block_select_mass<BF16>(keys, mass, nu, kfloor, target, mh, s_dn, &s_above, kp)) {
-      kfinal = kp;
-    } else if (!(topk || theta == kLowest)) {
-      // the crossing lies below the certified candidates: exact path
-      if (tid == 0) {
-        ri.flags = RF_SLOW;
-        a.info[r] = ri;
-      }
-      return;
-    }  // else rounding: keep the whole base set
-  }
-  const unsigned long long Sfx = mass_from(kfinal);
-  ri.S = (double)Sfx / scale;
-  ri.tau = key2f(kfinal);
-  if (kfinal == 0) ri.tau = kLowest;
-  // ---- kept list (token order is restored by the sampler when needed) ----
-  if (tid == 0) s_n = 0;
-  __syncthreads();
-  Cand* out = a.kept + r * (int64_t)a.kmax;
-  for (int i0 = 0; i0 < nu; i0 += 256) {
-    const int i = i0 + tid;
-    const bool keep = i < nu && keys[i] >= kfinal;
-    const int pos = wave_append_slot(keep, &s_n);
-    if (keep && pos < a.kmax) {
-      Cand e;
-      e.idx = idxs[i];
-      e.v = e_of(key2f(keys[i]), a.c, R);
-      out[pos] = e;
-    }
-  }
-  __syncthreads();
-  const int nkept = s_n;
-  if (tid == 0) {
-    if (nkept > a.kmax) {
-      ri.flags = RF_BIG;
-      ri.nkept = -1;
-    } else {
-      ri.nkept = nkept;
-    }
-    gather_draft<BF16>(a, b, j, rowoff, ri);
-    a.info[r] = ri;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Exact multi-pass path (rows flagged RF_SLOW): radix selection over the row
-// in global memory.  top-k selects by count over order-preserving keys;
+// Exact multi-pass path for rows the candidate lists cannot settle (run by
+// the row finisher's workgroup): radix selection over the row in global
+// memory.  top-k selects by count over order-preserving keys;
 // top-p selects by mass with a fixed-point histogram (integer atomics, so the
 // result does not depend on the order of the additions).
 // ---------------------------------------------------------------------------
@@ -443,15 +289,10 @@ __device__ double block_sum_d(double v, double* s_tmp) {
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(256) rowslow_kernel(RowFinalArgs a) {
+__device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_t rowoff, RowInfo ri) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int64_t r = blockIdx.x;
-  if (!(a.info[r].flags & RF_SLOW)) return;
-  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
-  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
   const int64_t V = a.V;
   const float c = a.c;
-  RowInfo ri = a.info[r];
   const float R = ri.R;
 
   __shared__ uint32_t hist[256];
@@ -613,6 +454,181 @@ __global__ void __launch_bounds__(256) rowslow_kernel(RowFinalArgs a) {
     ri.nkept = nkept;
   }
   if (tid == 0) {
+    gather_draft<BF16>(a, b, j, rowoff, ri);
+    a.info[r] = ri;
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
+  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
+
+  __shared__ float s_xm, s_th, s_R;
+  __shared__ double s_S;
+  __shared__ uint32_t s_fl;
+  __shared__ int s_n, s_dn[2];
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long mh[256], s_u64[4], s_above;
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  // union entries: keys, token ids, fixed-point masses
+  uint32_t* keys = reinterpret_cast<uint32_t*>(s_dyn);
+  int32_t* idxs = reinterpret_cast<int32_t*>(s_dyn + (size_t)a.um * 4);
+  unsigned long long* mass = reinterpret_cast<unsigned long long*>(s_dyn + (size_t)a.um * 8);
+
+  if (tid == 0) {
+    RowMerge m = merge_chunks(a.cout + r * a.nchunks, a.nchunks, a.c);
+    s_xm = m.xmax;
+    s_th = m.thr;
+    s_fl = m.flags;
+    s_R = m.R;
+    s_S = m.S;
+    s_n = 0;
+  }
+  __syncthreads();
+  RowInfo ri;
+  ri.S = s_S;
+  ri.R = s_R;
+  ri.tau = kLowest;
+  ri.nkept = -1;
+  ri.flags = 0;
+  ri.ed = 0.0f;
+  ri.qd = 0.0f;
+  ri.d = -1;
+  ri.pad = 0;
+  const uint32_t fl = s_fl;
+  if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf) || (s_S != s_S)) {
+    if (tid == 0) {
+      ri.flags = RF_NONFINITE;
+      a.info[r] = ri;
+    }
+    return;
+  }
+  if (!a.trunc) {
+    if (tid == 0) {
+      ri.flags = RF_BIG;
+      gather_draft<BF16>(a, b, j, rowoff, ri);
+      a.info[r] = ri;
+    }
+    return;
+  }
+  if ((fl & CF_OVERFLOW) || !a.fast) {
+    exact_row<BF16>(a, r, b, j, rowoff, ri);
+    return;
+  }
+
+  // ---- candidate union (entries >= the highest chunk threshold) ----
+  const float theta = s_th;
+  const float R = s_R;
+  const Cand* cd = a.cand + r * a.nchunks * (int64_t)a.cap_out;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const int nc = a.cout[r * a.nchunks + c].ncand;
+    for (int i0 = 0; i0 < nc; i0 += 256) {
+      const int i = i0 + tid;
+      Cand e;
+      e.v = kNegInf;
+      e.idx = 0;
+      if (i < nc) e = cd[(int64_t)c * a.cap_out + i];
+      const bool keep = i < nc && e.v >= theta;
+      const int pos = wave_append_slot(keep, &s_n);
+      if (keep && pos < a.um) {
+        keys[pos] = f2key(e.v);
+        idxs[pos] = e.idx;
+        mass[pos] = to_fixed(e_of(e.v, a.c, R));
+      }
+    }
+  }
+  __syncthreads();
+  const int nu = s_n;
+  if (nu > a.um) {
+    exact_row<BF16>(a, r, b, j, rowoff, ri);
+    return;
+  }
+
+  // ---- thresholds ----
+  const bool topk = a.top_k > 0 && (int64_t)a.top_k < a.V;
+  const bool topp = a.top_p < 1.0f;
+  uint32_t kfloor = 0;  // keys below this are outside the top-k set
+  if (topk && nu >= a.top_k) kfloor = block_select_count<BF16>(keys, nu, a.top_k, hist, s_dn);
+  auto mass_from = [&](uint32_t kf) -> unsigned long long {
+    unsigned long long part = 0ull;
+    for (int i = tid; i < nu; i += 256)
+      if (keys[i] >= kf) part += mass[i];
+    return block_sum_u64(part, s_u64);
+  };
+  uint32_t kfinal = kfloor;
+  const double scale = 1099511627776.0;  // 2^40
+  if (topp) {
+    const double Sref = topk ? (double)mass_from(kfloor) : s_S * scale;
+    const double target = (double)a.top_p * Sref;
+    uint32_t kp;
+    if (block_select_mass<BF16>(keys, mass, nu, kfloor, target, mh, s_dn, &s_above, kp)) {
+      kfinal = kp;
+    } else if (!(topk || theta == kLowest)) {
+      // the crossing lies below the certified candidates: exact path
+      exact_row<BF16>(a, r, b, j, rowoff, ri);
+      return;
+    }  // else rounding: keep the whole base set
+  }
+  const unsigned long long Sfx = mass_from(kfinal);
+  ri.S = (double)Sfx / scale;
+  ri.tau = key2f(kfinal);
+  if (kfinal == 0) ri.tau = kLowest;
+  // ---- kept list in token-id order: compact the kept entries (in any
+  //      order) into the mass array, no longer needed, then store each at
+  //      its rank by id (ids are unique within a row) ----
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  int32_t* kid = reinterpret_cast<int32_t*>(mass);
+  float* kev = reinterpret_cast<float*>(mass) + a.um;
+  for (int i0 = 0; i0 < nu; i0 += 256) {
+    const int i = i0 + tid;
+    const bool keep = i < nu && keys[i] >= kfinal;
+    const int pos = wave_append_slot(keep, &s_n);
+    if (keep) {
+      kid[pos] = idxs[i];
+      kev[pos] = e_of(key2f(keys[i]), a.c, R);
+    }
+  }
+  __syncthreads();
+  const int nkept = s_n;
+  if (nkept <= a.kmax) {
+    Cand* out = a.kept + r * (int64_t)a.kmax;
+    constexpr int kPer = 4;  // entries ranked per thread in one sweep
+    for (int i0 = 0; i0 < nkept; i0 += 256 * kPer) {
+      int id[kPer], rank[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = i0 + q * 256 + tid;
+        id[q] = i < nkept ? kid[i] : 0x7fffffff;
+        rank[q] = 0;
+      }
+      for (int x = 0; x < nkept; ++x) {
+        const int v = kid[x];  // same address for every lane: a broadcast read
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) rank[q] += v < id[q] ? 1 : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = i0 + q * 256 + tid;
+        if (i < nkept) {
+          Cand e;
+          e.idx = id[q];
+          e.v = kev[i];
+          out[rank[q]] = e;
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    if (nkept > a.kmax) {
+      ri.flags = RF_BIG;
+      ri.nkept = -1;
+    } else {
+      ri.nkept = nkept;
+    }
     gather_draft<BF16>(a, b, j, rowoff, ri);
     a.info[r] = ri;
   }

@@ -88,7 +88,9 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
 // exponential sum (s, R) and NaN evidence.  Unit sums collect in a float
 // partial `sb` (at most 64 elements, each <= 1, between flushes) that is
 // folded into the double `s` by flush() and before every rescale.
-template <bool BF16, bool DO_S>
+// TRACK_MAX = false: the caller keeps the running max itself (and stores it
+// in xmax before finish_flags()).
+template <bool BF16, bool DO_S, bool TRACK_MAX = true>
 struct UnitAcc {
   static constexpr int EPV = BF16 ? 8 : 4;
   float xmax = kNegInf;
@@ -129,16 +131,18 @@ struct UnitAcc {
     float vm = x[0];
 #pragma unroll
     for (int i = 1; i < EPV; ++i) vm = fmaxf(vm, x[i]);
-    xmax = fmaxf(xmax, vm);
+    if constexpr (TRACK_MAX) xmax = fmaxf(xmax, vm);
     if constexpr (DO_S) {
       const float vc = vm * c;
-      if (vc > R && vm < kPosInf) {
-        const float Rn = ceilf(vc);
-        s += (double)sb;
-        if (R != kNegInf) s = ldexp(s, (int)(R - Rn));
-        sb = 0.0f;
-        R = Rn;
-        Re = Rn;
+      if (vc > R) {
+        if (vm < kPosInf) {  // +Inf gets no reference (the row is flagged)
+          const float Rn = ceilf(vc);
+          s += (double)sb;
+          if (R != kNegInf) s = ldexp(s, (int)(R - Rn));
+          sb = 0.0f;
+          R = Rn;
+          Re = Rn;
+        }
       }
       // a NaN logit turns s into NaN, which the row merge reports
       float ev[EPV];
@@ -212,8 +216,8 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     }
   }
 
-  UnitAcc<BF16, DO_S> acc;
-  float bestv = kNegInf;
+  UnitAcc<BF16, DO_S, MODE != M_ARGMAX> acc;
+  float bestv = kNegInf;  // running max (argmax mode)
   int aidx = 0x7fffffff;  // row index of this thread's first maximum
 
   auto process = [&](int64_t u, const uint4& w, auto edge_tag) {
@@ -261,6 +265,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     }
     acc.flush();
   }
+  if constexpr (MODE == M_ARGMAX) acc.xmax = bestv;
   acc.finish_flags();
 
   // ---- workgroup reductions (fixed order) ----

@@ -39,48 +39,8 @@ struct AcceptArgs {
   BigJob* jobs;
 };
 
-// Copy a kept list into LDS sorted by token id (one wave, bitonic sort on
-// (id, e) keys).  The stored list has no order; drawing walks it by id.
-__device__ void wave_sort_kept(const Cand* src, int n, Cand* dst /* LDS, >= pow2(n) */) {
-  const int lane = lane_id();
-  uint64_t* k = reinterpret_cast<uint64_t*>(dst);
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  for (int i = lane; i < np2; i += kWave) {
-    uint64_t v = ~0ull;
-    if (i < n) {
-      Cand e = src[i];
-      v = ((uint64_t)(uint32_t)e.idx << 32) | (uint64_t)__float_as_uint(e.v);
-    }
-    k[i] = v;
-  }
-  wave_sync();
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = lane; t < (np2 >> 1); t += kWave) {
-        const int lo = 2 * stride * (t / stride) + (t % stride);
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t x = k[lo], y = k[hi];
-        if (up ? (x > y) : (x < y)) {
-          k[lo] = y;
-          k[hi] = x;
-        }
-      }
-      wave_sync();
-    }
-  }
-  for (int i = lane; i < n; i += kWave) {
-    const uint64_t v = k[i];
-    Cand e;
-    e.idx = (int32_t)(v >> 32);
-    e.v = __uint_as_float((uint32_t)v);
-    dst[i] = e;
-  }
-  wave_sync();
-}
-
-// Draw from the kept list of one row (called by a whole wave).
+// Draw from the kept list of one row, stored in token-id order (called by a
+// whole wave).
 // residual: weights (e/S - q)_+ on the list; otherwise e/S.
 __device__ int draw_from_list(const Cand* L, int n, double S, const float* qrow, bool& residual, float u,
                               uint32_t& fl) {
@@ -260,10 +220,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl
     return;
   }
   const float* qr = residual ? a.q + qrow * a.V : nullptr;
-  extern __shared__ __align__(16) unsigned char s_dyn[];
-  Cand* sorted = reinterpret_cast<Cand*>(s_dyn) + (threadIdx.x >> 6) * a.kmax;
-  wave_sort_kept(a.kept + trow * a.kmax, rs.nkept, sorted);
-  int token = draw_from_list(sorted, rs.nkept, rs.S, qr, residual, u, fl);
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
   if (lane == 0) {
     out[nacc] = token;
     a.out_nacc[b] = nacc;
@@ -1103,9 +1060,7 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     zpq = acc4[1];
     zqp = acc4[2];
   } else {
-    extern __shared__ __align__(16) unsigned char s_dyn[];
-    Cand* L = reinterpret_cast<Cand*>(s_dyn) + wid * a.kmax;
-    wave_sort_kept(a.kept + r * a.kmax, ri.nkept, L);
+    const Cand* L = a.kept + r * a.kmax;  // token-id order
     const float* qr = a.q + r * a.V;
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     for (int i = lane; i < ri.nkept; i += kWave) {
