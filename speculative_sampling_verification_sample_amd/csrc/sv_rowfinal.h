@@ -14,6 +14,8 @@
 // q(d) so the acceptance test needs no further pass ([WR] §6).
 #pragma once
 
+#include <type_traits>
+
 #include "sv_device.h"
 
 namespace sv {
@@ -596,22 +598,36 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   const int nkept = s_n;
   if (nkept <= a.kmax) {
     Cand* out = a.kept + r * (int64_t)a.kmax;
-    constexpr int kPer = 4;  // entries ranked per thread in one sweep
-    for (int i0 = 0; i0 < nkept; i0 += 256 * kPer) {
-      int id[kPer], rank[kPer];
+    // kid sits at the start of the 8-byte-aligned mass array, whose size
+    // (um >= cap_out entries) keeps it 16-byte aligned: ids are read four at
+    // a time, the same address for every lane (a broadcast read).
+    const int4* kid4 = reinterpret_cast<const int4*>(kid);
+    const int nk4 = nkept >> 2;
+    // KP entries ranked per thread in one sweep of 256 * KP entries
+    auto sweep = [&](int i0, auto kp_tag) {
+      constexpr int KP = decltype(kp_tag)::value;
+      if (i0 + (tid & ~(kWave - 1)) >= nkept) return;  // this wave holds no entry
+      int id[KP], rank[KP];
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
+      for (int q = 0; q < KP; ++q) {
         const int i = i0 + q * 256 + tid;
         id[q] = i < nkept ? kid[i] : 0x7fffffff;
         rank[q] = 0;
       }
-      for (int x = 0; x < nkept; ++x) {
-        const int v = kid[x];  // same address for every lane: a broadcast read
+#pragma unroll 4
+      for (int x = 0; x < nk4; ++x) {
+        const int4 v = kid4[x];
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) rank[q] += v < id[q] ? 1 : 0;
+        for (int q = 0; q < KP; ++q)
+          rank[q] += (v.x < id[q] ? 1 : 0) + (v.y < id[q] ? 1 : 0) + (v.z < id[q] ? 1 : 0) + (v.w < id[q] ? 1 : 0);
+      }
+      for (int x = nk4 * 4; x < nkept; ++x) {
+        const int v = kid[x];
+#pragma unroll
+        for (int q = 0; q < KP; ++q) rank[q] += v < id[q] ? 1 : 0;
       }
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
+      for (int q = 0; q < KP; ++q) {
         const int i = i0 + q * 256 + tid;
         if (i < nkept) {
           Cand e;
@@ -620,6 +636,11 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
           out[rank[q]] = e;
         }
       }
+    };
+    if (nkept <= 256) {
+      sweep(0, std::integral_constant<int, 1>{});
+    } else {
+      for (int i0 = 0; i0 < nkept; i0 += 256 * 4) sweep(i0, std::integral_constant<int, 4>{});
     }
   }
   if (tid == 0) {
