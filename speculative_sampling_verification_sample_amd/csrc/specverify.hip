@@ -30,8 +30,7 @@ constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 p
 constexpr int kKMax = 2048;       // longest kept set stored as a list
 constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
 constexpr int kNwTopP = 128;      // chunk elements a top-p candidate threshold certifies
-constexpr int kNoutTrunc = 1024;  // entries an oversized chunk list is trimmed to
-constexpr int kTieSlack = 256;    // room for ties at a chunk's cut
+constexpr int kCapOut = 1280;     // candidate list capacity of one chunk (longer: exact path)
 constexpr int kTruncMinWG = 2048; // truncated pass: shorter chunks until this many workgroups
 constexpr int kUnionMax = 2048;   // LDS entries of the row finisher's candidate union
 // Below this many requests the sampled rows are weighed by many workgroups
@@ -48,7 +47,7 @@ struct Plan {
   bool trunc = false, need_s = false, fast = true;
   int nchunks = 1;
   int64_t chunk = 8;
-  int nw = 0, nout = 0, cap_out = 0, um = 0;
+  int nw = 0, cap_out = 0, um = 0;
   int nu = 16;  // truncated pass: 16-byte units per thread
   int nch4 = 1;
   int scale_bits = 40;
@@ -70,8 +69,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.fast = !topk || prm.top_k <= kFastTopK;
   if (p.trunc) {
     p.nw = topk ? std::min<int>(prm.top_k, kFastTopK) : kNwTopP;
-    p.nout = kNoutTrunc;
-    p.cap_out = p.nout + kTieSlack;
+    p.cap_out = kCapOut;
   }
   int64_t nch, chunk;
   if (p.trunc) {
@@ -176,11 +174,10 @@ void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
 template <bool BF16, bool NEED_S>
 void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  const size_t dyn = (size_t)kStageCap * sizeof(Cand);
   record_timer(g_timer_start, st);
-  if (p.nu == 16) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 16>), grid, dim3(kTruncBS), dyn, st, a);
-  else if (p.nu == 8) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 8>), grid, dim3(kTruncBS), dyn, st, a);
-  else hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 4>), grid, dim3(kTruncBS), dyn, st, a);
+  if (p.nu == 16) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 16>), grid, dim3(kTruncBS), 0, st, a);
+  else if (p.nu == 8) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 8>), grid, dim3(kTruncBS), 0, st, a);
+  else hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 4>), grid, dim3(kTruncBS), 0, st, a);
   record_timer(g_timer_stop, st);
 }
 
@@ -200,7 +197,6 @@ sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, floa
   a.nchunks = p.nchunks;
   a.c = c;
   a.nw = p.nw;
-  a.nout = p.nout;
   a.cap_out = p.cap_out;
   a.out = ws_at<ChunkOut>(ws, p.off_cout);
   a.cand = p.trunc ? ws_at<Cand>(ws, p.off_cand) : nullptr;

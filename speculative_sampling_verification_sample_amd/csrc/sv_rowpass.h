@@ -22,9 +22,8 @@
 // Any chunk's nw-th largest is <= the row's nw-th largest, so the merged
 // lists contain every token of the row's top-k set (nw = k), and for top-p
 // the row finisher certifies that the mass above the highest chunk
-// threshold covers the nucleus.  A list longer than cap_out is trimmed to
-// the chunk's nout largest (plus ties) through LDS; one that does not fit
-// there is flagged CF_OVERFLOW and the row takes the exact path.
+// threshold covers the nucleus.  A list longer than cap_out (ties, flat
+// rows) is flagged CF_OVERFLOW and the row takes the exact path.
 #pragma once
 
 #include <type_traits>
@@ -44,7 +43,6 @@ struct RowPassArgs {
   int32_t nchunks;
   float c;
   int32_t nw;          // chunk elements the candidate threshold must certify
-  int32_t nout;        // entries an oversized list is trimmed to
   int32_t cap_out;     // capacity of one chunk's list
   ChunkOut* out;  // [rows][nchunks]
   Cand* cand;     // [rows][nchunks][cap_out]
@@ -56,8 +54,7 @@ struct RowPassArgs {
   float2* gath;
 };
 
-constexpr int kTruncBS = 512;    // threads of the truncated-row pass
-constexpr int kStageCap = 4096;  // LDS entries for trimming an oversized list
+constexpr int kTruncBS = 512;  // threads of the truncated-row pass
 
 // Geometry of the chunk a workgroup owns: flat element range [F0, F1) and
 // 16-byte unit range [U0, U1) (a unit may straddle the range ends).
@@ -314,14 +311,13 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
 // thread's NU units and the data of its best unit (the chunk has at most
 // NU * kTruncBS units, checked by the host).  Once t0 is known, the best
 // units cut their candidates from registers; the other units whose max
-// reaches t0 (a fraction of a per cent) are listed in LDS and read again.
+// reaches t0 (a fraction of a per cent) are read again by their lane.
 template <bool BF16, bool NEED_S, int NU>
 __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) {
   constexpr int BS = kTruncBS;
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NWV = BS / kWave;
   constexpr int kUnroll = NU < 8 ? NU : 8;
-  constexpr int kListCap = 2 * BS;  // listed units: each thread re-reads at most two
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const ChunkGeom g = chunk_geom<EPV>(a);
@@ -332,14 +328,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   __shared__ double s_s[NWV];
   __shared__ float s_R[NWV];
   __shared__ uint32_t s_fl[NWV], s_kw[NWV];
-  __shared__ int s_tot[NWV];
-  __shared__ int s_list[kListCap];
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_nl, s_digit, s_need, s_out;
-  extern __shared__ __align__(16) unsigned char s_dyn[];
-  Cand* stage = reinterpret_cast<Cand*>(s_dyn);  // kStageCap entries
-
-  if (tid == 0) s_nl = 0;
+  __shared__ int s_out;
 
   // ---- streaming pass: statistics and per-unit maxima ----
   // Unit k of this thread is unit k*BS + tid of the chunk; its first
@@ -408,170 +397,120 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
     s_fl[wid] = wfl;
     s_kw[wid] = K;
   }
+  if (tid == 0) s_out = 0;
   __syncthreads();
   uint32_t t0key = s_kw[0];
   for (int k = 1; k < NWV; ++k) t0key = min(t0key, s_kw[k]);
   t0key = max(t0key, f2key(kLowest));  // -inf logits never become candidates
   const float t0 = key2f(t0key);
 
-  // ---- list the other units whose max reaches t0 (units past the chunk
-  //      have um = -inf < t0) ----
+  // ---- candidates: every element >= t0 of the units whose max reaches it.
+  //      The best unit is in registers; the lane reads its other such units
+  //      again (a fraction of a per cent of the units; units past the chunk
+  //      have um = -inf < t0).  Places are taken with one LDS atomic per
+  //      wave, so the list has no fixed order (the row finisher does not
+  //      need one); a list longer than cap_out sends the row to the exact
+  //      path. ----
+  uint32_t more = 0;  // bit k: unit k (other than the best) reaches t0
 #pragma unroll
-  for (int k = 0; k < NU; ++k) {
-    const bool p = um[k] >= t0 && k != bestk;
-    const uint64_t m = ballot(p);
-    if (m != 0) {
-      int bp = 0;
-      if (lane == 0) bp = atomicAdd(&s_nl, (int)__popcll(m));
-      bp = __shfl(bp, 0, kWave);
-      const int slot = bp + lanes_below(m);
-      if (p && slot < kListCap) s_list[slot] = k * BS + tid;
+  for (int k = 0; k < NU; ++k) more |= (um[k] >= t0 && k != bestk) ? (1u << k) : 0u;
+  Cand* dst = a.cand + ((int64_t)g.r * a.nchunks + g.ci) * a.cap_out;
+  const int id0 = (int)g.e0;  // token id of chunk element 0
+  uint4 lw[3];
+  int lrel[3];
+  bool lon[3];
+  lw[0] = bw;
+  lrel[0] = rel0 + bestk * BS * EPV;
+  lon[0] = bestk >= 0 && bestv >= t0;
+#pragma unroll
+  for (int r = 1; r < 3; ++r) {
+    lon[r] = more != 0;
+    lrel[r] = 0;
+    lw[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (lon[r]) {
+      const int k = __builtin_ctz(more);
+      more &= more - 1;
+      lw[r] = base[g.U0 + k * BS + tid];
+      lrel[r] = rel0 + k * BS * EPV;
+    }
+  }
+  auto count_unit = [&](const uint4& w, int rel) {
+    float x[EPV];
+    widen<BF16>(w, x);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) cnt += (x[e] >= t0 && (unsigned)(rel + e) < (unsigned)n) ? 1 : 0;
+    return cnt;
+  };
+  auto emit_unit = [&](const uint4& w, int rel, int& pos) {
+    float x[EPV];
+    widen<BF16>(w, x);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if (x[e] >= t0 && (unsigned)(rel + e) < (unsigned)n) {
+        if (pos < a.cap_out) {
+          Cand ce;
+          ce.v = x[e];
+          ce.idx = id0 + rel + e;
+          dst[pos] = ce;
+        }
+        ++pos;
+      }
+    }
+  };
+  int nc = 0;
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (lon[r]) nc += count_unit(lw[r], lrel[r]);
+  const int incl = wave_incl_scan_i(nc);
+  const int wtot = __shfl(incl, kWave - 1, kWave);
+  int wbase = 0;
+  if (lane == kWave - 1 && wtot > 0) wbase = atomicAdd(&s_out, wtot);
+  wbase = __shfl(wbase, kWave - 1, kWave);
+  int pos = wbase + incl - nc;
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (lon[r]) emit_unit(lw[r], lrel[r], pos);
+  // lanes with more than two further units (ties, flat rows): one at a time
+  while (more != 0) {
+    const int k = __builtin_ctz(more);
+    more &= more - 1;
+    const uint4 w = base[g.U0 + k * BS + tid];
+    const int rel = rel0 + k * BS * EPV;
+    const int cnt = count_unit(w, rel);
+    if (cnt > 0) {
+      int p2 = atomicAdd(&s_out, cnt);
+      emit_unit(w, rel, p2);
     }
   }
   __syncthreads();
-  const int nl = s_nl;
 
-  Cand* dst = a.cand + ((int64_t)g.r * a.nchunks + g.ci) * a.cap_out;
-  uint32_t Kc = t0key;
-  int nout_written = 0;
-  uint32_t extra = 0;
-  if (nl > kListCap) {
-    extra = CF_OVERFLOW;  // ties fill too many units: exact path
-  } else {
-    // ---- the best unit (slot 0) and up to two re-read listed units,
-    //      counted, placed and emitted ----
-    uint4 lw[3];
-    int lrel[3];
-    bool lon[3];
-    int nc = 0;
-    lw[0] = bw;
-    lrel[0] = rel0 + bestk * BS * EPV;
-    lon[0] = bestk >= 0 && bestv >= t0;
-#pragma unroll
-    for (int r = 1; r < 3; ++r) {
-      const int i = (r - 1) * BS + tid;
-      lrel[r] = 0;
-      lw[r] = make_uint4(0u, 0u, 0u, 0u);
-      lon[r] = i < nl;
-      if (lon[r]) {
-        const int ul = s_list[i];
-        lw[r] = base[g.U0 + ul];
-        lrel[r] = relu + ul * EPV;
+  // ---- chunk result: wave 0 merges the per-wave partials ----
+  if (wid == 0) {
+    const bool own = lane < NWV;
+    float xm = own ? s_xm[lane] : kNegInf;
+    uint32_t fl = own ? s_fl[lane] : 0u;
+    double ss = own ? s_s[lane] : 0.0;
+    float RR = own ? s_R[lane] : kNegInf;
+    xm = wave_max(xm);
+    fl = wave_or(fl);
+    if constexpr (NEED_S) wave_sr_merge(ss, RR);
+    if (lane == 0) {
+      int total = s_out;
+      if (total > a.cap_out) {
+        fl |= CF_OVERFLOW;
+        total = a.cap_out;
       }
+      ChunkOut o;
+      o.xmax = xm;
+      o.argmax = -1;
+      o.thr = t0;
+      o.ncand = total;
+      o.s = NEED_S ? ss : 0.0;
+      o.Rs = NEED_S ? RR : kNegInf;
+      o.flags = fl;
+      a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
     }
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      if (lon[r]) {
-        float x[EPV];
-        widen<BF16>(lw[r], x);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) nc += (x[e] >= t0 && (unsigned)(lrel[r] + e) < (unsigned)n) ? 1 : 0;
-      }
-    }
-    const int incl = wave_incl_scan_i(nc);
-    if (lane == kWave - 1) s_tot[wid] = incl;
-    __syncthreads();
-    int pos = incl - nc, total = 0;
-    for (int k = 0; k < NWV; ++k) {
-      const int t = s_tot[k];
-      if (k < wid) pos += t;
-      total += t;
-    }
-
-    const bool direct = total <= a.cap_out;
-    if (direct || total <= kStageCap) {
-      // straight into the chunk's list, or into LDS for trimming
-      Cand* to = direct ? dst : stage;
-      const int id0 = (int)g.e0;  // token id of chunk element 0
-#pragma unroll
-      for (int r = 0; r < 3; ++r) {
-        if (lon[r]) {
-          float x[EPV];
-          widen<BF16>(lw[r], x);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            if (x[e] >= t0 && (unsigned)(lrel[r] + e) < (unsigned)n) {
-              Cand ce;
-              ce.v = x[e];
-              ce.idx = id0 + lrel[r] + e;
-              to[pos++] = ce;
-            }
-          }
-        }
-      }
-    }
-    if (direct) {
-      nout_written = total;
-    } else if (total <= kStageCap) {
-      // trim to the nout largest (ties at the cut kept)
-      __syncthreads();
-      uint32_t prefix = 0, pmask = 0;
-      int need = a.nout;
-      constexpr int kLow = BF16 ? 16 : 0;
-      for (int shift = 24; shift >= kLow; shift -= 8) {
-        if (tid < 256) s_hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < total; i += BS) {
-          const uint32_t key = f2key(stage[i].v);
-          if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wid == 0) {
-          const int d = wave_find_digit(s_hist, need);
-          if (lane == 0) {
-            s_digit = d;
-            s_need = need;
-          }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)s_digit << shift;
-        pmask |= 255u << shift;
-        need = s_need;
-        __syncthreads();
-      }
-      Kc = prefix;
-      if (tid == 0) s_out = 0;
-      __syncthreads();
-      for (int bse = 0; bse < total; bse += BS) {
-        const int i = bse + tid;
-        const bool keep = i < total && f2key(stage[i].v) >= Kc;
-        const uint64_t m = ballot(keep);
-        int bp = 0;
-        if (lane == 0 && m) bp = atomicAdd(&s_out, (int)__popcll(m));
-        bp = __shfl(bp, 0, kWave);
-        const int p = bp + lanes_below(m);
-        if (keep && p < a.cap_out) dst[p] = stage[i];
-      }
-      __syncthreads();
-      nout_written = s_out;
-      if (nout_written > a.cap_out) {
-        extra = CF_OVERFLOW;
-        nout_written = a.cap_out;
-      }
-    } else {
-      extra = CF_OVERFLOW;  // ties alone exceed the staging room
-    }
-  }
-
-  if (tid == 0) {
-    float xm = s_xm[0];
-    uint32_t fl = s_fl[0] | extra;
-    double ss = s_s[0];
-    float RR = s_R[0];
-    for (int k = 1; k < NWV; ++k) {
-      xm = fmaxf(xm, s_xm[k]);
-      fl |= s_fl[k];
-      if constexpr (NEED_S) sr_merge(ss, RR, s_s[k], s_R[k]);
-    }
-    ChunkOut o;
-    o.xmax = xm;
-    o.argmax = -1;
-    o.thr = key2f(Kc);
-    o.ncand = nout_written;
-    o.s = NEED_S ? ss : 0.0;
-    o.Rs = NEED_S ? RR : kNegInf;
-    o.flags = fl;
-    a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
   }
 }
 
