@@ -30,7 +30,12 @@ constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 p
 constexpr int kKMax = 2048;       // longest kept set stored as a list
 constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
 constexpr int kNwTopP = 128;      // chunk elements a top-p candidate threshold certifies
-constexpr int kCapOut = 1280;     // candidate list capacity of one chunk (longer: exact path)
+// Candidate list capacity of one chunk: a multiple of the certified count
+// (lists measure about 1.5-3x nw on the workloads' rows); a longer list sends
+// the row to the exact path.  It also sizes the row finisher's LDS union.
+constexpr int kCapPerNw = 4;
+constexpr int kCapMin = 256;
+constexpr int kCapMax = 1280;
 constexpr int kTruncMinWG = 2048; // truncated pass: shorter chunks until this many workgroups
 constexpr int kUnionMax = 2048;   // LDS entries of the row finisher's candidate union
 // Below this many requests the sampled rows are weighed by many workgroups
@@ -69,7 +74,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.fast = !topk || prm.top_k <= kFastTopK;
   if (p.trunc) {
     p.nw = topk ? std::min<int>(prm.top_k, kFastTopK) : kNwTopP;
-    p.cap_out = kCapOut;
+    p.cap_out = std::min(kCapMax, std::max(kCapMin, kCapPerNw * p.nw));
   }
   int64_t nch, chunk;
   if (p.trunc) {

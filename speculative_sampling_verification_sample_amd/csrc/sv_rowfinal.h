@@ -184,9 +184,10 @@ __device__ uint32_t block_select_count(const uint32_t* keys, int n, int need, ui
   for (int shift = 24; shift >= kLow; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      uint32_t k = keys[i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      const int i = i0 + tid;
+      const uint32_t k = i < n ? keys[i] : 0u;
+      if (i < n && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wid == 0) {
@@ -218,9 +219,10 @@ __device__ bool block_select_mass(const uint32_t* keys, const unsigned long long
   for (int shift = 24; shift >= kLow; shift -= 8) {
     mh[tid] = 0ull;
     __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      uint32_t k = keys[i];
-      if (k >= floor_key && (k & pmask) == prefix) atomicAdd(&mh[(k >> shift) & 255u], mass[i]);
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      const int i = i0 + tid;
+      const uint32_t k = i < n ? keys[i] : 0u;
+      if (i < n && k >= floor_key && (k & pmask) == prefix) atomicAdd(&mh[(k >> shift) & 255u], mass[i]);
     }
     __syncthreads();
     if (wid == 0) {
@@ -472,6 +474,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   __shared__ double s_S;
   __shared__ uint32_t s_fl;
   __shared__ int s_n, s_dn[2];
+  __shared__ int s_off[kWave], s_tot;  // candidate offsets per chunk (<= 64 chunks)
   __shared__ uint32_t hist[256];
   __shared__ unsigned long long mh[256], s_u64[4], s_above;
   extern __shared__ __align__(16) unsigned char s_dyn[];
@@ -480,14 +483,45 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   int32_t* idxs = reinterpret_cast<int32_t*>(s_dyn + (size_t)a.um * 4);
   unsigned long long* mass = reinterpret_cast<unsigned long long*>(s_dyn + (size_t)a.um * 8);
 
-  if (tid == 0) {
-    RowMerge m = merge_chunks(a.cout + r * a.nchunks, a.nchunks, a.c);
-    s_xm = m.xmax;
-    s_th = m.thr;
-    s_fl = m.flags;
-    s_R = m.R;
-    s_S = m.S;
-    s_n = 0;
+  const int nch = a.nchunks;
+  const bool flat = nch <= kWave;  // the union walks one flat index over the chunk lists
+  if (tid < kWave) {
+    // wave 0 merges the chunk results (lane l: chunks l, l + 64, ...)
+    const int lane = tid;
+    const ChunkOut* co = a.cout + r * nch;
+    float xm = kNegInf, th = kLowest, Rs = kNegInf;
+    uint32_t flg = 0;
+    double ss = 0.0;
+    int ncl = 0;
+    for (int c = lane; c < nch; c += kWave) {
+      const ChunkOut o = co[c];
+      xm = fmaxf(xm, o.xmax);
+      th = fmaxf(th, o.thr);
+      flg |= o.flags;
+      sr_merge(ss, Rs, o.s, o.Rs);
+      ncl = o.ncand;
+    }
+    xm = wave_max(xm);
+    th = wave_max(th);
+    flg = wave_or(flg);
+    const float Rm = wave_max(Rs);
+    double sl = 0.0;
+    if (Rs != kNegInf) sl = ldexp(ss, (int)(Rs - Rm));
+    ss = wave_sum_d(sl);
+    if (flat) {
+      const int incl = wave_incl_scan_i(ncl);
+      s_off[lane] = incl - ncl;
+      if (lane == kWave - 1) s_tot = incl;
+    }
+    if (lane == 0) {
+      const float Rrow = ceilf(xm * a.c);
+      s_xm = xm;
+      s_th = th;
+      s_fl = flg;
+      s_R = Rrow;
+      s_S = (Rm == kNegInf) ? 0.0 : ldexp(ss, (int)(Rm - Rrow));
+      s_n = 0;
+    }
   }
   __syncthreads();
   RowInfo ri;
@@ -524,21 +558,49 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   // ---- candidate union (entries >= the highest chunk threshold) ----
   const float theta = s_th;
   const float R = s_R;
-  const Cand* cd = a.cand + r * a.nchunks * (int64_t)a.cap_out;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const int nc = a.cout[r * a.nchunks + c].ncand;
-    for (int i0 = 0; i0 < nc; i0 += 256) {
-      const int i = i0 + tid;
-      Cand e;
-      e.v = kNegInf;
-      e.idx = 0;
-      if (i < nc) e = cd[(int64_t)c * a.cap_out + i];
-      const bool keep = i < nc && e.v >= theta;
-      const int pos = wave_append_slot(keep, &s_n);
-      if (keep && pos < a.um) {
-        keys[pos] = f2key(e.v);
-        idxs[pos] = e.idx;
-        mass[pos] = to_fixed(e_of(e.v, a.c, R));
+  const Cand* cd = a.cand + r * nch * (int64_t)a.cap_out;
+  auto add_union = [&](bool valid, const Cand& e) {
+    const bool keep = valid && e.v >= theta;
+    const int pos = wave_append_slot(keep, &s_n);
+    if (keep && pos < a.um) {
+      keys[pos] = f2key(e.v);
+      idxs[pos] = e.idx;
+      mass[pos] = to_fixed(e_of(e.v, a.c, R));
+    }
+  };
+  if (flat) {
+    // entry t of the concatenated lists lives in chunk c with
+    // s_off[c] <= t < s_off[c + 1]; kU independent loads per thread
+    constexpr int kU = 4;
+    const int tot = s_tot;
+    for (int t0 = 0; t0 < tot; t0 += 256 * kU) {
+      Cand e[kU];
+      bool v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int t = t0 + u * 256 + tid;
+        v[u] = t < tot;
+        e[u].v = kNegInf;
+        e[u].idx = 0;
+        if (v[u]) {
+          int c = 0;
+          while (c + 1 < nch && s_off[c + 1] <= t) ++c;
+          e[u] = cd[(int64_t)c * a.cap_out + (t - s_off[c])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add_union(v[u], e[u]);
+    }
+  } else {
+    for (int c = 0; c < nch; ++c) {
+      const int nc = a.cout[r * nch + c].ncand;
+      for (int i0 = 0; i0 < nc; i0 += 256) {
+        const int i = i0 + tid;
+        Cand e;
+        e.v = kNegInf;
+        e.idx = 0;
+        if (i < nc) e = cd[(int64_t)c * a.cap_out + i];
+        add_union(i < nc, e);
       }
     }
   }
