@@ -282,18 +282,18 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     s_fl[wid] = wfl;
   }
   __syncthreads();
-  if (tid == 0) {
-    float xm = s_xm[0];
-    int ai = s_ai[0];
-    uint32_t fl = s_fl[0];
-    double ss = s_s[0];
-    float RR = s_R[0];
-    for (int k = 1; k < NWV; ++k) {
-      if constexpr (MODE == M_ARGMAX) argmax_merge(xm, ai, s_xm[k], s_ai[k]);
-      else xm = fmaxf(xm, s_xm[k]);
-      fl |= s_fl[k];
-      if constexpr (DO_S) sr_merge(ss, RR, s_s[k], s_R[k]);
-    }
+  if (wid == 0) {
+    // wave 0 merges the per-wave partials (lane l holds wave l's)
+    const bool own = lane < NWV;
+    float xm = own ? s_xm[lane] : kNegInf;
+    int ai = own ? s_ai[lane] : 0x7fffffff;
+    uint32_t fl = own ? s_fl[lane] : 0u;
+    double ss = own ? s_s[lane] : 0.0;
+    float RR = own ? s_R[lane] : kNegInf;
+    if constexpr (MODE == M_ARGMAX) wave_argmax(xm, ai);
+    else xm = wave_max(xm);
+    fl = wave_or(fl);
+    if constexpr (DO_S) wave_sr_merge(ss, RR);
     if (MODE == M_ARGMAX && xm == kNegInf) ai = (int)g.e0;  // all -inf: first element
     ChunkOut o;
     o.xmax = xm;
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     o.s = DO_S ? ss : 0.0;
     o.Rs = DO_S ? RR : kNegInf;
     o.flags = fl;
-    a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
+    if (lane == 0) a.out[(int64_t)g.r * a.nchunks + g.ci] = o;
   }
 }
 
