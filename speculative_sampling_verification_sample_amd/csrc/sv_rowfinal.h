@@ -474,7 +474,9 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   __shared__ double s_S;
   __shared__ uint32_t s_fl;
   __shared__ int s_n, s_dn[2];
-  __shared__ int s_off[kWave], s_tot;  // candidate offsets per chunk (<= 64 chunks)
+  __shared__ int s_nc[kWave], s_maxnc;  // candidates per chunk (<= 64 chunks)
+  __shared__ int s_gd;                 // draft gather, read early by one lane of wave 1
+  __shared__ float s_gz, s_gq;
   __shared__ uint32_t hist[256];
   __shared__ unsigned long long mh[256], s_u64[4], s_above;
   extern __shared__ __align__(16) unsigned char s_dyn[];
@@ -485,6 +487,29 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
 
   const int nch = a.nchunks;
   const bool flat = nch <= kWave;  // the union walks one flat index over the chunk lists
+  // The draft's id, logit and q(d) are fetched by lane 0 of wave 1 while
+  // wave 0 merges the chunks, so the row's result does not wait on them.
+  const bool has_draft = j < a.gamma;
+  int gd = -1;
+  float gz = 0.0f, gq = 0.0f;
+  if (tid == kWave && has_draft) gd = a.ids[(int64_t)b * a.gamma + j];
+  // Candidate loads are issued now, before the chunk counts are known:
+  // thread t takes slots t / nch + u * per of chunk t % nch (per = 256 / nch),
+  // every slot inside the list's capacity; the counts decide later which
+  // loads hold candidates.
+  constexpr int kU = 4;
+  const Cand* cd = a.cand + r * nch * (int64_t)a.cap_out;
+  const int per = flat ? 256 / nch : 0;
+  const int cmine = flat ? tid % nch : 0;
+  const int s0 = flat ? tid / nch : 0;
+  Cand pre[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    pre[u].v = kNegInf;
+    pre[u].idx = 0;
+    const int sl = s0 + u * per;
+    if (a.trunc && flat && tid < per * nch && sl < a.cap_out) pre[u] = cd[(int64_t)cmine * a.cap_out + sl];
+  }
   if (tid < kWave) {
     // wave 0 merges the chunk results (lane l: chunks l, l + 64, ...)
     const int lane = tid;
@@ -509,9 +534,9 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     if (Rs != kNegInf) sl = ldexp(ss, (int)(Rs - Rm));
     ss = wave_sum_d(sl);
     if (flat) {
-      const int incl = wave_incl_scan_i(ncl);
-      s_off[lane] = incl - ncl;
-      if (lane == kWave - 1) s_tot = incl;
+      s_nc[lane] = ncl;
+      const int mx = (int)wave_max_u32((uint32_t)ncl);
+      if (lane == 0) s_maxnc = mx;
     }
     if (lane == 0) {
       const float Rrow = ceilf(xm * a.c);
@@ -555,10 +580,14 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     return;
   }
 
+  if (tid == kWave && gd >= 0 && (int64_t)gd < a.V) {
+    gz = load_logit<BF16>(a.logits, rowoff + gd);
+    gq = a.q[((int64_t)b * a.gamma + j) * a.V + gd];
+  }
+
   // ---- candidate union (entries >= the highest chunk threshold) ----
   const float theta = s_th;
   const float R = s_R;
-  const Cand* cd = a.cand + r * nch * (int64_t)a.cap_out;
   auto add_union = [&](bool valid, const Cand& e) {
     const bool keep = valid && e.v >= theta;
     const int pos = wave_append_slot(keep, &s_n);
@@ -569,27 +598,19 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     }
   };
   if (flat) {
-    // entry t of the concatenated lists lives in chunk c with
-    // s_off[c] <= t < s_off[c + 1]; kU independent loads per thread
-    constexpr int kU = 4;
-    const int tot = s_tot;
-    for (int t0 = 0; t0 < tot; t0 += 256 * kU) {
-      Cand e[kU];
-      bool v[kU];
+    const bool mine = tid < per * nch;
+    const int ncm = mine ? s_nc[cmine] : 0;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int t = t0 + u * 256 + tid;
-        v[u] = t < tot;
-        e[u].v = kNegInf;
-        e[u].idx = 0;
-        if (v[u]) {
-          int c = 0;
-          while (c + 1 < nch && s_off[c + 1] <= t) ++c;
-          e[u] = cd[(int64_t)c * a.cap_out + (t - s_off[c])];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) add_union(v[u], e[u]);
+    for (int u = 0; u < kU; ++u) add_union(mine && s0 + u * per < ncm, pre[u]);
+    // lists longer than kU * per entries (uniform trip count)
+    for (int sl0 = kU * per; sl0 < s_maxnc; sl0 += per) {
+      const int sl = sl0 + s0;
+      const bool v = mine && sl < ncm;
+      Cand e;
+      e.v = kNegInf;
+      e.idx = 0;
+      if (v) e = cd[(int64_t)cmine * a.cap_out + sl];
+      add_union(v, e);
     }
   } else {
     for (int c = 0; c < nch; ++c) {
@@ -603,6 +624,11 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
         add_union(i < nc, e);
       }
     }
+  }
+  if (tid == kWave) {
+    s_gd = gd;
+    s_gz = gz;
+    s_gq = gq;
   }
   __syncthreads();
   const int nu = s_n;
@@ -712,7 +738,19 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     } else {
       ri.nkept = nkept;
     }
-    gather_draft<BF16>(a, b, j, rowoff, ri);
+    ri.ed = 0.0f;
+    ri.qd = 0.0f;
+    ri.d = -1;
+    if (has_draft) {
+      const int d = s_gd;
+      if (d < 0 || (int64_t)d >= a.V) {
+        ri.d = -2;
+      } else {
+        ri.d = d;
+        ri.ed = (s_gz >= ri.tau) ? e_of(s_gz, a.c, ri.R) : 0.0f;
+        ri.qd = s_gq;
+      }
+    }
     a.info[r] = ri;
   }
 }
