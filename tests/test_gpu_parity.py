@@ -283,6 +283,27 @@ def test_full_size_sample(name):
     assert all((tok[b, : nacc[b]] == ids[b, : nacc[b]]).all() for b in range(w.cfg.B))
 
 
+@pytest.mark.parametrize("name,kw", [
+    # bf16, 8 units per thread in the truncated row pass (64 requests of 5 rows)
+    ("c5", dict(B=64)),
+    ("c3", dict(B=100)),
+    # fp32 truncated rows over several chunks, 16 units per thread
+    ("c2", dict(B=128, V=100000, top_p=0.9)),
+    ("c2", dict(B=128, V=100000, top_k=40)),
+])
+def test_row_pass_shapes(name, kw):
+    """Batch and vocabulary sizes that give the truncated row pass its other
+    chunk shapes (units per thread, dtype); sampled requests against the
+    oracle, every request checked for well-formed outputs."""
+    w = generate(name, DEV, **kw)
+    gpu = gpu_sample(w)
+    compare_sample(w, requests=_sampled(w.cfg.B, n=8, seed=3), label=f"{name} {kw}", gpu=gpu)
+    tok, nacc, fl = gpu
+    pos = np.arange(w.cfg.gamma + 1)[None, :]
+    assert ((tok >= 0) == (pos <= nacc[:, None])).all()
+    assert (fl == 0).all()
+
+
 def test_full_size_greedy():
     w = generate("c4", DEV)
     compare_greedy(w, requests=_sampled(w.cfg.B), label="c4 full")
