@@ -1,17 +1,18 @@
-// K2 -- per-row finalisation of the processed target distribution p, and
-// the exact multi-pass fallback for rows the fast path cannot certify.
+// K2 -- per-row finalisation of the processed target distribution p, with
+// the exact multi-pass path for rows the candidate lists cannot settle.
 //
-// K2 merges the chunk results of a row: the row max gives the integral
-// reference R, the chunk sums give the full-row mass S (temperature softmax,
-// [WR] §7.2).  With truncation ([WR] §7.3) it gathers the candidate union
-// (every element >= the highest chunk threshold is in it), sorts it by
-// logit, and applies
+// One workgroup per row merges the chunk results: the row max gives the
+// integral reference R, the chunk sums give the full-row mass S
+// (temperature softmax, [WR] §7.2).  With truncation ([WR] §7.3) it builds
+// the candidate union in LDS (every element >= the highest chunk threshold
+// is in it) and selects by radix passes over order-preserving keys
 //   top-k : keep every token whose logit >= the k-th largest logit;
 //   top-p : keep the most probable tokens until their mass reaches
-//           top_p * S (on the top-k set when both are active), plus ties.
-// The kept set is stored as a list sorted by token id (for the inverse CDF)
-// together with S over it.  Finally it reads this row's draft logit and
-// q(d) so the acceptance test needs no further pass ([WR] §6).
+//           top_p * S (on the top-k set when both are active), plus ties
+//           (masses as 2^40 fixed point, so sums are exact and order-free).
+// The kept set is stored as a list in token-id order (for the inverse CDF)
+// together with S over it.  It also reads this row's draft logit and q(d) so
+// the acceptance test needs no further pass ([WR] §6).
 #pragma once
 
 #include <type_traits>
