@@ -82,22 +82,34 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
 }
 
 // Per-thread running statistics of the units it has seen: max, the online
-// exponential sum (s, R) and NaN evidence.  Unit sums collect in a float
-// partial `sb` (at most 64 elements, each <= 1, between flushes) that is
-// folded into the double `s` by flush() and before every rescale.
+// exponential sum (s, R) and NaN evidence.  The integral reference R lags
+// the running max: it moves up (to ceil(max * c)) only when a unit's max
+// times c passes R + kRefLag, so the exponentials stay within about
+// 2^kRefLag and a wave seldom takes the rescale branch once its first
+// units are in.  The row merges rescale every (s, R) to R = ceil(row max
+// * c) exactly.  Unit
+// sums collect in a float partial `sb` (at most 64 elements between
+// flushes) that is folded into the double `s` by flush() and before every
+// rescale.  The unit max ignores nothing: a NaN element makes it NaN, so
+// such a unit never counts as a maximum (its row is flagged non-finite).
 // TRACK_MAX = false: the caller keeps the running max itself (and stores it
 // in xmax before finish_flags()).
+constexpr float kRefLag = 16.0f;
+
 template <bool BF16, bool DO_S, bool TRACK_MAX = true>
 struct UnitAcc {
   static constexpr int EPV = BF16 ? 8 : 4;
   float xmax = kNegInf;
   double s = 0.0;
   float sb = 0.0f;
-  float R = kNegInf;  // integral reference; -inf until a finite value is seen
-  // Reference the exponentials use: R once it exists, before that a huge
-  // finite value, so finite logits add exactly 0 while NaN still reaches s
-  // (and +Inf, which the row flags anyway, makes s infinite).
+  // Reference the exponentials use: the integral reference R once it
+  // exists, before that a huge finite value, so finite logits add exactly 0
+  // while NaN still reaches s (and +Inf, which the row flags anyway, makes
+  // s infinite).
   float Re = 0x1p126f;
+  // A unit max above vt moves R: (R + kRefLag) / c once R exists, -inf
+  // before (so vt == -inf tells that there is no reference yet).
+  float vt = kNegInf;
   uint32_t nan_words = 0;  // max of |bits| over whole units (per 16-bit half for bf16)
   uint32_t flags = 0;
 
@@ -125,20 +137,20 @@ struct UnitAcc {
         nan_words = max(nan_words, m);
       }
     }
+    // NaN-propagating max (one v_maximum3_f32 per three elements)
     float vm = x[0];
 #pragma unroll
-    for (int i = 1; i < EPV; ++i) vm = fmaxf(vm, x[i]);
+    for (int i = 1; i < EPV; ++i) vm = __builtin_elementwise_maximum(vm, x[i]);
     if constexpr (TRACK_MAX) xmax = fmaxf(xmax, vm);
     if constexpr (DO_S) {
-      const float vc = vm * c;
-      if (vc > R) {
+      if (vm > vt) {
         if (vm < kPosInf) {  // +Inf gets no reference (the row is flagged)
-          const float Rn = ceilf(vc);
+          const float Rn = ceilf(vm * c);
           s += (double)sb;
-          if (R != kNegInf) s = ldexp(s, (int)(R - Rn));
+          if (vt != kNegInf) s = ldexp(s, (int)(Re - Rn));
           sb = 0.0f;
-          R = Rn;
           Re = Rn;
+          vt = (Rn + kRefLag) / c;
         }
       }
       // a NaN logit turns s into NaN, which the row merge reports
@@ -153,6 +165,9 @@ struct UnitAcc {
     return vm;
   }
 
+  // The integral reference R of (s, R); -inf until a finite value is seen.
+  __device__ __forceinline__ float ref() const { return vt == kNegInf ? kNegInf : Re; }
+
   __device__ __forceinline__ void flush() {
     if constexpr (DO_S) {
       s += (double)sb;
@@ -165,7 +180,7 @@ struct UnitAcc {
     // merges drop sums without a reference: keep the evidence they carry
     // (only NaN or +Inf logits make such a sum nonzero)
     if constexpr (DO_S) {
-      if (R == kNegInf && s != 0.0) flags |= CF_NAN;
+      if (vt == kNegInf && s != 0.0) flags |= CF_NAN;
     }
     if constexpr (BF16) {
       if (nan_words > 0x7f80u) flags |= CF_NAN;
@@ -272,7 +287,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   else wxm = wave_max(wxm);
   const uint32_t wfl = wave_or(acc.flags);
   double ws = acc.s;
-  float wR = acc.R;
+  float wR = acc.ref();
   if constexpr (DO_S) wave_sr_merge(ws, wR);
   if (lane == 0) {
     s_xm[wid] = wxm;
@@ -340,7 +355,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const int rel0 = relu + tid * EPV;
   const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
   const int nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
-  UnitAcc<BF16, NEED_S> acc;
+  UnitAcc<BF16, NEED_S, false> acc;  // the running max is bestv
   float um[NU];
   // The thread's best unit stays in registers: most units that reach t0
   // are their thread's best, so few need a second read.
@@ -373,6 +388,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
     }
     acc.flush();
   }
+  acc.xmax = bestv;
   acc.finish_flags();
 
   // ---- this wave's ceil(nw/NWV)-th largest thread maximum (bitwise
@@ -388,7 +404,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const float wxm = wave_max(acc.xmax);
   const uint32_t wfl = wave_or(acc.flags);
   double ws = acc.s;
-  float wR = acc.R;
+  float wR = acc.ref();
   if constexpr (NEED_S) wave_sr_merge(ws, wR);
   if (lane == 0) {
     s_xm[wid] = wxm;
