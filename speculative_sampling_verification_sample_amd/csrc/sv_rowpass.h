@@ -141,7 +141,7 @@ struct UnitAcc {
     float vm = x[0];
 #pragma unroll
     for (int i = 1; i < EPV; ++i) vm = __builtin_elementwise_maximum(vm, x[i]);
-    if constexpr (TRACK_MAX) xmax = fmaxf(xmax, vm);
+    if constexpr (TRACK_MAX) xmax = __builtin_elementwise_maximum(xmax, vm);
     if constexpr (DO_S) {
       if (vm > vt) {
         if (vm < kPosInf) {  // +Inf gets no reference (the row is flagged)
@@ -323,10 +323,12 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
 }
 
 // Truncated rows: a streaming pass that keeps the max of each of the
-// thread's NU units and the data of its best unit (the chunk has at most
-// NU * kTruncBS units, checked by the host).  Once t0 is known, the best
-// units cut their candidates from registers; the other units whose max
-// reaches t0 (a fraction of a per cent) are read again by their lane.
+// thread's NU units (the chunk has at most NU * kTruncBS units, checked by
+// the host).  Once t0 is known, the units whose max reaches it (a fraction
+// of a per cent) are read again by their lane.  Top-p rows (NEED_S) also
+// keep each thread's best unit in registers: their lower threshold gives
+// many lanes a candidate, and the second reads cost more than the per-unit
+// tracking; top-k rows do without it.
 template <bool BF16, bool NEED_S, int NU>
 __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) {
   constexpr int BS = kTruncBS;
@@ -355,10 +357,11 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const int rel0 = relu + tid * EPV;
   const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
   const int nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
-  UnitAcc<BF16, NEED_S, false> acc;  // the running max is bestv
+  constexpr bool kKeepBest = NEED_S;
+  UnitAcc<BF16, NEED_S, !kKeepBest> acc;  // with kKeepBest the running max is bestv
   float um[NU];
-  // The thread's best unit stays in registers: most units that reach t0
-  // are their thread's best, so few need a second read.
+  // kKeepBest: the thread's best unit stays in registers; most units that
+  // reach t0 are their thread's best, so few need a second read.
   uint4 bw = make_uint4(0u, 0u, 0u, 0u);
   float bestv = kNegInf;
   int bestk = -1;
@@ -380,23 +383,29 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
         if (aligned || (ul > 0 && ul + 1 < nunits)) um[k] = acc.template add<false>(wv[i], rel, n, c, x);
         else um[k] = acc.template add<true>(wv[i], rel, n, c, x);
       }
-      if (um[k] > bestv) {
-        bestv = um[k];
-        bestk = k;
-        bw = wv[i];
+      if constexpr (kKeepBest) {
+        if (um[k] > bestv) {
+          bestv = um[k];
+          bestk = k;
+          bw = wv[i];
+        }
       }
     }
     acc.flush();
   }
-  acc.xmax = bestv;
+  if constexpr (kKeepBest) acc.xmax = bestv;
   acc.finish_flags();
 
   // ---- this wave's ceil(nw/NWV)-th largest thread maximum (bitwise
-  //      search on order-preserving keys) ----
+  //      search on order-preserving keys).  A bf16 value's key ends in 16
+  //      equal bits, so the search stops after the upper half: the low half
+  //      stays 0, which puts t0 just below that value and no bf16 value in
+  //      between, so the same elements reach it. ----
   const int kw = (a.nw + NWV - 1) / NWV;
   const uint32_t tkey = f2key(acc.xmax);
   uint32_t K = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  constexpr int kLowBit = BF16 ? 16 : 0;
+  for (int bit = 31; bit >= kLowBit; --bit) {
     const uint32_t cand = K | (1u << bit);
     if ((int)__popcll(ballot(tkey >= cand)) >= kw) K = cand;
   }
@@ -421,25 +430,28 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const float t0 = key2f(t0key);
 
   // ---- candidates: every element >= t0 of the units whose max reaches it.
-  //      The best unit is in registers; the lane reads its other such units
-  //      again (a fraction of a per cent of the units; units past the chunk
-  //      have um = -inf < t0).  Places are taken with one LDS atomic per
+  //      The lane reads such units again, apart from a best unit kept in
+  //      registers (a fraction of a per cent of the units; units past the
+  //      chunk have um = -inf < t0).  Places are taken with one LDS atomic per
   //      wave, so the list has no fixed order (the row finisher does not
   //      need one); a list longer than cap_out sends the row to the exact
   //      path. ----
-  uint32_t more = 0;  // bit k: unit k (other than the best) reaches t0
+  uint32_t more = 0;  // bit k: unit k (other than a kept best) reaches t0
 #pragma unroll
-  for (int k = 0; k < NU; ++k) more |= (um[k] >= t0 && k != bestk) ? (1u << k) : 0u;
+  for (int k = 0; k < NU; ++k) more |= (um[k] >= t0 && !(kKeepBest && k == bestk)) ? (1u << k) : 0u;
   Cand* dst = a.cand + ((int64_t)g.r * a.nchunks + g.ci) * a.cap_out;
   const int id0 = (int)g.e0;  // token id of chunk element 0
   uint4 lw[3];
   int lrel[3];
   bool lon[3];
-  lw[0] = bw;
-  lrel[0] = rel0 + bestk * BS * EPV;
-  lon[0] = bestk >= 0 && bestv >= t0;
+  constexpr int r0 = kKeepBest ? 1 : 0;
+  if constexpr (kKeepBest) {
+    lw[0] = bw;
+    lrel[0] = rel0 + bestk * BS * EPV;
+    lon[0] = bestk >= 0 && bestv >= t0;
+  }
 #pragma unroll
-  for (int r = 1; r < 3; ++r) {
+  for (int r = r0; r < 3; ++r) {
     lon[r] = more != 0;
     lrel[r] = 0;
     lw[r] = make_uint4(0u, 0u, 0u, 0u);
