@@ -130,11 +130,11 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
 
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
  * arguments are non-NULL, every later spec_verify_sample /
- * spec_verify_greedy / spec_accept_stats call records `start_event` just
- * before and `stop_event` just after its streaming row-pass kernel (the
- * HBM-bound pass over the logits) on the call's stream.  Both are hipEvent_t
- * handles owned by the caller.  Passing NULL for either turns it off.  Event
- * records are plain stream operations; nothing else changes. */
+ * spec_verify_greedy / spec_accept_stats call attaches the two events to the
+ * dispatch of its streaming row-pass kernel (the HBM-bound pass over the
+ * logits) on the call's stream: `start_event` takes the kernel's start time
+ * and `stop_event` its end time.  Both are hipEvent_t handles owned by the
+ * caller.  Passing NULL for either turns it off.  Nothing else changes. */
 sv_status spec_set_rowpass_timer(void* start_event, void* stop_event);
 
 /* Static description of a status code. */

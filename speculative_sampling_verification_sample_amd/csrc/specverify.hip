@@ -9,6 +9,7 @@
 //
 // Nothing here allocates or frees device memory: every scratch buffer is a
 // slice of the caller's workspace.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -164,26 +165,28 @@ sv_status launched() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_H
 
 hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;  // profiling hook
 
-void record_timer(hipEvent_t e, hipStream_t st) {
-  if (g_timer_start && g_timer_stop) (void)hipEventRecord(e, st);
+// Launches a row pass.  With the profiling hook set, the two events are
+// attached to the kernel's own dispatch, so they take its start and end
+// times.
+void launch_row_kernel(void (*kernel)(RowPassArgs), dim3 grid, dim3 block, hipStream_t st, const RowPassArgs& a) {
+  if (g_timer_start && g_timer_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timer_start, g_timer_stop, 0, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
 }
 
 template <int MODE, bool BF16>
 void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  record_timer(g_timer_start, st);
-  hipLaunchKernelGGL((rowpass_kernel<MODE, BF16, 256>), grid, dim3(256), 0, st, a);
-  record_timer(g_timer_stop, st);
+  launch_row_kernel(rowpass_kernel<MODE, BF16, 256>, grid, dim3(256), st, a);
 }
 
 template <bool BF16, bool NEED_S>
 void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  record_timer(g_timer_start, st);
-  if (p.nu == 16) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 16>), grid, dim3(kTruncBS), 0, st, a);
-  else if (p.nu == 8) hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 8>), grid, dim3(kTruncBS), 0, st, a);
-  else hipLaunchKernelGGL((trunc_pass_kernel<BF16, NEED_S, 4>), grid, dim3(kTruncBS), 0, st, a);
-  record_timer(g_timer_stop, st);
+  if (p.nu == 16) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 16>, grid, dim3(kTruncBS), st, a);
+  else if (p.nu == 8) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 8>, grid, dim3(kTruncBS), st, a);
+  else launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 4>, grid, dim3(kTruncBS), st, a);
 }
 
 template <bool BF16>
