@@ -53,4 +53,9 @@ from .verify import (  # noqa: F401
     verify_greedy,
     stats_request,
     accept_stats,
+    draft_q_rows,
+    verify_request_draft_logits,
+    verify_sample_draft_logits,
+    stats_request_draft_logits,
+    accept_stats_draft_logits,
 )

@@ -355,3 +355,68 @@ def accept_stats(logits, q, ids, T, top_k=0, top_p=1.0, requests=None):
         return tuple(np.zeros((0, gamma)) for _ in range(4))
     arr = np.stack(res)  # [B', 4, gamma]
     return arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3]
+
+
+# --------------------------------------------------------------------------
+# q formed from the draft's logits
+# --------------------------------------------------------------------------
+
+def draft_q_rows(dz_rows, T, top_k=0, top_p=1.0):
+    """The draft distributions q_j formed from the draft's logits.
+
+    [WR] §2.3 and [MN] §二 (notation): q, like p, is the distribution after
+    the decoding rules, so q_j is the draft's logits row put through exactly
+    the processing of ``process_row`` with the same parameters.  A draft row
+    holding NaN / +Inf (or all -Inf) has no q: its row is NaN.
+    Returns (rows, top_p_boundary), the second flag as in ``process_row``.
+    """
+    rows = []
+    boundary = False
+    for z in dz_rows:
+        r = process_row(z, T, top_k, top_p)
+        rows.append(np.full(np.asarray(z).size, np.nan) if r.nonfinite else r.p)
+        boundary = boundary or r.top_p_boundary
+    return rows, boundary
+
+
+def verify_request_draft_logits(z_rows, dz_rows, ids, u_accept, u_resample, T, top_k=0, top_p=1.0):
+    """``verify_request`` with q_j = the processed draft logits row j."""
+    q_rows, q_boundary = draft_q_rows(dz_rows, T, top_k, top_p)
+    res = verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k, top_p)
+    res.top_p_boundary = res.top_p_boundary or q_boundary
+    return res
+
+
+def verify_sample_draft_logits(logits, draft_logits, ids, u_accept, u_resample, T, top_k=0, top_p=1.0,
+                               requests=None):
+    """Batched ``verify_request_draft_logits``; draft_logits: float64 [B, gamma, V]."""
+    req = range(logits.shape[0]) if requests is None else requests
+    gamma = ids.shape[1]
+    res = [
+        verify_request_draft_logits(logits[b], draft_logits[b], ids[b], u_accept[b], u_resample[b], T, top_k,
+                                    top_p)
+        for b in req
+    ]
+    return _batch_result(res, gamma)
+
+
+def stats_request_draft_logits(z_rows, dz_rows, ids, T, top_k=0, top_p=1.0):
+    """``stats_request`` with q_j = the processed draft logits row j; a
+    position whose draft row has no q gives NaN in all four outputs."""
+    q_rows, _ = draft_q_rows(dz_rows, T, top_k, top_p)
+    out = stats_request(z_rows, q_rows, ids, T, top_k, top_p)
+    for j, q in enumerate(q_rows):
+        if np.isnan(q).all():
+            out[:, j] = np.nan
+    return out
+
+
+def accept_stats_draft_logits(logits, draft_logits, ids, T, top_k=0, top_p=1.0, requests=None):
+    """Batched ``stats_request_draft_logits``; returns (alpha, z_pq, z_qp, accept_prob)."""
+    req = range(logits.shape[0]) if requests is None else requests
+    res = [stats_request_draft_logits(logits[b], draft_logits[b], ids[b], T, top_k, top_p) for b in req]
+    gamma = ids.shape[1]
+    if not res:
+        return tuple(np.zeros((0, gamma)) for _ in range(4))
+    arr = np.stack(res)
+    return arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3]
