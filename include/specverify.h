@@ -128,12 +128,47 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
                             float* out_z_qp, float* out_accept_prob, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ---- q formed in the library from the draft's logits -----------------------
+ * [WR] §2.3 and [MN] §二 (notation): q, like p, is the distribution after the
+ * decoding rules.  These calls take the draft model's logits instead of q and
+ * form q_j with the same rules and the same parameters as p_j (temperature,
+ * top-k on the logits, top-p on the renormalised top-k distribution,
+ * renormalise), then verify or measure exactly as the calls above do with
+ * that q.
+ *   draft_logits [B, gamma, V]  draft_dt (float32 or bfloat16), contiguous,
+ *                               16-byte aligned base; read-only.
+ * A draft row holding NaN or +Inf (or all -Inf) has no q: it reads as a NaN
+ * q row, so a valid draft id at that position makes the request
+ * SV_ROW_NONFINITE (as a NaN q(d) does above), and the statistics of that
+ * position are NaN.  A draft id outside the draft's own kept set has
+ * q(d) = 0 (SV_ROW_Q_ZERO rules).
+ * The workspace holds both the target's and the draft rows' intermediate
+ * results; size it with spec_verify_draft_logits_workspace_size (0 for
+ * invalid sizes).  Everything else (outputs, errors, streams, determinism)
+ * is as for spec_verify_sample / spec_accept_stats. */
+size_t spec_verify_draft_logits_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt,
+                                               sv_dtype draft_dt, sv_sampling_params prm);
+
+sv_status spec_verify_sample_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                          sv_dtype draft_dt, const int32_t* draft_ids, const float* u_accept,
+                                          const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                                          sv_sampling_params prm, int32_t* out_tokens, int32_t* out_num_accepted,
+                                          uint32_t* out_row_flags, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                         sv_dtype draft_dt, const int32_t* draft_ids, int32_t B, int32_t gamma,
+                                         int32_t V, sv_sampling_params prm, float* out_alpha, float* out_z_pq,
+                                         float* out_z_qp, float* out_accept_prob, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
  * arguments are non-NULL, every later spec_verify_sample /
  * spec_verify_greedy / spec_accept_stats call attaches the two events to the
  * dispatch of its streaming row-pass kernel (the HBM-bound pass over the
- * logits) on the call's stream: `start_event` takes the kernel's start time
- * and `stop_event` its end time.  Both are hipEvent_t handles owned by the
+ * target logits; not the draft rows' pass of the draft-logits calls) on the
+ * call's stream: `start_event` takes the kernel's start time and
+ * `stop_event` its end time.  Both are hipEvent_t handles owned by the
  * caller.  Passing NULL for either turns it off.  Nothing else changes. */
 sv_status spec_set_rowpass_timer(void* start_event, void* stop_event);
 

@@ -12,7 +12,10 @@ from .api import (  # noqa: F401
     FLAG_Q_ZERO,
     FLAG_Z_DEGENERATE,
     accept_stats,
+    accept_stats_draft_logits,
+    draft_logits_workspace_size,
     verify_greedy,
     verify_sample,
+    verify_sample_draft_logits,
     workspace_size,
 )

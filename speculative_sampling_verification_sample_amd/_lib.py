@@ -39,6 +39,18 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
          _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_draft_logits_workspace_size": (
+        _size, [_c_int32, _c_int32, _c_int32, ctypes.c_int, ctypes.c_int, SamplingParamsC]),
+    "spec_verify_sample_draft_logits": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32,
+         SamplingParamsC, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
+    "spec_accept_stats_draft_logits": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
+         _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "spec_set_rowpass_timer": (ctypes.c_int, [_ptr, _ptr]),
 }

@@ -149,3 +149,79 @@ def accept_stats(logits, q, ids, temperature=1.0, top_k=0, top_p=1.0,
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_accept_stats")
     return alpha, zpq, zqp, acc
+
+
+def draft_logits_workspace_size(B: int, gamma: int, V: int, dtype=torch.bfloat16, draft_dtype=torch.bfloat16,
+                                temperature=1.0, top_k=0, top_p=1.0) -> int:
+    n = load_library().spec_verify_draft_logits_workspace_size(
+        B, gamma, V, _DT[dtype], _DT[draft_dtype], _params(temperature, top_k, top_p))
+    if n == 0:
+        raise ValueError("invalid sizes or sampling parameters")
+    return int(n)
+
+
+def verify_sample_draft_logits(logits, draft_logits, ids, u_accept, u_resample, temperature=1.0, top_k=0,
+                               top_p=1.0, workspace: Optional[torch.Tensor] = None, out=None):
+    """Sampling verify step with q formed from the draft's logits [B, gamma, V]
+    by the same rules as p; returns (tokens, n_accepted, flags)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    ddt = logits.dtype
+    if G > 0:
+        _check(draft_logits, "draft_logits", None, (B, G, V))
+        if draft_logits.dtype not in _DT:
+            raise ValueError("draft_logits must be float32 or bfloat16")
+        ddt = draft_logits.dtype
+        _check(ids, "ids", torch.int32, (B, G))
+        _check(u_accept, "u_accept", torch.float32, (B, G))
+    _check(u_resample, "u_resample", torch.float32, (B, G1))
+    if out is None:
+        out = (torch.empty((B, G1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    tokens, nacc, flags = out
+    need = draft_logits_workspace_size(B, G, V, logits.dtype, ddt, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_draft_logits(
+        logits.data_ptr(), _DT[logits.dtype],
+        draft_logits.data_ptr() if G > 0 else None, _DT[ddt], ids.data_ptr() if G > 0 else None,
+        u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_draft_logits")
+    return tokens, nacc, flags
+
+
+def accept_stats_draft_logits(logits, draft_logits, ids, temperature=1.0, top_k=0, top_p=1.0,
+                              workspace: Optional[torch.Tensor] = None, out=None):
+    """Per-position (alpha, Z, Z', accept_prob) with q formed from the draft's logits."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    _check(draft_logits, "draft_logits", None, (B, G, V))
+    if draft_logits.dtype not in _DT:
+        raise ValueError("draft_logits must be float32 or bfloat16")
+    _check(ids, "ids", torch.int32, (B, G))
+    if out is None:
+        out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
+    alpha, zpq, zqp, acc = out
+    need = draft_logits_workspace_size(B, G, V, logits.dtype, draft_logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_accept_stats_draft_logits(
+        logits.data_ptr(), _DT[logits.dtype], draft_logits.data_ptr(), _DT[draft_logits.dtype], ids.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p), alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(),
+        acc.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_accept_stats_draft_logits")
+    return alpha, zpq, zqp, acc

@@ -44,7 +44,9 @@ constexpr int kUnionMax = 2048;   // LDS entries of the row finisher's candidate
 // fills the GPU and the single launch wins.
 constexpr int kOneLaunchMinB = 256;
 
-enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS };
+// CALL_DRAFT: the row passes over a draft's logits [B, gamma, V] (q formed
+// in the library): statistics and kept lists only.
+enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS, CALL_DRAFT };
 
 struct Plan {
   int64_t rows = 0;
@@ -67,7 +69,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   Plan p;
   const bool topk = prm.top_k > 0 && (int64_t)prm.top_k < V;
   const bool topp = prm.top_p < 1.0f;
-  p.rows_per_req = (kind == CALL_STATS) ? gamma : gamma + 1;
+  p.rows_per_req = (kind == CALL_STATS || kind == CALL_DRAFT) ? gamma : gamma + 1;
   p.rows = (int64_t)B * p.rows_per_req;
   p.trunc = (kind != CALL_GREEDY) && (topk || topp);
   p.mode = (kind == CALL_GREEDY) ? M_ARGMAX : (p.trunc ? M_TRUNC : M_SOFTMAX);
@@ -168,30 +170,47 @@ hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;  // profiling hook
 // Launches a row pass.  With the profiling hook set, the two events are
 // attached to the kernel's own dispatch, so they take its start and end
 // times.
-void launch_row_kernel(void (*kernel)(RowPassArgs), dim3 grid, dim3 block, hipStream_t st, const RowPassArgs& a) {
-  if (g_timer_start && g_timer_stop)
+void launch_row_kernel(void (*kernel)(RowPassArgs), dim3 grid, dim3 block, hipStream_t st, const RowPassArgs& a,
+                       bool timed) {
+  if (timed && g_timer_start && g_timer_stop)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timer_start, g_timer_stop, 0, a);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
 }
 
 template <int MODE, bool BF16>
-void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st) {
+void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st, bool timed) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  launch_row_kernel(rowpass_kernel<MODE, BF16, 256>, grid, dim3(256), st, a);
+  launch_row_kernel(rowpass_kernel<MODE, BF16, 256>, grid, dim3(256), st, a, timed);
 }
 
 template <bool BF16, bool NEED_S>
-void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st) {
+void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st, bool timed) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  if (p.nu == 16) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 16>, grid, dim3(kTruncBS), st, a);
-  else if (p.nu == 8) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 8>, grid, dim3(kTruncBS), st, a);
-  else launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 4>, grid, dim3(kTruncBS), st, a);
+  if (p.nu == 16) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 16>, grid, dim3(kTruncBS), st, a, timed);
+  else if (p.nu == 8) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 8>, grid, dim3(kTruncBS), st, a, timed);
+  else launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 4>, grid, dim3(kTruncBS), st, a, timed);
 }
 
+QSrc q_src_dense(const float* q, int64_t V) {
+  QSrc s;
+  s.dense = q;
+  s.z = nullptr;
+  s.info = nullptr;
+  s.V = V;
+  s.c = 0.0f;
+  s.zbf16 = 0;
+  return s;
+}
+
+QSrc q_src_none(int64_t V) { return q_src_dense(nullptr, V); }
+
+// `timed`: this launch carries the profiling hook's events (the target rows'
+// pass; not the draft rows').
 template <bool BF16>
 sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st,
-                      const int32_t* ids = nullptr, const float* q = nullptr, int gamma = 0, float2* gath = nullptr) {
+                      const int32_t* ids = nullptr, QSrc q = QSrc{}, int gamma = 0, float2* gath = nullptr,
+                      bool timed = true) {
   RowPassArgs a;
   a.ids = ids;
   a.q = q;
@@ -212,12 +231,12 @@ sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, floa
     // every chunk's units must fit the registers of one workgroup
     const int64_t epv = BF16 ? 8 : 4;
     if (p.chunk / epv + 2 > (int64_t)p.nu * kTruncBS) return SV_ERR_UNSUPPORTED;
-    if (p.need_s) launch_trunc<BF16, true>(p, a, st);
-    else launch_trunc<BF16, false>(p, a, st);
+    if (p.need_s) launch_trunc<BF16, true>(p, a, st, timed);
+    else launch_trunc<BF16, false>(p, a, st, timed);
   } else if (p.mode == M_SOFTMAX) {
-    launch_rowpass<M_SOFTMAX, BF16>(p, a, st);
+    launch_rowpass<M_SOFTMAX, BF16>(p, a, st, timed);
   } else {
-    launch_rowpass<M_ARGMAX, BF16>(p, a, st);
+    launch_rowpass<M_ARGMAX, BF16>(p, a, st, timed);
   }
   return launched();
 }
@@ -236,7 +255,7 @@ void set_kernel_attrs() {
 }
 
 template <bool BF16>
-sv_status run_rowfinal(const Plan& p, const void* logits, const float* q, const int32_t* ids, int64_t V, int G1,
+sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int G1,
                        int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st) {
   RowFinalArgs a;
   a.logits = logits;
@@ -273,47 +292,23 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
   return SV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
-  float c;
-  if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
-  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm).total;
-  size_t g = make_plan(CALL_GREEDY, B, gamma, V, dt, prm).total;
-  size_t s = make_plan(CALL_STATS, B, gamma, V, dt, prm).total;
-  return std::max(a, std::max(g, s));
-}
-
-sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float* draft_probs,
-                             const int32_t* draft_ids, const float* u_accept, const float* u_resample,
-                             int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, int32_t* out_tokens,
-                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  sv_status s = common_checks(target_logits, dt, B, gamma, V);
-  if (s != SV_OK) return s;
-  float c;
-  s = check_params(prm, &c);
-  if (s != SV_OK) return s;
-  if (B == 0) return SV_OK;
-  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
-  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
-    return SV_ERR_INVALID_ARG;
-  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
-  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+// The sampling verify once q's source is known (dense, or the draft's
+// logits after their row passes).  `workspace` holds plan p's regions.
+sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
+                             const int32_t* draft_ids, const float* u_accept, const float* u_resample, int32_t B,
+                             int32_t gamma, int32_t V, sv_sampling_params prm, float c, int32_t* out_tokens,
+                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
   // untruncated rows: the row pass also gathers each draft's logit and q(d)
   float2* gath = p.trunc ? nullptr : ws_at<float2>(workspace, p.off_gath);
-  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, draft_probs, gamma, gath)
-         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, draft_probs, gamma, gath);
+  sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath)
+                   : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath);
   if (s != SV_OK) return s;
   if (p.trunc) {
-    s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
-           : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
+    s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
+           : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
     if (s != SV_OK) return s;
   }
 
@@ -326,7 +321,7 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   ac.gath = gath;
   ac.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
   ac.kmax = kKMax;
-  ac.q = draft_probs;
+  ac.q = q;
   ac.ids = draft_ids;
   ac.ua = u_accept;
   ac.ur = u_resample;
@@ -348,7 +343,7 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
 
   BigArgs bg;
   bg.logits = target_logits;
-  bg.q = draft_probs;
+  bg.q = q;
   bg.V = V;
   bg.G1 = G1;
   bg.nch4 = p.nch4;
@@ -387,6 +382,115 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   if (bf) hipLaunchKernelGGL((big_finish_kernel<true>), dim3((unsigned)B), dim3(256), 0, st, bg);
   else hipLaunchKernelGGL((big_finish_kernel<false>), dim3((unsigned)B), dim3(256), 0, st, bg);
   return launched();
+}
+
+// The statistics once q's source is known; `qkept` holds q's kept lists
+// when q comes from truncated draft logits.
+sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q, const Cand* qkept,
+                            const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
+                            float c, float* out_alpha, float* out_z_pq, float* out_z_qp, float* out_accept_prob,
+                            void* workspace, hipStream_t st) {
+  const bool bf = dt == SV_BF16;
+  const int G1 = gamma + 1;
+  sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
+                   : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  if (s != SV_OK) return s;
+  s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
+         : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
+  if (s != SV_OK) return s;
+  StatsArgs a;
+  a.logits = target_logits;
+  a.q = q;
+  a.qkept = qkept;
+  a.ids = draft_ids;
+  a.V = V;
+  a.gamma = gamma;
+  a.nchunks = p.nchunks;
+  a.chunk = p.chunk;
+  a.c = c;
+  a.info = ws_at<RowInfo>(workspace, p.off_info);
+  a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
+  a.kmax = kKMax;
+  a.partials = ws_at<double>(workspace, p.off_part);
+  a.out_alpha = out_alpha;
+  a.out_zpq = out_z_pq;
+  a.out_zqp = out_z_qp;
+  a.out_acc = out_accept_prob;
+  a.rows = p.rows;
+  dim3 grid((unsigned)(p.rows * p.nchunks));
+  if (bf) hipLaunchKernelGGL((stats_chunk_kernel<true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
+  s = launched();
+  if (s != SV_OK) return s;
+  if (bf) hipLaunchKernelGGL((stats_final_kernel<true>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((stats_final_kernel<false>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
+  return launched();
+}
+
+// Row passes over the draft's logits [B, gamma, V] (plan CALL_DRAFT, in its
+// own workspace region): their statistics and kept lists define q, which
+// the target's passes then read through the returned source.
+sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* draft_ids, int32_t B, int32_t gamma,
+                         int32_t V, sv_sampling_params prm, float c, void* ws, hipStream_t st, QSrc* q_out,
+                         const Cand** qkept_out) {
+  const Plan pq = make_plan(CALL_DRAFT, B, gamma, V, ddt, prm);
+  const bool bf = ddt == SV_BF16;
+  sv_status s = bf ? run_rowpass<true>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false)
+                   : run_rowpass<false>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false);
+  if (s != SV_OK) return s;
+  s = bf ? run_rowfinal<true>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st)
+         : run_rowfinal<false>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st);
+  if (s != SV_OK) return s;
+  QSrc q;
+  q.dense = nullptr;
+  q.z = draft_logits;
+  q.info = ws_at<RowInfo>(ws, pq.off_info);
+  q.V = V;
+  q.c = c;
+  q.zbf16 = bf ? 1 : 0;
+  *q_out = q;
+  *qkept_out = pq.trunc ? ws_at<Cand>(ws, pq.off_kept) : nullptr;
+  return SV_OK;
+}
+
+// Workspace of the draft-logits calls: the target call's regions, then the
+// draft rows' (at draft_ws_offset).
+size_t draft_ws_offset(CallKind kind, int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
+  return align_up(make_plan(kind, B, gamma, V, dt, prm).total, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
+  float c;
+  if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
+  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm).total;
+  size_t g = make_plan(CALL_GREEDY, B, gamma, V, dt, prm).total;
+  size_t s = make_plan(CALL_STATS, B, gamma, V, dt, prm).total;
+  return std::max(a, std::max(g, s));
+}
+
+sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                             const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                             int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, int32_t* out_tokens,
+                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
+                            gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st);
 }
 
 sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32_t* draft_ids, int32_t B,
@@ -435,39 +539,81 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = dt == SV_BF16;
-  const int G1 = gamma + 1;
-  s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
-         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  return accept_stats_impl(p, target_logits, dt, q_src_dense(draft_probs, V), nullptr, draft_ids, B, gamma, V, prm, c,
+                           out_alpha, out_z_pq, out_z_qp, out_accept_prob, workspace, st);
+}
+
+size_t spec_verify_draft_logits_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_dtype draft_dt,
+                                               sv_sampling_params prm) {
+  float c;
+  if (check_sizes(B, gamma, V, dt) != SV_OK || check_sizes(B, gamma, V, draft_dt) != SV_OK ||
+      check_params(prm, &c) != SV_OK)
+    return 0;
+  const size_t d = make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
+  const size_t a = draft_ws_offset(CALL_SAMPLE, B, gamma, V, dt, prm) + d;
+  const size_t s = draft_ws_offset(CALL_STATS, B, gamma, V, dt, prm) + d;
+  return std::max(a, s);
+}
+
+sv_status spec_verify_sample_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                          sv_dtype draft_dt, const int32_t* draft_ids, const float* u_accept,
+                                          const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                                          sv_sampling_params prm, int32_t* out_tokens, int32_t* out_num_accepted,
+                                          uint32_t* out_row_flags, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  s = bf ? run_rowfinal<true>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st)
-         : run_rowfinal<false>(p, target_logits, draft_probs, draft_ids, V, G1, gamma, c, prm, workspace, st);
+  if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
+  float c;
+  s = check_params(prm, &c);
   if (s != SV_OK) return s;
-  StatsArgs a;
-  a.logits = target_logits;
-  a.q = draft_probs;
-  a.ids = draft_ids;
-  a.V = V;
-  a.gamma = gamma;
-  a.nchunks = p.nchunks;
-  a.chunk = p.chunk;
-  a.c = c;
-  a.info = ws_at<RowInfo>(workspace, p.off_info);
-  a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
-  a.kmax = kKMax;
-  a.partials = ws_at<double>(workspace, p.off_part);
-  a.out_alpha = out_alpha;
-  a.out_zpq = out_z_pq;
-  a.out_zqp = out_z_qp;
-  a.out_acc = out_accept_prob;
-  a.rows = p.rows;
-  dim3 grid((unsigned)(p.rows * p.nchunks));
-  if (bf) hipLaunchKernelGGL((stats_chunk_kernel<true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
-  s = launched();
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_logits == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_logits)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
+  const size_t qoff = draft_ws_offset(CALL_SAMPLE, B, gamma, V, dt, prm);
+  const size_t need = qoff + make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  QSrc q = q_src_none(V);
+  const Cand* qkept = nullptr;
+  if (gamma > 0) {
+    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c, static_cast<unsigned char*>(workspace) + qoff,
+                       st, &q, &qkept);
+    if (s != SV_OK) return s;
+  }
+  return verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c, out_tokens,
+                            out_num_accepted, out_row_flags, workspace, st);
+}
+
+sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                         sv_dtype draft_dt, const int32_t* draft_ids, int32_t B, int32_t gamma,
+                                         int32_t V, sv_sampling_params prm, float* out_alpha, float* out_z_pq,
+                                         float* out_z_qp, float* out_accept_prob, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
-  return launched();
+  if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0 || gamma == 0) return SV_OK;
+  if (draft_logits == nullptr || draft_ids == nullptr || !aligned16(draft_logits) || out_alpha == nullptr ||
+      out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr)
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
+  const size_t qoff = draft_ws_offset(CALL_STATS, B, gamma, V, dt, prm);
+  const size_t need = qoff + make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  QSrc q;
+  const Cand* qkept = nullptr;
+  s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c, static_cast<unsigned char*>(workspace) + qoff,
+                     st, &q, &qkept);
+  if (s != SV_OK) return s;
+  return accept_stats_impl(p, target_logits, dt, q, qkept, draft_ids, B, gamma, V, prm, c, out_alpha, out_z_pq,
+                           out_z_qp, out_accept_prob, workspace, st);
 }
 
 sv_status spec_set_rowpass_timer(void* start_event, void* stop_event) {

@@ -92,6 +92,134 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // e(x) relative to the integral reference R.
 __device__ __forceinline__ float e_of(float x, float c, float R) { return ex2(__builtin_fmaf(x, c, -R)); }
 
+template <bool BF16>
+__device__ __forceinline__ float load_logit(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    uint32_t h = reinterpret_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(h << 16);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// ---- the draft distribution q -----------------------------------------------
+// q is either a dense float32 tensor [B * gamma][V] handed over by the caller,
+// or the draft's logits [B * gamma][V] processed by the same rules as the
+// target's ([WR] §2.3: p and q are both the distributions after the decoding
+// rules): q_j(x) = e_j(z(x)) / S_j on the draft row's kept set {z >= tau_j},
+// 0 elsewhere, from that row's statistics (S, R, tau) found by the same
+// row passes.  A draft row without usable statistics (NaN / +Inf logits, or
+// all -Inf) gives q = NaN.
+struct QSrc {
+  const float* dense;   // dense q, or null
+  const void* z;        // draft logits when dense is null; both null: no q (reads give 0)
+  const RowInfo* info;  // statistics of the draft rows (with z)
+  int64_t V;
+  float c;              // log2(e) / T, shared with the target
+  int32_t zbf16;        // the draft logits are bfloat16
+};
+
+// One q row.
+struct QRow {
+  const float* dense;  // start of the dense row, or null
+  const void* z;
+  int64_t zoff;        // element offset of the row in z
+  double invS;
+  float R, tau, c;
+  int32_t zbf16;
+  int32_t bad;         // unusable draft row: q is NaN
+
+  __device__ __forceinline__ float from_logit(float zz) const {
+    if (bad) return __builtin_nanf("");
+    return zz >= tau ? (float)((double)e_of(zz, c, R) * invS) : 0.0f;
+  }
+  __device__ __forceinline__ float at(int64_t x) const {
+    if (dense) return dense[x];
+    if (z == nullptr) return 0.0f;
+    return from_logit(zbf16 ? load_logit<true>(z, zoff + x) : load_logit<false>(z, zoff + x));
+  }
+  // q at x0 .. x0+7 (0 past V); 16-byte loads where the segment is whole and
+  // aligned.
+  __device__ __forceinline__ void seg8(int64_t x0, int64_t V, float* qv) const {
+    const bool full = x0 + 8 <= V;
+    if (dense) {
+      const float* p = dense + x0;
+      if (full && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        widen<false>(reinterpret_cast<const uint4*>(p)[0], qv);
+        widen<false>(reinterpret_cast<const uint4*>(p)[1], qv + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qv[k] = (x0 + k < V) ? p[k] : 0.0f;
+      }
+      return;
+    }
+    if (z == nullptr) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = 0.0f;
+      return;
+    }
+    const int64_t o = zoff + x0;
+    float zz[8];
+    if (zbf16) {
+      if (full && (o & 7) == 0) {
+        widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], zz);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) zz[k] = (x0 + k < V) ? load_logit<true>(z, o + k) : kNegInf;
+      }
+    } else {
+      if (full && (o & 3) == 0) {
+        const uint4* p = reinterpret_cast<const uint4*>(z) + (o >> 2);
+        widen<false>(p[0], zz);
+        widen<false>(p[1], zz + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) zz[k] = (x0 + k < V) ? load_logit<false>(z, o + k) : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = (x0 + k < V) ? from_logit(zz[k]) : 0.0f;
+  }
+};
+
+__device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
+  QRow r;
+  r.dense = s.dense ? s.dense + row * s.V : nullptr;
+  r.z = s.dense ? nullptr : s.z;
+  r.zoff = row * s.V;
+  r.c = s.c;
+  r.zbf16 = s.zbf16;
+  r.invS = 0.0;
+  r.R = 0.0f;
+  r.tau = kLowest;
+  r.bad = 0;
+  if (r.z != nullptr) {
+    const RowInfo ri = s.info[row];
+    r.bad = (ri.flags & RF_NONFINITE) ? 1 : 0;
+    r.invS = 1.0 / ri.S;
+    r.R = ri.R;
+    r.tau = ri.tau;
+  }
+  return r;
+}
+
+// A row view that reads 0 everywhere (no q: bonus draws).
+__device__ __forceinline__ QRow q_none() {
+  QRow r;
+  r.dense = nullptr;
+  r.z = nullptr;
+  r.zoff = 0;
+  r.invS = 0.0;
+  r.R = 0.0f;
+  r.tau = kLowest;
+  r.c = 0.0f;
+  r.zbf16 = 0;
+  r.bad = 0;
+  return r;
+}
+
+__device__ __forceinline__ float q_at(const QSrc& s, int64_t row, int64_t x) { return q_row(s, row).at(x); }
+
 // Order-preserving key of a float (-0 folded onto +0, so keys of equal
 // values are equal).
 __device__ __forceinline__ uint32_t f2key(float f) {

@@ -23,7 +23,7 @@ namespace sv {
 
 struct RowFinalArgs {
   const void* logits;
-  const float* q;       // [B, gamma, V]
+  QSrc q;               // draft distribution, rows [B * gamma]
   const int32_t* ids;   // [B, gamma]
   int64_t V;
   int32_t rows_per_req;
@@ -45,20 +45,10 @@ struct RowFinalArgs {
   Cand* kept;           // [rows][kmax]  (v = e(x), idx = token id), id order
 };
 
-template <bool BF16>
-__device__ __forceinline__ float load_logit(const void* p, int64_t i) {
-  if constexpr (BF16) {
-    uint32_t h = reinterpret_cast<const uint16_t*>(p)[i];
-    return __uint_as_float(h << 16);
-  } else {
-    return reinterpret_cast<const float*>(p)[i];
-  }
-}
-
 // Draft gather for a row whose kept set and normaliser are final: the
 // draft's logit and q(d) (acceptance needs e(d), q(d) and S only).
 template <bool BF16>
-__device__ void gather_draft_at(const void* logits, const float* q, const int32_t* ids, int64_t V, int gamma,
+__device__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int gamma,
                                 float c, int b, int j, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
@@ -72,7 +62,7 @@ __device__ void gather_draft_at(const void* logits, const float* q, const int32_
   ri.d = d;
   float z = load_logit<BF16>(logits, rowoff + d);
   ri.ed = (z >= ri.tau) ? e_of(z, c, ri.R) : 0.0f;
-  ri.qd = q[((int64_t)b * gamma + j) * V + d];
+  ri.qd = q_at(q, (int64_t)b * gamma + j, d);
 }
 
 template <bool BF16>
@@ -119,7 +109,7 @@ __device__ inline bool merge_nonfinite(const RowMerge& m) {
 // Row info of an untruncated row straight from its chunk results; the
 // draft's logit and q(d) come from the row pass's gather when `gath` is set.
 template <bool BF16>
-__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const float* q,
+__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const QSrc& q,
                                     const int32_t* ids, int64_t V, int gamma, int b, int j, int64_t rowoff,
                                     const float2* gath = nullptr) {
   RowMerge m = merge_chunks(co, nchunks, c);
@@ -583,7 +573,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
 
   if (tid == kWave && gd >= 0 && (int64_t)gd < a.V) {
     gz = load_logit<BF16>(a.logits, rowoff + gd);
-    gq = a.q[((int64_t)b * a.gamma + j) * a.V + gd];
+    gq = q_at(a.q, (int64_t)b * a.gamma + j, gd);
   }
 
   // ---- candidate union (entries >= the highest chunk threshold) ----

@@ -49,7 +49,7 @@ struct RowPassArgs {
   // Optional draft gather (untruncated sampling): the workgroup whose chunk
   // holds d_j stores (z(d_j), q_j(d_j)) in gath[row].
   const int32_t* ids;
-  const float* q;
+  QSrc q;
   int32_t gamma;
   float2* gath;
 };
@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     if ((int64_t)d >= g.e0 && (int64_t)d < g.e1) {
       const float zd = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.logits)[g.rowoff + d] << 16)
                             : reinterpret_cast<const float*>(a.logits)[g.rowoff + d];
-      a.gath[g.r] = make_float2(zd, a.q[((int64_t)g.b * a.gamma + g.j) * a.V + d]);
+      a.gath[g.r] = make_float2(zd, q_at(a.q, (int64_t)g.b * a.gamma + g.j, d));
     }
   }
 

@@ -26,7 +26,7 @@ struct AcceptArgs {
   float c;
   const Cand* kept;     // [rows][kmax]
   int32_t kmax;
-  const float* q;
+  QSrc q;
   const int32_t* ids;
   const float* ua;
   const float* ur;
@@ -42,7 +42,7 @@ struct AcceptArgs {
 // Draw from the kept list of one row, stored in token-id order (called by a
 // whole wave).
 // residual: weights (e/S - q)_+ on the list; otherwise e/S.
-__device__ int draw_from_list(const Cand* L, int n, double S, const float* qrow, bool& residual, float u,
+__device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bool& residual, float u,
                               uint32_t& fl) {
   const int lane = lane_id();
   const double invS = 1.0 / S;
@@ -51,7 +51,7 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const float* qrow,
     Cand e = L[i];
     double p = (double)e.v * invS;
     if (!res) return p;
-    double d = p - (double)qrow[e.idx];
+    double d = p - (double)qr.at(e.idx);
     return d > 0.0 ? d : 0.0;
   };
   auto total = [&](bool res) -> double {
@@ -91,8 +91,8 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const float* qrow,
 // Full-row draw by one wave (oversized kept sets of truncated rows, which
 // are rare): two passes over the row, weights as in the chunked sampler.
 template <bool BF16>
-__device__ int draw_full_row_wave(const void* logits, const float* q, int64_t V, float c, int64_t row, int64_t qrow,
-                                  double S, float R, float tau, float u, bool& residual, uint32_t& fl) {
+__device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V, float c, int64_t row, double S,
+                                  float R, float tau, float u, bool& residual, uint32_t& fl) {
   const int lane = lane_id();
   auto weight = [&](int64_t x, bool res) -> double {
     if (x >= V) return 0.0;
@@ -100,7 +100,7 @@ __device__ int draw_full_row_wave(const void* logits, const float* q, int64_t V,
     if (!(z >= tau)) return 0.0;
     double e = (double)e_of(z, c, R);
     if (!res) return e;
-    double d = e - (double)q[qrow * V + x] * S;
+    double d = e - (double)qr.at(x) * S;
     return d > 0.0 ? d : 0.0;
   };
   auto total = [&](bool res) -> double {
@@ -191,8 +191,9 @@ __device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl
   const float u = a.ur[(int64_t)b * G1 + nacc];
   const int64_t trow = (int64_t)b * G1 + nacc;
   const int64_t qrow = residual ? (int64_t)b * G + nacc : -1;
+  const QRow qr = residual ? q_row(a.q, qrow) : q_none();
   if ((rs.flags & RF_BIG) && BIG_INWAVE) {
-    int token = draw_full_row_wave<BF16>(a.logits, a.q, a.V, a.c, trow, qrow, rs.S, rs.R, rs.tau, u, residual, fl);
+    int token = draw_full_row_wave<BF16>(a.logits, qr, a.V, a.c, trow, rs.S, rs.R, rs.tau, u, residual, fl);
     if (lane == 0) {
       out[nacc] = token;
       a.out_nacc[b] = nacc;
@@ -219,7 +220,6 @@ __device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl
     }
     return;
   }
-  const float* qr = residual ? a.q + qrow * a.V : nullptr;
   int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
   if (lane == 0) {
     out[nacc] = token;
@@ -369,12 +369,12 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
 // the same arithmetic to find the token.  Workgroups never wait on or signal
 // each other inside a launch.
 // ---------------------------------------------------------------------------
-constexpr int kSeg = 8;
+constexpr int kSeg = 8;  // tokens per thread segment (QRow::seg8)
 constexpr int kChunk4 = 256 * kSeg;
 
 struct BigArgs {
   const void* logits;
-  const float* q;
+  QSrc q;
   int64_t V;
   int32_t G1;
   int32_t nch4;
@@ -411,17 +411,7 @@ __device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, 
     }
   }
   float qv[kSeg];
-  if (residual) {
-    const int64_t qo = (int64_t)jb.qrow * V + x0;
-    if (full && (qo & 3) == 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.q) + (qo >> 2);
-      widen<false>(p[0], qv);
-      widen<false>(p[1], qv + 4);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q[qo + k] : 0.0f;
-    }
-  }
+  if (residual) q_row(a.q, jb.qrow).seg8(x0, V, qv);
 #pragma unroll
   for (int k = 0; k < kSeg; ++k) {
     double wk = 0.0;
@@ -676,17 +666,7 @@ __device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, boo
       for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
     }
   }
-  if (residual) {
-    const int64_t qo = (int64_t)jb.qrow * V + x0;
-    if (full && (qo & 3) == 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.q) + (qo >> 2);
-      widen<false>(p[0], qv);
-      widen<false>(p[1], qv + 4);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q[qo + k] : 0.0f;
-    }
-  }
+  if (residual) q_row(a.q, jb.qrow).seg8(x0, V, qv);
 }
 
 __device__ __forceinline__ void seg_weigh(const BigJob& jb, float c, bool residual, const float* z, const float* qv,
@@ -925,13 +905,19 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
 
 // ---------------------------------------------------------------------------
 // Statistics ([WR] §4.2, [RL] §2): per (row, chunk) partial sums, then a
-// per-row finish.  Rows with a stored kept list need only sum(q) from the
-// chunk pass; the min / positive-part sums over the kept set come from the
-// list.  Other rows stream logits and q together.
+// per-row finish.
+//   dense q: rows with a stored kept list need only sum(q) from the chunk
+//     pass; the min / positive-part sums over the kept set come from the
+//     list.  Other rows stream logits and q together.
+//   q from the draft's logits: q is 0 off the draft's kept set, so when both
+//     rows have stored lists alpha and Z come from p's list and Z' from q's
+//     list (p evaluated at its ids), with no chunk pass; otherwise the row is
+//     streamed like an untruncated one.
 // ---------------------------------------------------------------------------
 struct StatsArgs {
   const void* logits;
-  const float* q;
+  QSrc q;
+  const Cand* qkept;    // q's kept lists [B * gamma][kmax] (q from logits, truncated rows), else null
   const int32_t* ids;
   int64_t V;
   int32_t gamma;
@@ -949,6 +935,12 @@ struct StatsArgs {
   int64_t rows;
 };
 
+// Does the row need the full-row sums of the chunk pass?
+__device__ __forceinline__ bool stats_streamed(const StatsArgs& a, const RowInfo& ri, int64_t r) {
+  if (a.q.dense != nullptr) return (ri.flags & RF_BIG) != 0;
+  return ((ri.flags | a.q.info[r].flags) & RF_BIG) != 0 || a.qkept == nullptr;
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -958,12 +950,13 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   const RowInfo ri = a.info[r];
   const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
   const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
-  const int64_t qrowo = r * a.V;
   const int64_t x0 = (int64_t)ci * a.chunk, x1 = min(x0 + a.chunk, a.V);
   double mn = 0.0, pq = 0.0, qp = 0.0, sq = 0.0;
   __shared__ double s_p[4][4];
-  if (!(ri.flags & RF_NONFINITE)) {
-    const bool big = (ri.flags & RF_BIG) != 0;
+  const bool big = stats_streamed(a, ri, r);
+  // with q from logits, rows finished from their lists skip the pass
+  if (!(ri.flags & RF_NONFINITE) && (big || a.q.dense != nullptr)) {
+    const QRow qr = q_row(a.q, r);
     const double invS = 1.0 / ri.S;
     // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
     const bool vec = (a.V & 7) == 0;
@@ -975,9 +968,7 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
       for (int u = 0; u < kU; ++u) {
         const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
         if (vec && x + 8 <= x1) {
-          const uint4* qp4 = reinterpret_cast<const uint4*>(a.q + qrowo + x);
-          widen<false>(qp4[0], qv[u]);
-          widen<false>(qp4[1], qv[u] + 4);
+          qr.seg8(x, a.V, qv[u]);
           if (big) {
             if constexpr (BF16) {
               widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
@@ -991,7 +982,7 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const bool in = x + k < x1;
-            qv[u][k] = in ? a.q[qrowo + x + k] : 0.0f;
+            qv[u][k] = in ? qr.at(x + k) : 0.0f;
             zv[u][k] = (in && big) ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
           }
         }
@@ -1032,13 +1023,15 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   }
 }
 
+template <bool BF16>
 __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wid;
   if (r >= a.rows) return;
   const RowInfo ri = a.info[r];
   const float qnan = __builtin_nanf("");
-  if (ri.flags & RF_NONFINITE) {
+  const bool qbad = a.q.dense == nullptr && (a.q.info[r].flags & RF_NONFINITE);
+  if ((ri.flags & RF_NONFINITE) || qbad) {
     if (lane == 0) {
       a.out_alpha[r] = qnan;
       a.out_zpq[r] = qnan;
@@ -1047,39 +1040,57 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     }
     return;
   }
-  double acc4[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int k = 0; k < 4; ++k) {
-    double v = 0.0;
-    for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * 4 + k];
-    acc4[k] = wave_sum_d(v);
-  }
   const double invS = 1.0 / ri.S;
+  const QRow qr = q_row(a.q, r);
   double alpha, zpq, zqp;
-  if (ri.flags & RF_BIG) {
+  if (stats_streamed(a, ri, r)) {
+    double acc4[3];
+    for (int k = 0; k < 3; ++k) {
+      double v = 0.0;
+      for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * 4 + k];
+      acc4[k] = wave_sum_d(v);
+    }
     alpha = acc4[0];
     zpq = acc4[1];
     zqp = acc4[2];
   } else {
     const Cand* L = a.kept + r * a.kmax;  // token-id order
-    const float* qr = a.q + r * a.V;
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     for (int i = lane; i < ri.nkept; i += kWave) {
       Cand e = L[i];
       double p = (double)e.v * invS;
-      double qv = (double)qr[e.idx];
+      double qv = (double)qr.at(e.idx);
       double d = p - qv;
       mn += fmin(p, qv);
       if (d > 0.0) pq += d;
       if (d < 0.0) qp -= d;
       sqk += qv;
     }
-    mn = wave_sum_d(mn);
-    pq = wave_sum_d(pq);
+    alpha = wave_sum_d(mn);
+    zpq = wave_sum_d(pq);
     qp = wave_sum_d(qp);
     sqk = wave_sum_d(sqk);
-    alpha = mn;
-    zpq = pq;
-    zqp = (acc4[3] - sqk) + qp;
+    if (a.q.dense != nullptr) {
+      double sq = 0.0;
+      for (int c = lane; c < a.nchunks; c += kWave) sq += a.partials[(r * a.nchunks + c) * 4 + 3];
+      zqp = (wave_sum_d(sq) - sqk) + qp;
+    } else {
+      // Z' = sum over q's kept set of (q - p)_+, with p read at its ids
+      const RowInfo qi = a.q.info[r];
+      const double qinvS = 1.0 / qi.S;
+      const Cand* Lq = a.qkept + r * a.kmax;
+      const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
+      const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
+      double zq = 0.0;
+      for (int i = lane; i < qi.nkept; i += kWave) {
+        Cand e = Lq[i];
+        const double qv = (double)e.v * qinvS;
+        const float z = load_logit<BF16>(a.logits, lrow + e.idx);
+        const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
+        if (qv > p) zq += qv - p;
+      }
+      zqp = wave_sum_d(zq);
+    }
   }
   if (lane == 0) {
     a.out_alpha[r] = (float)alpha;

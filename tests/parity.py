@@ -19,17 +19,24 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def gpu_sample(w, **kw):
+def gpu_sample(w, draft_logits=False, **kw):
+    """The library's sampling verify; with draft_logits, q is formed by the
+    library from w.draft_logits."""
     c = w.cfg
     prm = dict(temperature=c.temperature, top_k=c.top_k, top_p=c.top_p)
     prm.update(kw)
-    tok, nacc, fl = sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, **prm)
+    if draft_logits:
+        tok, nacc, fl = sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                                      **prm)
+    else:
+        tok, nacc, fl = sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, **prm)
     torch.cuda.synchronize()
     return _np(tok), _np(nacc), _np(fl).astype(np.uint32)
 
 
-def compare_sample(w, requests=None, label="", gpu=None, **kw):
-    """Run both sides; exact match required outside boundary rows."""
+def compare_sample(w, requests=None, label="", gpu=None, draft_logits=False, **kw):
+    """Run both sides; exact match required outside boundary rows.
+    draft_logits: both sides form q from w.draft_logits."""
     c = w.cfg
     prm = dict(T=c.temperature, top_k=c.top_k, top_p=c.top_p)
     if "temperature" in kw:
@@ -38,7 +45,7 @@ def compare_sample(w, requests=None, label="", gpu=None, **kw):
         prm["top_k"] = kw["top_k"]
     if "top_p" in kw:
         prm["top_p"] = kw["top_p"]
-    tok, nacc, fl = gpu if gpu is not None else gpu_sample(w, **kw)
+    tok, nacc, fl = gpu if gpu is not None else gpu_sample(w, draft_logits=draft_logits, **kw)
     req = np.arange(c.B) if requests is None else np.asarray(requests)
     ridx = torch.as_tensor(req, device=w.logits.device)
     lg = widen(w.logits.index_select(0, ridx))
@@ -47,7 +54,11 @@ def compare_sample(w, requests=None, label="", gpu=None, **kw):
     ids = _np(w.ids.index_select(0, ridx))
     ua = _np(w.u_accept.index_select(0, ridx))
     ur = _np(w.u_resample.index_select(0, ridx))
-    o = oracle.verify_sample(lg, q, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"])
+    if draft_logits:
+        dlg = widen(w.draft_logits.index_select(0, ridx)) if G > 0 else np.zeros((len(req), 0, lg.shape[2]))
+        o = oracle.verify_sample_draft_logits(lg, dlg, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"])
+    else:
+        o = oracle.verify_sample(lg, q, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"])
     g_tok, g_nacc, g_fl = tok[req], nacc[req], fl[req]
     mism = (g_tok != o["tokens"]).any(axis=1) | (g_nacc != o["n_accepted"]) | (g_fl != o["flags"])
     boundary = o["accept_boundary"] | o["cdf_boundary"] | o["top_p_boundary"]
@@ -80,16 +91,24 @@ def compare_greedy(w, requests=None, label=""):
         raise AssertionError(f"[{label}] request {int(req[i])}: gpu {tok[req][i].tolist()} vs oracle {o['tokens'][i].tolist()}")
 
 
-def compare_stats(w, requests=None, label="", rtol=1e-5, atol=2e-7):
+def compare_stats(w, requests=None, label="", rtol=1e-5, atol=2e-7, draft_logits=False):
     c = w.cfg
-    al, zpq, zqp, acc = sv.accept_stats(w.logits, w.q, w.ids, c.temperature, c.top_k, c.top_p)
+    if draft_logits:
+        al, zpq, zqp, acc = sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, c.temperature, c.top_k,
+                                                         c.top_p)
+    else:
+        al, zpq, zqp, acc = sv.accept_stats(w.logits, w.q, w.ids, c.temperature, c.top_k, c.top_p)
     torch.cuda.synchronize()
     req = np.arange(c.B) if requests is None else np.asarray(requests)
     ridx = torch.as_tensor(req, device=w.logits.device)
     lg = widen(w.logits.index_select(0, ridx))
-    q = _np(w.q.index_select(0, ridx))
     ids = _np(w.ids.index_select(0, ridx))
-    o = oracle.accept_stats(lg, q, ids, c.temperature, c.top_k, c.top_p)
+    if draft_logits:
+        dlg = widen(w.draft_logits.index_select(0, ridx))
+        o = oracle.accept_stats_draft_logits(lg, dlg, ids, c.temperature, c.top_k, c.top_p)
+    else:
+        q = _np(w.q.index_select(0, ridx))
+        o = oracle.accept_stats(lg, q, ids, c.temperature, c.top_k, c.top_p)
     worst = 0.0
     for name, g, ov in zip(("alpha", "z_pq", "z_qp", "accept_prob"), (al, zpq, zqp, acc), o):
         g = _np(g)[req].astype(np.float64)

@@ -117,6 +117,56 @@ def test_greedy_and_stats_argument_errors():
     assert lib.spec_accept_stats(FAKE, 1, FAKE, FAKE, 2, 0, 100, _P(), FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
 
 
+def _sample_dl(lib, **kw):
+    a = dict(logits=FAKE, dt=1, dz=FAKE, ddt=1, ids=FAKE, ua=FAKE, ur=FAKE, B=2, G=3, V=100, prm=_P(),
+             tok=FAKE, nacc=FAKE, fl=None, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return lib.spec_verify_sample_draft_logits(
+        a["logits"], a["dt"], a["dz"], a["ddt"], a["ids"], a["ua"], a["ur"], a["B"], a["G"], a["V"], a["prm"],
+        a["tok"], a["nacc"], a["fl"], a["ws"], a["wsb"], a["st"])
+
+
+def _stats_dl(lib, **kw):
+    a = dict(logits=FAKE, dt=1, dz=FAKE, ddt=1, ids=FAKE, B=2, G=3, V=100, prm=_P(), ws=None, wsb=0)
+    a.update(kw)
+    return lib.spec_accept_stats_draft_logits(
+        a["logits"], a["dt"], a["dz"], a["ddt"], a["ids"], a["B"], a["G"], a["V"], a["prm"],
+        FAKE, FAKE, FAKE, FAKE, a["ws"], a["wsb"], None)
+
+
+def test_draft_logits_workspace_size():
+    lib = _lib()
+    f = lib.spec_verify_draft_logits_workspace_size
+    n = f(64, 4, 32000, 1, 1, _P(k=50))
+    # the target call's regions plus the draft rows'
+    assert n > lib.spec_verify_workspace_size(64, 4, 32000, 1, _P(k=50)) > 0
+    assert f(64, 4, 32000, 1, 0, _P()) > 0      # float32 draft, bfloat16 target
+    assert f(64, 4, 32000, 1, 7, _P()) == 0     # unknown draft dtype
+    assert f(-1, 4, 32000, 1, 1, _P()) == 0
+    assert f(1, 4, 10, 0, 0, _P(T=0.0)) == 0
+
+
+def test_draft_logits_argument_errors():
+    lib = _lib()
+    INVALID, WORKSPACE = 1, 3
+    assert _sample_dl(lib, ddt=9) == INVALID
+    assert _sample_dl(lib, dz=None) == INVALID
+    assert _sample_dl(lib, dz=FAKE + 2) == INVALID  # misaligned
+    assert _sample_dl(lib, ids=None) == INVALID
+    assert _sample_dl(lib, ua=None) == INVALID
+    assert _sample_dl(lib, logits=None) == INVALID
+    assert _sample_dl(lib, prm=_P(T=0.0)) == INVALID
+    assert _sample_dl(lib) == WORKSPACE
+    wsb = lib.spec_verify_workspace_size(2, 3, 100, 1, _P())
+    assert _sample_dl(lib, ws=FAKE, wsb=wsb) == WORKSPACE  # room for the target rows only
+    assert _sample_dl(lib, B=0) == 0
+    assert _stats_dl(lib, ddt=9) == INVALID
+    assert _stats_dl(lib, dz=None) == INVALID
+    assert _stats_dl(lib, dz=FAKE + 4) == INVALID
+    assert _stats_dl(lib) == WORKSPACE
+    assert _stats_dl(lib, G=0) == 0
+
+
 def test_product_path_fails_loudly_without_library(tmp_path):
     from speculative_sampling_verification_sample_amd import _lib as L
 

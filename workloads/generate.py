@@ -20,6 +20,8 @@ class Workload:
     ids: torch.Tensor  # [B, gamma] int32
     u_accept: torch.Tensor  # [B, gamma] float32
     u_resample: torch.Tensor  # [B, gamma+1] float32
+    # [B, gamma, V] the draft's logits that q was formed from (None for greedy)
+    draft_logits: Optional[torch.Tensor] = None
 
     @property
     def device(self):
@@ -81,12 +83,12 @@ def _sample_ids(q: torch.Tensor, gen, device) -> torch.Tensor:
     return ids.squeeze(-1).to(torch.int32)
 
 
-def _finish(cfg, logits, q, ids, gens, device) -> Workload:
+def _finish(cfg, logits, q, ids, gens, device, draft=None) -> Workload:
     u = _uniform24((cfg.B, cfg.gamma + 1, 2), gens[3], device)
     u_accept = u[:, : cfg.gamma, 0].contiguous()
     u_resample = u[:, :, 1].contiguous()
     return Workload(cfg, logits.contiguous(), None if q is None else q.contiguous(),
-                    ids.contiguous(), u_accept, u_resample)
+                    ids.contiguous(), u_accept, u_resample, None if draft is None else draft.contiguous())
 
 
 def generate(cfg, device="cpu", **override) -> Workload:
@@ -113,7 +115,7 @@ def generate(cfg, device="cpu", **override) -> Workload:
         draft = z[:, :G] + 0.5 * torch.randn((B, G, V), generator=gens[1], device=device)
         q = _draft_distribution(draft, T, cfg.top_k, cfg.top_p)
         ids = _sample_ids(q, gens[2], device)
-        return _finish(cfg, z.to(torch.float32), q, ids, gens, device)
+        return _finish(cfg, z.to(torch.float32), q, ids, gens, device, draft.to(torch.float32))
 
     if cfg.name.startswith("c3"):
         z = 3.0 * torch.randn(shape, generator=gens[0], device=device)
@@ -128,7 +130,7 @@ def generate(cfg, device="cpu", **override) -> Workload:
         del z
         q = _draft_distribution(draft.to(torch.float32), T, cfg.top_k, cfg.top_p)
         ids = _sample_ids(q, gens[2], device)
-        return _finish(cfg, logits, q, ids, gens, device)
+        return _finish(cfg, logits, q, ids, gens, device, draft)
 
     if cfg.name.startswith("c4"):
         logits = (2.5 * torch.randn(shape, generator=gens[0], device=device)).to(torch.bfloat16)
@@ -147,9 +149,8 @@ def generate(cfg, device="cpu", **override) -> Workload:
         logits = z.to(torch.bfloat16)
         del z
         q = _draft_distribution(draft.to(torch.float32), T, cfg.top_k, cfg.top_p)
-        del draft
         ids = _sample_ids(q, gens[2], device)
-        return _finish(cfg, logits, q, ids, gens, device)
+        return _finish(cfg, logits, q, ids, gens, device, draft)
 
     raise ValueError(f"unknown workload {cfg.name}")
 
@@ -174,4 +175,6 @@ def _toy(cfg, gens, device) -> Workload:
     logits = logits1.unsqueeze(0).expand(B, G + 1, V)
     q = Q.unsqueeze(0).expand(B, G, V)
     ids = _sample_ids(q, gens[2], device)
-    return _finish(cfg, logits, q, ids, gens, device)
+    # draft logits whose processed distribution (T = 1, no truncation) is Q
+    draft = torch.log(Q.to(torch.float64)).to(torch.float32).unsqueeze(0).expand(B, G, V)
+    return _finish(cfg, logits, q, ids, gens, device, draft)
