@@ -418,8 +418,14 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
   a.out_acc = out_accept_prob;
   a.rows = p.rows;
   dim3 grid((unsigned)(p.rows * p.nchunks));
-  if (bf) hipLaunchKernelGGL((stats_chunk_kernel<true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((stats_chunk_kernel<false>), grid, dim3(256), 0, st, a);
+  const bool qlog = q.dense == nullptr;
+  if (bf) {
+    if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<true, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((stats_chunk_kernel<true, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<false, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((stats_chunk_kernel<false, false>), grid, dim3(256), 0, st, a);
+  }
   s = launched();
   if (s != SV_OK) return s;
   if (bf) hipLaunchKernelGGL((stats_final_kernel<true>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);

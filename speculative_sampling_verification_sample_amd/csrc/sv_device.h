@@ -138,6 +138,28 @@ struct QRow {
     if (z == nullptr) return 0.0f;
     return from_logit(zbf16 ? load_logit<true>(z, zoff + x) : load_logit<false>(z, zoff + x));
   }
+  // q at x0 .. x0+7 of a whole segment whose 16-byte loads the caller knows
+  // to be aligned (dense rows: row * V + x0 a multiple of 4; logits: of 8
+  // for bf16, 4 for fp32).  Straight-line code, so that a caller's unrolled
+  // loop keeps several segments' loads in flight.
+  __device__ __forceinline__ void dense8(int64_t x0, float* qv) const {
+    const uint4* p = reinterpret_cast<const uint4*>(dense + x0);
+    widen<false>(p[0], qv);
+    widen<false>(p[1], qv + 4);
+  }
+  __device__ __forceinline__ void logits8(int64_t x0, float* qv) const {
+    const int64_t o = zoff + x0;
+    float zz[8];
+    if (zbf16) {
+      widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], zz);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(z) + (o >> 2);
+      widen<false>(p[0], zz);
+      widen<false>(p[1], zz + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = from_logit(zz[k]);
+  }
   // q at x0 .. x0+7 (0 past V); 16-byte loads where the segment is whole and
   // aligned.
   __device__ __forceinline__ void seg8(int64_t x0, int64_t V, float* qv) const {

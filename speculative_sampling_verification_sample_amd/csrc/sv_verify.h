@@ -411,7 +411,21 @@ __device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, 
     }
   }
   float qv[kSeg];
-  if (residual) q_row(a.q, jb.qrow).seg8(x0, V, qv);
+  if (residual) {
+    if (a.q.dense != nullptr) {
+      const int64_t qo = (int64_t)jb.qrow * V + x0;
+      if (full && (qo & 3) == 0) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.q.dense) + (qo >> 2);
+        widen<false>(p[0], qv);
+        widen<false>(p[1], qv + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q.dense[qo + k] : 0.0f;
+      }
+    } else {
+      q_row(a.q, jb.qrow).seg8(x0, V, qv);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kSeg; ++k) {
     double wk = 0.0;
@@ -666,7 +680,21 @@ __device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, boo
       for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
     }
   }
-  if (residual) q_row(a.q, jb.qrow).seg8(x0, V, qv);
+  if (residual) {
+    if (a.q.dense != nullptr) {
+      const int64_t qo = (int64_t)jb.qrow * V + x0;
+      if (full && (qo & 3) == 0) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.q.dense) + (qo >> 2);
+        widen<false>(p[0], qv);
+        widen<false>(p[1], qv + 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q.dense[qo + k] : 0.0f;
+      }
+    } else {
+      q_row(a.q, jb.qrow).seg8(x0, V, qv);
+    }
+  }
 }
 
 __device__ __forceinline__ void seg_weigh(const BigJob& jb, float c, bool residual, const float* z, const float* qv,
@@ -941,7 +969,8 @@ __device__ __forceinline__ bool stats_streamed(const StatsArgs& a, const RowInfo
   return ((ri.flags | a.q.info[r].flags) & RF_BIG) != 0 || a.qkept == nullptr;
 }
 
-template <bool BF16>
+// QLOG: q comes from the draft's logits (else dense).
+template <bool BF16, bool QLOG>
 __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t blk = blockIdx.x;
@@ -955,7 +984,7 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   __shared__ double s_p[4][4];
   const bool big = stats_streamed(a, ri, r);
   // with q from logits, rows finished from their lists skip the pass
-  if (!(ri.flags & RF_NONFINITE) && (big || a.q.dense != nullptr)) {
+  if (!(ri.flags & RF_NONFINITE) && (big || !QLOG)) {
     const QRow qr = q_row(a.q, r);
     const double invS = 1.0 / ri.S;
     // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
@@ -968,7 +997,8 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
       for (int u = 0; u < kU; ++u) {
         const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
         if (vec && x + 8 <= x1) {
-          qr.seg8(x, a.V, qv[u]);
+          if constexpr (QLOG) qr.logits8(x, qv[u]);
+          else qr.dense8(x, qv[u]);
           if (big) {
             if constexpr (BF16) {
               widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
