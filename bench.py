@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=["toy", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--draft-logits", action="store_true",
+                    help="hand the draft's logits instead of q (the library forms q); sampling workloads only")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -130,7 +132,8 @@ def main():
     def nbytes(t):
         return 0 if t is None else t.numel() * t.element_size()
 
-    per_copy = sum(nbytes(t) for t in (w0.logits, w0.q, w0.ids, w0.u_accept, w0.u_resample))
+    qsrc = w0.draft_logits if args.draft_logits else w0.q  # what the step reads for q
+    per_copy = sum(nbytes(t) for t in (w0.logits, qsrc, w0.ids, w0.u_accept, w0.u_resample))
     R = max(1, math.ceil(args.rotate_mb * 1e6 / per_copy)) if per_copy < args.rotate_mb * 1e6 else 1
     copies = [w0]
     for _ in range(R - 1):
@@ -141,8 +144,15 @@ def main():
 
     G, B, V = cfg.gamma, cfg.B, cfg.V
     greedy = cfg.mode == "greedy"
-    ws = torch.empty(sv.workspace_size(B, G, V, w0.logits.dtype, cfg.temperature, cfg.top_k, cfg.top_p),
-                     dtype=torch.uint8, device=dev)
+    dl = args.draft_logits
+    if dl and (greedy or w0.draft_logits is None):
+        raise SystemExit("--draft-logits applies to the sampling workloads (toy, c2, c3, c5)")
+    if dl:
+        need = sv.draft_logits_workspace_size(B, G, V, w0.logits.dtype, w0.draft_logits.dtype, cfg.temperature,
+                                              cfg.top_k, cfg.top_p)
+    else:
+        need = sv.workspace_size(B, G, V, w0.logits.dtype, cfg.temperature, cfg.top_k, cfg.top_p)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     outs = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
             torch.empty((B,), dtype=torch.int32, device=dev),
             torch.empty((B,), dtype=torch.int32, device=dev))
@@ -156,12 +166,18 @@ def main():
             lib.spec_set_rowpass_timer(timer[0], timer[1])
         if greedy:
             sv.verify_greedy(w.logits, w.ids, workspace=ws, out=outs)
+        elif dl:
+            sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                          cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs)
         else:
             sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, cfg.temperature, cfg.top_k,
                              cfg.top_p, workspace=ws, out=outs)
         if timer is not None:
             lib.spec_set_rowpass_timer(None, None)
-        if cfg.stats:
+        if cfg.stats and dl:
+            sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, cfg.temperature, cfg.top_k, cfg.top_p,
+                                         workspace=ws, out=sout)
+        elif cfg.stats:
             sv.accept_stats(w.logits, w.q, w.ids, cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws,
                             out=sout)
 
@@ -242,10 +258,18 @@ def main():
         step_bytes = B * (G + 1) * row_bytes + B * G * 4 + B * (G + 2) * 4
     else:
         rejected = int((nacc < G).sum())
-        q_rows = rejected * V * 4 if (cfg.top_k == 0 and cfg.top_p >= 1.0) else 0
+        untrunc = cfg.top_k == 0 and cfg.top_p >= 1.0
+        # q bytes per token: dense float32, or the draft's logits (read once
+        # per call for their statistics, again on a rejected untruncated row)
+        qb = w0.draft_logits.element_size() if dl else 4
+        q_rows = rejected * V * qb if untrunc else 0
         step_bytes = B * (G + 1) * row_bytes + q_rows + B * G * 12 + B * (G + 1) * 8 + B * 4
+        if dl:
+            step_bytes += B * G * V * qb
         if cfg.stats:
-            step_bytes += B * G * V * (cfg.logit_bytes + 4)
+            # the statistics call: the target's gamma rows and q (dense, or
+            # the draft's logits for their statistics)
+            step_bytes += B * G * V * (cfg.logit_bytes + qb)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     # ---- CPU oracle baseline on a bounded sample ----
@@ -263,12 +287,21 @@ def main():
             q = w0.q[:nsamp].cpu().numpy()
             ua = w0.u_accept[:nsamp].cpu().numpy()
             ur = w0.u_resample[:nsamp].cpu().numpy()
+        if dl:
+            dz = w0.draft_logits[:nsamp].detach().cpu()
+            dz = oracle.bf16_bits_to_f64(dz.view(torch.int16).numpy()) if dz.dtype == torch.bfloat16 \
+                else dz.double().numpy()
         done = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < args.cpu_seconds:
             b = done % nsamp
             if greedy:
                 oracle.greedy_request(lg[b], ids[b])
+            elif dl:
+                oracle.verify_request_draft_logits(lg[b], dz[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k,
+                                                   cfg.top_p)
+                if cfg.stats:
+                    oracle.stats_request_draft_logits(lg[b], dz[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             else:
                 oracle.verify_request(lg[b], q[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k, cfg.top_p)
                 if cfg.stats:
@@ -308,6 +341,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {desc}", "B": B, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temperature, "top_k": cfg.top_k, "top_p": cfg.top_p,
+                   "q": "formed from the draft's logits" if dl else "dense float32 input",
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,
                    "wall_s_timed": wall, "step_alg_bytes": step_bytes, "step_alg_GBps": step_gbps},
         "roofline": {"bound": "hbm", "kernel": "rowpass (K1)", "achieved": achieved, "peak": PEAK_GBPS,

@@ -48,7 +48,7 @@ struct RowFinalArgs {
 // Draft gather for a row whose kept set and normaliser are final: the
 // draft's logit and q(d) (acceptance needs e(d), q(d) and S only).
 template <bool BF16>
-__device__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int gamma,
+__device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int gamma,
                                 float c, int b, int j, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
@@ -66,7 +66,7 @@ __device__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t
 }
 
 template <bool BF16>
-__device__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
+__device__ __forceinline__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
   gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.gamma, a.c, b, j, rowoff, ri);
 }
 
@@ -200,7 +200,7 @@ __device__ uint32_t block_select_count(const uint32_t* keys, int n, int need, ui
 // Largest key v with mass(entries with key >= v, key >= floor) >= target.
 // Returns false when the whole mass stays below target.
 template <bool BF16>
-__device__ bool block_select_mass(const uint32_t* keys, const unsigned long long* mass, int n, uint32_t floor_key,
+__device__ __forceinline__ bool block_select_mass(const uint32_t* keys, const unsigned long long* mass, int n, uint32_t floor_key,
                                   double target, unsigned long long* mh, int* s_dn, unsigned long long* s_above,
                                   uint32_t& out_key) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -272,7 +272,7 @@ __device__ __forceinline__ int wave_append_slot(bool keep, int* counter) {
 // result does not depend on the order of the additions).
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__device__ double block_sum_d(double v, double* s_tmp) {
+__device__ __forceinline__ double block_sum_d(double v, double* s_tmp) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   v = wave_sum_d(v);
   __syncthreads();
@@ -284,7 +284,7 @@ __device__ double block_sum_d(double v, double* s_tmp) {
 }
 
 template <bool BF16>
-__device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_t rowoff, RowInfo ri) {
+__device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_t rowoff, RowInfo ri) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t V = a.V;
   const float c = a.c;
@@ -296,6 +296,89 @@ __device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_
   __shared__ int s_digit, s_need, s_cnt[4];
   __shared__ unsigned long long s_above;
   constexpr int kLow = BF16 ? 16 : 0;
+  // the lambdas below capture this copy, not the argument block, so that
+  // the block is not copied to private memory and the loads stay global
+  const void* const lg = a.logits;
+  // tokens x .. x+7 of the row (-inf past V): one 16-byte load (two for
+  // fp32) where the row is 16-byte aligned, else one load per token
+  const bool rowvec = (rowoff % (BF16 ? 8 : 4)) == 0;
+  auto seg8 = [&](int64_t x, float* z) {
+    if (rowvec && x + 8 <= V) {
+      if constexpr (BF16) {
+        widen<true>(reinterpret_cast<const uint4*>(lg)[(rowoff + x) >> 3], z);
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(lg) + rowoff + x);
+        widen<false>(p[0], z);
+        widen<false>(p[1], z + 4);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = (x + e < V) ? load_logit<BF16>(lg, rowoff + x + e) : kNegInf;
+    }
+  };
+  // body(x, z[8]) over the whole row in 8-token segments, lane-interleaved
+  // (segment tid of every 256).  A lone workgroup is bound by load latency,
+  // so batches of kEU segments per thread are loaded (as raw 16-byte words)
+  // before any is used.
+  constexpr int kW = BF16 ? 1 : 2;      // 16-byte words per segment
+  constexpr int kEU = 1;                // segments in flight per thread
+  auto load_whole = [&](int64_t x, uint4* w) {  // a whole aligned segment inside the row
+    const uint4* p = BF16 ? reinterpret_cast<const uint4*>(lg) + ((rowoff + x) >> 3)
+                          : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(lg) + rowoff + x);
+#pragma unroll
+    for (int i = 0; i < kW; ++i) w[i] = p[i];
+  };
+  auto widen_seg = [&](const uint4* w, float* z) {
+    if constexpr (BF16) {
+      widen<true>(w[0], z);
+    } else {
+      widen<false>(w[0], z);
+      widen<false>(w[1], z + 4);
+    }
+  };
+  auto for_row = [&](auto&& body) {
+    int64_t b0 = 0;
+    if (rowvec) {
+      for (; b0 + (int64_t)kEU * 2048 <= V; b0 += (int64_t)kEU * 2048) {
+        uint4 ws[kEU][kW];
+#pragma unroll
+        for (int u = 0; u < kEU; ++u) load_whole(b0 + u * 2048 + tid * 8, ws[u]);
+#pragma unroll
+        for (int u = 0; u < kEU; ++u) {
+          float zs[8];
+          widen_seg(ws[u], zs);
+          body(b0 + u * 2048 + tid * 8, zs);
+        }
+      }
+    }
+    for (int64_t x0 = b0 + (int64_t)tid * 8; x0 < V; x0 += 2048) {
+      float zs[8];
+      seg8(x0, zs);
+      body(x0, zs);
+    }
+  };
+  // the same over this thread's contiguous range [x0, x1) (x0 a multiple of 8)
+  auto for_range = [&](int64_t x0, int64_t x1, auto&& body) {
+    int64_t x = x0;
+    if (rowvec) {
+      for (; x + 8 * kEU <= x1; x += 8 * kEU) {
+        uint4 ws[kEU][kW];
+#pragma unroll
+        for (int u = 0; u < kEU; ++u) load_whole(x + u * 8, ws[u]);
+#pragma unroll
+        for (int u = 0; u < kEU; ++u) {
+          float zs[8];
+          widen_seg(ws[u], zs);
+          body(x + u * 8, zs);
+        }
+      }
+    }
+    for (; x < x1; x += 8) {
+      float zs[8];
+      seg8(x, zs);
+      body(x, zs);
+    }
+  };
 
   // ---- top-k threshold (count) ----
   float tau = kLowest;
@@ -307,12 +390,14 @@ __device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_
     for (int shift = 24; shift >= kLow; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
-      for (int64_t x = tid; x < V; x += 256) {
-        float z = load_logit<BF16>(a.logits, rowoff + x);
-        if (!(z > kNegInf)) continue;
-        uint32_t key = f2key(z);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
+      for_row([&](int64_t, const float* zs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(zs[e] > kNegInf)) continue;
+          const uint32_t key = f2key(zs[e]);
+          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+      });
       __syncthreads();
       if (shift == 24) {
         int64_t tot = 0;
@@ -335,32 +420,34 @@ __device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_
     }
     if (nfinite >= a.top_k) tau = key2f(prefix);
   }
-  // ---- mass of the top-k set ----
-  double part = 0.0;
-  for (int64_t x = tid; x < V; x += 256) {
-    float z = load_logit<BF16>(a.logits, rowoff + x);
-    if (z >= tau) part += (double)e_of(z, c, R);
-  }
-  double S = block_sum_d<BF16>(part, s_tmp);
-  // ---- top-p threshold (mass) ----
+  // ---- top-p threshold (mass), against the mass of the top-k set ----
   if (a.top_p < 1.0f) {
+    double part = 0.0;
+    for_row([&](int64_t, const float* zs) {
+      float f = 0.0f;  // a segment's 8 terms (each <= 1) in float, then into the double
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (zs[e] >= tau) f += e_of(zs[e], c, R);
+      part += (double)f;
+    });
+    const double Sk = block_sum_d<BF16>(part, s_tmp);
     const double sc = ldexp(1.0, a.scale_bits);
-    const double target = (double)a.top_p * S * sc;
+    const double target = (double)a.top_p * Sk * sc;
     uint32_t prefix = 0, pmask = 0;
     if (tid == 0) s_above = 0ull;
     bool found_all = true;
     for (int shift = 24; shift >= kLow; shift -= 8) {
       mhist[tid] = 0ull;
       __syncthreads();
-      for (int64_t x = tid; x < V; x += 256) {
-        float z = load_logit<BF16>(a.logits, rowoff + x);
-        if (!(z >= tau)) continue;
-        uint32_t key = f2key(z);
-        if ((key & pmask) == prefix) {
-          unsigned long long m = (unsigned long long)rint((double)e_of(z, c, R) * sc);
-          atomicAdd(&mhist[(key >> shift) & 255u], m);
+      for_row([&](int64_t, const float* zs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(zs[e] >= tau)) continue;
+          const uint32_t key = f2key(zs[e]);
+          if ((key & pmask) == prefix)
+            atomicAdd(&mhist[(key >> shift) & 255u], (unsigned long long)rint((double)e_of(zs[e], c, R) * sc));
         }
-      }
+      });
       __syncthreads();
       if (wid == 0) {
         // lane l holds bins 255-4l .. 252-4l
@@ -400,23 +487,32 @@ __device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_
       pmask |= 255u << shift;
     }
     if (found_all) tau = fmaxf(tau, key2f(prefix));
-    // mass of the final kept set
-    part = 0.0;
-    for (int64_t x = tid; x < V; x += 256) {
-      float z = load_logit<BF16>(a.logits, rowoff + x);
-      if (z >= tau) part += (double)e_of(z, c, R);
-    }
-    S = block_sum_d<BF16>(part, s_tmp);
   }
-  // ---- kept count and (if small) the id-ordered list ----
+  // ---- the kept set {z >= tau}: each thread takes one contiguous segment
+  //      of the row (segments in id order), counts and weighs its kept
+  //      tokens, and after one block scan writes them at their place in the
+  //      id-ordered list (no barrier inside the passes over the row) ----
+  const int64_t seglen = ((V + 255) / 256 + 7) / 8 * 8;
+  const int64_t sx0 = min((int64_t)tid * seglen, V), sx1 = min(sx0 + seglen, V);
   int cntp = 0;
-  for (int64_t x = tid; x < V; x += 256) {
-    float z = load_logit<BF16>(a.logits, rowoff + x);
-    cntp += (z >= tau) ? 1 : 0;
-  }
-  cntp = wave_sum_i(cntp);
-  if (lane == 0) s_cnt[wid] = cntp;
+  double part = 0.0;
+  for_range(sx0, sx1, [&](int64_t, const float* zs) {
+    float f = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (zs[e] >= tau) {
+        ++cntp;
+        f += e_of(zs[e], c, R);
+      }
+    }
+    part += (double)f;
+  });
+  const double S = block_sum_d<BF16>(part, s_tmp);  // fixed segments and order: deterministic
+  const int incl = wave_incl_scan_i(cntp);
+  if (lane == kWave - 1) s_cnt[wid] = incl;
   __syncthreads();
+  int before = incl - cntp;
+  for (int w = 0; w < wid; ++w) before += s_cnt[w];
   const int nkept = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
   __syncthreads();
   ri.tau = tau;
@@ -427,24 +523,19 @@ __device__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_
     ri.nkept = -1;
   } else {
     Cand* out = a.kept + r * (int64_t)a.kmax;
-    int basepos = 0;
-    for (int64_t x0 = 0; x0 < V; x0 += 256) {
-      int64_t x = x0 + tid;
-      float z = x < V ? load_logit<BF16>(a.logits, rowoff + x) : kNegInf;
-      bool k = x < V && z >= tau;
-      uint64_t m = ballot(k);
-      if (lane == 0) s_cnt[wid] = (int)__popcll(m);
-      __syncthreads();
-      int off = basepos;
-      for (int w = 0; w < wid; ++w) off += s_cnt[w];
-      if (k) {
-        Cand e;
-        e.idx = (int32_t)x;
-        e.v = e_of(z, c, R);
-        out[off + lanes_below(m)] = e;
-      }
-      basepos += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-      __syncthreads();
+    int pos = before;
+    if (cntp > 0) {
+      for_range(sx0, sx1, [&](int64_t x, const float* zs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (zs[e] >= tau) {
+            Cand ce;
+            ce.idx = (int32_t)(x + e);
+            ce.v = e_of(zs[e], c, R);
+            out[pos++] = ce;
+          }
+        }
+      });
     }
     ri.nkept = nkept;
   }
