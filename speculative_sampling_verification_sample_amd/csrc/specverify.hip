@@ -31,6 +31,9 @@ constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 p
 constexpr int kKMax = 2048;       // longest kept set stored as a list
 constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
 constexpr int kNwTopP = 128;      // chunk elements a top-p candidate threshold certifies
+// ... for the draft's own rows (q formed in the library): drafts tend to be
+// flatter, with nuclei reaching below 128 certified elements per chunk
+constexpr int kNwTopPDraft = 256;
 // Candidate list capacity of one chunk: a multiple of the certified count
 // (lists measure about 1.5-3x nw on the workloads' rows); a longer list sends
 // the row to the exact path.  It also sizes the row finisher's LDS union.
@@ -76,7 +79,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.need_s = p.trunc && topp && !topk;
   p.fast = !topk || prm.top_k <= kFastTopK;
   if (p.trunc) {
-    p.nw = topk ? std::min<int>(prm.top_k, kFastTopK) : kNwTopP;
+    p.nw = topk ? std::min<int>(prm.top_k, kFastTopK) : (kind == CALL_DRAFT ? kNwTopPDraft : kNwTopP);
     p.cap_out = std::min(kCapMax, std::max(kCapMin, kCapPerNw * p.nw));
   }
   int64_t nch, chunk;
