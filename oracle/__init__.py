@@ -38,6 +38,8 @@ from .verify import (  # noqa: F401
     FLAG_Q_ZERO,
     FLAG_Z_DEGENERATE,
     FLAG_NONFINITE,
+    FLAG_EOS,
+    FLAG_BAD_SPAN,
     BOUNDARY_EPS,
     ProcessedRow,
     RequestResult,
@@ -58,4 +60,7 @@ from .verify import (  # noqa: F401
     verify_sample_draft_logits,
     stats_request_draft_logits,
     accept_stats_draft_logits,
+    ragged_span,
+    verify_sample_ragged,
+    verify_greedy_ragged,
 )

@@ -31,7 +31,14 @@ reason, in the design notes of the repository):
 * a draft id outside [0, V) is rejected at its position and raises
   FLAG_BAD_ID;
 * the residual weight is ``p - q`` where that difference is > 0 and 0
-  otherwise (so a NaN q entry contributes no weight).
+  otherwise (so a NaN q entry contributes no weight);
+* with an end-of-sequence id (``eos >= 0``) nothing is committed after the
+  first EOS: an accepted draft equal to EOS ends the request's output there
+  (it becomes the last emitted token, so n_accepted counts the drafts before
+  it and no token is drawn), and FLAG_EOS is raised whenever an EOS is
+  emitted;
+* in a ragged batch, a request whose draft span is out of order, out of
+  range or longer than gamma_max raises FLAG_BAD_SPAN and emits nothing.
 """
 
 from __future__ import annotations
@@ -47,6 +54,8 @@ FLAG_BAD_ID = 1
 FLAG_Q_ZERO = 2
 FLAG_Z_DEGENERATE = 4
 FLAG_NONFINITE = 8
+FLAG_EOS = 16
+FLAG_BAD_SPAN = 32
 
 # Half-width of the band around an acceptance, CDF or top-p boundary inside
 # which float32 vs float64 rounding may legitimately flip a decision.
@@ -177,7 +186,7 @@ def _no_output(gamma: int, flags: int) -> RequestResult:
     return RequestResult(np.full(gamma + 1, -1, np.int32), 0, flags)
 
 
-def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_boundary=False):
+def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_boundary=False, eos=-1):
     """Left-to-right verification of gamma drafts given processed p rows.
 
     [WR] §6 (verify d_1 with p_1 / q_1, stop at the first rejection, draw the
@@ -185,7 +194,9 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
     p_{gamma+1} when all gamma drafts pass), [WR] §4.1 (acceptance
     min(1, p/q), zero q handled explicitly), [WR] §5 and [BS] §四 eq. (2)
     (residual (p - q)_+ / Z), [RL] §1 steps 3-4, [WR] §10 (a round emits
-    n_accepted + 1 tokens).
+    n_accepted + 1 tokens).  With ``eos >= 0``: [WR] §14.3 (runtime
+    invariants: no token is committed after an EOS) -- an accepted draft
+    equal to eos is the last emitted token and verification stops there.
     """
     gamma = len(ids)
     V = p_rows[0].size
@@ -218,6 +229,10 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
         if not accept:
             n_acc = j
             break
+        if d == eos:
+            tokens = np.full(gamma + 1, -1, np.int32)
+            tokens[: j + 1] = ids[: j + 1]
+            return RequestResult(tokens, j, flags | FLAG_EOS, acc_boundary, False, top_p_boundary)
     if n_acc < gamma:
         w = residual_weights(p_rows[n_acc], q_rows[n_acc])
         if not (w.sum() > 0.0):
@@ -229,10 +244,12 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
     tokens = np.full(gamma + 1, -1, np.int32)
     tokens[:n_acc] = ids[:n_acc]
     tokens[n_acc] = token
+    if eos >= 0 and token == eos:
+        flags |= FLAG_EOS
     return RequestResult(tokens, n_acc, flags, acc_boundary, cdf_boundary, top_p_boundary)
 
 
-def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=1.0):
+def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, eos=-1):
     """One request of the sampling verify step, from logits.
 
     Processes every position j = 0..gamma ([WR] §6: the target forward gives
@@ -246,7 +263,7 @@ def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=
     q64 = [np.asarray(q_rows[j], dtype=np.float64) for j in range(gamma)]
     return verify_from_processed(
         [r.p for r in rows], q64, ids, u_accept, u_resample,
-        top_p_boundary=any(r.top_p_boundary for r in rows),
+        top_p_boundary=any(r.top_p_boundary for r in rows), eos=eos,
     )
 
 
@@ -279,7 +296,7 @@ def verify_sample(logits, q, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, r
     return _batch_result(res, gamma)
 
 
-def greedy_request(z_rows, ids) -> RequestResult:
+def greedy_request(z_rows, ids, eos=-1) -> RequestResult:
     """Greedy verify: the longest draft prefix equal to the target argmax.
 
     [WR] §7.1 (accept d_i iff it is the target's most probable token,
@@ -287,6 +304,8 @@ def greedy_request(z_rows, ids) -> RequestResult:
     longest matching prefix), [BS] §二 worked example (mat/and/the/dog vs
     the target's top-1).  Argmax ties go to the lowest id (first occurrence).
     A row holding NaN raises FLAG_NONFINITE and the request emits nothing.
+    With ``eos >= 0`` a matching draft equal to eos ends the output there
+    ([WR] §14.3), as in ``verify_from_processed``.
     """
     z_rows = np.asarray(z_rows, dtype=np.float64)
     gamma = len(ids)
@@ -296,15 +315,20 @@ def greedy_request(z_rows, ids) -> RequestResult:
     g = [int(np.argmax(z_rows[j])) for j in range(gamma + 1)]
     n_acc = gamma
     flags = 0
+    tokens = np.full(gamma + 1, -1, np.int32)
     for j in range(gamma):
         if int(ids[j]) != g[j]:
             n_acc = j
             if not (0 <= int(ids[j]) < V):
                 flags |= FLAG_BAD_ID
             break
-    tokens = np.full(gamma + 1, -1, np.int32)
+        if g[j] == eos:
+            tokens[: j + 1] = [int(d) for d in ids[: j + 1]]
+            return RequestResult(tokens, j, flags | FLAG_EOS)
     tokens[:n_acc] = [int(d) for d in ids[:n_acc]]
     tokens[n_acc] = g[n_acc]
+    if eos >= 0 and g[n_acc] == eos:
+        flags |= FLAG_EOS
     return RequestResult(tokens, n_acc, flags)
 
 
@@ -420,3 +444,72 @@ def accept_stats_draft_logits(logits, draft_logits, ids, T, top_k=0, top_p=1.0, 
         return tuple(np.zeros((0, gamma)) for _ in range(4))
     arr = np.stack(res)
     return arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3]
+
+
+# --------------------------------------------------------------------------
+# Ragged batches: request b drafted gamma_b tokens
+# --------------------------------------------------------------------------
+
+def ragged_span(cu, b, n_draft, gamma_max):
+    """Draft positions [lo, hi) of request b in the packed arrays, or None
+    when the span is out of order, out of range or longer than gamma_max.
+
+    The packed layout: request b's gamma_b = cu[b+1] - cu[b] drafts are
+    positions cu[b] .. cu[b+1]-1 of the draft arrays, and its gamma_b + 1
+    target rows (and resampling uniforms) are rows cu[b] + b .. cu[b+1] + b
+    ([WR] §11.2 and [MN] §九 point 3: no one draft length suits every
+    request, so gamma is adapted per request and a batch holds different
+    gamma_b).
+    """
+    lo, hi = int(cu[b]), int(cu[b + 1])
+    if not (0 <= lo <= hi <= n_draft and hi - lo <= gamma_max):
+        return None
+    return lo, hi
+
+
+def _pad_result(res, gamma_max):
+    tokens = np.full(gamma_max + 1, -1, np.int32)
+    tokens[: res.tokens.size] = res.tokens
+    res.tokens = tokens
+    return res
+
+
+def verify_sample_ragged(logits, q, ids, cu, u_accept, u_resample, gamma_max, T, top_k=0, top_p=1.0, eos=-1,
+                         requests=None):
+    """Sampling verify of a ragged batch: ``verify_request`` on each
+    request's own gamma_b rows (layout in ``ragged_span``).
+
+    logits: float64 [N + B, V]; q: [N, V]; ids, u_accept: [N];
+    u_resample: [N + B]; cu: [B + 1].  Tokens are returned padded to
+    gamma_max + 1.
+    """
+    B = len(cu) - 1
+    N = ids.shape[0]
+    req = range(B) if requests is None else requests
+    res = []
+    for b in req:
+        sp = ragged_span(cu, b, N, gamma_max)
+        if sp is None:
+            res.append(_no_output(gamma_max, FLAG_BAD_SPAN))
+            continue
+        lo, hi = sp
+        r = verify_request(logits[lo + b: hi + b + 1], q[lo:hi], ids[lo:hi], u_accept[lo:hi],
+                           u_resample[lo + b: hi + b + 1], T, top_k, top_p, eos)
+        res.append(_pad_result(r, gamma_max))
+    return _batch_result(res, gamma_max)
+
+
+def verify_greedy_ragged(logits, ids, cu, gamma_max, eos=-1, requests=None):
+    """Greedy verify of a ragged batch (``greedy_request`` per request)."""
+    B = len(cu) - 1
+    N = ids.shape[0]
+    req = range(B) if requests is None else requests
+    res = []
+    for b in req:
+        sp = ragged_span(cu, b, N, gamma_max)
+        if sp is None:
+            res.append(_no_output(gamma_max, FLAG_BAD_SPAN))
+            continue
+        lo, hi = sp
+        res.append(_pad_result(greedy_request(logits[lo + b: hi + b + 1], ids[lo:hi], eos), gamma_max))
+    return _batch_result(res, gamma_max)
