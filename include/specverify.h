@@ -70,6 +70,10 @@ typedef struct {
 #define SV_ROW_Z_DEGENERATE 4u /* rejected with an empty residual; token drawn from p */
 #define SV_ROW_NONFINITE 8u    /* NaN/+Inf logits (or an all -Inf row), or q(d) NaN,
                                   negative or +Inf: no token emitted              */
+#define SV_ROW_EOS 16u         /* ragged calls: an end-of-sequence token was emitted */
+#define SV_ROW_BAD_SPAN 32u    /* ragged calls: the request's draft span is out of order,
+                                  out of range or longer than gamma_max: no token
+                                  emitted                                          */
 
 /* Bytes of workspace that spec_verify_sample, spec_verify_greedy and
  * spec_accept_stats need for these sizes (the maximum over the three).
@@ -161,6 +165,47 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
                                          int32_t V, sv_sampling_params prm, float* out_alpha, float* out_z_pq,
                                          float* out_z_qp, float* out_accept_prob, void* workspace,
                                          size_t workspace_bytes, void* stream);
+
+/* ---- ragged batches: a draft length per request ----------------------------
+ * [WR] §11.2 and [MN] §九 (point 3): no single draft length suits every
+ * request, so gamma is chosen per request and one verify batch holds
+ * requests with different gamma_b (0 <= gamma_b <= gamma_max).  The inputs
+ * are packed, with no padding rows:
+ *   cu_draft     [B + 1]              int32 DEVICE array, cu_draft[0] = 0,
+ *                                     non-decreasing, cu_draft[B] = n_draft;
+ *                                     gamma_b = cu_draft[b+1] - cu_draft[b]
+ *   draft_ids    [n_draft]            int32, request b's at cu_draft[b] ..
+ *   draft_probs  [n_draft, V]         float32 q rows, same positions
+ *   u_accept     [n_draft]            float32, same positions
+ *   target_logits [n_draft + B, V]    request b's gamma_b + 1 rows start at
+ *                                     row cu_draft[b] + b
+ *   u_resample   [n_draft + B]        float32, same rows as the logits
+ * n_draft (a host value) must equal cu_draft[B] and be <= B * gamma_max.
+ * Outputs are padded: out_tokens [B, gamma_max + 1] (-1 after the emitted
+ * tokens), out_num_accepted [B], out_row_flags [B].  A request whose span is
+ * out of order, out of range or longer than gamma_max is not read: it emits
+ * nothing and is flagged SV_ROW_BAD_SPAN.  gamma_b = 0 is plain sampling.
+ *
+ * End of sequence ([WR] §14.3: no token is committed after an EOS).  With
+ * eos_id >= 0, verification also stops at an accepted draft equal to
+ * eos_id: that draft is the last emitted token (at slot n_accepted, so
+ * n_accepted counts the drafts before it) and no token is drawn.  Any
+ * emitted EOS (an accepted draft, a replacement or the bonus token) raises
+ * SV_ROW_EOS.  eos_id < 0 disables the rule; eos_id >= V is an argument
+ * error.
+ * Everything else is as for spec_verify_sample / spec_verify_greedy; the
+ * workspace is spec_verify_workspace_size(B, gamma_max, V, dt, prm). */
+sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                    const int32_t* draft_ids, const int32_t* cu_draft, int32_t n_draft,
+                                    const float* u_accept, const float* u_resample, int32_t B, int32_t gamma_max,
+                                    int32_t V, sv_sampling_params prm, int32_t eos_id, int32_t* out_tokens,
+                                    int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,
+                                    const int32_t* cu_draft, int32_t n_draft, int32_t B, int32_t gamma_max,
+                                    int32_t V, int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,
+                                    uint32_t* out_row_flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
  * arguments are non-NULL, every later spec_verify_sample /

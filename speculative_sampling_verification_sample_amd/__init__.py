@@ -8,6 +8,8 @@ Python binding.
 from ._lib import LIB_PATH, load_library, status_string  # noqa: F401
 from .api import (  # noqa: F401
     FLAG_BAD_ID,
+    FLAG_BAD_SPAN,
+    FLAG_EOS,
     FLAG_NONFINITE,
     FLAG_Q_ZERO,
     FLAG_Z_DEGENERATE,
@@ -15,7 +17,9 @@ from .api import (  # noqa: F401
     accept_stats_draft_logits,
     draft_logits_workspace_size,
     verify_greedy,
+    verify_greedy_ragged,
     verify_sample,
     verify_sample_draft_logits,
+    verify_sample_ragged,
     workspace_size,
 )

@@ -51,6 +51,16 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
          _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_sample_ragged": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _c_int32, _ptr, _ptr, _c_int32, _c_int32, _c_int32,
+         SamplingParamsC, _c_int32, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
+    "spec_verify_greedy_ragged": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, _ptr, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _ptr, _ptr, _ptr,
+         _ptr, _size, _ptr],
+    ),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "spec_set_rowpass_timer": (ctypes.c_int, [_ptr, _ptr]),
 }

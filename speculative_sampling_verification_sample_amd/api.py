@@ -18,6 +18,8 @@ FLAG_BAD_ID = 1
 FLAG_Q_ZERO = 2
 FLAG_Z_DEGENERATE = 4
 FLAG_NONFINITE = 8
+FLAG_EOS = 16
+FLAG_BAD_SPAN = 32
 
 _DT = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
 
@@ -225,3 +227,69 @@ def accept_stats_draft_logits(logits, draft_logits, ids, temperature=1.0, top_k=
         acc.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_accept_stats_draft_logits")
     return alpha, zpq, zqp, acc
+
+
+def _ragged_shapes(logits, ids, cu):
+    if logits.dim() != 2:
+        raise ValueError("ragged logits must be packed [n_draft + B, V]")
+    _check(cu, "cu_draft", torch.int32, (cu.shape[0],))
+    B = cu.shape[0] - 1
+    if B < 0:
+        raise ValueError("cu_draft must hold B + 1 offsets")
+    N = ids.shape[0] if ids is not None else 0
+    V = logits.shape[1]
+    _check(logits, "logits", None, (N + B, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    if N > 0:
+        _check(ids, "ids", torch.int32, (N,))
+    return B, N, V
+
+
+def _ragged_out(out, B, gamma_max, dev):
+    if out is None:
+        out = (torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    return out
+
+
+def verify_sample_ragged(logits, q, ids, cu_draft, u_accept, u_resample, gamma_max: int, temperature=1.0, top_k=0,
+                         top_p=1.0, eos_id: int = -1, workspace: Optional[torch.Tensor] = None, out=None):
+    """Sampling verify of a ragged batch (request b has cu_draft[b+1] - cu_draft[b]
+    drafts); packed inputs: logits [n_draft + B, V], q [n_draft, V], ids and
+    u_accept [n_draft], u_resample [n_draft + B], cu_draft [B + 1] int32 on the
+    device.  Returns (tokens [B, gamma_max + 1], n_accepted [B], flags [B])."""
+    B, N, V = _ragged_shapes(logits, ids, cu_draft)
+    dev = logits.device
+    if N > 0:
+        _check(q, "q", torch.float32, (N, V))
+        _check(u_accept, "u_accept", torch.float32, (N,))
+    _check(u_resample, "u_resample", torch.float32, (N + B,))
+    tokens, nacc, flags = _ragged_out(out, B, gamma_max, dev)
+    need = workspace_size(B, gamma_max, V, logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_ragged(
+        logits.data_ptr(), _DT[logits.dtype], q.data_ptr() if N > 0 else None, ids.data_ptr() if N > 0 else None,
+        cu_draft.data_ptr(), N, u_accept.data_ptr() if N > 0 else None, u_resample.data_ptr(),
+        B, gamma_max, V, _params(temperature, top_k, top_p), int(eos_id),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_ragged")
+    return tokens, nacc, flags
+
+
+def verify_greedy_ragged(logits, ids, cu_draft, gamma_max: int, eos_id: int = -1,
+                         workspace: Optional[torch.Tensor] = None, out=None):
+    """Greedy verify of a ragged batch (layout as in verify_sample_ragged)."""
+    B, N, V = _ragged_shapes(logits, ids, cu_draft)
+    dev = logits.device
+    tokens, nacc, flags = _ragged_out(out, B, gamma_max, dev)
+    need = workspace_size(B, gamma_max, V, logits.dtype)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_greedy_ragged(
+        logits.data_ptr(), _DT[logits.dtype], ids.data_ptr() if N > 0 else None, cu_draft.data_ptr(), N,
+        B, gamma_max, V, int(eos_id), tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_greedy_ragged")
+    return tokens, nacc, flags

@@ -210,15 +210,18 @@ QSrc q_src_none(int64_t V) { return q_src_dense(nullptr, V); }
 
 // `timed`: this launch carries the profiling hook's events (the target rows'
 // pass; not the draft rows').
+// `cu`, `n_draft`: the ragged layout of the batch (null: uniform).
 template <bool BF16>
 sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st,
                       const int32_t* ids = nullptr, QSrc q = QSrc{}, int gamma = 0, float2* gath = nullptr,
-                      bool timed = true) {
+                      bool timed = true, const int32_t* cu = nullptr, int32_t n_draft = 0) {
   RowPassArgs a;
   a.ids = ids;
   a.q = q;
   a.gamma = gamma;
   a.gath = gath;
+  a.cu = cu;
+  a.n_draft = n_draft;
   a.logits = logits;
   a.V = V;
   a.chunk = p.chunk;
@@ -259,8 +262,11 @@ void set_kernel_attrs() {
 
 template <bool BF16>
 sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int G1,
-                       int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st) {
+                       int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st,
+                       const int32_t* cu = nullptr, int32_t n_draft = 0) {
   RowFinalArgs a;
+  a.cu = cu;
+  a.n_draft = n_draft;
   a.logits = logits;
   a.q = q;
   a.ids = ids;
@@ -297,21 +303,25 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
 
 // The sampling verify once q's source is known (dense, or the draft's
 // logits after their row passes).  `workspace` holds plan p's regions.
+// Ragged batches pass their draft offsets `cu` (gamma is then the maximum
+// gamma_b); `eos` < 0 disables the end-of-sequence cut.
 sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
                              const int32_t* draft_ids, const float* u_accept, const float* u_resample, int32_t B,
                              int32_t gamma, int32_t V, sv_sampling_params prm, float c, int32_t* out_tokens,
-                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st) {
+                             int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
+                             const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
   // untruncated rows: the row pass also gathers each draft's logit and q(d)
   float2* gath = p.trunc ? nullptr : ws_at<float2>(workspace, p.off_gath);
-  sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath)
-                   : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath);
+  sv_status s =
+      bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_draft)
+         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_draft);
   if (s != SV_OK) return s;
   if (p.trunc) {
-    s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
-           : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
+    s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_draft)
+           : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_draft);
     if (s != SV_OK) return s;
   }
 
@@ -335,6 +345,9 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   ac.out_nacc = out_num_accepted;
   ac.out_flags = out_row_flags;
   ac.jobs = ws_at<BigJob>(workspace, p.off_jobs);
+  ac.cu = cu;
+  ac.n_draft = n_draft;
+  ac.eos = eos;
   const dim3 agrid((unsigned)((B + 3) / 4));
   if (p.trunc) {
     // kept lists (stored in token-id order) and the rare oversized kept set
@@ -355,6 +368,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   bg.partials = ws_at<double>(workspace, p.off_part);
   bg.out_tokens = out_tokens;
   bg.out_flags = out_row_flags;
+  bg.eos = eos;
   const int64_t tiles_big = (V + 1024 * kSeg - 1) / (1024 * kSeg);  // tiles of the 1024-thread sampler
   if (G1 <= kWave && tiles_big <= kMaxTiles && B >= kOneLaunchMinB) {
     // one workgroup per request: decision, row weights and the draw
@@ -468,6 +482,47 @@ size_t draft_ws_offset(CallKind kind, int32_t B, int32_t gamma, int32_t V, sv_dt
   return align_up(make_plan(kind, B, gamma, V, dt, prm).total, 256);
 }
 
+// Greedy verify (uniform, or ragged with draft offsets `cu`).
+sv_status verify_greedy_impl(const void* target_logits, sv_dtype dt, const int32_t* draft_ids, int32_t B,
+                             int32_t gamma, int32_t V, int32_t* out_tokens, int32_t* out_num_accepted,
+                             uint32_t* out_row_flags, void* workspace, size_t workspace_bytes, hipStream_t st,
+                             const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1) {
+  sv_sampling_params prm = {1.0f, 0, 1.0f};
+  const Plan p = make_plan(CALL_GREEDY, B, gamma, V, dt, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  const bool bf = dt == SV_BF16;
+  sv_status s =
+      bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
+                             true, cu, n_draft)
+         : run_rowpass<false>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
+                              true, cu, n_draft);
+  if (s != SV_OK) return s;
+  GreedyArgs g;
+  g.cout = ws_at<ChunkOut>(workspace, p.off_cout);
+  g.nchunks = p.nchunks;
+  g.ids = draft_ids;
+  g.B = B;
+  g.gamma = gamma;
+  g.V = V;
+  g.out_tokens = out_tokens;
+  g.out_nacc = out_num_accepted;
+  g.out_flags = out_row_flags;
+  g.cu = cu;
+  g.n_draft = n_draft;
+  g.eos = eos;
+  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, g);
+  return launched();
+}
+
+// Host checks of a ragged call's scalar arguments (the offsets themselves
+// are device data, checked per request by the kernels).
+sv_status ragged_checks(const int32_t* cu, int32_t n_draft, int32_t B, int32_t gamma_max, int32_t V, int32_t eos) {
+  if (n_draft < 0 || (int64_t)n_draft > (int64_t)B * gamma_max) return SV_ERR_INVALID_ARG;
+  if (B > 0 && cu == nullptr) return SV_ERR_INVALID_ARG;
+  if (eos >= V) return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -510,26 +565,8 @@ sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32
   if (B == 0) return SV_OK;
   if (out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
   if (gamma > 0 && draft_ids == nullptr) return SV_ERR_INVALID_ARG;
-  sv_sampling_params prm = {1.0f, 0, 1.0f};
-  const Plan p = make_plan(CALL_GREEDY, B, gamma, V, dt, prm);
-  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = dt == SV_BF16;
-  s = bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, 1.0f, workspace, st)
-         : run_rowpass<false>(p, target_logits, V, gamma + 1, 1.0f, workspace, st);
-  if (s != SV_OK) return s;
-  GreedyArgs g;
-  g.cout = ws_at<ChunkOut>(workspace, p.off_cout);
-  g.nchunks = p.nchunks;
-  g.ids = draft_ids;
-  g.B = B;
-  g.gamma = gamma;
-  g.V = V;
-  g.out_tokens = out_tokens;
-  g.out_nacc = out_num_accepted;
-  g.out_flags = out_row_flags;
-  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, g);
-  return launched();
+  return verify_greedy_impl(target_logits, dt, draft_ids, B, gamma, V, out_tokens, out_num_accepted, out_row_flags,
+                            workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
 sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
@@ -623,6 +660,48 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   if (s != SV_OK) return s;
   return accept_stats_impl(p, target_logits, dt, q, qkept, draft_ids, B, gamma, V, prm, c, out_alpha, out_z_pq,
                            out_z_qp, out_accept_prob, workspace, st);
+}
+
+sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                    const int32_t* draft_ids, const int32_t* cu_draft, int32_t n_draft,
+                                    const float* u_accept, const float* u_resample, int32_t B, int32_t gamma_max,
+                                    int32_t V, sv_sampling_params prm, int32_t eos_id, int32_t* out_tokens,
+                                    int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma_max, V);
+  if (s != SV_OK) return s;
+  s = ragged_checks(cu_draft, n_draft, B, gamma_max, V, eos_id);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (n_draft > 0 &&
+      (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma_max, V, dt, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
+                            gamma_max, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st, cu_draft,
+                            n_draft, eos_id < 0 ? -1 : eos_id);
+}
+
+sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,
+                                    const int32_t* cu_draft, int32_t n_draft, int32_t B, int32_t gamma_max,
+                                    int32_t V, int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,
+                                    uint32_t* out_row_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma_max, V);
+  if (s != SV_OK) return s;
+  s = ragged_checks(cu_draft, n_draft, B, gamma_max, V, eos_id);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (n_draft > 0 && draft_ids == nullptr) return SV_ERR_INVALID_ARG;
+  return verify_greedy_impl(target_logits, dt, draft_ids, B, gamma_max, V, out_tokens, out_num_accepted,
+                            out_row_flags, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                            cu_draft, n_draft, eos_id < 0 ? -1 : eos_id);
 }
 
 sv_status spec_set_rowpass_timer(void* start_event, void* stop_event) {

@@ -65,12 +65,62 @@ struct alignas(16) BigJob {
   float R;
   float tau;
   float u;
-  int32_t row;       // tensor row (b * (gamma + 1) + j)
-  int32_t qrow;      // q row (b * gamma + j) when residual, else -1
+  int32_t row;       // target tensor row of the sampled position
+  int32_t qrow;      // q row (draft position) when residual, else -1
   int32_t slot;      // output slot (= n_accepted)
   int32_t active;
   int32_t pad;
 };
+
+// ---- where a request's rows sit in the caller's arrays -------------------------
+// Uniform batches (cu == null): every request has gamma drafts, at draft
+// positions [b * gamma, b * gamma + gamma).  Ragged batches (the draft
+// length is chosen per request, [WR] §11.2, [MN] §九): request b's
+// gamma_b = cu[b+1] - cu[b] drafts are positions [cu[b], cu[b+1]) of packed
+// arrays holding n_draft drafts, and gamma bounds every gamma_b.  Either way
+// request b's target rows (and resampling uniforms) are rows
+// lo + b .. lo + b + gamma_b of the packed target tensor (one more row than
+// drafts).  A ragged span that is out of order, out of range or longer than
+// gamma is never read (ok = false).
+struct Layout {
+  const int32_t* cu;  // [B + 1] draft offsets, or null (uniform)
+  int32_t n_draft;
+  int32_t gamma;
+};
+struct Span {
+  int32_t lo, g;
+  bool ok;
+};
+__device__ __forceinline__ Span span_of(const Layout& L, int b) {
+  Span s;
+  if (L.cu == nullptr) {
+    s.lo = b * L.gamma;
+    s.g = L.gamma;
+    s.ok = true;
+    return s;
+  }
+  const int32_t lo = L.cu[b], hi = L.cu[b + 1];
+  s.ok = 0 <= lo && lo <= hi && hi <= L.n_draft && hi - lo <= L.gamma;
+  s.lo = s.ok ? lo : 0;
+  s.g = s.ok ? hi - lo : 0;
+  return s;
+}
+
+// Row r of a plan (request b = r / rows_per_req, position j): the offset of
+// its logits row, its draft position (-1: none) and whether the request has
+// that row at all.
+struct RowAt {
+  int64_t rowoff, dpos;
+  bool live;
+};
+__device__ __forceinline__ RowAt row_at(const Layout& L, int rows_per_req, int G1, int64_t V, int b, int j) {
+  const Span sp = span_of(L, b);
+  RowAt o;
+  o.live = sp.ok && j < sp.g + (rows_per_req - L.gamma);
+  o.rowoff = ((int64_t)sp.lo + (int64_t)b * (G1 - L.gamma) + j) * V;
+  o.dpos = j < sp.g ? (int64_t)sp.lo + j : -1;
+  return o;
+}
 
 // ---- scalar helpers ---------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

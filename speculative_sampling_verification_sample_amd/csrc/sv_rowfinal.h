@@ -23,12 +23,14 @@ namespace sv {
 
 struct RowFinalArgs {
   const void* logits;
-  QSrc q;               // draft distribution, rows [B * gamma]
-  const int32_t* ids;   // [B, gamma]
+  QSrc q;               // draft distribution, one row per draft position
+  const int32_t* ids;   // one id per draft position
   int64_t V;
   int32_t rows_per_req;
   int32_t G1;
   int32_t gamma;
+  const int32_t* cu;    // ragged draft offsets [B + 1], or null
+  int32_t n_draft;
   int32_t nchunks;
   int32_t cap_out;
   int32_t trunc;        // 0: untruncated rows, 1: top-k and/or top-p
@@ -46,15 +48,16 @@ struct RowFinalArgs {
 };
 
 // Draft gather for a row whose kept set and normaliser are final: the
-// draft's logit and q(d) (acceptance needs e(d), q(d) and S only).
+// draft's logit and q(d) (acceptance needs e(d), q(d) and S only).  dpos is
+// the row's draft position, < 0 for a row without a draft (the bonus row).
 template <bool BF16>
-__device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int gamma,
-                                float c, int b, int j, int64_t rowoff, RowInfo& ri) {
+__device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V,
+                                                float c, int64_t dpos, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
-  if (j >= gamma) return;  // bonus row: no draft
-  int d = ids[(int64_t)b * gamma + j];
+  if (dpos < 0) return;
+  int d = ids[dpos];
   if (d < 0 || (int64_t)d >= V) {
     ri.d = -2;
     return;
@@ -62,13 +65,14 @@ __device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& 
   ri.d = d;
   float z = load_logit<BF16>(logits, rowoff + d);
   ri.ed = (z >= ri.tau) ? e_of(z, c, ri.R) : 0.0f;
-  ri.qd = q_at(q, (int64_t)b * gamma + j, d);
+  ri.qd = q_at(q, dpos, d);
 }
 
 template <bool BF16>
-__device__ __forceinline__ void gather_draft(const RowFinalArgs& a, int b, int j, int64_t rowoff, RowInfo& ri) {
-  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.gamma, a.c, b, j, rowoff, ri);
+__device__ __forceinline__ void gather_draft(const RowFinalArgs& a, int64_t dpos, int64_t rowoff, RowInfo& ri) {
+  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, dpos, rowoff, ri);
 }
+
 
 // Merge the chunk results of one row in chunk order (one thread).
 struct RowMerge {
@@ -107,11 +111,12 @@ __device__ inline bool merge_nonfinite(const RowMerge& m) {
 }
 
 // Row info of an untruncated row straight from its chunk results; the
-// draft's logit and q(d) come from the row pass's gather when `gath` is set.
+// draft's logit and q(d) come from the row pass's gather (gath[grow], the
+// plan row) when `gath` is set.
 template <bool BF16>
 __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const QSrc& q,
-                                    const int32_t* ids, int64_t V, int gamma, int b, int j, int64_t rowoff,
-                                    const float2* gath = nullptr) {
+                                    const int32_t* ids, int64_t V, int64_t dpos, int64_t rowoff,
+                                    const float2* gath = nullptr, int64_t grow = 0) {
   RowMerge m = merge_chunks(co, nchunks, c);
   RowInfo ri;
   ri.S = m.S;
@@ -128,12 +133,12 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
     return ri;
   }
   if (gath != nullptr) {
-    if (j < gamma) {
-      const int d = ids[(int64_t)b * gamma + j];
+    if (dpos >= 0) {
+      const int d = ids[dpos];
       if (d < 0 || (int64_t)d >= V) {
         ri.d = -2;
       } else {
-        const float2 g = gath[rowoff / V];
+        const float2 g = gath[grow];
         ri.d = d;
         ri.ed = (g.x >= ri.tau) ? e_of(g.x, c, ri.R) : 0.0f;
         ri.qd = g.y;
@@ -141,7 +146,7 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
     }
     return ri;
   }
-  gather_draft_at<BF16>(logits, q, ids, V, gamma, c, b, j, rowoff, ri);
+  gather_draft_at<BF16>(logits, q, ids, V, c, dpos, rowoff, ri);
   return ri;
 }
 
@@ -284,7 +289,7 @@ __device__ __forceinline__ double block_sum_d(double v, double* s_tmp) {
 }
 
 template <bool BF16>
-__device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int b, int j, int64_t rowoff, RowInfo ri) {
+__device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int64_t dpos, int64_t rowoff, RowInfo ri) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t V = a.V;
   const float c = a.c;
@@ -540,7 +545,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int 
     ri.nkept = nkept;
   }
   if (tid == 0) {
-    gather_draft<BF16>(a, b, j, rowoff, ri);
+    gather_draft<BF16>(a, dpos, rowoff, ri);
     a.info[r] = ri;
   }
 }
@@ -550,7 +555,9 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
-  const int64_t rowoff = ((int64_t)b * a.G1 + j) * a.V;
+  const RowAt at = row_at(Layout{a.cu, a.n_draft, a.gamma}, a.rows_per_req, a.G1, a.V, b, j);
+  if (!at.live) return;  // a ragged request without this row
+  const int64_t rowoff = at.rowoff, dpos = at.dpos;
 
   __shared__ float s_xm, s_th, s_R;
   __shared__ double s_S;
@@ -571,10 +578,10 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   const bool flat = nch <= kWave;  // the union walks one flat index over the chunk lists
   // The draft's id, logit and q(d) are fetched by lane 0 of wave 1 while
   // wave 0 merges the chunks, so the row's result does not wait on them.
-  const bool has_draft = j < a.gamma;
+  const bool has_draft = dpos >= 0;
   int gd = -1;
   float gz = 0.0f, gq = 0.0f;
-  if (tid == kWave && has_draft) gd = a.ids[(int64_t)b * a.gamma + j];
+  if (tid == kWave && has_draft) gd = a.ids[dpos];
   // Candidate loads are issued now, before the chunk counts are known:
   // thread t takes slots t / nch + u * per of chunk t % nch (per = 256 / nch),
   // every slot inside the list's capacity; the counts decide later which
@@ -652,19 +659,19 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   if (!a.trunc) {
     if (tid == 0) {
       ri.flags = RF_BIG;
-      gather_draft<BF16>(a, b, j, rowoff, ri);
+      gather_draft<BF16>(a, dpos, rowoff, ri);
       a.info[r] = ri;
     }
     return;
   }
   if ((fl & CF_OVERFLOW) || !a.fast) {
-    exact_row<BF16>(a, r, b, j, rowoff, ri);
+    exact_row<BF16>(a, r, dpos, rowoff, ri);
     return;
   }
 
   if (tid == kWave && gd >= 0 && (int64_t)gd < a.V) {
     gz = load_logit<BF16>(a.logits, rowoff + gd);
-    gq = q_at(a.q, (int64_t)b * a.gamma + j, gd);
+    gq = q_at(a.q, dpos, gd);
   }
 
   // ---- candidate union (entries >= the highest chunk threshold) ----
@@ -715,7 +722,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   __syncthreads();
   const int nu = s_n;
   if (nu > a.um) {
-    exact_row<BF16>(a, r, b, j, rowoff, ri);
+    exact_row<BF16>(a, r, dpos, rowoff, ri);
     return;
   }
 
@@ -740,7 +747,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
       kfinal = kp;
     } else if (!(topk || theta == kLowest)) {
       // the crossing lies below the certified candidates: exact path
-      exact_row<BF16>(a, r, b, j, rowoff, ri);
+      exact_row<BF16>(a, r, dpos, rowoff, ri);
       return;
     }  // else rounding: keep the whole base set
   }

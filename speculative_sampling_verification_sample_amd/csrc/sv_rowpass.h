@@ -52,6 +52,10 @@ struct RowPassArgs {
   QSrc q;
   int32_t gamma;
   float2* gath;
+  // Ragged batches: draft offsets [B + 1] (null: uniform).  Workgroups of a
+  // row the request does not have return at once.
+  const int32_t* cu;
+  int32_t n_draft;
 };
 
 constexpr int kTruncBS = 512;  // threads of the truncated-row pass
@@ -59,8 +63,9 @@ constexpr int kTruncBS = 512;  // threads of the truncated-row pass
 // Geometry of the chunk a workgroup owns: flat element range [F0, F1) and
 // 16-byte unit range [U0, U1) (a unit may straddle the range ends).
 struct ChunkGeom {
-  int r, ci, b, j;
-  int64_t rowoff, e0, e1, F0, F1, U0, U1;
+  int r, ci;
+  bool live;
+  int64_t dpos, rowoff, e0, e1, F0, F1, U0, U1;
 };
 
 template <int EPV>
@@ -69,9 +74,12 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
   const int64_t blk = blockIdx.x;
   g.r = (int)(blk / a.nchunks);
   g.ci = (int)(blk - (int64_t)g.r * a.nchunks);
-  g.b = g.r / a.rows_per_req;
-  g.j = g.r - g.b * a.rows_per_req;
-  g.rowoff = ((int64_t)g.b * a.G1 + g.j) * a.V;
+  const int b = g.r / a.rows_per_req;
+  const int j = g.r - b * a.rows_per_req;
+  const RowAt at = row_at(Layout{a.cu, a.n_draft, a.gamma}, a.rows_per_req, a.G1, a.V, b, j);
+  g.live = at.live;
+  g.dpos = at.dpos;
+  g.rowoff = at.rowoff;
   g.e0 = (int64_t)g.ci * a.chunk;
   g.e1 = min(g.e0 + a.chunk, a.V);
   g.F0 = g.rowoff + g.e0;
@@ -219,12 +227,13 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   __shared__ float s_R[NWV];
   __shared__ uint32_t s_fl[NWV];
 
-  if (a.gath != nullptr && tid == 0 && g.j < a.gamma) {
-    const int d = a.ids[(int64_t)g.b * a.gamma + g.j];
+  if (!g.live) return;
+  if (a.gath != nullptr && tid == 0 && g.dpos >= 0) {
+    const int d = a.ids[g.dpos];
     if ((int64_t)d >= g.e0 && (int64_t)d < g.e1) {
       const float zd = BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.logits)[g.rowoff + d] << 16)
                             : reinterpret_cast<const float*>(a.logits)[g.rowoff + d];
-      a.gath[g.r] = make_float2(zd, q_at(a.q, (int64_t)g.b * a.gamma + g.j, d));
+      a.gath[g.r] = make_float2(zd, q_at(a.q, g.dpos, d));
     }
   }
 
@@ -340,6 +349,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const ChunkGeom g = chunk_geom<EPV>(a);
   const uint4* __restrict__ base = reinterpret_cast<const uint4*>(a.logits);
   const float c = a.c;
+  if (!g.live) return;
 
   __shared__ float s_xm[NWV];
   __shared__ double s_s[NWV];

@@ -18,7 +18,7 @@
 namespace sv {
 
 struct AcceptArgs {
-  RowInfo* info;        // [B * (gamma+1)]
+  RowInfo* info;        // [B * (gamma+1)], plan rows
   const float2* gath;   // draft gather of the row pass (untruncated rows) or null
   const ChunkOut* cout; // chunk results, read when rows are untruncated (no K2)
   int32_t nchunks;
@@ -31,12 +31,15 @@ struct AcceptArgs {
   const float* ua;
   const float* ur;
   int32_t B;
-  int32_t gamma;
+  int32_t gamma;        // (maximum) drafts per request
   int64_t V;
-  int32_t* out_tokens;
+  int32_t* out_tokens;  // [B, gamma + 1]
   int32_t* out_nacc;
   uint32_t* out_flags;  // may be null
   BigJob* jobs;
+  const int32_t* cu;    // ragged draft offsets [B + 1], or null (Layout)
+  int32_t n_draft;
+  int32_t eos;          // end-of-sequence id, < 0: none
 };
 
 // Draw from the kept list of one row, stored in token-id order (called by a
@@ -179,22 +182,49 @@ __device__ __forceinline__ RowInfo shfl_info(const RowInfo& r, int src) {
   return o;
 }
 
-// Emit the outputs of one request once n_accepted is known (whole wave).
+// Acceptance decision of one request (whole wave): the first rejection,
+// cut at an accepted end-of-sequence draft ([WR] §14.3: nothing is
+// committed after an EOS; that draft becomes the last emitted token and no
+// token is drawn).
+struct Decision {
+  int nacc;
+  uint32_t fl;
+  bool bad;        // emit nothing; badfl says why
+  uint32_t badfl;  // SV_ROW_NONFINITE or SV_ROW_BAD_SPAN
+  bool eos_cut;
+  int lo, G;       // the request's first draft position and gamma_b
+  RowInfo rs;      // info of row n_accepted (the row the token is drawn from)
+};
+
+// Emit the outputs of one request once its decision is known (whole wave).
 template <bool BF16, bool BIG_INWAVE>
-__device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl, const RowInfo& rs,
-                               int32_t* out) {
+__device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, int32_t* out) {
   const int lane = lane_id();
-  const int G = a.gamma, G1 = G + 1;
-  for (int jj = lane; jj < G1; jj += kWave)
-    if (jj != nacc) out[jj] = jj < nacc ? a.ids[(int64_t)b * G + jj] : -1;
+  const int nacc = dc.nacc, G = dc.G, P1 = a.gamma + 1;
+  const int64_t lo = dc.lo;
+  uint32_t fl = dc.fl;
+  const int nids = nacc + (dc.eos_cut ? 1 : 0);  // slots holding draft ids
+  for (int jj = lane; jj < P1; jj += kWave)
+    if (dc.eos_cut || jj != nacc) out[jj] = jj < nids ? a.ids[lo + jj] : -1;
+  if (dc.eos_cut) {
+    if (lane == 0) {
+      a.out_nacc[b] = nacc;
+      if (a.out_flags) a.out_flags[b] = fl;
+      a.jobs[b].active = 0;
+    }
+    return;
+  }
   bool residual = nacc < G;
-  const float u = a.ur[(int64_t)b * G1 + nacc];
-  const int64_t trow = (int64_t)b * G1 + nacc;
-  const int64_t qrow = residual ? (int64_t)b * G + nacc : -1;
+  const float u = a.ur[lo + b + nacc];
+  const int64_t trow = lo + b + nacc;             // target logits row of the draw
+  const int64_t prow = (int64_t)b * P1 + nacc;    // its plan row (kept list)
+  const int64_t qrow = residual ? lo + nacc : -1;
   const QRow qr = residual ? q_row(a.q, qrow) : q_none();
+  const RowInfo& rs = dc.rs;
   if ((rs.flags & RF_BIG) && BIG_INWAVE) {
     int token = draw_full_row_wave<BF16>(a.logits, qr, a.V, a.c, trow, rs.S, rs.R, rs.tau, u, residual, fl);
     if (lane == 0) {
+      if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
       out[nacc] = token;
       a.out_nacc[b] = nacc;
       if (a.out_flags) a.out_flags[b] = fl;
@@ -220,8 +250,9 @@ __device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl
     }
     return;
   }
-  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
+  int token = draw_from_list(a.kept + prow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
   if (lane == 0) {
+    if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
     out[nacc] = token;
     a.out_nacc[b] = nacc;
     if (a.out_flags) a.out_flags[b] = fl;
@@ -229,29 +260,24 @@ __device__ void finish_request(const AcceptArgs& a, int b, int nacc, uint32_t fl
   }
 }
 
-__device__ void nonfinite_request(const AcceptArgs& a, int b, int32_t* out) {
+// A request that emits nothing: fl = SV_ROW_NONFINITE or SV_ROW_BAD_SPAN.
+__device__ void empty_request(const AcceptArgs& a, int b, int32_t* out, uint32_t fl) {
   const int lane = lane_id();
   for (int jj = lane; jj < a.gamma + 1; jj += kWave) out[jj] = -1;
   if (lane == 0) {
     a.out_nacc[b] = 0;
-    if (a.out_flags) a.out_flags[b] = 8u;  // SV_ROW_NONFINITE
+    if (a.out_flags) a.out_flags[b] = fl;
     a.jobs[b].active = 0;
   }
 }
 
 // Acceptance decision of one request with gamma + 1 <= 64 (whole wave, one
 // lane per position, all in registers).
-struct Decision {
-  int nacc;
-  uint32_t fl;
-  bool bad;
-  RowInfo rs;  // info of row n_accepted (the row the token is drawn from)
-};
-
 template <bool BF16, bool FROM_CHUNKS>
 __device__ Decision decide_short(const AcceptArgs& a, int b) {
   const int lane = lane_id();
-  const int G = a.gamma, G1 = G + 1;
+  const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
+  const int G = sp.g, P1 = a.gamma + 1;
   RowInfo ri;
   ri.flags = 0;
   ri.d = -1;
@@ -262,20 +288,33 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   ri.tau = kLowest;
   ri.nkept = -1;
   ri.pad = 0;
-  float ua = 0.0f;
-  if (lane < G) ua = a.ua[(int64_t)b * G + lane];
-  if (lane <= G) {
-    const int64_t row = (int64_t)b * G1 + lane;
-    if constexpr (FROM_CHUNKS)
-      ri = untrunc_row_info<BF16>(a.cout + row * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, G, b, lane,
-                                  row * a.V, a.gath);
-    else
-      ri = a.info[row];
-  }
   Decision dc;
+  dc.lo = sp.lo;
+  dc.G = G;
+  dc.eos_cut = false;
+  dc.fl = 0;
+  dc.nacc = 0;
+  if (!sp.ok) {
+    dc.bad = true;
+    dc.badfl = 32u;  // SV_ROW_BAD_SPAN
+    dc.rs = ri;
+    return dc;
+  }
+  float ua = 0.0f;
+  if (lane < G) ua = a.ua[(int64_t)sp.lo + lane];
+  if (lane <= G) {
+    const int64_t prow = (int64_t)b * P1 + lane;
+    if constexpr (FROM_CHUNKS)
+      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V,
+                                  lane < G ? (int64_t)sp.lo + lane : -1, ((int64_t)sp.lo + b + lane) * a.V, a.gath,
+                                  prow);
+    else
+      ri = a.info[prow];
+  }
   bool bad = (lane <= G) && ((ri.flags & RF_NONFINITE) ||
                               (lane < G && ri.d >= 0 && !(ri.qd >= 0.0f && ri.qd < kPosInf)));
   dc.bad = ballot(bad) != 0;
+  dc.badfl = 8u;  // SV_ROW_NONFINITE
   bool acc = true;
   if (lane < G) {
     if (ri.d < 0) acc = false;
@@ -284,10 +323,17 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   }
   uint64_t rej = ballot(!acc);
   dc.nacc = rej ? (int)__builtin_ctzll(rej) : G;
-  dc.fl = 0;
+  if (a.eos >= 0) {
+    const uint64_t em = ballot(lane < dc.nacc && ri.d == a.eos);
+    if (em) {
+      dc.nacc = (int)__builtin_ctzll(em);
+      dc.eos_cut = true;
+      dc.fl |= 16u;  // SV_ROW_EOS
+    }
+  }
   if (ballot(lane < G && lane <= dc.nacc && ri.d >= 0 && ri.qd == 0.0f) != 0) dc.fl |= 2u;  // SV_ROW_Q_ZERO
   dc.rs = shfl_info(ri, dc.nacc);
-  if (dc.nacc < G && dc.rs.d == -2) dc.fl |= 1u;  // SV_ROW_BAD_ID
+  if (!dc.eos_cut && dc.nacc < G && dc.rs.d == -2) dc.fl |= 1u;  // SV_ROW_BAD_ID
   return dc;
 }
 
@@ -296,27 +342,34 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wid;
   if (b >= a.B) return;
-  const int G = a.gamma, G1 = G + 1;
-  RowInfo* inf = a.info + (int64_t)b * G1;
-  int32_t* out = a.out_tokens + (int64_t)b * G1;
+  const int P1 = a.gamma + 1;
+  RowInfo* inf = a.info + (int64_t)b * P1;
+  int32_t* out = a.out_tokens + (int64_t)b * P1;
   constexpr bool kInwave = !FROM_CHUNKS;  // truncated rows draw oversized kept sets in the wave
 
-  if (G1 <= kWave) {
+  if (P1 <= kWave) {
     Decision dc = decide_short<BF16, FROM_CHUNKS>(a, b);
     if (dc.bad) {
-      nonfinite_request(a, b, out);
+      empty_request(a, b, out, dc.badfl);
       return;
     }
-    finish_request<BF16, kInwave>(a, b, dc.nacc, dc.fl, dc.rs, out);
+    finish_request<BF16, kInwave>(a, b, dc, out);
     return;
   }
 
   // Long drafts: rows go through the workspace copy of the row infos.
+  const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
+  if (!sp.ok) {
+    empty_request(a, b, out, 32u);  // SV_ROW_BAD_SPAN
+    return;
+  }
+  const int G = sp.g;
+  const int64_t lo = sp.lo;
   if constexpr (FROM_CHUNKS) {
     for (int jj = lane; jj <= G; jj += kWave) {
-      const int64_t row = (int64_t)b * G1 + jj;
-      inf[jj] = untrunc_row_info<BF16>(a.cout + row * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, G, b,
-                                       jj, row * a.V);
+      const int64_t prow = (int64_t)b * P1 + jj;
+      inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V,
+                                       jj < G ? lo + jj : -1, (lo + b + jj) * a.V);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     wave_sync();
@@ -328,7 +381,7 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
     if (jj < G && ri.d >= 0 && !(ri.qd >= 0.0f && ri.qd < kPosInf)) bad = true;
   }
   if (ballot(bad) != 0) {
-    nonfinite_request(a, b, out);
+    empty_request(a, b, out, 8u);  // SV_ROW_NONFINITE
     return;
   }
   int nacc = G;
@@ -339,7 +392,7 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
       RowInfo ri = inf[jj];
       if (ri.d < 0) acc = false;
       else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
-      else acc = (double)a.ua[(int64_t)b * G + jj] * (double)ri.qd * ri.S < (double)ri.ed;
+      else acc = (double)a.ua[lo + jj] * (double)ri.qd * ri.S < (double)ri.ed;
     }
     uint64_t rej = ballot(!acc);
     if (rej) {
@@ -347,16 +400,35 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
       break;
     }
   }
-  uint32_t fl = 0;
+  Decision dc;
+  dc.fl = 0;
+  dc.eos_cut = false;
+  if (a.eos >= 0) {
+    for (int j0 = 0; j0 < nacc; j0 += kWave) {
+      const int jj = j0 + lane;
+      const uint64_t em = ballot(jj < nacc && inf[jj].d == a.eos);
+      if (em) {
+        nacc = j0 + (int)__builtin_ctzll(em);
+        dc.eos_cut = true;
+        dc.fl |= 16u;  // SV_ROW_EOS
+        break;
+      }
+    }
+  }
   bool qz = false;
   for (int jj = lane; jj < min(nacc + 1, G); jj += kWave) {
     RowInfo ri = inf[jj];
     if (ri.d >= 0 && ri.qd == 0.0f) qz = true;
   }
-  if (ballot(qz) != 0) fl |= 2u;  // SV_ROW_Q_ZERO
-  const RowInfo rs = inf[nacc];
-  if (nacc < G && rs.d == -2) fl |= 1u;  // SV_ROW_BAD_ID
-  finish_request<BF16, kInwave>(a, b, nacc, fl, rs, out);
+  if (ballot(qz) != 0) dc.fl |= 2u;  // SV_ROW_Q_ZERO
+  dc.rs = inf[nacc];
+  if (!dc.eos_cut && nacc < G && dc.rs.d == -2) dc.fl |= 1u;  // SV_ROW_BAD_ID
+  dc.nacc = nacc;
+  dc.bad = false;
+  dc.badfl = 0;
+  dc.lo = sp.lo;
+  dc.G = G;
+  finish_request<BF16, kInwave>(a, b, dc, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,6 +455,7 @@ struct BigArgs {
   double* partials;  // [B][nch4]
   int32_t* out_tokens;
   uint32_t* out_flags;
+  int32_t eos;       // end-of-sequence id, < 0: none
 };
 
 // Weights of tokens x0 .. x0+7 of the job's row (0 past the end).
@@ -484,29 +557,32 @@ __global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs 
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < kWave) {
       Decision dc = decide_short<BF16, true>(ac, b);
-      const int G = ac.gamma, G1 = G + 1;
-      int32_t* out = ac.out_tokens + (int64_t)b * G1;
+      const int P1 = ac.gamma + 1;
+      int32_t* out = ac.out_tokens + (int64_t)b * P1;
       if (dc.bad) {
-        if (ci == 0) nonfinite_request(ac, b, out);
+        if (ci == 0) empty_request(ac, b, out, dc.badfl);
+        if (lane == 0) s_job.active = 0;
+      } else if (dc.eos_cut) {
+        if (ci == 0) finish_request<BF16, false>(ac, b, dc, out);  // no draw
         if (lane == 0) s_job.active = 0;
       } else {
-        const bool residual = dc.nacc < G;
+        const bool residual = dc.nacc < dc.G;
         if (lane == 0) {
           BigJob j;
           j.S = dc.rs.S;
           j.R = dc.rs.R;
           j.tau = dc.rs.tau;
-          j.u = ac.ur[(int64_t)b * G1 + dc.nacc];
-          j.row = (int32_t)((int64_t)b * G1 + dc.nacc);
-          j.qrow = residual ? (int32_t)((int64_t)b * G + dc.nacc) : -1;
+          j.u = ac.ur[(int64_t)dc.lo + b + dc.nacc];
+          j.row = (int32_t)((int64_t)dc.lo + b + dc.nacc);
+          j.qrow = residual ? (int32_t)(dc.lo + dc.nacc) : -1;
           j.slot = dc.nacc;
           j.active = 1;
           j.pad = 0;
           s_job = j;
         }
         if (ci == 0) {
-          for (int jj = lane; jj < G1; jj += kWave)
-            if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)b * G + jj] : -1;
+          for (int jj = lane; jj < P1; jj += kWave)
+            if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)dc.lo + jj] : -1;
           if (lane == 0) {
             ac.out_nacc[b] = dc.nacc;
             if (ac.out_flags) ac.out_flags[b] = dc.fl;
@@ -624,6 +700,7 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
   }
   if (tid == 0) {
     a.out_tokens[(int64_t)b * a.G1 + jb.slot] = token;
+    if (a.eos >= 0 && token == a.eos) extra |= 16u;  // SV_ROW_EOS
     if (extra && a.out_flags) a.out_flags[b] |= extra;
   }
 }
@@ -727,25 +804,28 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
   __shared__ double s_tile[kMaxTiles];
   __shared__ int s_kstar, s_wf[NW], s_wl[NW];
   __shared__ double s_cex, s_t, s_W;
-  const int G = ac.gamma, G1 = G + 1;
-  int32_t* out = ac.out_tokens + (int64_t)b * G1;
+  const int P1 = ac.gamma + 1;
+  int32_t* out = ac.out_tokens + (int64_t)b * P1;
   if (tid < kWave) {
     Decision dc = decide_short<BF16, true>(ac, b);
     if (dc.bad) {
-      nonfinite_request(ac, b, out);
+      empty_request(ac, b, out, dc.badfl);
+      if (lane == 0) s_job.active = 0;
+    } else if (dc.eos_cut) {
+      finish_request<BF16, false>(ac, b, dc, out);  // no draw
       if (lane == 0) s_job.active = 0;
     } else {
-      const bool residual = dc.nacc < G;
-      for (int jj = lane; jj < G1; jj += kWave)
-        if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)b * G + jj] : -1;
+      const bool residual = dc.nacc < dc.G;
+      for (int jj = lane; jj < P1; jj += kWave)
+        if (jj != dc.nacc) out[jj] = jj < dc.nacc ? ac.ids[(int64_t)dc.lo + jj] : -1;
       if (lane == 0) {
         BigJob j;
         j.S = dc.rs.S;
         j.R = dc.rs.R;
         j.tau = dc.rs.tau;
-        j.u = ac.ur[(int64_t)b * G1 + dc.nacc];
-        j.row = (int32_t)((int64_t)b * G1 + dc.nacc);
-        j.qrow = residual ? (int32_t)((int64_t)b * G + dc.nacc) : -1;
+        j.u = ac.ur[(int64_t)dc.lo + b + dc.nacc];
+        j.row = (int32_t)((int64_t)dc.lo + b + dc.nacc);
+        j.qrow = residual ? (int32_t)(dc.lo + dc.nacc) : -1;
         j.slot = dc.nacc;
         j.active = 1;
         j.pad = (int32_t)dc.fl;
@@ -854,6 +934,7 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
     token = block_first_or_last<NW>(found, lp, s_wf, s_wl);
   }
   if (tid == 0) {
+    if (ac.eos >= 0 && token == ac.eos) fl |= 16u;  // SV_ROW_EOS
     out[jb.slot] = token;
     if (ac.out_flags) ac.out_flags[b] = fl;
   }
@@ -868,23 +949,38 @@ struct GreedyArgs {
   int32_t nchunks;
   const int32_t* ids;
   int32_t B;
-  int32_t gamma;
+  int32_t gamma;        // (maximum) drafts per request
   int64_t V;
-  int32_t* out_tokens;
+  int32_t* out_tokens;  // [B, gamma + 1]
   int32_t* out_nacc;
   uint32_t* out_flags;
+  const int32_t* cu;    // ragged draft offsets [B + 1], or null (Layout)
+  int32_t n_draft;
+  int32_t eos;          // end-of-sequence id, < 0: none
 };
 
 __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wid;
   if (b >= a.B) return;
-  const int G = a.gamma, G1 = G + 1;
+  const int P1 = a.gamma + 1;
+  int32_t* out = a.out_tokens + (int64_t)b * P1;
+  const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
+  if (!sp.ok) {
+    for (int jj = lane; jj < P1; jj += kWave) out[jj] = -1;
+    if (lane == 0) {
+      a.out_nacc[b] = 0;
+      if (a.out_flags) a.out_flags[b] = 32u;  // SV_ROW_BAD_SPAN
+    }
+    return;
+  }
+  const int G = sp.g;
+  const int64_t lo = sp.lo;
   bool nan_any = false;
   int n = G, gn = -1;
-  bool decided = false;
+  bool decided = false, eos_cut = false;
   for (int jj = 0; jj <= G; ++jj) {
-    const ChunkOut* co = a.cout + ((int64_t)b * G1 + jj) * a.nchunks;
+    const ChunkOut* co = a.cout + ((int64_t)b * P1 + jj) * a.nchunks;
     float v = kNegInf;
     int i = 0x7fffffff;
     uint32_t fl = 0;
@@ -901,32 +997,38 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
         gn = i;
         decided = true;
       } else {
-        int d = a.ids[(int64_t)b * G + jj];
+        int d = a.ids[lo + jj];
         if (d != i) {
           n = jj;
           gn = i;
           decided = true;
+        } else if (a.eos >= 0 && d == a.eos) {
+          // an accepted end of sequence ends the output ([WR] §14.3)
+          n = jj;
+          gn = d;
+          decided = true;
+          eos_cut = true;
         }
       }
     }
   }
-  int32_t* out = a.out_tokens + (int64_t)b * G1;
   if (nan_any) {
-    for (int jj = lane; jj < G1; jj += kWave) out[jj] = -1;
+    for (int jj = lane; jj < P1; jj += kWave) out[jj] = -1;
     if (lane == 0) {
       a.out_nacc[b] = 0;
       if (a.out_flags) a.out_flags[b] = 8u;
     }
     return;
   }
-  for (int jj = lane; jj < G1; jj += kWave) out[jj] = jj < n ? a.ids[(int64_t)b * G + jj] : (jj == n ? gn : -1);
+  for (int jj = lane; jj < P1; jj += kWave) out[jj] = jj < n ? a.ids[lo + jj] : (jj == n ? gn : -1);
   if (lane == 0) {
     a.out_nacc[b] = n;
     uint32_t fl = 0;
-    if (n < G) {
-      int d = a.ids[(int64_t)b * G + n];
+    if (n < G && !eos_cut) {
+      int d = a.ids[lo + n];
       if (d < 0 || (int64_t)d >= a.V) fl |= 1u;
     }
+    if (a.eos >= 0 && gn == a.eos) fl |= 16u;  // SV_ROW_EOS
     if (a.out_flags) a.out_flags[b] = fl;
   }
 }

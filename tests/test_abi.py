@@ -167,6 +167,52 @@ def test_draft_logits_argument_errors():
     assert _stats_dl(lib, G=0) == 0
 
 
+def _sample_rg(lib, **kw):
+    a = dict(logits=FAKE, dt=1, q=FAKE, ids=FAKE, cu=FAKE, N=5, ua=FAKE, ur=FAKE, B=2, G=3, V=100, prm=_P(),
+             eos=-1, tok=FAKE, nacc=FAKE, fl=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.spec_verify_sample_ragged(
+        a["logits"], a["dt"], a["q"], a["ids"], a["cu"], a["N"], a["ua"], a["ur"], a["B"], a["G"], a["V"],
+        a["prm"], a["eos"], a["tok"], a["nacc"], a["fl"], a["ws"], a["wsb"], None)
+
+
+def _greedy_rg(lib, **kw):
+    a = dict(logits=FAKE, dt=1, ids=FAKE, cu=FAKE, N=5, B=2, G=3, V=100, eos=-1, tok=FAKE, nacc=FAKE, ws=None,
+             wsb=0)
+    a.update(kw)
+    return lib.spec_verify_greedy_ragged(
+        a["logits"], a["dt"], a["ids"], a["cu"], a["N"], a["B"], a["G"], a["V"], a["eos"], a["tok"], a["nacc"],
+        None, a["ws"], a["wsb"], None)
+
+
+def test_ragged_argument_errors():
+    """Host checks of the ragged calls; the offsets themselves are device
+    data, checked per request by the kernels (SV_ROW_BAD_SPAN)."""
+    lib = _lib()
+    INVALID, WORKSPACE = 1, 3
+    for f in (_sample_rg, _greedy_rg):
+        assert f(lib) == WORKSPACE
+        assert f(lib, cu=None) == INVALID
+        assert f(lib, N=7) == INVALID       # more drafts than B * gamma_max
+        assert f(lib, N=-1) == INVALID
+        assert f(lib, eos=100) == INVALID   # an end-of-sequence id outside [0, V)
+        assert f(lib, eos=99) == WORKSPACE
+        assert f(lib, eos=-5) == WORKSPACE  # any negative id disables the rule
+        assert f(lib, ids=None) == INVALID
+        assert f(lib, logits=FAKE + 2) == INVALID
+        assert f(lib, B=0, cu=None, N=0) == 0
+        assert f(lib, G=-1) == INVALID
+    assert _sample_rg(lib, q=None) == INVALID
+    assert _sample_rg(lib, q=FAKE + 4) == INVALID
+    assert _sample_rg(lib, ua=None) == INVALID
+    assert _sample_rg(lib, ur=None) == INVALID
+    assert _sample_rg(lib, prm=_P(p=0.0)) == INVALID
+    # no drafts at all: q, ids and u_accept may be null
+    assert _sample_rg(lib, N=0, q=None, ids=None, ua=None) == WORKSPACE
+    wsb = lib.spec_verify_workspace_size(2, 3, 100, 1, _P())
+    assert _sample_rg(lib, ws=FAKE + 8, wsb=wsb) == WORKSPACE  # misaligned workspace
+
+
 def test_product_path_fails_loudly_without_library(tmp_path):
     from speculative_sampling_verification_sample_amd import _lib as L
 

@@ -28,6 +28,11 @@ Workloads (sizes B x (gamma+1) x V):
   target + N(0, 0.8^2); T = 0.7, top-p = 0.95 on both; also the acceptance
   statistics.
 
+Ragged batches (a draft length per request): ``pack_ragged(w, gammas)``
+keeps the first gammas[b] drafts of each request of a uniform workload and
+packs them without padding; ``ragged_gammas`` draws gammas[b] uniformly from
+{0, .., gamma} with its own seed.
+
 Random streams: ``numpy.random.SeedSequence(seed).spawn(4)`` seeds four torch
 generators on the chosen device: [0] target logits, [1] draft noise,
 [2] draft-id sampling, [3] uniforms.  CPU and GPU generators give different
@@ -35,4 +40,4 @@ numbers for one seed; a test uses one device for both sides.
 """
 
 from .configs import CONFIGS, Config  # noqa: F401
-from .generate import Workload, generate  # noqa: F401
+from .generate import RaggedWorkload, Workload, generate, pack_ragged, ragged_gammas  # noqa: F401

@@ -178,3 +178,49 @@ def _toy(cfg, gens, device) -> Workload:
     # draft logits whose processed distribution (T = 1, no truncation) is Q
     draft = torch.log(Q.to(torch.float64)).to(torch.float32).unsqueeze(0).expand(B, G, V)
     return _finish(cfg, logits, q, ids, gens, device, draft)
+
+
+@dataclass
+class RaggedWorkload:
+    """A batch whose request b drafted gammas[b] tokens, in the packed layout:
+    request b's drafts are positions cu[b] .. cu[b+1]-1 of ids / q /
+    u_accept (/ draft_logits) and its gammas[b] + 1 target rows (and
+    resampling uniforms) start at row cu[b] + b."""
+    cfg: Config
+    gamma_max: int
+    gammas: np.ndarray              # [B] int
+    cu: torch.Tensor                # [B + 1] int32
+    logits: torch.Tensor            # [N + B, V]
+    q: Optional[torch.Tensor]       # [N, V] float32 (None for greedy)
+    ids: torch.Tensor               # [N] int32
+    u_accept: torch.Tensor          # [N] float32
+    u_resample: torch.Tensor        # [N + B] float32
+
+
+def ragged_gammas(B: int, gamma_max: int, seed: int) -> np.ndarray:
+    """Per-request draft lengths, uniform on {0, .., gamma_max} (seeded)."""
+    return np.random.default_rng(seed).integers(0, gamma_max + 1, B)
+
+
+def pack_ragged(w: Workload, gammas) -> RaggedWorkload:
+    """Keep the first gammas[b] drafts of each request of a uniform workload
+    (and its first gammas[b] + 1 target rows), packed without padding."""
+    gammas = np.asarray(gammas, dtype=np.int64)
+    B, G1, V = w.logits.shape
+    G = G1 - 1
+    if gammas.shape != (B,) or gammas.min(initial=0) < 0 or gammas.max(initial=0) > G:
+        raise ValueError("gammas must be [B] values in [0, gamma]")
+    dev = w.logits.device
+    rows = np.concatenate([b * G1 + np.arange(g + 1) for b, g in enumerate(gammas)]).astype(np.int64)
+    drafts = np.concatenate([b * G + np.arange(g) for b, g in enumerate(gammas)] + [np.zeros(0, np.int64)])
+    ri = torch.as_tensor(rows, device=dev)
+    di = torch.as_tensor(drafts.astype(np.int64), device=dev)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(gammas)]).astype(np.int32), device=dev)
+    return RaggedWorkload(
+        w.cfg, G, gammas, cu,
+        w.logits.reshape(B * G1, V).index_select(0, ri).contiguous(),
+        None if w.q is None else w.q.reshape(B * G, V).index_select(0, di).contiguous(),
+        w.ids.reshape(-1).index_select(0, di).contiguous(),
+        w.u_accept.reshape(-1).index_select(0, di).contiguous(),
+        w.u_resample.reshape(-1).index_select(0, ri).contiguous(),
+    )
