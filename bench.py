@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--draft-logits", action="store_true",
                     help="hand the draft's logits instead of q (the library forms q); sampling workloads only")
+    ap.add_argument("--ragged", action="store_true",
+                    help="ragged batch: request b keeps gamma_b ~ uniform{0..gamma} drafts (packed inputs; the "
+                         "sampling or greedy call only)")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -119,7 +122,7 @@ def main():
     import torch
 
     import speculative_sampling_verification_sample_amd as sv
-    from workloads import CONFIGS, generate
+    from workloads import CONFIGS, generate, pack_ragged, ragged_gammas
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -128,25 +131,36 @@ def main():
     log(f"generating {cfg.name}: B={cfg.B} gamma={cfg.gamma} V={cfg.V} {cfg.dtype}")
     w0 = generate(cfg, dev)
     torch.cuda.synchronize()
+    G, B, V = cfg.gamma, cfg.B, cfg.V
+    rg = args.ragged
+    if rg and args.draft_logits:
+        raise SystemExit("--ragged and --draft-logits are separate calls")
+    gammas = ragged_gammas(B, G, 1000 + B) if rg else None
 
     def nbytes(t):
         return 0 if t is None else t.numel() * t.element_size()
 
+    def make(w):
+        return pack_ragged(w, gammas) if rg else w
+
+    wu = w0  # the uniform batch (the CPU baseline slices its requests)
+    w0 = make(w0)
     qsrc = w0.draft_logits if args.draft_logits else w0.q  # what the step reads for q
     per_copy = sum(nbytes(t) for t in (w0.logits, qsrc, w0.ids, w0.u_accept, w0.u_resample))
     R = max(1, math.ceil(args.rotate_mb * 1e6 / per_copy)) if per_copy < args.rotate_mb * 1e6 else 1
     copies = [w0]
     for _ in range(R - 1):
-        c = generate(cfg, dev)  # same recipe and seed, distinct memory
+        c = make(generate(cfg, dev))  # same recipe and seed, distinct memory
         copies.append(c)
     torch.cuda.synchronize()
     log(f"{R} resident copies of {per_copy / 1e6:.1f} MB")
 
-    G, B, V = cfg.gamma, cfg.B, cfg.V
     greedy = cfg.mode == "greedy"
     dl = args.draft_logits
     if dl and (greedy or w0.draft_logits is None):
         raise SystemExit("--draft-logits applies to the sampling workloads (toy, c2, c3, c5)")
+    n_draft = int(gammas.sum()) if rg else B * G
+    rows = n_draft + B  # target rows the step reads
     if dl:
         need = sv.draft_logits_workspace_size(B, G, V, w0.logits.dtype, w0.draft_logits.dtype, cfg.temperature,
                                               cfg.top_k, cfg.top_p)
@@ -156,7 +170,8 @@ def main():
     outs = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
             torch.empty((B,), dtype=torch.int32, device=dev),
             torch.empty((B,), dtype=torch.int32, device=dev))
-    sout = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4)) if cfg.stats else None
+    stats = cfg.stats and not rg  # the statistics call takes uniform batches
+    sout = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4)) if stats else None
 
     def step(i, timer=None):
         """One verify step; `timer` = (start, stop) hipEvents around the row
@@ -164,7 +179,12 @@ def main():
         w = copies[i % R]
         if timer is not None:
             lib.spec_set_rowpass_timer(timer[0], timer[1])
-        if greedy:
+        if rg and greedy:
+            sv.verify_greedy_ragged(w.logits, w.ids, w.cu, G, workspace=ws, out=outs)
+        elif rg:
+            sv.verify_sample_ragged(w.logits, w.q, w.ids, w.cu, w.u_accept, w.u_resample, G, cfg.temperature,
+                                    cfg.top_k, cfg.top_p, workspace=ws, out=outs)
+        elif greedy:
             sv.verify_greedy(w.logits, w.ids, workspace=ws, out=outs)
         elif dl:
             sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
@@ -174,10 +194,10 @@ def main():
                              cfg.top_p, workspace=ws, out=outs)
         if timer is not None:
             lib.spec_set_rowpass_timer(None, None)
-        if cfg.stats and dl:
+        if stats and dl:
             sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, cfg.temperature, cfg.top_k, cfg.top_p,
                                          workspace=ws, out=sout)
-        elif cfg.stats:
+        elif stats:
             sv.accept_stats(w.logits, w.q, w.ids, cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws,
                             out=sout)
 
@@ -228,7 +248,6 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
-    rows = B * (G + 1)
     value = rows / (ms_step * 1e-3)
 
     # ---- row-pass kernel duration (HIP events recorded by the library) ----
@@ -248,25 +267,25 @@ def main():
             raise RuntimeError("outputs changed between steps")
     k_ms = float(np.mean(durs))
     row_bytes = V * cfg.logit_bytes
-    alg_launch = (B * (G + 1)) * row_bytes  # the row pass reads every logit of the batch once
+    alg_launch = rows * row_bytes  # the row pass reads every logit of the batch once
     achieved = alg_launch / (k_ms * 1e-3) / 1e9
-    traffic = read_traffic(cfg.name)
+    traffic = None if rg else read_traffic(cfg.name)  # counters are taken on the uniform batches
 
     # ---- whole-step algorithmic bytes ----
     nacc = ref[1].cpu().numpy()
     if greedy:
-        step_bytes = B * (G + 1) * row_bytes + B * G * 4 + B * (G + 2) * 4
+        step_bytes = rows * row_bytes + n_draft * 4 + B * (G + 2) * 4
     else:
-        rejected = int((nacc < G).sum())
+        rejected = int((nacc < (gammas if rg else G)).sum())
         untrunc = cfg.top_k == 0 and cfg.top_p >= 1.0
         # q bytes per token: dense float32, or the draft's logits (read once
         # per call for their statistics, again on a rejected untruncated row)
         qb = w0.draft_logits.element_size() if dl else 4
         q_rows = rejected * V * qb if untrunc else 0
-        step_bytes = B * (G + 1) * row_bytes + q_rows + B * G * 12 + B * (G + 1) * 8 + B * 4
+        step_bytes = rows * row_bytes + q_rows + n_draft * 12 + rows * 4 + B * (G + 1) * 4 + B * 4
         if dl:
             step_bytes += B * G * V * qb
-        if cfg.stats:
+        if stats:
             # the statistics call: the target's gamma rows and q (dense, or
             # the draft's logits for their statistics)
             step_bytes += B * G * V * (cfg.logit_bytes + qb)
@@ -279,22 +298,35 @@ def main():
 
         log(f"cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
         nsamp = min(B, 64)
-        lg = w0.logits[:nsamp].detach().cpu()
+        lg = wu.logits[:nsamp].detach().cpu()
         lg = oracle.bf16_bits_to_f64(lg.view(torch.int16).numpy()) if lg.dtype == torch.bfloat16 \
             else lg.double().numpy()
-        ids = w0.ids[:nsamp].cpu().numpy()
+        ids = wu.ids[:nsamp].cpu().numpy()
         if not greedy:
-            q = w0.q[:nsamp].cpu().numpy()
-            ua = w0.u_accept[:nsamp].cpu().numpy()
-            ur = w0.u_resample[:nsamp].cpu().numpy()
+            q = wu.q[:nsamp].cpu().numpy()
+            ua = wu.u_accept[:nsamp].cpu().numpy()
+            ur = wu.u_resample[:nsamp].cpu().numpy()
         if dl:
-            dz = w0.draft_logits[:nsamp].detach().cpu()
+            dz = wu.draft_logits[:nsamp].detach().cpu()
             dz = oracle.bf16_bits_to_f64(dz.view(torch.int16).numpy()) if dz.dtype == torch.bfloat16 \
                 else dz.double().numpy()
         done = 0
+        nrows = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < args.cpu_seconds:
             b = done % nsamp
+            if rg:
+                # request b of the ragged batch: the first gammas[b] drafts
+                g = int(gammas[b])
+                if greedy:
+                    oracle.greedy_request(lg[b, : g + 1], ids[b, :g])
+                else:
+                    oracle.verify_request(lg[b, : g + 1], q[b, :g], ids[b, :g], ua[b, :g], ur[b, : g + 1],
+                                          cfg.temperature, cfg.top_k, cfg.top_p)
+                nrows += g + 1
+                done += 1
+                continue
+            nrows += G + 1
             if greedy:
                 oracle.greedy_request(lg[b], ids[b])
             elif dl:
@@ -308,8 +340,8 @@ def main():
                     oracle.stats_request(lg[b], q[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             done += 1
         el = time.perf_counter() - t0
-        cpu = {"value": done * (G + 1) / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} requests ({done * (G + 1)} rows) cycled over the first {nsamp} requests of the "
+        cpu = {"value": nrows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} requests ({nrows} rows) cycled over the first {nsamp} requests of the "
                          f"same {cfg.name} batch, one process, one thread, {el:.1f} s"}
 
     if args.copy_calibration_mb > 0:
@@ -342,6 +374,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {desc}", "B": B, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temperature, "top_k": cfg.top_k, "top_p": cfg.top_p,
                    "q": "formed from the draft's logits" if dl else "dense float32 input",
+                   "batch": (f"ragged: gamma_b uniform on 0..{G}, {n_draft} drafts, packed; sampling / greedy "
+                             f"call only" if rg else "uniform"),
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,
                    "wall_s_timed": wall, "step_alg_bytes": step_bytes, "step_alg_GBps": step_gbps},
         "roofline": {"bound": "hbm", "kernel": "rowpass (K1)", "achieved": achieved, "peak": PEAK_GBPS,

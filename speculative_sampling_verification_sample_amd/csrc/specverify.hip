@@ -210,18 +210,19 @@ QSrc q_src_none(int64_t V) { return q_src_dense(nullptr, V); }
 
 // `timed`: this launch carries the profiling hook's events (the target rows'
 // pass; not the draft rows').
-// `cu`, `n_draft`: the ragged layout of the batch (null: uniform).
+// `cu`, `n_live`: a ragged batch's draft offsets and its packed rows
+// (n_draft + B); cu = null: uniform.
 template <bool BF16>
 sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st,
                       const int32_t* ids = nullptr, QSrc q = QSrc{}, int gamma = 0, float2* gath = nullptr,
-                      bool timed = true, const int32_t* cu = nullptr, int32_t n_draft = 0) {
+                      bool timed = true, const int32_t* cu = nullptr, int32_t n_live = 0) {
   RowPassArgs a;
   a.ids = ids;
   a.q = q;
   a.gamma = gamma;
   a.gath = gath;
   a.cu = cu;
-  a.n_draft = n_draft;
+  a.n_live = n_live;
   a.logits = logits;
   a.V = V;
   a.chunk = p.chunk;
@@ -263,10 +264,10 @@ void set_kernel_attrs() {
 template <bool BF16>
 sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int G1,
                        int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st,
-                       const int32_t* cu = nullptr, int32_t n_draft = 0) {
+                       const int32_t* cu = nullptr, int32_t n_live = 0) {
   RowFinalArgs a;
   a.cu = cu;
-  a.n_draft = n_draft;
+  a.n_live = n_live;
   a.logits = logits;
   a.q = q;
   a.ids = ids;
@@ -315,13 +316,14 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
 
   // untruncated rows: the row pass also gathers each draft's logit and q(d)
   float2* gath = p.trunc ? nullptr : ws_at<float2>(workspace, p.off_gath);
+  const int32_t n_live = n_draft + B;  // ragged: packed target rows
   sv_status s =
-      bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_draft)
-         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_draft);
+      bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live)
+         : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live);
   if (s != SV_OK) return s;
   if (p.trunc) {
-    s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_draft)
-           : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_draft);
+    s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live)
+           : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live);
     if (s != SV_OK) return s;
   }
 
@@ -493,9 +495,9 @@ sv_status verify_greedy_impl(const void* target_logits, sv_dtype dt, const int32
   const bool bf = dt == SV_BF16;
   sv_status s =
       bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
-                             true, cu, n_draft)
+                             true, cu, n_draft + B)
          : run_rowpass<false>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
-                              true, cu, n_draft);
+                              true, cu, n_draft + B);
   if (s != SV_OK) return s;
   GreedyArgs g;
   g.cout = ws_at<ChunkOut>(workspace, p.off_cout);

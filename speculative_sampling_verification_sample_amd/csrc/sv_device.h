@@ -81,7 +81,7 @@ struct alignas(16) BigJob {
 // request b's target rows (and resampling uniforms) are rows
 // lo + b .. lo + b + gamma_b of the packed target tensor (one more row than
 // drafts).  A ragged span that is out of order, out of range or longer than
-// gamma is never read (ok = false).
+// gamma is never used (ok = false).
 struct Layout {
   const int32_t* cu;  // [B + 1] draft offsets, or null (uniform)
   int32_t n_draft;
@@ -106,19 +106,32 @@ __device__ __forceinline__ Span span_of(const Layout& L, int b) {
   return s;
 }
 
-// Row r of a plan (request b = r / rows_per_req, position j): the offset of
-// its logits row, its draft position (-1: none) and whether the request has
-// that row at all.
+// Row r of a row-pass plan: the offset of its logits row, its draft
+// position (-1: none, or not gathered here) and whether the row exists.
+// Uniform batches: request b = r / rows_per_req, position j; the logits row
+// is b * G1 + j and the draft position b * gamma + j (j < gamma).  Ragged
+// batches (cu != null, sampling and greedy plans): plan rows are the packed
+// target rows themselves, n_live = n_draft + B of them, so the row passes
+// need no request index; a grid sized for B * (gamma + 1) rows leaves the
+// rest of it idle (those workgroups return before touching memory), and
+// the drafts are gathered by the acceptance kernel, which knows each span.
 struct RowAt {
   int64_t rowoff, dpos;
   bool live;
 };
-__device__ __forceinline__ RowAt row_at(const Layout& L, int rows_per_req, int G1, int64_t V, int b, int j) {
-  const Span sp = span_of(L, b);
+__device__ __forceinline__ RowAt row_at(const int32_t* cu, int64_t n_live, int rows_per_req, int G1, int gamma,
+                                        int64_t V, int64_t r) {
   RowAt o;
-  o.live = sp.ok && j < sp.g + (rows_per_req - L.gamma);
-  o.rowoff = ((int64_t)sp.lo + (int64_t)b * (G1 - L.gamma) + j) * V;
-  o.dpos = j < sp.g ? (int64_t)sp.lo + j : -1;
+  if (cu != nullptr) {
+    o.live = r < n_live;
+    o.rowoff = r * V;
+    o.dpos = -1;
+    return o;
+  }
+  const int64_t b = r / rows_per_req, j = r - b * rows_per_req;
+  o.live = true;
+  o.rowoff = (b * G1 + j) * V;
+  o.dpos = j < gamma ? b * gamma + j : -1;
   return o;
 }
 

@@ -30,7 +30,7 @@ struct RowFinalArgs {
   int32_t G1;
   int32_t gamma;
   const int32_t* cu;    // ragged draft offsets [B + 1], or null
-  int32_t n_draft;
+  int32_t n_live;       // ragged: packed rows that exist (n_draft + B)
   int32_t nchunks;
   int32_t cap_out;
   int32_t trunc;        // 0: untruncated rows, 1: top-k and/or top-p
@@ -554,9 +554,8 @@ template <bool BF16>
 __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
-  const int b = (int)(r / a.rows_per_req), j = (int)(r - (int64_t)b * a.rows_per_req);
-  const RowAt at = row_at(Layout{a.cu, a.n_draft, a.gamma}, a.rows_per_req, a.G1, a.V, b, j);
-  if (!at.live) return;  // a ragged request without this row
+  const RowAt at = row_at(a.cu, a.n_live, a.rows_per_req, a.G1, a.gamma, a.V, r);
+  if (!at.live) return;  // past the rows of a ragged batch
   const int64_t rowoff = at.rowoff, dpos = at.dpos;
 
   __shared__ float s_xm, s_th, s_R;

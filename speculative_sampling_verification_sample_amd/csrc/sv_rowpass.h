@@ -52,10 +52,10 @@ struct RowPassArgs {
   QSrc q;
   int32_t gamma;
   float2* gath;
-  // Ragged batches: draft offsets [B + 1] (null: uniform).  Workgroups of a
-  // row the request does not have return at once.
+  // Ragged batches: draft offsets [B + 1] (null: uniform) and the packed
+  // rows that exist (n_draft + B); workgroups past them return at once.
   const int32_t* cu;
-  int32_t n_draft;
+  int32_t n_live;
 };
 
 constexpr int kTruncBS = 512;  // threads of the truncated-row pass
@@ -74,9 +74,7 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
   const int64_t blk = blockIdx.x;
   g.r = (int)(blk / a.nchunks);
   g.ci = (int)(blk - (int64_t)g.r * a.nchunks);
-  const int b = g.r / a.rows_per_req;
-  const int j = g.r - b * a.rows_per_req;
-  const RowAt at = row_at(Layout{a.cu, a.n_draft, a.gamma}, a.rows_per_req, a.G1, a.V, b, j);
+  const RowAt at = row_at(a.cu, a.n_live, a.rows_per_req, a.G1, a.gamma, a.V, g.r);
   g.live = at.live;
   g.dpos = at.dpos;
   g.rowoff = at.rowoff;

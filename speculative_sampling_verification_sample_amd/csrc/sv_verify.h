@@ -17,8 +17,10 @@
 
 namespace sv {
 
+// Plan rows: request b's rows are lo + b .. lo + b + gamma_b (lo = its first
+// draft position), which is b * (gamma + 1) + j for uniform batches.
 struct AcceptArgs {
-  RowInfo* info;        // [B * (gamma+1)], plan rows
+  RowInfo* info;        // per plan row
   const float2* gath;   // draft gather of the row pass (untruncated rows) or null
   const ChunkOut* cout; // chunk results, read when rows are untruncated (no K2)
   int32_t nchunks;
@@ -216,8 +218,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
   }
   bool residual = nacc < G;
   const float u = a.ur[lo + b + nacc];
-  const int64_t trow = lo + b + nacc;             // target logits row of the draw
-  const int64_t prow = (int64_t)b * P1 + nacc;    // its plan row (kept list)
+  const int64_t trow = lo + b + nacc;  // plan row of the draw (= its logits row)
   const int64_t qrow = residual ? lo + nacc : -1;
   const QRow qr = residual ? q_row(a.q, qrow) : q_none();
   const RowInfo& rs = dc.rs;
@@ -250,7 +251,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     }
     return;
   }
-  int token = draw_from_list(a.kept + prow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
   if (lane == 0) {
     if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
     out[nacc] = token;
@@ -277,7 +278,7 @@ template <bool BF16, bool FROM_CHUNKS>
 __device__ Decision decide_short(const AcceptArgs& a, int b) {
   const int lane = lane_id();
   const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
-  const int G = sp.g, P1 = a.gamma + 1;
+  const int G = sp.g;
   RowInfo ri;
   ri.flags = 0;
   ri.d = -1;
@@ -303,13 +304,17 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   float ua = 0.0f;
   if (lane < G) ua = a.ua[(int64_t)sp.lo + lane];
   if (lane <= G) {
-    const int64_t prow = (int64_t)b * P1 + lane;
-    if constexpr (FROM_CHUNKS)
-      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V,
-                                  lane < G ? (int64_t)sp.lo + lane : -1, ((int64_t)sp.lo + b + lane) * a.V, a.gath,
-                                  prow);
-    else
+    const int64_t prow = (int64_t)sp.lo + b + lane;
+    const int64_t dpos = lane < G ? (int64_t)sp.lo + lane : -1;
+    if constexpr (FROM_CHUNKS) {
+      // ragged rows were not gathered by the row pass: gather here
+      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, dpos,
+                                  prow * a.V, a.cu != nullptr ? nullptr : a.gath, prow);
+    } else {
       ri = a.info[prow];
+      if (a.cu != nullptr && !(ri.flags & RF_NONFINITE))
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, dpos, prow * a.V, ri);
+    }
   }
   bool bad = (lane <= G) && ((ri.flags & RF_NONFINITE) ||
                               (lane < G && ri.d >= 0 && !(ri.qd >= 0.0f && ri.qd < kPosInf)));
@@ -343,7 +348,6 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   const int b = blockIdx.x * 4 + wid;
   if (b >= a.B) return;
   const int P1 = a.gamma + 1;
-  RowInfo* inf = a.info + (int64_t)b * P1;
   int32_t* out = a.out_tokens + (int64_t)b * P1;
   constexpr bool kInwave = !FROM_CHUNKS;  // truncated rows draw oversized kept sets in the wave
 
@@ -365,11 +369,22 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   }
   const int G = sp.g;
   const int64_t lo = sp.lo;
+  RowInfo* inf = a.info + lo + b;
   if constexpr (FROM_CHUNKS) {
     for (int jj = lane; jj <= G; jj += kWave) {
-      const int64_t prow = (int64_t)b * P1 + jj;
+      const int64_t prow = lo + b + jj;
       inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V,
-                                       jj < G ? lo + jj : -1, (lo + b + jj) * a.V);
+                                       jj < G ? lo + jj : -1, prow * a.V);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wave_sync();
+  } else if (a.cu != nullptr) {
+    // ragged rows were not gathered by the row finisher: gather here
+    for (int jj = lane; jj <= G; jj += kWave) {
+      RowInfo ri = inf[jj];
+      if (!(ri.flags & RF_NONFINITE))
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, jj < G ? lo + jj : -1, (lo + b + jj) * a.V, ri);
+      inf[jj] = ri;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     wave_sync();
@@ -980,7 +995,7 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
   int n = G, gn = -1;
   bool decided = false, eos_cut = false;
   for (int jj = 0; jj <= G; ++jj) {
-    const ChunkOut* co = a.cout + ((int64_t)b * P1 + jj) * a.nchunks;
+    const ChunkOut* co = a.cout + (lo + b + jj) * a.nchunks;
     float v = kNegInf;
     int i = 0x7fffffff;
     uint32_t fl = 0;
