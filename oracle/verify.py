@@ -38,7 +38,10 @@ reason, in the design notes of the repository):
   it and no token is drawn), and FLAG_EOS is raised whenever an EOS is
   emitted;
 * in a ragged batch, a request whose draft span is out of order, out of
-  range or longer than gamma_max raises FLAG_BAD_SPAN and emits nothing.
+  range or longer than gamma_max raises FLAG_BAD_SPAN and emits nothing;
+* lenient acceptance with factor beta in (0, 1] compares the target with the
+  draft scaled to beta * q, in the acceptance (u < p / (beta q)) and in the
+  residual ((p - beta q)_+); beta = 1 is the lossless rule.
 """
 
 from __future__ import annotations
@@ -186,7 +189,7 @@ def _no_output(gamma: int, flags: int) -> RequestResult:
     return RequestResult(np.full(gamma + 1, -1, np.int32), 0, flags)
 
 
-def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_boundary=False, eos=-1):
+def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_boundary=False, eos=-1, beta=1.0):
     """Left-to-right verification of gamma drafts given processed p rows.
 
     [WR] §6 (verify d_1 with p_1 / q_1, stop at the first rejection, draw the
@@ -197,6 +200,12 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
     n_accepted + 1 tokens).  With ``eos >= 0``: [WR] §14.3 (runtime
     invariants: no token is committed after an EOS) -- an accepted draft
     equal to eos is the last emitted token and verification stops there.
+    With ``beta < 1``: [MN] §八 (lenience) -- the draft distribution is
+    scaled to beta * q before it is compared with the target, so a draft is
+    accepted with min(1, p / (beta q)); the pages give no residual for this
+    variant, and the plainest reading of "scale, then compare" keeps the
+    rest of the step with beta * q in place of q: the replacement comes
+    from (p - beta q)_+.
     """
     gamma = len(ids)
     V = p_rows[0].size
@@ -207,6 +216,8 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
             qd = float(q_rows[j][d])
             if not (qd >= 0.0) or np.isinf(qd):
                 return _no_output(gamma, FLAG_NONFINITE)
+    if beta != 1.0:
+        q_rows = [float(beta) * np.asarray(q, dtype=np.float64) for q in q_rows]
     flags = 0
     acc_boundary = False
     n_acc = gamma
@@ -249,7 +260,7 @@ def verify_from_processed(p_rows, q_rows, ids, u_accept, u_resample, top_p_bound
     return RequestResult(tokens, n_acc, flags, acc_boundary, cdf_boundary, top_p_boundary)
 
 
-def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, eos=-1):
+def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, eos=-1, beta=1.0):
     """One request of the sampling verify step, from logits.
 
     Processes every position j = 0..gamma ([WR] §6: the target forward gives
@@ -263,7 +274,7 @@ def verify_request(z_rows, q_rows, ids, u_accept, u_resample, T, top_k=0, top_p=
     q64 = [np.asarray(q_rows[j], dtype=np.float64) for j in range(gamma)]
     return verify_from_processed(
         [r.p for r in rows], q64, ids, u_accept, u_resample,
-        top_p_boundary=any(r.top_p_boundary for r in rows), eos=eos,
+        top_p_boundary=any(r.top_p_boundary for r in rows), eos=eos, beta=beta,
     )
 
 
@@ -280,17 +291,18 @@ def _batch_result(results, gamma):
     return out
 
 
-def verify_sample(logits, q, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, requests=None):
+def verify_sample(logits, q, ids, u_accept, u_resample, T, top_k=0, top_p=1.0, requests=None, beta=1.0):
     """Batched sampling verify: loops ``verify_request`` over requests.
 
     logits: float64 [B, gamma+1, V] (already widened); q: [B, gamma, V];
     ids: [B, gamma]; u_accept: [B, gamma]; u_resample: [B, gamma+1].
-    ``requests`` optionally restricts the loop to a list of request indices.
+    ``requests`` optionally restricts the loop to a list of request indices;
+    ``beta`` is the lenience factor (1: lossless).
     """
     req = range(logits.shape[0]) if requests is None else requests
     gamma = ids.shape[1]
     res = [
-        verify_request(logits[b], q[b], ids[b], u_accept[b], u_resample[b], T, top_k, top_p)
+        verify_request(logits[b], q[b], ids[b], u_accept[b], u_resample[b], T, top_k, top_p, beta=beta)
         for b in req
     ]
     return _batch_result(res, gamma)
