@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--ragged", action="store_true",
                     help="ragged batch: request b keeps gamma_b ~ uniform{0..gamma} drafts (packed inputs; the "
                          "sampling or greedy call only)")
+    ap.add_argument("--lenience", type=float, default=None,
+                    help="lenient acceptance factor in (0, 1] for the sampling call (dense q, uniform batch)")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -135,6 +137,9 @@ def main():
     rg = args.ragged
     if rg and args.draft_logits:
         raise SystemExit("--ragged and --draft-logits are separate calls")
+    lenient = args.lenience is not None
+    if lenient and (rg or args.draft_logits or cfg.mode == "greedy"):
+        raise SystemExit("--lenience applies to the uniform sampling call with a dense q")
     gammas = ragged_gammas(B, G, 1000 + B) if rg else None
 
     def nbytes(t):
@@ -189,6 +194,9 @@ def main():
         elif dl:
             sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
                                           cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs)
+        elif lenient:
+            sv.verify_sample_lenient(w.logits, w.q, w.ids, w.u_accept, w.u_resample, cfg.temperature, cfg.top_k,
+                                     cfg.top_p, lenience=args.lenience, workspace=ws, out=outs)
         else:
             sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, cfg.temperature, cfg.top_k,
                              cfg.top_p, workspace=ws, out=outs)
@@ -335,7 +343,8 @@ def main():
                 if cfg.stats:
                     oracle.stats_request_draft_logits(lg[b], dz[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             else:
-                oracle.verify_request(lg[b], q[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k, cfg.top_p)
+                oracle.verify_request(lg[b], q[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k, cfg.top_p,
+                                      beta=float(np.float32(args.lenience)) if lenient else 1.0)
                 if cfg.stats:
                     oracle.stats_request(lg[b], q[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             done += 1
@@ -374,6 +383,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {desc}", "B": B, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temperature, "top_k": cfg.top_k, "top_p": cfg.top_p,
                    "q": "formed from the draft's logits" if dl else "dense float32 input",
+                   "acceptance": f"lenient, beta = {args.lenience}" if lenient else "lossless",
                    "batch": (f"ragged: gamma_b uniform on 0..{G}, {n_draft} drafts, packed; sampling / greedy "
                              f"call only" if rg else "uniform"),
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,

@@ -166,6 +166,23 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
                                          float* out_z_qp, float* out_accept_prob, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* ---- lenient acceptance -------------------------------------------------------
+ * [MN] §八 (lenience): the draft distribution is scaled to beta * q before it
+ * is compared with the target, so d_j is accepted iff
+ *   u_accept[b,j] < p_j(d_j) / (lenience * q_j(d_j)),
+ * a looser test that is no longer lossless: a token is emitted with at most
+ * 1/lenience times its target probability.  The pages give no replacement
+ * rule for this variant; the one taken here keeps the step with beta * q in
+ * place of q, so a rejection draws from (p_j - lenience * q_j)_+ (which keeps
+ * that bound).  lenience must be in (0, 1]; 1 gives exactly spec_verify_sample.
+ * Everything else (layout, outputs, flags, workspace) is as for
+ * spec_verify_sample. */
+sv_status spec_verify_sample_lenient(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                     const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                     int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, float lenience,
+                                     int32_t* out_tokens, int32_t* out_num_accepted, uint32_t* out_row_flags,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- ragged batches: a draft length per request ----------------------------
  * [WR] §11.2 and [MN] §九 (point 3): no single draft length suits every
  * request, so gamma is chosen per request and one verify batch holds

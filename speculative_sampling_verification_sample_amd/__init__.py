@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     verify_greedy_ragged,
     verify_sample,
     verify_sample_draft_logits,
+    verify_sample_lenient,
     verify_sample_ragged,
     workspace_size,
 )

@@ -51,6 +51,11 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
          _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_sample_lenient": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
+         ctypes.c_float, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
     "spec_verify_sample_ragged": (
         ctypes.c_int,
         [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _c_int32, _ptr, _ptr, _c_int32, _c_int32, _c_int32,

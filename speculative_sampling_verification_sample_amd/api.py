@@ -100,6 +100,41 @@ def verify_sample(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0
     return tokens, nacc, flags
 
 
+def verify_sample_lenient(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0,
+                          lenience=1.0, workspace: Optional[torch.Tensor] = None, out=None):
+    """Sampling verify step with lenient acceptance u < p / (lenience * q),
+    0 < lenience <= 1 (1: exactly verify_sample); returns (tokens, n_accepted, flags)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    if G > 0:
+        _check(q, "q", torch.float32, (B, G, V))
+        _check(ids, "ids", torch.int32, (B, G))
+        _check(u_accept, "u_accept", torch.float32, (B, G))
+    _check(u_resample, "u_resample", torch.float32, (B, G1))
+    if out is None:
+        out = (torch.empty((B, G1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    tokens, nacc, flags = out
+    need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_lenient(
+        logits.data_ptr(), _DT[logits.dtype],
+        q.data_ptr() if G > 0 else None, ids.data_ptr() if G > 0 else None,
+        u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p), float(lenience),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_lenient")
+    return tokens, nacc, flags
+
+
 def verify_greedy(logits, ids, workspace: Optional[torch.Tensor] = None, out=None):
     """Greedy verify step; returns (tokens, n_accepted, flags)."""
     if logits.dim() != 3:

@@ -305,12 +305,14 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
 // The sampling verify once q's source is known (dense, or the draft's
 // logits after their row passes).  `workspace` holds plan p's regions.
 // Ragged batches pass their draft offsets `cu` (gamma is then the maximum
-// gamma_b); `eos` < 0 disables the end-of-sequence cut.
+// gamma_b); `eos` < 0 disables the end-of-sequence cut; `beta` < 1 is the
+// lenient acceptance (the draft compared as beta * q).
 sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
                              const int32_t* draft_ids, const float* u_accept, const float* u_resample, int32_t B,
                              int32_t gamma, int32_t V, sv_sampling_params prm, float c, int32_t* out_tokens,
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
-                             const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1) {
+                             const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
+                             double beta = 1.0) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
@@ -350,6 +352,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   ac.cu = cu;
   ac.n_draft = n_draft;
   ac.eos = eos;
+  ac.beta = beta;
   const dim3 agrid((unsigned)((B + 3) / 4));
   if (p.trunc) {
     // kept lists (stored in token-id order) and the rare oversized kept set
@@ -371,6 +374,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   bg.out_tokens = out_tokens;
   bg.out_flags = out_row_flags;
   bg.eos = eos;
+  bg.beta = beta;
   const int64_t tiles_big = (V + 1024 * kSeg - 1) / (1024 * kSeg);  // tiles of the 1024-thread sampler
   if (G1 <= kWave && tiles_big <= kMaxTiles && B >= kOneLaunchMinB) {
     // one workgroup per request: decision, row weights and the draw
@@ -662,6 +666,29 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   if (s != SV_OK) return s;
   return accept_stats_impl(p, target_logits, dt, q, qkept, draft_ids, B, gamma, V, prm, c, out_alpha, out_z_pq,
                            out_z_qp, out_accept_prob, workspace, st);
+}
+
+sv_status spec_verify_sample_lenient(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                     const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                     int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, float lenience,
+                                     int32_t* out_tokens, int32_t* out_num_accepted, uint32_t* out_row_flags,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(lenience > 0.0f && lenience <= 1.0f)) return SV_ERR_INVALID_ARG;
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
+                            gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0,
+                            -1, (double)lenience);
 }
 
 sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, const float* draft_probs,

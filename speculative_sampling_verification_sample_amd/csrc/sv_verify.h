@@ -42,13 +42,14 @@ struct AcceptArgs {
   const int32_t* cu;    // ragged draft offsets [B + 1], or null (Layout)
   int32_t n_draft;
   int32_t eos;          // end-of-sequence id, < 0: none
+  double beta;          // lenience: the draft is compared as beta * q (1: lossless)
 };
 
 // Draw from the kept list of one row, stored in token-id order (called by a
 // whole wave).
-// residual: weights (e/S - q)_+ on the list; otherwise e/S.
+// residual: weights (e/S - qs q)_+ on the list (qs = beta); otherwise e/S.
 __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bool& residual, float u,
-                              uint32_t& fl) {
+                              uint32_t& fl, double qs) {
   const int lane = lane_id();
   const double invS = 1.0 / S;
   auto weight = [&](int i, bool res) -> double {
@@ -56,7 +57,7 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
     Cand e = L[i];
     double p = (double)e.v * invS;
     if (!res) return p;
-    double d = p - (double)qr.at(e.idx);
+    double d = p - qs * (double)qr.at(e.idx);
     return d > 0.0 ? d : 0.0;
   };
   auto total = [&](bool res) -> double {
@@ -97,7 +98,7 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
 // are rare): two passes over the row, weights as in the chunked sampler.
 template <bool BF16>
 __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V, float c, int64_t row, double S,
-                                  float R, float tau, float u, bool& residual, uint32_t& fl) {
+                                  float R, float tau, float u, bool& residual, uint32_t& fl, double qs) {
   const int lane = lane_id();
   auto weight = [&](int64_t x, bool res) -> double {
     if (x >= V) return 0.0;
@@ -105,7 +106,7 @@ __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V,
     if (!(z >= tau)) return 0.0;
     double e = (double)e_of(z, c, R);
     if (!res) return e;
-    double d = e - (double)qr.at(x) * S;
+    double d = e - (qs * (double)qr.at(x)) * S;
     return d > 0.0 ? d : 0.0;
   };
   auto total = [&](bool res) -> double {
@@ -223,7 +224,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
   const QRow qr = residual ? q_row(a.q, qrow) : q_none();
   const RowInfo& rs = dc.rs;
   if ((rs.flags & RF_BIG) && BIG_INWAVE) {
-    int token = draw_full_row_wave<BF16>(a.logits, qr, a.V, a.c, trow, rs.S, rs.R, rs.tau, u, residual, fl);
+    int token = draw_full_row_wave<BF16>(a.logits, qr, a.V, a.c, trow, rs.S, rs.R, rs.tau, u, residual, fl, a.beta);
     if (lane == 0) {
       if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
       out[nacc] = token;
@@ -251,7 +252,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     }
     return;
   }
-  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl);
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl, a.beta);
   if (lane == 0) {
     if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
     out[nacc] = token;
@@ -324,7 +325,7 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   if (lane < G) {
     if (ri.d < 0) acc = false;
     else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
-    else acc = (double)ua * (double)ri.qd * ri.S < (double)ri.ed;
+    else acc = (double)ua * (a.beta * (double)ri.qd) * ri.S < (double)ri.ed;  // u < p / (beta q)
   }
   uint64_t rej = ballot(!acc);
   dc.nacc = rej ? (int)__builtin_ctzll(rej) : G;
@@ -407,7 +408,7 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
       RowInfo ri = inf[jj];
       if (ri.d < 0) acc = false;
       else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
-      else acc = (double)a.ua[lo + jj] * (double)ri.qd * ri.S < (double)ri.ed;
+      else acc = (double)a.ua[lo + jj] * (a.beta * (double)ri.qd) * ri.S < (double)ri.ed;
     }
     uint64_t rej = ballot(!acc);
     if (rej) {
@@ -471,6 +472,7 @@ struct BigArgs {
   int32_t* out_tokens;
   uint32_t* out_flags;
   int32_t eos;       // end-of-sequence id, < 0: none
+  double beta;       // lenience (the residual is (p - beta q)_+)
 };
 
 // Weights of tokens x0 .. x0+7 of the job's row (0 past the end).
@@ -520,7 +522,7 @@ __device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, 
     if (z[k] >= jb.tau) {
       double e = (double)e_of(z[k], a.c, jb.R);
       if (residual) {
-        double d = e - (double)qv[k] * jb.S;
+        double d = e - (a.beta * (double)qv[k]) * jb.S;
         wk = d > 0.0 ? d : 0.0;
       } else {
         wk = e;
@@ -790,14 +792,14 @@ __device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, boo
 }
 
 __device__ __forceinline__ void seg_weigh(const BigJob& jb, float c, bool residual, const float* z, const float* qv,
-                                          double* w) {
+                                          double* w, double qs) {
 #pragma unroll
   for (int k = 0; k < kSeg; ++k) {
     double wk = 0.0;
     if (z[k] >= jb.tau) {
       double e = (double)e_of(z[k], c, jb.R);
       if (residual) {
-        double d = e - (double)qv[k] * jb.S;
+        double d = e - (qs * (double)qv[k]) * jb.S;
         wk = d > 0.0 ? d : 0.0;
       } else {
         wk = e;
@@ -869,7 +871,7 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
       for (int u = 0; u < kU; ++u) {
         if (k0 + u >= ntiles) break;
         double w[kSeg];
-        seg_weigh(jb, a.c, res, z[u], qv[u], w);
+        seg_weigh(jb, a.c, res, z[u], qv[u], w, a.beta);
         double seg = 0.0;
 #pragma unroll
         for (int i = 0; i < kSeg; ++i) seg += w[i];
@@ -931,7 +933,7 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
     float z[kSeg], qv[kSeg];
     double w[kSeg];
     seg_load<BF16>(a, jb, residual, x0, z, qv);
-    seg_weigh(jb, a.c, residual, z, qv, w);
+    seg_weigh(jb, a.c, residual, z, qv, w, a.beta);
     double seg = 0.0;
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) seg += w[i];

@@ -19,13 +19,16 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def gpu_sample(w, draft_logits=False, **kw):
+def gpu_sample(w, draft_logits=False, lenience=None, **kw):
     """The library's sampling verify; with draft_logits, q is formed by the
-    library from w.draft_logits."""
+    library from w.draft_logits; with lenience, the lenient call."""
     c = w.cfg
     prm = dict(temperature=c.temperature, top_k=c.top_k, top_p=c.top_p)
     prm.update(kw)
-    if draft_logits:
+    if lenience is not None:
+        tok, nacc, fl = sv.verify_sample_lenient(w.logits, w.q, w.ids, w.u_accept, w.u_resample, lenience=lenience,
+                                                 **prm)
+    elif draft_logits:
         tok, nacc, fl = sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
                                                       **prm)
     else:
@@ -34,9 +37,10 @@ def gpu_sample(w, draft_logits=False, **kw):
     return _np(tok), _np(nacc), _np(fl).astype(np.uint32)
 
 
-def compare_sample(w, requests=None, label="", gpu=None, draft_logits=False, **kw):
+def compare_sample(w, requests=None, label="", gpu=None, draft_logits=False, lenience=None, **kw):
     """Run both sides; exact match required outside boundary rows.
-    draft_logits: both sides form q from w.draft_logits."""
+    draft_logits: both sides form q from w.draft_logits; lenience: both
+    sides use the lenient acceptance with that factor."""
     c = w.cfg
     prm = dict(T=c.temperature, top_k=c.top_k, top_p=c.top_p)
     if "temperature" in kw:
@@ -45,7 +49,7 @@ def compare_sample(w, requests=None, label="", gpu=None, draft_logits=False, **k
         prm["top_k"] = kw["top_k"]
     if "top_p" in kw:
         prm["top_p"] = kw["top_p"]
-    tok, nacc, fl = gpu if gpu is not None else gpu_sample(w, draft_logits=draft_logits, **kw)
+    tok, nacc, fl = gpu if gpu is not None else gpu_sample(w, draft_logits=draft_logits, lenience=lenience, **kw)
     req = np.arange(c.B) if requests is None else np.asarray(requests)
     ridx = torch.as_tensor(req, device=w.logits.device)
     lg = widen(w.logits.index_select(0, ridx))
@@ -58,7 +62,8 @@ def compare_sample(w, requests=None, label="", gpu=None, draft_logits=False, **k
         dlg = widen(w.draft_logits.index_select(0, ridx)) if G > 0 else np.zeros((len(req), 0, lg.shape[2]))
         o = oracle.verify_sample_draft_logits(lg, dlg, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"])
     else:
-        o = oracle.verify_sample(lg, q, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"])
+        beta = 1.0 if lenience is None else float(np.float32(lenience))
+        o = oracle.verify_sample(lg, q, ids, ua, ur, prm["T"], prm["top_k"], prm["top_p"], beta=beta)
     g_tok, g_nacc, g_fl = tok[req], nacc[req], fl[req]
     mism = (g_tok != o["tokens"]).any(axis=1) | (g_nacc != o["n_accepted"]) | (g_fl != o["flags"])
     boundary = o["accept_boundary"] | o["cdf_boundary"] | o["top_p_boundary"]

@@ -213,6 +213,23 @@ def test_ragged_argument_errors():
     assert _sample_rg(lib, ws=FAKE + 8, wsb=wsb) == WORKSPACE  # misaligned workspace
 
 
+def test_lenient_argument_errors():
+    lib = _lib()
+    INVALID, WORKSPACE = 1, 3
+
+    def f(lenience, **kw):
+        a = dict(logits=FAKE, q=FAKE, B=2, G=3)
+        a.update(kw)
+        return lib.spec_verify_sample_lenient(a["logits"], 1, a["q"], FAKE, FAKE, FAKE, a["B"], a["G"], 100, _P(),
+                                              lenience, FAKE, FAKE, None, None, 0, None)
+
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert f(bad) == INVALID
+    assert f(1.0) == WORKSPACE and f(0.3) == WORKSPACE
+    assert f(0.5, q=None) == INVALID
+    assert f(0.5, B=0) == 0
+
+
 def test_product_path_fails_loudly_without_library(tmp_path):
     from speculative_sampling_verification_sample_amd import _lib as L
 

@@ -1,0 +1,99 @@
+"""GPU parity of the lenient acceptance (u < p / (beta q), replacement from
+(p - beta q)_+) against the oracle with the same beta: exact tokens /
+lengths / flags outside the boundary band."""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_sampling_verification_sample_amd as sv
+from parity import compare_sample, gpu_sample
+from workloads import generate
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+@pytest.mark.parametrize("beta", [0.5, 0.8, 0.1])
+@pytest.mark.parametrize("name,kw", [
+    ("c2", dict(B=8)),
+    ("c3", dict(B=6)),
+    ("c5", dict(B=4)),
+    ("c2", dict(B=5, gamma=3, V=10007)),
+    ("c3", dict(B=4, gamma=2, V=40003)),
+])
+def test_sample_small(name, kw, beta):
+    compare_sample(generate(name, DEV, **kw), label=f"lenient {beta} {name} {kw}", lenience=beta)
+
+
+def test_toy():
+    w = generate("toy", DEV, B=20000)
+    o, _ = compare_sample(w, label="lenient toy 0.5", lenience=0.5)
+    o1, _ = compare_sample(w, label="lenient toy 1.0", lenience=1.0)
+    # the looser test accepts more
+    assert o["n_accepted"].mean() > o1["n_accepted"].mean() + 0.1
+
+
+def test_beta_one_is_the_lossless_call():
+    for name, kw in (("c2", dict(B=6)), ("c3", dict(B=5)), ("c5", dict(B=4)), ("toy", dict(B=5000))):
+        w = generate(name, DEV, **kw)
+        a = gpu_sample(w)
+        b = gpu_sample(w, lenience=1.0)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_long_gamma():
+    w = generate("c2", DEV, B=3, gamma=70, V=600)
+    compare_sample(w, label="lenient gamma=70", lenience=0.3)
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_full_size(name):
+    w = generate(name, DEV)
+    gpu = gpu_sample(w, lenience=0.5)
+    req = np.sort(np.random.default_rng(0).choice(w.cfg.B, 16, replace=False))
+    compare_sample(w, requests=req, label=f"lenient {name} full", gpu=gpu, lenience=0.5)
+    lossless = gpu_sample(w)
+    assert gpu[1].mean() > lossless[1].mean()
+
+
+def test_graph_replay_matches_eager():
+    w = generate("c2", DEV, B=8)
+    c = w.cfg
+    ws = torch.empty(sv.workspace_size(c.B, c.gamma, c.V, w.logits.dtype, c.temperature, c.top_k, c.top_p),
+                     dtype=torch.uint8, device=DEV)
+    outs = (torch.empty((c.B, c.gamma + 1), dtype=torch.int32, device=DEV),
+            torch.empty((c.B,), dtype=torch.int32, device=DEV),
+            torch.empty((c.B,), dtype=torch.int32, device=DEV))
+
+    def call():
+        sv.verify_sample_lenient(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature, c.top_k, c.top_p,
+                                 lenience=0.6, workspace=ws, out=outs)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outs:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
