@@ -30,7 +30,11 @@ Pages (all on speculative decoding / speculative sampling):
 
 Parity status of every function is stated in its docstring; all functions
 here are pinned by ``tests/test_oracle_*.py`` (worked examples, closed forms,
-brute force on tiny inputs, chi-square of the output law).
+brute force on tiny inputs, chi-square of the output law).  One step is
+"parity unpinned" by the pages: the replacement rule of the lenient
+acceptance (``beta < 1``), which the pages do not give.  It is a reading
+((p - beta q)_+), pinned only to the pages' 1/beta bound and to its own
+closed-form law by exact enumeration.
 """
 
 from .verify import (  # noqa: F401
