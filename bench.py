@@ -176,6 +176,9 @@ def main():
             torch.empty((B,), dtype=torch.int32, device=dev),
             torch.empty((B,), dtype=torch.int32, device=dev))
     stats = cfg.stats and not rg  # the statistics call takes uniform batches
+    # sampling and statistics in one call (one pass over the logits), except
+    # with lenience, whose call has no statistics: then the separate call
+    fused = stats and not lenient
     sout = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4)) if stats else None
 
     def step(i, timer=None):
@@ -191,6 +194,13 @@ def main():
                                     cfg.top_k, cfg.top_p, workspace=ws, out=outs)
         elif greedy:
             sv.verify_greedy(w.logits, w.ids, workspace=ws, out=outs)
+        elif fused and dl:
+            sv.verify_sample_stats_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                                cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs,
+                                                stats_out=sout)
+        elif fused:
+            sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample, cfg.temperature, cfg.top_k,
+                                   cfg.top_p, workspace=ws, out=outs, stats_out=sout)
         elif dl:
             sv.verify_sample_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
                                           cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs)
@@ -202,10 +212,7 @@ def main():
                              cfg.top_p, workspace=ws, out=outs)
         if timer is not None:
             lib.spec_set_rowpass_timer(None, None)
-        if stats and dl:
-            sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, cfg.temperature, cfg.top_k, cfg.top_p,
-                                         workspace=ws, out=sout)
-        elif stats:
+        if stats and not fused:
             sv.accept_stats(w.logits, w.q, w.ids, cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws,
                             out=sout)
 
@@ -293,10 +300,14 @@ def main():
         step_bytes = rows * row_bytes + q_rows + n_draft * 12 + rows * 4 + B * (G + 1) * 4 + B * 4
         if dl:
             step_bytes += B * G * V * qb
-        if stats:
-            # the statistics call: the target's gamma rows and q (dense, or
-            # the draft's logits for their statistics)
+        if stats and not fused:
+            # the separate statistics call: the target's gamma rows and q
             step_bytes += B * G * V * (cfg.logit_bytes + qb)
+        elif stats:
+            # the combined call's statistics: untruncated rows stream logits
+            # and q again; truncated rows read sum(q) of a dense q, nothing
+            # more when q comes from the draft's logits
+            step_bytes += B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl else B * G * V * 4)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     # ---- CPU oracle baseline on a bounded sample ----
@@ -384,6 +395,8 @@ def main():
                    "logits": cfg.dtype, "temperature": cfg.temperature, "top_k": cfg.top_k, "top_p": cfg.top_p,
                    "q": "formed from the draft's logits" if dl else "dense float32 input",
                    "acceptance": f"lenient, beta = {args.lenience}" if lenient else "lossless",
+                   "statistics": ("none" if not stats else
+                                  "combined sampling + statistics call" if fused else "separate statistics call"),
                    "batch": (f"ragged: gamma_b uniform on 0..{G}, {n_draft} drafts, packed; sampling / greedy "
                              f"call only" if rg else "uniform"),
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,

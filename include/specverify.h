@@ -132,6 +132,21 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
                             float* out_z_qp, float* out_accept_prob, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Sampling verify and acceptance statistics together: the outputs of
+ * spec_verify_sample and of spec_accept_stats for the same inputs, from one
+ * pass over the target logits (the statistics reuse the sampling call's row
+ * results for rows 0..gamma-1 instead of recomputing them).  Arguments are
+ * those of the two calls; the statistics outputs may be NULL only when
+ * gamma = 0.  Workspace: spec_verify_workspace_size (which covers this
+ * call).  [WR] §4.2 and §6; [RL] §2; [MN] §三 (acceptance rate, monitored per
+ * round to adapt gamma: [MN] §九, point 3). */
+sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                   const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                   int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, int32_t* out_tokens,
+                                   int32_t* out_num_accepted, uint32_t* out_row_flags, float* out_alpha,
+                                   float* out_z_pq, float* out_z_qp, float* out_accept_prob, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* ---- q formed in the library from the draft's logits -----------------------
  * [WR] §2.3 and [MN] §二 (notation): q, like p, is the distribution after the
  * decoding rules.  These calls take the draft model's logits instead of q and
@@ -223,6 +238,18 @@ sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, cons
                                     const int32_t* cu_draft, int32_t n_draft, int32_t B, int32_t gamma_max,
                                     int32_t V, int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,
                                     uint32_t* out_row_flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify_sample_stats with q formed from the draft's logits: the
+ * outputs of spec_verify_sample_draft_logits and spec_accept_stats_draft_logits
+ * from one pass over the draft's and one over the target's logits.
+ * Workspace: spec_verify_draft_logits_workspace_size. */
+sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                               sv_dtype draft_dt, const int32_t* draft_ids, const float* u_accept,
+                                               const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                                               sv_sampling_params prm, int32_t* out_tokens, int32_t* out_num_accepted,
+                                               uint32_t* out_row_flags, float* out_alpha, float* out_z_pq,
+                                               float* out_z_qp, float* out_accept_prob, void* workspace,
+                                               size_t workspace_bytes, void* stream);
 
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
  * arguments are non-NULL, every later spec_verify_sample /

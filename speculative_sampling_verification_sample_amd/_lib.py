@@ -51,6 +51,16 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
          _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_sample_stats": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
+         _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
+    "spec_verify_sample_stats_draft_logits": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
+         _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
     "spec_verify_sample_lenient": (
         ctypes.c_int,
         [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,

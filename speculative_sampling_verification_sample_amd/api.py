@@ -328,3 +328,81 @@ def verify_greedy_ragged(logits, ids, cu_draft, gamma_max: int, eos_id: int = -1
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_verify_greedy_ragged")
     return tokens, nacc, flags
+
+
+def _sample_stats_outs(out, stats_out, B, G, dev):
+    if out is None:
+        out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    if stats_out is None:
+        stats_out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
+    return out, stats_out
+
+
+def verify_sample_stats(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0,
+                        workspace: Optional[torch.Tensor] = None, out=None, stats_out=None):
+    """verify_sample and accept_stats of the same inputs from one pass over the
+    logits; returns (tokens, n_accepted, flags, alpha, z_pq, z_qp, accept_prob)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    if G > 0:
+        _check(q, "q", torch.float32, (B, G, V))
+        _check(ids, "ids", torch.int32, (B, G))
+        _check(u_accept, "u_accept", torch.float32, (B, G))
+    _check(u_resample, "u_resample", torch.float32, (B, G1))
+    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev)
+    need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_stats(
+        logits.data_ptr(), _DT[logits.dtype],
+        q.data_ptr() if G > 0 else None, ids.data_ptr() if G > 0 else None,
+        u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_stats")
+    return tokens, nacc, flags, alpha, zpq, zqp, acc
+
+
+def verify_sample_stats_draft_logits(logits, draft_logits, ids, u_accept, u_resample, temperature=1.0, top_k=0,
+                                     top_p=1.0, workspace: Optional[torch.Tensor] = None, out=None, stats_out=None):
+    """verify_sample_draft_logits and accept_stats_draft_logits of the same
+    inputs from one pass over each logits tensor."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, G1, V = logits.shape
+    G = G1 - 1
+    _check(logits, "logits", None, (B, G1, V))
+    if logits.dtype not in _DT:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    ddt = logits.dtype
+    if G > 0:
+        _check(draft_logits, "draft_logits", None, (B, G, V))
+        if draft_logits.dtype not in _DT:
+            raise ValueError("draft_logits must be float32 or bfloat16")
+        ddt = draft_logits.dtype
+        _check(ids, "ids", torch.int32, (B, G))
+        _check(u_accept, "u_accept", torch.float32, (B, G))
+    _check(u_resample, "u_resample", torch.float32, (B, G1))
+    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev)
+    need = draft_logits_workspace_size(B, G, V, logits.dtype, ddt, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_stats_draft_logits(
+        logits.data_ptr(), _DT[logits.dtype],
+        draft_logits.data_ptr() if G > 0 else None, _DT[ddt], ids.data_ptr() if G > 0 else None,
+        u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
+        B, G, V, _params(temperature, top_k, top_p),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_stats_draft_logits")
+    return tokens, nacc, flags, alpha, zpq, zqp, acc

@@ -48,8 +48,9 @@ constexpr int kUnionMax = 2048;   // LDS entries of the row finisher's candidate
 constexpr int kOneLaunchMinB = 256;
 
 // CALL_DRAFT: the row passes over a draft's logits [B, gamma, V] (q formed
-// in the library): statistics and kept lists only.
-enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS, CALL_DRAFT };
+// in the library): statistics and kept lists only.  CALL_SAMPLE_STATS: the
+// sampling call whose row results also serve the statistics.
+enum CallKind { CALL_SAMPLE, CALL_GREEDY, CALL_STATS, CALL_DRAFT, CALL_SAMPLE_STATS };
 
 struct Plan {
   int64_t rows = 0;
@@ -63,6 +64,7 @@ struct Plan {
   int nch4 = 1;
   int scale_bits = 40;
   size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
+  size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][4] (CALL_STATS, CALL_SAMPLE_STATS)
   size_t total = 0;
 };
 
@@ -75,6 +77,7 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.rows_per_req = (kind == CALL_STATS || kind == CALL_DRAFT) ? gamma : gamma + 1;
   p.rows = (int64_t)B * p.rows_per_req;
   p.trunc = (kind != CALL_GREEDY) && (topk || topp);
+  const bool sampling = kind == CALL_SAMPLE || kind == CALL_SAMPLE_STATS;
   p.mode = (kind == CALL_GREEDY) ? M_ARGMAX : (p.trunc ? M_TRUNC : M_SOFTMAX);
   p.need_s = p.trunc && topp && !topk;
   p.fast = !topk || prm.top_k <= kFastTopK;
@@ -95,8 +98,10 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
       if (p.nu == 4 || p.rows * nch >= kTruncMinWG) break;
     }
   } else {
-    // Short workgroups in several waves of residency keep the launch tail short.
-    const int64_t minchunk = 4096;
+    // Short workgroups in several waves of residency keep the launch tail
+    // short; short launches (few rows) take chunks of at least 6400 elements,
+    // which measured a few per cent faster than 4096 on 64 x 5 rows of 32000.
+    const int64_t minchunk = 6400;
     const int64_t target = kTargetWG * 4;
     const int64_t want = p.rows > 0 ? (target + p.rows - 1) / p.rows : 1;
     const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
@@ -129,12 +134,14 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.off_kept = off;
   if (p.trunc) off = align_up(off + rows * (size_t)kKMax * sizeof(Cand), 256);
   p.off_jobs = off;
-  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * sizeof(BigJob), 256);
+  if (sampling) off = align_up(off + (size_t)B * sizeof(BigJob), 256);
   p.off_gath = off;
-  if (kind == CALL_SAMPLE) off = align_up(off + rows * sizeof(float2), 256);
+  if (sampling) off = align_up(off + rows * sizeof(float2), 256);
   p.off_part = off;
-  if (kind == CALL_SAMPLE) off = align_up(off + (size_t)B * p.nch4 * sizeof(double), 256);
-  if (kind == CALL_STATS) off = align_up(off + rows * nch * 4 * sizeof(double), 256);
+  if (sampling) off = align_up(off + (size_t)B * p.nch4 * sizeof(double), 256);
+  p.off_spart = off;
+  if (kind == CALL_STATS || kind == CALL_SAMPLE_STATS)
+    off = align_up(off + (size_t)B * gamma * nch * 4 * sizeof(double), 256);
   p.total = std::max<size_t>(off, 256);
   return p;
 }
@@ -312,7 +319,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
                              int32_t gamma, int32_t V, sv_sampling_params prm, float c, int32_t* out_tokens,
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
                              const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
-                             double beta = 1.0) {
+                             double beta = 1.0, bool force_rowfinal = false) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
@@ -323,7 +330,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
       bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live)
          : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live);
   if (s != SV_OK) return s;
-  if (p.trunc) {
+  if (p.trunc || force_rowfinal) {
     s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live)
            : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live);
     if (s != SV_OK) return s;
@@ -407,24 +414,25 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   return launched();
 }
 
-// The statistics once q's source is known; `qkept` holds q's kept lists
-// when q comes from truncated draft logits.
-sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q, const Cand* qkept,
-                            const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
-                            float c, float* out_alpha, float* out_z_pq, float* out_z_qp, float* out_accept_prob,
-                            void* workspace, hipStream_t st) {
-  const bool bf = dt == SV_BF16;
-  const int G1 = gamma + 1;
-  sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
-                   : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
-  if (s != SV_OK) return s;
-  s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
-         : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
-  if (s != SV_OK) return s;
+// Outputs of the acceptance statistics (each [B, gamma] float32), and q's
+// kept lists when q comes from truncated draft logits.
+struct StatsOut {
+  float* alpha;
+  float* z_pq;
+  float* z_qp;
+  float* accept_prob;
+  const Cand* qkept;
+};
+
+// The statistics kernels over target rows 0..gamma-1 whose row results sit
+// in plan p's info / kept regions at rows b * info_rpr + j.
+sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const QSrc& q, const StatsOut& so,
+                       const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, float c, int info_rpr,
+                       void* workspace, hipStream_t st) {
   StatsArgs a;
   a.logits = target_logits;
   a.q = q;
-  a.qkept = qkept;
+  a.qkept = so.qkept;
   a.ids = draft_ids;
   a.V = V;
   a.gamma = gamma;
@@ -433,14 +441,16 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
   a.c = c;
   a.info = ws_at<RowInfo>(workspace, p.off_info);
   a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
+  a.info_rpr = info_rpr;
   a.kmax = kKMax;
-  a.partials = ws_at<double>(workspace, p.off_part);
-  a.out_alpha = out_alpha;
-  a.out_zpq = out_z_pq;
-  a.out_zqp = out_z_qp;
-  a.out_acc = out_accept_prob;
-  a.rows = p.rows;
-  dim3 grid((unsigned)(p.rows * p.nchunks));
+  a.partials = ws_at<double>(workspace, p.off_spart);
+  a.out_alpha = so.alpha;
+  a.out_zpq = so.z_pq;
+  a.out_zqp = so.z_qp;
+  a.out_acc = so.accept_prob;
+  a.rows = (int64_t)B * gamma;
+  if (a.rows == 0) return SV_OK;
+  dim3 grid((unsigned)(a.rows * p.nchunks));
   const bool qlog = q.dense == nullptr;
   if (bf) {
     if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<true, true>), grid, dim3(256), 0, st, a);
@@ -449,11 +459,27 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
     if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<false, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((stats_chunk_kernel<false, false>), grid, dim3(256), 0, st, a);
   }
-  s = launched();
+  sv_status s = launched();
   if (s != SV_OK) return s;
-  if (bf) hipLaunchKernelGGL((stats_final_kernel<true>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((stats_final_kernel<false>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, st, a);
+  if (bf) hipLaunchKernelGGL((stats_final_kernel<true>), dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((stats_final_kernel<false>), dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
   return launched();
+}
+
+// The statistics call once q's source is known (its own row passes over the
+// target's rows 0..gamma-1, plan CALL_STATS).
+sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q, const StatsOut& so,
+                            const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
+                            float c, void* workspace, hipStream_t st) {
+  const bool bf = dt == SV_BF16;
+  const int G1 = gamma + 1;
+  sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
+                   : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
+  if (s != SV_OK) return s;
+  s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
+         : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
+  if (s != SV_OK) return s;
+  return launch_stats(p, target_logits, bf, q, so, draft_ids, B, gamma, V, c, gamma, workspace, st);
 }
 
 // Row passes over the draft's logits [B, gamma, V] (plan CALL_DRAFT, in its
@@ -486,6 +512,21 @@ sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* 
 // draft rows' (at draft_ws_offset).
 size_t draft_ws_offset(CallKind kind, int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
   return align_up(make_plan(kind, B, gamma, V, dt, prm).total, 256);
+}
+
+// The sampling call and the statistics of its rows 0..gamma-1 from one pass
+// over the target logits (plan CALL_SAMPLE_STATS): the statistics kernels
+// read the sampling call's row results instead of recomputing them.
+sv_status verify_sample_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
+                                   const StatsOut& so, const int32_t* draft_ids, const float* u_accept,
+                                   const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                                   sv_sampling_params prm, float c, int32_t* out_tokens, int32_t* out_num_accepted,
+                                   uint32_t* out_row_flags, void* workspace, hipStream_t st) {
+  sv_status s = verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
+                                   out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0,
+                                   /*force_rowfinal=*/true);
+  if (s != SV_OK) return s;
+  return launch_stats(p, target_logits, dt == SV_BF16, q, so, draft_ids, B, gamma, V, c, gamma + 1, workspace, st);
 }
 
 // Greedy verify (uniform, or ragged with draft offsets `cu`).
@@ -536,7 +577,7 @@ extern "C" {
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
   float c;
   if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
-  size_t a = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm).total;
+  size_t a = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm).total;  // covers CALL_SAMPLE
   size_t g = make_plan(CALL_GREEDY, B, gamma, V, dt, prm).total;
   size_t s = make_plan(CALL_STATS, B, gamma, V, dt, prm).total;
   return std::max(a, std::max(g, s));
@@ -561,6 +602,31 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
                             gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st);
+}
+
+sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                   const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                   int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, int32_t* out_tokens,
+                                   int32_t* out_num_accepted, uint32_t* out_row_flags, float* out_alpha,
+                                   float* out_z_pq, float* out_z_qp, float* out_accept_prob, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs) ||
+                    out_alpha == nullptr || out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);
+  if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, nullptr};
+  return verify_sample_stats_impl(p, target_logits, dt, q_src_dense(draft_probs, V), so, draft_ids, u_accept,
+                                  u_resample, B, gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags,
+                                  workspace, st);
 }
 
 sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32_t* draft_ids, int32_t B,
@@ -591,8 +657,9 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return accept_stats_impl(p, target_logits, dt, q_src_dense(draft_probs, V), nullptr, draft_ids, B, gamma, V, prm, c,
-                           out_alpha, out_z_pq, out_z_qp, out_accept_prob, workspace, st);
+  const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, nullptr};
+  return accept_stats_impl(p, target_logits, dt, q_src_dense(draft_probs, V), so, draft_ids, B, gamma, V, prm, c,
+                           workspace, st);
 }
 
 size_t spec_verify_draft_logits_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_dtype draft_dt,
@@ -602,7 +669,7 @@ size_t spec_verify_draft_logits_workspace_size(int32_t B, int32_t gamma, int32_t
       check_params(prm, &c) != SV_OK)
     return 0;
   const size_t d = make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
-  const size_t a = draft_ws_offset(CALL_SAMPLE, B, gamma, V, dt, prm) + d;
+  const size_t a = draft_ws_offset(CALL_SAMPLE_STATS, B, gamma, V, dt, prm) + d;  // covers CALL_SAMPLE
   const size_t s = draft_ws_offset(CALL_STATS, B, gamma, V, dt, prm) + d;
   return std::max(a, s);
 }
@@ -664,8 +731,44 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c, static_cast<unsigned char*>(workspace) + qoff,
                      st, &q, &qkept);
   if (s != SV_OK) return s;
-  return accept_stats_impl(p, target_logits, dt, q, qkept, draft_ids, B, gamma, V, prm, c, out_alpha, out_z_pq,
-                           out_z_qp, out_accept_prob, workspace, st);
+  const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, qkept};
+  return accept_stats_impl(p, target_logits, dt, q, so, draft_ids, B, gamma, V, prm, c, workspace, st);
+}
+
+sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                               sv_dtype draft_dt, const int32_t* draft_ids, const float* u_accept,
+                                               const float* u_resample, int32_t B, int32_t gamma, int32_t V,
+                                               sv_sampling_params prm, int32_t* out_tokens, int32_t* out_num_accepted,
+                                               uint32_t* out_row_flags, float* out_alpha, float* out_z_pq,
+                                               float* out_z_qp, float* out_accept_prob, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_logits == nullptr || draft_ids == nullptr || u_accept == nullptr ||
+                    !aligned16(draft_logits) || out_alpha == nullptr || out_z_pq == nullptr || out_z_qp == nullptr ||
+                    out_accept_prob == nullptr))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);
+  const size_t qoff = draft_ws_offset(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);
+  const size_t need = qoff + make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  QSrc q = q_src_none(V);
+  const Cand* qkept = nullptr;
+  if (gamma > 0) {
+    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c,
+                       static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept);
+    if (s != SV_OK) return s;
+  }
+  const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, qkept};
+  return verify_sample_stats_impl(p, target_logits, dt, q, so, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
+                                  out_tokens, out_num_accepted, out_row_flags, workspace, st);
 }
 
 sv_status spec_verify_sample_lenient(const void* target_logits, sv_dtype dt, const float* draft_probs,

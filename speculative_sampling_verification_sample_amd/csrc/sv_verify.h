@@ -1071,8 +1071,13 @@ struct StatsArgs {
   int32_t nchunks;
   int64_t chunk;
   float c;
-  const RowInfo* info;  // [B * gamma]
+  // Row results of the target's rows 0..gamma-1: info and kept lists of
+  // position j of request b at row b * info_rpr + j (info_rpr = gamma for
+  // the statistics call's own row passes, gamma + 1 when they are the
+  // sampling call's).
+  const RowInfo* info;
   const Cand* kept;
+  int32_t info_rpr;
   int32_t kmax;
   double* partials;     // [rows][nchunks][4]
   float* out_alpha;
@@ -1081,6 +1086,11 @@ struct StatsArgs {
   float* out_acc;
   int64_t rows;
 };
+
+__device__ __forceinline__ int64_t info_row(const StatsArgs& a, int64_t r) {
+  const int64_t b = r / a.gamma;
+  return b * a.info_rpr + (r - b * a.gamma);
+}
 
 // Does the row need the full-row sums of the chunk pass?
 __device__ __forceinline__ bool stats_streamed(const StatsArgs& a, const RowInfo& ri, int64_t r) {
@@ -1095,7 +1105,7 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   const int64_t blk = blockIdx.x;
   const int64_t r = blk / a.nchunks;
   const int ci = (int)(blk - r * a.nchunks);
-  const RowInfo ri = a.info[r];
+  const RowInfo ri = a.info[info_row(a, r)];
   const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
   const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
   const int64_t x0 = (int64_t)ci * a.chunk, x1 = min(x0 + a.chunk, a.V);
@@ -1177,7 +1187,8 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wid;
   if (r >= a.rows) return;
-  const RowInfo ri = a.info[r];
+  const int64_t ir = info_row(a, r);
+  const RowInfo ri = a.info[ir];
   const float qnan = __builtin_nanf("");
   const bool qbad = a.q.dense == nullptr && (a.q.info[r].flags & RF_NONFINITE);
   if ((ri.flags & RF_NONFINITE) || qbad) {
@@ -1203,7 +1214,7 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     zpq = acc4[1];
     zqp = acc4[2];
   } else {
-    const Cand* L = a.kept + r * a.kmax;  // token-id order
+    const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     for (int i = lane; i < ri.nkept; i += kWave) {
       Cand e = L[i];

@@ -96,9 +96,13 @@ def compare_greedy(w, requests=None, label=""):
         raise AssertionError(f"[{label}] request {int(req[i])}: gpu {tok[req][i].tolist()} vs oracle {o['tokens'][i].tolist()}")
 
 
-def compare_stats(w, requests=None, label="", rtol=1e-5, atol=2e-7, draft_logits=False):
+def compare_stats(w, requests=None, label="", rtol=1e-5, atol=2e-7, draft_logits=False, gpu=None):
+    """gpu: the four statistics outputs already computed (else the library's
+    statistics call is run here)."""
     c = w.cfg
-    if draft_logits:
+    if gpu is not None:
+        al, zpq, zqp, acc = gpu
+    elif draft_logits:
         al, zpq, zqp, acc = sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, c.temperature, c.top_k,
                                                          c.top_p)
     else:

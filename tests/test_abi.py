@@ -230,6 +230,37 @@ def test_lenient_argument_errors():
     assert f(0.5, B=0) == 0
 
 
+def test_sample_stats_argument_errors():
+    lib = _lib()
+    INVALID, WORKSPACE = 1, 3
+
+    def f(**kw):
+        a = dict(logits=FAKE, q=FAKE, al=FAKE, B=2, G=3, ws=None, wsb=0)
+        a.update(kw)
+        return lib.spec_verify_sample_stats(a["logits"], 1, a["q"], FAKE, FAKE, FAKE, a["B"], a["G"], 100, _P(),
+                                            FAKE, FAKE, None, a["al"], FAKE, FAKE, FAKE, a["ws"], a["wsb"], None)
+
+    def g(**kw):
+        a = dict(dz=FAKE, ddt=1, al=FAKE, G=3, ws=None, wsb=0)
+        a.update(kw)
+        return lib.spec_verify_sample_stats_draft_logits(FAKE, 1, a["dz"], a["ddt"], FAKE, FAKE, FAKE, 2, a["G"], 100,
+                                                         _P(), FAKE, FAKE, None, a["al"], FAKE, FAKE, FAKE, a["ws"],
+                                                         a["wsb"], None)
+
+    assert f() == WORKSPACE
+    assert f(al=None) == INVALID
+    assert f(q=None) == INVALID
+    assert f(G=0, q=None, al=None) == WORKSPACE  # no drafts: no statistics outputs needed
+    assert f(B=0) == 0
+    # the combined call's workspace is what spec_verify_workspace_size reports
+    wsb = lib.spec_verify_workspace_size(2, 3, 100, 1, _P())
+    assert f(ws=FAKE, wsb=wsb - 256) == WORKSPACE
+    assert g() == WORKSPACE
+    assert g(ddt=5) == INVALID
+    assert g(al=None) == INVALID
+    assert g(dz=FAKE + 2) == INVALID
+
+
 def test_product_path_fails_loudly_without_library(tmp_path):
     from speculative_sampling_verification_sample_amd import _lib as L
 
