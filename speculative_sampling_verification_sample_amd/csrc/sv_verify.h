@@ -993,6 +993,61 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
   }
   const int G = sp.g;
   const int64_t lo = sp.lo;
+  if (P1 <= kWave) {
+    // lane j <= gamma_b: row j's argmax from its chunk results (the loads of
+    // all rows in flight together), then the first mismatch by ballot; the
+    // (max, lowest id) merge does not depend on the order of the chunks
+    float v = kNegInf;
+    int i = 0x7fffffff, d = -1;
+    uint32_t fl = 0;
+    if (lane <= G) {
+      const ChunkOut* co = a.cout + (lo + b + lane) * a.nchunks;
+      if (lane < G) d = a.ids[lo + lane];
+      for (int c0 = 0; c0 < a.nchunks; c0 += 8) {
+        ChunkOut o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (c0 + k < a.nchunks) o[k] = co[c0 + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (c0 + k >= a.nchunks) break;
+          argmax_merge(v, i, o[k].xmax, o[k].argmax);
+          fl |= o[k].flags;
+        }
+      }
+    }
+    if (ballot(lane <= G && (fl & CF_NAN)) != 0) {
+      if (lane < P1) out[lane] = -1;
+      if (lane == 0) {
+        a.out_nacc[b] = 0;
+        if (a.out_flags) a.out_flags[b] = 8u;  // SV_ROW_NONFINITE
+      }
+      return;
+    }
+    const uint64_t mism = ballot(lane < G && d != i);
+    int n = mism ? (int)__builtin_ctzll(mism) : G;
+    bool eos_cut = false;
+    if (a.eos >= 0) {
+      // an accepted end of sequence ends the output ([WR] §14.3)
+      const uint64_t em = ballot(lane < n && d == a.eos);
+      if (em) {
+        n = (int)__builtin_ctzll(em);
+        eos_cut = true;
+      }
+    }
+    const int gn = eos_cut ? a.eos : __shfl(i, n, kWave);
+    const int dn = __shfl(d, n, kWave);
+    if (lane < P1) out[lane] = lane < n ? d : (lane == n ? gn : -1);
+    if (lane == 0) {
+      a.out_nacc[b] = n;
+      uint32_t f = 0;
+      if (n < G && !eos_cut && (dn < 0 || (int64_t)dn >= a.V)) f |= 1u;  // SV_ROW_BAD_ID
+      if (a.eos >= 0 && gn == a.eos) f |= 16u;                          // SV_ROW_EOS
+      if (a.out_flags) a.out_flags[b] = f;
+    }
+    return;
+  }
+  // long drafts: row by row
   bool nan_any = false;
   int n = G, gn = -1;
   bool decided = false, eos_cut = false;
