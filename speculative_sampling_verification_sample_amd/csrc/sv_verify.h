@@ -48,23 +48,53 @@ struct AcceptArgs {
 // Draw from the kept list of one row, stored in token-id order (called by a
 // whole wave).
 // residual: weights (e/S - qs q)_+ on the list (qs = beta); otherwise e/S.
+// The list is walked 64 entries at a time in id order (prefix sums by wave
+// scans, carried between steps); the loads of kDrawBlk steps (list entries,
+// then q at their ids) are issued together before their scans.
+constexpr int kDrawBlk = 4;
 __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bool& residual, float u,
                               uint32_t& fl, double qs) {
   const int lane = lane_id();
   const double invS = 1.0 / S;
-  auto weight = [&](int i, bool res) -> double {
-    if (i >= n) return 0.0;
-    Cand e = L[i];
-    double p = (double)e.v * invS;
-    if (!res) return p;
-    double d = p - qs * (double)qr.at(e.idx);
-    return d > 0.0 ? d : 0.0;
+  // weights of entries i0 + 64 k + lane, k < kDrawBlk (0 past the end)
+  auto weights = [&](int i0, bool res, double (&w)[kDrawBlk], int (&id)[kDrawBlk]) {
+    Cand e[kDrawBlk];
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) {
+      const int i = i0 + k * kWave + lane;
+      e[k].v = 0.0f;
+      e[k].idx = -1;
+      if (i < n) e[k] = L[i];
+    }
+    float qv[kDrawBlk];
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) qv[k] = (res && e[k].idx >= 0) ? qr.at(e[k].idx) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) {
+      id[k] = e[k].idx;
+      const double p = (double)e[k].v * invS;
+      if (e[k].idx < 0) {
+        w[k] = 0.0;
+      } else if (!res) {
+        w[k] = p;
+      } else {
+        const double d = p - qs * (double)qv[k];
+        w[k] = d > 0.0 ? d : 0.0;
+      }
+    }
   };
   auto total = [&](bool res) -> double {
     double carry = 0.0;
-    for (int i0 = 0; i0 < n; i0 += kWave) {
-      double incl = wave_incl_scan_d(weight(i0 + lane, res));
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+    for (int i0 = 0; i0 < n; i0 += kDrawBlk * kWave) {
+      double w[kDrawBlk];
+      int id[kDrawBlk];
+      weights(i0, res, w, id);
+#pragma unroll
+      for (int k = 0; k < kDrawBlk; ++k) {
+        if (i0 + k * kWave >= n) break;
+        const double incl = wave_incl_scan_d(w[k]);
+        carry = carry + __shfl(incl, kWave - 1, kWave);
+      }
     }
     return carry;
   };
@@ -77,19 +107,26 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
   const double t = (double)u * W;
   double carry = 0.0;
   int token = -1, lastpos = -1;
-  for (int i0 = 0; i0 < n; i0 += kWave) {
-    const int i = i0 + lane;
-    const double w = weight(i, residual);
-    const double incl = wave_incl_scan_d(w);
-    const double C = carry + incl;
-    uint64_t hit = ballot(i < n && C > t);
-    if (hit) {
-      token = L[i0 + (int)__builtin_ctzll(hit)].idx;
-      break;
+  for (int i0 = 0; i0 < n && token < 0; i0 += kDrawBlk * kWave) {
+    double w[kDrawBlk];
+    int id[kDrawBlk];
+    weights(i0, residual, w, id);
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) {
+      const int j0 = i0 + k * kWave;
+      if (j0 >= n) break;
+      const int i = j0 + lane;
+      const double incl = wave_incl_scan_d(w[k]);
+      const double C = carry + incl;
+      const uint64_t hit = ballot(i < n && C > t);
+      if (hit) {
+        token = __shfl(id[k], (int)__builtin_ctzll(hit), kWave);
+        break;
+      }
+      const uint64_t pos = ballot(i < n && w[k] > 0.0);
+      if (pos) lastpos = __shfl(id[k], 63 - (int)__builtin_clzll(pos), kWave);
+      carry = carry + __shfl(incl, kWave - 1, kWave);
     }
-    uint64_t pos = ballot(i < n && w > 0.0);
-    if (pos) lastpos = L[i0 + 63 - (int)__builtin_clzll(pos)].idx;
-    carry = carry + __shfl(incl, kWave - 1, kWave);
   }
   return token >= 0 ? token : lastpos;
 }

@@ -97,3 +97,40 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(outs, ref):
             assert torch.equal(a, b)
+
+
+def test_toy_law_on_gpu_outputs():
+    """1e6 rounds of one request at beta = 0.5: every emitted slot follows the
+    lenient law min(q, p/beta) + P(reject) (p - beta q)_+ / W (the bonus slot
+    follows p), no token exceeds 1/beta times its p, and tokens per round
+    match E[N] with acceptance rates alpha_j = sum min(q_j, p_j / beta)."""
+    from scipy import stats
+
+    import oracle
+
+    beta = 0.5
+    w = generate("toy", DEV, B=1_000_000)
+    tok, nacc, fl = gpu_sample(w, lenience=beta)
+    assert (fl == 0).all()
+    z = w.logits[0].double().cpu().numpy()
+    q = w.q[0].double().cpu().numpy()
+    G = w.cfg.gamma
+    p_rows = [oracle.process_row(z[j], 1.0).p for j in range(G + 1)]
+    alpha = [np.minimum(q[j], p_rows[j] / beta).sum() for j in range(G)]
+    pv = []
+    for j in range(G + 1):
+        if j < G:
+            res = np.maximum(p_rows[j] - beta * q[j], 0.0)
+            law = np.minimum(q[j], p_rows[j] / beta) + (1.0 - alpha[j]) * res / res.sum()
+        else:
+            law = p_rows[j]
+        reached = nacc >= j
+        counts = np.bincount(tok[reached, j], minlength=5)
+        pv.append(stats.chisquare(counts, law * reached.sum()).pvalue)
+        freq = counts / reached.sum()
+        assert (freq <= p_rows[j] / beta + 5 * np.sqrt(freq / reached.sum()) + 1e-12).all()
+    print("lenient chi-square p-values per slot:", [f"{x:.3g}" for x in pv], flush=True)
+    assert min(pv) > 1e-4
+    EN = 1 + sum(np.prod(alpha[: i + 1]) for i in range(G))
+    N = nacc + 1
+    assert abs(N.mean() - EN) < 4 * N.std() / np.sqrt(len(N))
