@@ -297,7 +297,7 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const i
   a.info = ws_at<RowInfo>(ws, p.off_info);
   a.kept = p.trunc ? ws_at<Cand>(ws, p.off_kept) : nullptr;
   set_kernel_attrs();
-  size_t dyn = p.trunc ? (size_t)p.um * 16 : 0;  // key, id, fixed-point mass per entry
+  size_t dyn = p.trunc ? (size_t)p.um * 8 : 0;  // key and token id per union entry
   hipLaunchKernelGGL((rowfinal_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), dyn, st, a);
   return launched();
 }

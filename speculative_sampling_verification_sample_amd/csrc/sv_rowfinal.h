@@ -202,10 +202,11 @@ __device__ uint32_t block_select_count(const uint32_t* keys, int n, int need, ui
   return prefix;
 }
 
-// Largest key v with mass(entries with key >= v, key >= floor) >= target.
+// Largest key v with mass(entries with key >= v, key >= floor) >= target,
+// an entry's mass being the fixed-point e(x) of its key (x = key2f(key)).
 // Returns false when the whole mass stays below target.
 template <bool BF16>
-__device__ __forceinline__ bool block_select_mass(const uint32_t* keys, const unsigned long long* mass, int n, uint32_t floor_key,
+__device__ __forceinline__ bool block_select_mass(const uint32_t* keys, float c, float R, int n, uint32_t floor_key,
                                   double target, unsigned long long* mh, int* s_dn, unsigned long long* s_above,
                                   uint32_t& out_key) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -218,7 +219,8 @@ __device__ __forceinline__ bool block_select_mass(const uint32_t* keys, const un
     for (int i0 = 0; i0 < n; i0 += 256) {
       const int i = i0 + tid;
       const uint32_t k = i < n ? keys[i] : 0u;
-      if (i < n && k >= floor_key && (k & pmask) == prefix) atomicAdd(&mh[(k >> shift) & 255u], mass[i]);
+      if (i < n && k >= floor_key && (k & pmask) == prefix)
+        atomicAdd(&mh[(k >> shift) & 255u], to_fixed(e_of(key2f(k), c, R)));
     }
     __syncthreads();
     if (wid == 0) {
@@ -568,10 +570,11 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ unsigned long long mh[256], s_u64[4], s_above;
   extern __shared__ __align__(16) unsigned char s_dyn[];
-  // union entries: keys, token ids, fixed-point masses
+  // union entries: keys and token ids (an entry's fixed-point mass is a
+  // function of its key, recomputed where needed, which halves the LDS a
+  // workgroup holds and so doubles the row finishers resident per CU)
   uint32_t* keys = reinterpret_cast<uint32_t*>(s_dyn);
   int32_t* idxs = reinterpret_cast<int32_t*>(s_dyn + (size_t)a.um * 4);
-  unsigned long long* mass = reinterpret_cast<unsigned long long*>(s_dyn + (size_t)a.um * 8);
 
   const int nch = a.nchunks;
   const bool flat = nch <= kWave;  // the union walks one flat index over the chunk lists
@@ -682,7 +685,6 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     if (keep && pos < a.um) {
       keys[pos] = f2key(e.v);
       idxs[pos] = e.idx;
-      mass[pos] = to_fixed(e_of(e.v, a.c, R));
     }
   };
   if (flat) {
@@ -733,7 +735,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   auto mass_from = [&](uint32_t kf) -> unsigned long long {
     unsigned long long part = 0ull;
     for (int i = tid; i < nu; i += 256)
-      if (keys[i] >= kf) part += mass[i];
+      if (keys[i] >= kf) part += to_fixed(e_of(key2f(keys[i]), a.c, R));
     return block_sum_u64(part, s_u64);
   };
   uint32_t kfinal = kfloor;
@@ -742,7 +744,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     const double Sref = topk ? (double)mass_from(kfloor) : s_S * scale;
     const double target = (double)a.top_p * Sref;
     uint32_t kp;
-    if (block_select_mass<BF16>(keys, mass, nu, kfloor, target, mh, s_dn, &s_above, kp)) {
+    if (block_select_mass<BF16>(keys, a.c, R, nu, kfloor, target, mh, s_dn, &s_above, kp)) {
       kfinal = kp;
     } else if (!(topk || theta == kLowest)) {
       // the crossing lies below the certified candidates: exact path
@@ -755,28 +757,32 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   ri.tau = key2f(kfinal);
   if (kfinal == 0) ri.tau = kLowest;
   // ---- kept list in token-id order: compact the kept entries (in any
-  //      order) into the mass array, no longer needed, then store each at
-  //      its rank by id (ids are unique within a row) ----
+  //      order) in place over the union (ids over the keys, e over the
+  //      ids), then store each at its rank by id (ids are unique within a
+  //      row).  Each block of 256 entries is read before any of its slots is
+  //      written; earlier blocks only write slots below the current one. ----
   if (tid == 0) s_n = 0;
   __syncthreads();
-  int32_t* kid = reinterpret_cast<int32_t*>(mass);
-  float* kev = reinterpret_cast<float*>(mass) + a.um;
+  int32_t* kid = reinterpret_cast<int32_t*>(keys);
+  float* kev = reinterpret_cast<float*>(idxs);
   for (int i0 = 0; i0 < nu; i0 += 256) {
     const int i = i0 + tid;
-    const bool keep = i < nu && keys[i] >= kfinal;
+    const uint32_t k = i < nu ? keys[i] : 0u;
+    const int id = i < nu ? idxs[i] : 0;
+    const bool keep = i < nu && k >= kfinal;
+    __syncthreads();
     const int pos = wave_append_slot(keep, &s_n);
     if (keep) {
-      kid[pos] = idxs[i];
-      kev[pos] = e_of(key2f(keys[i]), a.c, R);
+      kid[pos] = id;
+      kev[pos] = e_of(key2f(k), a.c, R);
     }
   }
   __syncthreads();
   const int nkept = s_n;
   if (nkept <= a.kmax) {
     Cand* out = a.kept + r * (int64_t)a.kmax;
-    // kid sits at the start of the 8-byte-aligned mass array, whose size
-    // (um >= cap_out entries) keeps it 16-byte aligned: ids are read four at
-    // a time, the same address for every lane (a broadcast read).
+    // kid sits at the start of the dynamic LDS (16-byte aligned): ids are
+    // read four at a time, the same address for every lane (a broadcast read).
     const int4* kid4 = reinterpret_cast<const int4*>(kid);
     const int nk4 = nkept >> 2;
     // KP entries ranked per thread in one sweep of 256 * KP entries
