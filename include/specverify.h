@@ -14,11 +14,12 @@
  *   library never allocates, frees or retains caller memory and keeps no
  *   state between calls (apart from the optional profiling hook
  *   spec_set_rowpass_timer).  All scratch lives in the caller's `workspace`
- *   (device memory of at least spec_verify_workspace_size() bytes, 256-byte
+ *   (device memory of at least the reported workspace size, 16-byte
  *   aligned, contents need not be initialised).
  * - Layout is contiguous row-major.  `target_logits` is [B, gamma+1, V]
  *   (float32 or bfloat16, see sv_dtype); `draft_probs` (q) is [B, gamma, V]
- *   float32; `draft_ids` is [B, gamma] int32.  The logits and q base pointers
+ *   float32; `draft_ids` is [B, gamma] int32 (the ragged calls take packed
+ *   tensors instead, described with them).  The logits and q base pointers
  *   must be 16-byte aligned.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream).  The returned status reports only synchronous host-side
@@ -75,9 +76,10 @@ typedef struct {
                                   out of range or longer than gamma_max: no token
                                   emitted                                          */
 
-/* Bytes of workspace that spec_verify_sample, spec_verify_greedy and
- * spec_accept_stats need for these sizes (the maximum over the three).
- * Returns 0 when the sizes are invalid. */
+/* Bytes of workspace that spec_verify_sample, spec_verify_greedy,
+ * spec_accept_stats, spec_verify_sample_stats, spec_verify_sample_lenient
+ * and (with gamma = gamma_max) the ragged calls need for these sizes (the
+ * maximum over them).  Returns 0 when the sizes are invalid. */
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt,
                                   sv_sampling_params prm);
 
