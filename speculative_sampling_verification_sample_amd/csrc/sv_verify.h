@@ -131,49 +131,136 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
   return token >= 0 ? token : lastpos;
 }
 
-// Full-row draw by one wave (oversized kept sets of truncated rows, which
-// are rare): two passes over the row, weights as in the chunked sampler.
+// Full-row draw by one wave (truncated rows whose kept set is too large for
+// a list, e.g. a wide nucleus): two passes over the row, weights as in the
+// chunked samplers.  Each lane takes 8 consecutive tokens (16-byte loads),
+// so a step covers 512 tokens, and the loads of kFullU steps are in flight
+// together; a step's lane sums go through one wave scan.  The token is the
+// first whose running weight exceeds t = u * W (within the lane holding the
+// crossing, in token order), else that lane's last token of positive weight.
+constexpr int kFullU = 1;
+
+// Logits (and q when residual) of tokens x .. x+7 of a row (-inf / 0 past V).
+template <bool BF16>
+__device__ __forceinline__ void full_row_seg(const void* logits, const QRow& qr, int64_t rowoff, int64_t V, bool vec,
+                                             int64_t x, bool res, float* z, float* qv) {
+  if (x >= V) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      z[k] = kNegInf;
+      qv[k] = 0.0f;
+    }
+    return;
+  }
+  if (vec && x + 8 <= V) {
+    if constexpr (BF16) {
+      widen<true>(reinterpret_cast<const uint4*>(logits)[(rowoff + x) >> 3], z);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(logits) + rowoff + x);
+      widen<false>(p[0], z);
+      widen<false>(p[1], z + 4);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z[k] = (x + k < V) ? load_logit<BF16>(logits, rowoff + x + k) : kNegInf;
+  }
+  if (res) qr.seg8(x, V, qv);
+}
+
+// Weight of one token: e(z) on the kept set {z >= tau}, or the residual
+// (e - qs q S)_+ there.
+__device__ __forceinline__ double full_row_weight(float z, float q, bool res, float c, float R, float tau, double S,
+                                                  double qs) {
+  if (!(z >= tau)) return 0.0;
+  const double e = (double)e_of(z, c, R);
+  if (!res) return e;
+  const double d = e - (qs * (double)q) * S;
+  return d > 0.0 ? d : 0.0;
+}
+
 template <bool BF16>
 __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V, float c, int64_t row, double S,
                                   float R, float tau, float u, bool& residual, uint32_t& fl, double qs) {
   const int lane = lane_id();
-  auto weight = [&](int64_t x, bool res) -> double {
-    if (x >= V) return 0.0;
-    float z = load_logit<BF16>(logits, row * V + x);
-    if (!(z >= tau)) return 0.0;
-    double e = (double)e_of(z, c, R);
-    if (!res) return e;
-    double d = e - (qs * (double)qr.at(x)) * S;
-    return d > 0.0 ? d : 0.0;
-  };
-  auto total = [&](bool res) -> double {
+  constexpr int64_t kStep = 8 * kWave;
+  const int64_t rowoff = row * V;
+  const bool vec = (rowoff % (BF16 ? 8 : 4)) == 0;
+  double W = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool res = residual;
     double carry = 0.0;
-    for (int64_t x0 = 0; x0 < V; x0 += kWave) {
-      double incl = wave_incl_scan_d(weight(x0 + lane, res));
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+    for (int64_t x0 = 0; x0 < V; x0 += kFullU * kStep) {
+      float z[kFullU][8], qv[kFullU][8];
+#pragma unroll
+      for (int s2 = 0; s2 < kFullU; ++s2)
+        full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + s2 * kStep + (int64_t)lane * 8, res, z[s2], qv[s2]);
+#pragma unroll
+      for (int s2 = 0; s2 < kFullU; ++s2) {
+        double seg = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) seg += full_row_weight(z[s2][k], qv[s2][k], res, c, R, tau, S, qs);
+        const double incl = wave_incl_scan_d(seg);
+        carry = carry + __shfl(incl, kWave - 1, kWave);
+      }
     }
-    return carry;
-  };
-  double W = total(residual);
-  if (residual && !(W > 0.0)) {
-    fl |= 4u;  // SV_ROW_Z_DEGENERATE
-    residual = false;
-    W = total(false);
+    W = carry;
+    if (pass == 0 && residual && !(W > 0.0)) {
+      fl |= 4u;  // SV_ROW_Z_DEGENERATE: the weights of p instead
+      residual = false;
+      continue;
+    }
+    break;
   }
   const double t = (double)u * W;
   double carry = 0.0;
-  int64_t lastpos = -1;
-  for (int64_t x0 = 0; x0 < V; x0 += kWave) {
-    const int64_t x = x0 + lane;
-    const double w = weight(x, residual);
-    const double incl = wave_incl_scan_d(w);
-    uint64_t hit = ballot(x < V && carry + incl > t);
-    if (hit) return (int)(x0 + (int)__builtin_ctzll(hit));
-    uint64_t pos = ballot(x < V && w > 0.0);
-    if (pos) lastpos = x0 + 63 - (int)__builtin_clzll(pos);
-    carry = carry + __shfl(incl, kWave - 1, kWave);
+  int64_t token = -1, lastpos = -1;
+  for (int64_t x0 = 0; x0 < V && token < 0; x0 += kFullU * kStep) {
+    float z[kFullU][8], qv[kFullU][8];
+#pragma unroll
+    for (int s2 = 0; s2 < kFullU; ++s2)
+      full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + s2 * kStep + (int64_t)lane * 8, residual, z[s2], qv[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < kFullU; ++s2) {
+      const int64_t xs = x0 + s2 * kStep;
+      if (xs >= V) break;
+      const int64_t x = xs + (int64_t)lane * 8;
+      double seg = 0.0;
+      int lastk = -1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const double wk = full_row_weight(z[s2][k], qv[s2][k], residual, c, R, tau, S, qs);
+        seg += wk;
+        if (wk > 0.0) lastk = k;
+      }
+      const double incl = wave_incl_scan_d(seg);
+      const double C = carry + incl;
+      double ex = __shfl_up(C, 1, kWave);
+      if (lane == 0) ex = carry;
+      const uint64_t hit = ballot(x < V && C > t);
+      if (hit) {
+        const int src = (int)__builtin_ctzll(hit);
+        int64_t found = -1;
+        if (lane == src) {
+          double run = ex;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            run = run + full_row_weight(z[s2][k], qv[s2][k], residual, c, R, tau, S, qs);
+            if (found < 0 && run > t) found = x + k;
+          }
+          if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
+        }
+        token = __shfl(found, src, kWave);
+        break;
+      }
+      const uint64_t pos = ballot(x < V && lastk >= 0);
+      if (pos) {
+        const int src = 63 - (int)__builtin_clzll(pos);
+        lastpos = __shfl(x + lastk, src, kWave);
+      }
+      carry = carry + __shfl(incl, kWave - 1, kWave);
+    }
   }
-  return (int)lastpos;
+  return (int)(token >= 0 ? token : lastpos);
 }
 
 // Block-wide "first token whose running weight exceeds t, else the last
