@@ -397,14 +397,27 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
     for (int shift = 24; shift >= kLow; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
+      // per-thread runs of one bin are added with one atomic: a row's keys
+      // share their upper bits, so the first passes land in few bins
+      uint32_t cb = 0xffffffffu, ca = 0;
       for_row([&](int64_t, const float* zs) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (!(zs[e] > kNegInf)) continue;
           const uint32_t key = f2key(zs[e]);
-          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+          if ((key & pmask) == prefix) {
+            const uint32_t bin = (key >> shift) & 255u;
+            if (bin == cb) {
+              ++ca;
+            } else {
+              if (ca) atomicAdd(&hist[cb], ca);
+              cb = bin;
+              ca = 1;
+            }
+          }
         }
       });
+      if (ca) atomicAdd(&hist[cb], ca);
       __syncthreads();
       if (shift == 24) {
         int64_t tot = 0;
@@ -427,17 +440,21 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
     }
     if (nfinite >= a.top_k) tau = key2f(prefix);
   }
-  // ---- top-p threshold (mass), against the mass of the top-k set ----
+  // ---- top-p threshold (mass), against the mass of the top-k set (without
+  //      top-k: the row's mass from the chunk sums, as on the fast path) ----
   if (a.top_p < 1.0f) {
-    double part = 0.0;
-    for_row([&](int64_t, const float* zs) {
-      float f = 0.0f;  // a segment's 8 terms (each <= 1) in float, then into the double
+    double Sk = ri.S;
+    if (topk) {
+      double part = 0.0;
+      for_row([&](int64_t, const float* zs) {
+        float f = 0.0f;  // a segment's 8 terms (each <= 1) in float, then into the double
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (zs[e] >= tau) f += e_of(zs[e], c, R);
-      part += (double)f;
-    });
-    const double Sk = block_sum_d<BF16>(part, s_tmp);
+        for (int e = 0; e < 8; ++e)
+          if (zs[e] >= tau) f += e_of(zs[e], c, R);
+        part += (double)f;
+      });
+      Sk = block_sum_d<BF16>(part, s_tmp);
+    }
     const double sc = ldexp(1.0, a.scale_bits);
     const double target = (double)a.top_p * Sk * sc;
     uint32_t prefix = 0, pmask = 0;
@@ -446,15 +463,27 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
     for (int shift = 24; shift >= kLow; shift -= 8) {
       mhist[tid] = 0ull;
       __syncthreads();
+      uint32_t cb = 0xffffffffu;
+      unsigned long long ca = 0ull;
       for_row([&](int64_t, const float* zs) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (!(zs[e] >= tau)) continue;
           const uint32_t key = f2key(zs[e]);
-          if ((key & pmask) == prefix)
-            atomicAdd(&mhist[(key >> shift) & 255u], (unsigned long long)rint((double)e_of(zs[e], c, R) * sc));
+          if ((key & pmask) == prefix) {
+            const uint32_t bin = (key >> shift) & 255u;
+            const unsigned long long m = (unsigned long long)rint((double)e_of(zs[e], c, R) * sc);
+            if (bin == cb) {
+              ca += m;
+            } else {
+              if (cb != 0xffffffffu) atomicAdd(&mhist[cb], ca);
+              cb = bin;
+              ca = m;
+            }
+          }
         }
       });
+      if (cb != 0xffffffffu) atomicAdd(&mhist[cb], ca);
       __syncthreads();
       if (wid == 0) {
         // lane l holds bins 255-4l .. 252-4l
