@@ -132,12 +132,15 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
 }
 
 // Full-row draw by one wave (truncated rows whose kept set is too large for
-// a list, e.g. a wide nucleus): two passes over the row, weights as in the
-// chunked samplers.  Each lane takes 8 consecutive tokens (16-byte loads),
-// so a step covers 512 tokens, and the loads of kFullU steps are in flight
-// together; a step's lane sums go through one wave scan.  The token is the
-// first whose running weight exceeds t = u * W (within the lane holding the
-// crossing, in token order), else that lane's last token of positive weight.
+// a list, e.g. a wide nucleus): a pass for a residual's total (the weights
+// of p total the kept mass S) and a pass that finds the token, weights as in
+// the chunked samplers.  Each lane takes 8 consecutive tokens (16-byte loads),
+// so a step covers 512 tokens, and a step's lane sums go through one wave
+// scan.  (kFullU steps per batch: batching more steps, or longer runs per
+// lane, doubled this kernel's registers and slowed the common list draws.)
+// The token is the first whose running weight exceeds t = u * W (within the
+// lane holding the crossing, in token order), else that lane's last token of
+// positive weight.
 constexpr int kFullU = 1;
 
 // Logits (and q when residual) of tokens x .. x+7 of a row (-inf / 0 past V).
@@ -185,8 +188,10 @@ __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V,
   constexpr int64_t kStep = 8 * kWave;
   const int64_t rowoff = row * V;
   const bool vec = (rowoff % (BF16 ? 8 : 4)) == 0;
-  double W = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
+  // the weights of p total the kept set's mass S, known from the row
+  // finisher: only a residual needs a pass for its total
+  double W = S;
+  for (int pass = 0; pass < 2 && residual; ++pass) {
     const bool res = residual;
     double carry = 0.0;
     for (int64_t x0 = 0; x0 < V; x0 += kFullU * kStep) {
@@ -204,10 +209,10 @@ __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V,
       }
     }
     W = carry;
-    if (pass == 0 && residual && !(W > 0.0)) {
+    if (!(W > 0.0)) {
       fl |= 4u;  // SV_ROW_Z_DEGENERATE: the weights of p instead
       residual = false;
-      continue;
+      W = S;
     }
     break;
   }
