@@ -136,12 +136,10 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
 // of p total the kept mass S) and a pass that finds the token, weights as in
 // the chunked samplers.  Each lane takes 8 consecutive tokens (16-byte loads),
 // so a step covers 512 tokens, and a step's lane sums go through one wave
-// scan.  (kFullU steps per batch: batching more steps, or longer runs per
-// lane, doubled this kernel's registers and slowed the common list draws.)
-// The token is the first whose running weight exceeds t = u * W (within the
-// lane holding the crossing, in token order), else that lane's last token of
-// positive weight.
-constexpr int kFullU = 1;
+// scan.  (Batching several steps, or longer runs per lane, doubled this
+// kernel's registers and slowed the common list draws.)  The token is the
+// first whose running weight exceeds t = u * W (within the lane holding the
+// crossing, in token order), else that lane's last token of positive weight.
 
 // Logits (and q when residual) of tokens x .. x+7 of a row (-inf / 0 past V).
 template <bool BF16>
@@ -188,25 +186,17 @@ __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V,
   constexpr int64_t kStep = 8 * kWave;
   const int64_t rowoff = row * V;
   const bool vec = (rowoff % (BF16 ? 8 : 4)) == 0;
-  // the weights of p total the kept set's mass S, known from the row
-  // finisher: only a residual needs a pass for its total
   double W = S;
-  for (int pass = 0; pass < 2 && residual; ++pass) {
-    const bool res = residual;
+  if (residual) {
     double carry = 0.0;
-    for (int64_t x0 = 0; x0 < V; x0 += kFullU * kStep) {
-      float z[kFullU][8], qv[kFullU][8];
+    for (int64_t x0 = 0; x0 < V; x0 += kStep) {
+      float z[8], qv[8];
+      full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + (int64_t)lane * 8, true, z, qv);
+      double seg = 0.0;
 #pragma unroll
-      for (int s2 = 0; s2 < kFullU; ++s2)
-        full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + s2 * kStep + (int64_t)lane * 8, res, z[s2], qv[s2]);
-#pragma unroll
-      for (int s2 = 0; s2 < kFullU; ++s2) {
-        double seg = 0.0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) seg += full_row_weight(z[s2][k], qv[s2][k], res, c, R, tau, S, qs);
-        const double incl = wave_incl_scan_d(seg);
-        carry = carry + __shfl(incl, kWave - 1, kWave);
-      }
+      for (int k = 0; k < 8; ++k) seg += full_row_weight(z[k], qv[k], true, c, R, tau, S, qs);
+      const double incl = wave_incl_scan_d(seg);
+      carry = carry + __shfl(incl, kWave - 1, kWave);
     }
     W = carry;
     if (!(W > 0.0)) {
@@ -214,56 +204,45 @@ __device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V,
       residual = false;
       W = S;
     }
-    break;
   }
   const double t = (double)u * W;
   double carry = 0.0;
   int64_t token = -1, lastpos = -1;
-  for (int64_t x0 = 0; x0 < V && token < 0; x0 += kFullU * kStep) {
-    float z[kFullU][8], qv[kFullU][8];
+  for (int64_t x0 = 0; x0 < V; x0 += kStep) {
+    const int64_t x = x0 + (int64_t)lane * 8;
+    float z[8], qv[8];
+    full_row_seg<BF16>(logits, qr, rowoff, V, vec, x, residual, z, qv);
+    double seg = 0.0;
+    int lastk = -1;
 #pragma unroll
-    for (int s2 = 0; s2 < kFullU; ++s2)
-      full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + s2 * kStep + (int64_t)lane * 8, residual, z[s2], qv[s2]);
-#pragma unroll
-    for (int s2 = 0; s2 < kFullU; ++s2) {
-      const int64_t xs = x0 + s2 * kStep;
-      if (xs >= V) break;
-      const int64_t x = xs + (int64_t)lane * 8;
-      double seg = 0.0;
-      int lastk = -1;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const double wk = full_row_weight(z[s2][k], qv[s2][k], residual, c, R, tau, S, qs);
-        seg += wk;
-        if (wk > 0.0) lastk = k;
-      }
-      const double incl = wave_incl_scan_d(seg);
-      const double C = carry + incl;
-      double ex = __shfl_up(C, 1, kWave);
-      if (lane == 0) ex = carry;
-      const uint64_t hit = ballot(x < V && C > t);
-      if (hit) {
-        const int src = (int)__builtin_ctzll(hit);
-        int64_t found = -1;
-        if (lane == src) {
-          double run = ex;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            run = run + full_row_weight(z[s2][k], qv[s2][k], residual, c, R, tau, S, qs);
-            if (found < 0 && run > t) found = x + k;
-          }
-          if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
-        }
-        token = __shfl(found, src, kWave);
-        break;
-      }
-      const uint64_t pos = ballot(x < V && lastk >= 0);
-      if (pos) {
-        const int src = 63 - (int)__builtin_clzll(pos);
-        lastpos = __shfl(x + lastk, src, kWave);
-      }
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+    for (int k = 0; k < 8; ++k) {
+      const double wk = full_row_weight(z[k], qv[k], residual, c, R, tau, S, qs);
+      seg += wk;
+      if (wk > 0.0) lastk = k;
     }
+    const double incl = wave_incl_scan_d(seg);
+    const double C = carry + incl;
+    double ex = __shfl_up(C, 1, kWave);
+    if (lane == 0) ex = carry;
+    const uint64_t hit = ballot(x < V && C > t);
+    if (hit) {
+      const int src = (int)__builtin_ctzll(hit);
+      int64_t found = -1;
+      if (lane == src) {
+        double run = ex;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          run = run + full_row_weight(z[k], qv[k], residual, c, R, tau, S, qs);
+          if (found < 0 && run > t) found = x + k;
+        }
+        if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
+      }
+      token = __shfl(found, src, kWave);
+      break;
+    }
+    const uint64_t pos = ballot(x < V && lastk >= 0);
+    if (pos) lastpos = __shfl(x + lastk, 63 - (int)__builtin_clzll(pos), kWave);
+    carry = carry + __shfl(incl, kWave - 1, kWave);
   }
   return (int)(token >= 0 ? token : lastpos);
 }
