@@ -362,10 +362,10 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   ac.beta = beta;
   const dim3 agrid((unsigned)((B + 3) / 4));
   if (p.trunc) {
-    // kept lists (stored in token-id order) and the rare oversized kept set
-    // are drawn inside K3
-    if (bf) hipLaunchKernelGGL((accept_kernel<true, false>), agrid, dim3(256), 0, st, ac);
-    else hipLaunchKernelGGL((accept_kernel<false, false>), agrid, dim3(256), 0, st, ac);
+    // kept lists (stored in token-id order) and oversized kept sets are
+    // drawn inside K3, one workgroup per request
+    if (bf) hipLaunchKernelGGL((accept_trunc_kernel<true>), dim3((unsigned)B), dim3(256), 0, st, ac);
+    else hipLaunchKernelGGL((accept_trunc_kernel<false>), dim3((unsigned)B), dim3(256), 0, st, ac);
     return launched();
   }
 
@@ -400,8 +400,8 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
     if (bf) hipLaunchKernelGGL((big_partial_kernel<true, true>), grid, dim3(256), 0, st, bg, ac);
     else hipLaunchKernelGGL((big_partial_kernel<false, true>), grid, dim3(256), 0, st, bg, ac);
   } else {
-    if (bf) hipLaunchKernelGGL((accept_kernel<true, true>), agrid, dim3(256), 0, st, ac);
-    else hipLaunchKernelGGL((accept_kernel<false, true>), agrid, dim3(256), 0, st, ac);
+    if (bf) hipLaunchKernelGGL((accept_kernel<true>), agrid, dim3(256), 0, st, ac);
+    else hipLaunchKernelGGL((accept_kernel<false>), agrid, dim3(256), 0, st, ac);
     s = launched();
     if (s != SV_OK) return s;
     if (bf) hipLaunchKernelGGL((big_partial_kernel<true, false>), grid, dim3(256), 0, st, bg, ac);

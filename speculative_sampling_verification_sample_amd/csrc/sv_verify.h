@@ -8,8 +8,10 @@
 // Then the replacement from the residual (p - q)_+ ([WR] §5) or the bonus
 // token from p_gamma ([WR] §6): when the kept set of that row is a short
 // list the wave draws it at once (inverse CDF, fp64 wave scans); otherwise
-// it leaves a BigJob for K4, which sums the weights of a whole row in chunks
-// (one launch) and locates the token from the chunk totals (a second launch).
+// it leaves a BigJob for a full-row draw: by the request's own workgroup on
+// truncated rows, else by K4, which sums the weights of a whole row in
+// chunks (one launch) and locates the token from the chunk totals (a second
+// launch).
 #pragma once
 
 #include "sv_device.h"
@@ -131,16 +133,6 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
   return token >= 0 ? token : lastpos;
 }
 
-// Full-row draw by one wave (truncated rows whose kept set is too large for
-// a list, e.g. a wide nucleus): a pass for a residual's total (the weights
-// of p total the kept mass S) and a pass that finds the token, weights as in
-// the chunked samplers.  Each lane takes 8 consecutive tokens (16-byte loads),
-// so a step covers 512 tokens, and a step's lane sums go through one wave
-// scan.  (Batching several steps, or longer runs per lane, doubled this
-// kernel's registers and slowed the common list draws.)  The token is the
-// first whose running weight exceeds t = u * W (within the lane holding the
-// crossing, in token order), else that lane's last token of positive weight.
-
 // Logits (and q when residual) of tokens x .. x+7 of a row (-inf / 0 past V).
 template <bool BF16>
 __device__ __forceinline__ void full_row_seg(const void* logits, const QRow& qr, int64_t rowoff, int64_t V, bool vec,
@@ -177,74 +169,6 @@ __device__ __forceinline__ double full_row_weight(float z, float q, bool res, fl
   if (!res) return e;
   const double d = e - (qs * (double)q) * S;
   return d > 0.0 ? d : 0.0;
-}
-
-template <bool BF16>
-__device__ int draw_full_row_wave(const void* logits, const QRow& qr, int64_t V, float c, int64_t row, double S,
-                                  float R, float tau, float u, bool& residual, uint32_t& fl, double qs) {
-  const int lane = lane_id();
-  constexpr int64_t kStep = 8 * kWave;
-  const int64_t rowoff = row * V;
-  const bool vec = (rowoff % (BF16 ? 8 : 4)) == 0;
-  double W = S;
-  if (residual) {
-    double carry = 0.0;
-    for (int64_t x0 = 0; x0 < V; x0 += kStep) {
-      float z[8], qv[8];
-      full_row_seg<BF16>(logits, qr, rowoff, V, vec, x0 + (int64_t)lane * 8, true, z, qv);
-      double seg = 0.0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) seg += full_row_weight(z[k], qv[k], true, c, R, tau, S, qs);
-      const double incl = wave_incl_scan_d(seg);
-      carry = carry + __shfl(incl, kWave - 1, kWave);
-    }
-    W = carry;
-    if (!(W > 0.0)) {
-      fl |= 4u;  // SV_ROW_Z_DEGENERATE: the weights of p instead
-      residual = false;
-      W = S;
-    }
-  }
-  const double t = (double)u * W;
-  double carry = 0.0;
-  int64_t token = -1, lastpos = -1;
-  for (int64_t x0 = 0; x0 < V; x0 += kStep) {
-    const int64_t x = x0 + (int64_t)lane * 8;
-    float z[8], qv[8];
-    full_row_seg<BF16>(logits, qr, rowoff, V, vec, x, residual, z, qv);
-    double seg = 0.0;
-    int lastk = -1;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const double wk = full_row_weight(z[k], qv[k], residual, c, R, tau, S, qs);
-      seg += wk;
-      if (wk > 0.0) lastk = k;
-    }
-    const double incl = wave_incl_scan_d(seg);
-    const double C = carry + incl;
-    double ex = __shfl_up(C, 1, kWave);
-    if (lane == 0) ex = carry;
-    const uint64_t hit = ballot(x < V && C > t);
-    if (hit) {
-      const int src = (int)__builtin_ctzll(hit);
-      int64_t found = -1;
-      if (lane == src) {
-        double run = ex;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          run = run + full_row_weight(z[k], qv[k], residual, c, R, tau, S, qs);
-          if (found < 0 && run > t) found = x + k;
-        }
-        if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
-      }
-      token = __shfl(found, src, kWave);
-      break;
-    }
-    const uint64_t pos = ballot(x < V && lastk >= 0);
-    if (pos) lastpos = __shfl(x + lastk, 63 - (int)__builtin_clzll(pos), kWave);
-    carry = carry + __shfl(incl, kWave - 1, kWave);
-  }
-  return (int)(token >= 0 ? token : lastpos);
 }
 
 // Block-wide "first token whose running weight exceeds t, else the last
@@ -308,7 +232,7 @@ struct Decision {
 };
 
 // Emit the outputs of one request once its decision is known (whole wave).
-template <bool BF16, bool BIG_INWAVE>
+template <bool BF16>
 __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, int32_t* out) {
   const int lane = lane_id();
   const int nacc = dc.nacc, G = dc.G, P1 = a.gamma + 1;
@@ -331,16 +255,6 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
   const int64_t qrow = residual ? lo + nacc : -1;
   const QRow qr = residual ? q_row(a.q, qrow) : q_none();
   const RowInfo& rs = dc.rs;
-  if ((rs.flags & RF_BIG) && BIG_INWAVE) {
-    int token = draw_full_row_wave<BF16>(a.logits, qr, a.V, a.c, trow, rs.S, rs.R, rs.tau, u, residual, fl, a.beta);
-    if (lane == 0) {
-      if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
-      out[nacc] = token;
-      a.out_nacc[b] = nacc;
-      if (a.out_flags) a.out_flags[b] = fl;
-    }
-    return;
-  }
   if (rs.flags & RF_BIG) {
     if (lane == 0) {
       BigJob jb;
@@ -451,14 +365,13 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   return dc;
 }
 
+// One request's acceptance and draw, by one wave (a row whose kept set is
+// not a list leaves a BigJob for a full-row draw).
 template <bool BF16, bool FROM_CHUNKS>
-__global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int b = blockIdx.x * 4 + wid;
-  if (b >= a.B) return;
+__device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
+  const int lane = lane_id();
   const int P1 = a.gamma + 1;
   int32_t* out = a.out_tokens + (int64_t)b * P1;
-  constexpr bool kInwave = !FROM_CHUNKS;  // truncated rows draw oversized kept sets in the wave
 
   if (P1 <= kWave) {
     Decision dc = decide_short<BF16, FROM_CHUNKS>(a, b);
@@ -466,7 +379,7 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
       empty_request(a, b, out, dc.badfl);
       return;
     }
-    finish_request<BF16, kInwave>(a, b, dc, out);
+    finish_request<BF16>(a, b, dc, out);
     return;
   }
 
@@ -552,7 +465,137 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   dc.badfl = 0;
   dc.lo = sp.lo;
   dc.G = G;
-  finish_request<BF16, kInwave>(a, b, dc, out);
+  finish_request<BF16>(a, b, dc, out);
+}
+
+// Untruncated rows with gamma + 1 > 64: four requests per workgroup, one per
+// wave (the full-row draws are BigJobs for the chunked sampler).
+template <bool BF16>
+__global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
+  const int b = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (b >= a.B) return;
+  accept_request<BF16, true>(a, b);
+}
+
+// Truncated rows: one request per workgroup.  Wave 0 takes the decision and
+// draws from a kept list; a row whose kept set is too large for a list (a
+// wide nucleus) is drawn by the whole workgroup, one quarter of the row per
+// wave: each wave totals its quarter, and the wave whose quarter holds the
+// crossing of t = u * W finds the token (sums in a fixed order).
+template <bool BF16>
+__global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  __shared__ double s_tot[4];
+  __shared__ long long s_tok;
+  if (wid == 0) accept_request<BF16, false>(a, b);
+  __syncthreads();
+  const BigJob jb = a.jobs[b];
+  if (!jb.active) return;
+  const int64_t V = a.V;
+  const int64_t rowoff = (int64_t)jb.row * V;
+  const bool vec = (rowoff % (BF16 ? 8 : 4)) == 0;
+  bool residual = jb.qrow >= 0;
+  const QRow qr = residual ? q_row(a.q, jb.qrow) : q_none();
+  constexpr int64_t kStep = 8 * kWave;
+  const int64_t Lq = (V + 4 * kStep - 1) / (4 * kStep) * kStep;  // a quarter, whole steps
+  const int64_t q0 = min((int64_t)wid * Lq, V), q1 = min(q0 + Lq, V);
+  const double S = jb.S;
+  // this wave's quarter: its total (t < 0), or the search from `carry`
+  struct QOut {
+    double carry;
+    int64_t token, lastpos;
+  };
+  auto quarter = [&](bool res, double t, double carry) -> QOut {
+    int64_t token = -1, lastpos = -1;
+    for (int64_t x0 = q0; x0 < q1; x0 += kStep) {
+      const int64_t x = x0 + (int64_t)lane * 8;
+      const bool in = x < q1;
+      float z[8], qv[8];
+      full_row_seg<BF16>(a.logits, qr, rowoff, in ? V : 0, vec, x, res, z, qv);
+      double seg = 0.0;
+      int lastk = -1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const double wk = full_row_weight(z[k], qv[k], res, a.c, jb.R, jb.tau, S, a.beta);
+        seg += wk;
+        if (wk > 0.0) lastk = k;
+      }
+      const double incl = wave_incl_scan_d(seg);
+      if (t >= 0.0) {
+        const double C = carry + incl;
+        double ex = __shfl_up(C, 1, kWave);
+        if (lane == 0) ex = carry;
+        const uint64_t hit = ballot(in && C > t);
+        if (hit) {
+          const int src = (int)__builtin_ctzll(hit);
+          int64_t found = -1;
+          if (lane == src) {
+            double run = ex;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              run = run + full_row_weight(z[k], qv[k], res, a.c, jb.R, jb.tau, S, a.beta);
+              if (found < 0 && run > t) found = x + k;
+            }
+            if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
+          }
+          token = __shfl(found, src, kWave);
+          return QOut{carry, token, lastpos};
+        }
+        const uint64_t pos = ballot(in && lastk >= 0);
+        if (pos) lastpos = __shfl(x + lastk, 63 - (int)__builtin_clzll(pos), kWave);
+      }
+      carry = carry + __shfl(incl, kWave - 1, kWave);
+    }
+    return QOut{carry, token, lastpos};
+  };
+  uint32_t extra = 0;
+  double tq = quarter(residual, -1.0, 0.0).carry;
+  if (lane == 0) s_tot[wid] = tq;
+  __syncthreads();
+  double W = ((s_tot[0] + s_tot[1]) + s_tot[2]) + s_tot[3];
+  if (residual && !(W > 0.0)) {
+    extra |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
+    residual = false;
+    __syncthreads();
+    tq = quarter(false, -1.0, 0.0).carry;
+    if (lane == 0) s_tot[wid] = tq;
+    __syncthreads();
+    W = ((s_tot[0] + s_tot[1]) + s_tot[2]) + s_tot[3];
+  }
+  const double t = (double)jb.u * W;
+  // the quarter holding the crossing (running totals in the order of W),
+  // else the last quarter of positive weight (whose last positive token is
+  // the draw)
+  int kq = -1, lastq = -1;
+  double before = 0.0, cum = 0.0, before_last = 0.0;
+  for (int k = 0; k < 4; ++k) {
+    if (s_tot[k] > 0.0) {
+      lastq = k;
+      before_last = cum;
+    }
+    if (kq < 0 && cum + s_tot[k] > t) {
+      kq = k;
+      before = cum;
+    }
+    cum = cum + s_tot[k];
+  }
+  if (threadIdx.x == 0) s_tok = -1;
+  __syncthreads();
+  if (kq >= 0 && wid == kq) {
+    const QOut r = quarter(residual, t, before);
+    if (lane == 0) s_tok = r.token >= 0 ? r.token : r.lastpos;
+  } else if (kq < 0 && lastq >= 0 && wid == lastq) {
+    const QOut r = quarter(residual, 1.0 / 0.0, before_last);  // no crossing: the last positive token
+    if (lane == 0) s_tok = r.lastpos;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int token = (int)s_tok;
+    a.out_tokens[(int64_t)b * (a.gamma + 1) + jb.slot] = token;
+    if (a.eos >= 0 && token == a.eos) extra |= 16u;  // SV_ROW_EOS
+    if (extra && a.out_flags) a.out_flags[b] |= extra;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -688,7 +731,7 @@ __global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs 
         if (ci == 0) empty_request(ac, b, out, dc.badfl);
         if (lane == 0) s_job.active = 0;
       } else if (dc.eos_cut) {
-        if (ci == 0) finish_request<BF16, false>(ac, b, dc, out);  // no draw
+        if (ci == 0) finish_request<BF16>(ac, b, dc, out);  // no draw
         if (lane == 0) s_job.active = 0;
       } else {
         const bool residual = dc.nacc < dc.G;
@@ -937,7 +980,7 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
       empty_request(ac, b, out, dc.badfl);
       if (lane == 0) s_job.active = 0;
     } else if (dc.eos_cut) {
-      finish_request<BF16, false>(ac, b, dc, out);  // no draw
+      finish_request<BF16>(ac, b, dc, out);  // no draw
       if (lane == 0) s_job.active = 0;
     } else {
       const bool residual = dc.nacc < dc.G;
