@@ -328,7 +328,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
   // so batches of kEU segments per thread are loaded (as raw 16-byte words)
   // before any is used.
   constexpr int kW = BF16 ? 1 : 2;      // 16-byte words per segment
-  constexpr int kEU = 1;                // segments in flight per thread
+  constexpr int kEU = 2;                // segments in flight per thread
   auto load_whole = [&](int64_t x, uint4* w) {  // a whole aligned segment inside the row
     const uint4* p = BF16 ? reinterpret_cast<const uint4*>(lg) + ((rowoff + x) >> 3)
                           : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(lg) + rowoff + x);
