@@ -67,4 +67,5 @@ from .verify import (  # noqa: F401
     ragged_span,
     verify_sample_ragged,
     verify_greedy_ragged,
+    verify_sample_ragged_draft_logits,
 )

@@ -525,3 +525,25 @@ def verify_greedy_ragged(logits, ids, cu, gamma_max, eos=-1, requests=None):
         lo, hi = sp
         res.append(_pad_result(greedy_request(logits[lo + b: hi + b + 1], ids[lo:hi], eos), gamma_max))
     return _batch_result(res, gamma_max)
+
+
+def verify_sample_ragged_draft_logits(logits, draft_logits, ids, cu, u_accept, u_resample, gamma_max, T, top_k=0,
+                                      top_p=1.0, eos=-1, requests=None):
+    """``verify_sample_ragged`` with q formed from the draft's logits (packed
+    [N, V], one row per draft position) by ``draft_q_rows``."""
+    B = len(cu) - 1
+    N = ids.shape[0]
+    req = range(B) if requests is None else requests
+    res = []
+    for b in req:
+        sp = ragged_span(cu, b, N, gamma_max)
+        if sp is None:
+            res.append(_no_output(gamma_max, FLAG_BAD_SPAN))
+            continue
+        lo, hi = sp
+        q_rows, q_boundary = draft_q_rows(draft_logits[lo:hi], T, top_k, top_p)
+        r = verify_request(logits[lo + b: hi + b + 1], q_rows, ids[lo:hi], u_accept[lo:hi],
+                           u_resample[lo + b: hi + b + 1], T, top_k, top_p, eos)
+        r.top_p_boundary = r.top_p_boundary or q_boundary
+        res.append(_pad_result(r, gamma_max))
+    return _batch_result(res, gamma_max)

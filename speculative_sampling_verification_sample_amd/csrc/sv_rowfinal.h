@@ -117,6 +117,14 @@ template <bool BF16>
 __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const QSrc& q,
                                     const int32_t* ids, int64_t V, int64_t dpos, int64_t rowoff,
                                     const float2* gath = nullptr, int64_t grow = 0) {
+  // the draft's id and gathered (z(d), q(d)) do not depend on the merge:
+  // their loads go out first, with the chunk results'
+  int dg = -1;
+  float2 g = make_float2(0.0f, 0.0f);
+  if (gath != nullptr && dpos >= 0) {
+    dg = ids[dpos];
+    g = gath[grow];
+  }
   RowMerge m = merge_chunks(co, nchunks, c);
   RowInfo ri;
   ri.S = m.S;
@@ -134,11 +142,10 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
   }
   if (gath != nullptr) {
     if (dpos >= 0) {
-      const int d = ids[dpos];
+      const int d = dg;
       if (d < 0 || (int64_t)d >= V) {
         ri.d = -2;
       } else {
-        const float2 g = gath[grow];
         ri.d = d;
         ri.ed = (g.x >= ri.tau) ? e_of(g.x, c, ri.R) : 0.0f;
         ri.qd = g.y;

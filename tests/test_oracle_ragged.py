@@ -212,3 +212,23 @@ def test_ragged_bad_spans():
     out = oracle.verify_sample_ragged(pk["z"], pk["q"], pk["ids"], pk["cu"], pk["ua"], pk["ur"], 2, 1.0)
     assert out["flags"][1] == oracle.FLAG_BAD_SPAN and out["tokens"].shape == (B, 3)
     assert out["flags"][0] != oracle.FLAG_BAD_SPAN
+
+
+def test_ragged_draft_logits_is_per_request():
+    """Ragged batch with q from the draft's logits: request by request, the
+    single-request draft-logits verify on that request's own rows."""
+    rng = np.random.default_rng(8)
+    B, G, V = 6, 3, 10
+    gam = np.array([3, 0, 2, 1, 3, 2])
+    (z, q, ids, ua, ur), pk = _packed(rng, B, G, V, gam)
+    dz = rng.normal(0, 1.5, (B, G, V))
+    dz_pk = np.concatenate([dz[b, : gam[b]] for b in range(B)]).reshape(-1, V)
+    for top_k, top_p in ((0, 1.0), (4, 1.0), (0, 0.7)):
+        out = oracle.verify_sample_ragged_draft_logits(pk["z"], dz_pk, pk["ids"], pk["cu"], pk["ua"], pk["ur"], G,
+                                                       0.9, top_k, top_p)
+        for b in range(B):
+            g = gam[b]
+            r = oracle.verify_request_draft_logits(z[b, : g + 1], dz[b, :g], ids[b, :g], ua[b, :g],
+                                                   ur[b, : g + 1], 0.9, top_k, top_p)
+            assert out["tokens"][b].tolist() == r.tokens.tolist() + [-1] * (G - g)
+            assert out["n_accepted"][b] == r.n_accepted and out["flags"][b] == r.flags
