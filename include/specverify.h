@@ -236,6 +236,18 @@ sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, cons
                                     int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* spec_verify_sample_ragged with q formed from the draft's logits (as in
+ * spec_verify_sample_draft_logits): draft_logits [n_draft, V] (draft_dt),
+ * packed like draft_ids, one row per draft position.  Workspace:
+ * spec_verify_draft_logits_workspace_size(B, gamma_max, V, dt, draft_dt, prm). */
+sv_status spec_verify_sample_ragged_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                                sv_dtype draft_dt, const int32_t* draft_ids, const int32_t* cu_draft,
+                                                int32_t n_draft, const float* u_accept, const float* u_resample,
+                                                int32_t B, int32_t gamma_max, int32_t V, sv_sampling_params prm,
+                                                int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,
+                                                uint32_t* out_row_flags, void* workspace, size_t workspace_bytes,
+                                                void* stream);
+
 sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,
                                     const int32_t* cu_draft, int32_t n_draft, int32_t B, int32_t gamma_max,
                                     int32_t V, int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,

@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     verify_sample_draft_logits,
     verify_sample_lenient,
     verify_sample_ragged,
+    verify_sample_ragged_draft_logits,
     verify_sample_stats,
     verify_sample_stats_draft_logits,
     workspace_size,

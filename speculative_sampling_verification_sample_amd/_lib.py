@@ -71,6 +71,11 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _c_int32, _ptr, _ptr, _c_int32, _c_int32, _c_int32,
          SamplingParamsC, _c_int32, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_sample_ragged_draft_logits": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, ctypes.c_int, _ptr, _ptr, _c_int32, _ptr, _ptr, _c_int32, _c_int32, _c_int32,
+         SamplingParamsC, _c_int32, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    ),
     "spec_verify_greedy_ragged": (
         ctypes.c_int,
         [_ptr, ctypes.c_int, _ptr, _ptr, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _ptr, _ptr, _ptr,

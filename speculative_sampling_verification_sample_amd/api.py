@@ -406,3 +406,31 @@ def verify_sample_stats_draft_logits(logits, draft_logits, ids, u_accept, u_resa
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_verify_sample_stats_draft_logits")
     return tokens, nacc, flags, alpha, zpq, zqp, acc
+
+
+def verify_sample_ragged_draft_logits(logits, draft_logits, ids, cu_draft, u_accept, u_resample, gamma_max: int,
+                                      temperature=1.0, top_k=0, top_p=1.0, eos_id: int = -1,
+                                      workspace: Optional[torch.Tensor] = None, out=None):
+    """verify_sample_ragged with q formed from the draft's logits, packed
+    [n_draft, V] like ids."""
+    B, N, V = _ragged_shapes(logits, ids, cu_draft)
+    dev = logits.device
+    ddt = logits.dtype
+    if N > 0:
+        _check(draft_logits, "draft_logits", None, (N, V))
+        if draft_logits.dtype not in _DT:
+            raise ValueError("draft_logits must be float32 or bfloat16")
+        ddt = draft_logits.dtype
+        _check(u_accept, "u_accept", torch.float32, (N,))
+    _check(u_resample, "u_resample", torch.float32, (N + B,))
+    tokens, nacc, flags = _ragged_out(out, B, gamma_max, dev)
+    need = draft_logits_workspace_size(B, gamma_max, V, logits.dtype, ddt, temperature, top_k, top_p)
+    ws = _workspace(workspace, need, dev)
+    code = load_library().spec_verify_sample_ragged_draft_logits(
+        logits.data_ptr(), _DT[logits.dtype], draft_logits.data_ptr() if N > 0 else None, _DT[ddt],
+        ids.data_ptr() if N > 0 else None, cu_draft.data_ptr(), N, u_accept.data_ptr() if N > 0 else None,
+        u_resample.data_ptr(), B, gamma_max, V, _params(temperature, top_k, top_p), int(eos_id),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _raise(code, "spec_verify_sample_ragged_draft_logits")
+    return tokens, nacc, flags

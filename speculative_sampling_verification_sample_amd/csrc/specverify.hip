@@ -485,16 +485,22 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
 // Row passes over the draft's logits [B, gamma, V] (plan CALL_DRAFT, in its
 // own workspace region): their statistics and kept lists define q, which
 // the target's passes then read through the returned source.
+// A ragged batch (cu != null) packs its n_draft draft rows: plan row r is
+// packed row r, the draft position the target's kernels read q at.
 sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* draft_ids, int32_t B, int32_t gamma,
                          int32_t V, sv_sampling_params prm, float c, void* ws, hipStream_t st, QSrc* q_out,
-                         const Cand** qkept_out) {
+                         const Cand** qkept_out, const int32_t* cu = nullptr, int32_t n_draft = 0) {
   const Plan pq = make_plan(CALL_DRAFT, B, gamma, V, ddt, prm);
   const bool bf = ddt == SV_BF16;
-  sv_status s = bf ? run_rowpass<true>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false)
-                   : run_rowpass<false>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false);
+  sv_status s =
+      bf ? run_rowpass<true>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false, cu,
+                             n_draft)
+         : run_rowpass<false>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false, cu,
+                              n_draft);
   if (s != SV_OK) return s;
-  s = bf ? run_rowfinal<true>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st)
-         : run_rowfinal<false>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st);
+  s = bf ? run_rowfinal<true>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st, cu, n_draft)
+         : run_rowfinal<false>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st, cu,
+                               n_draft);
   if (s != SV_OK) return s;
   QSrc q;
   q.dense = nullptr;
@@ -818,6 +824,43 @@ sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, cons
   return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
                             gamma_max, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st, cu_draft,
                             n_draft, eos_id < 0 ? -1 : eos_id);
+}
+
+sv_status spec_verify_sample_ragged_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
+                                                sv_dtype draft_dt, const int32_t* draft_ids, const int32_t* cu_draft,
+                                                int32_t n_draft, const float* u_accept, const float* u_resample,
+                                                int32_t B, int32_t gamma_max, int32_t V, sv_sampling_params prm,
+                                                int32_t eos_id, int32_t* out_tokens, int32_t* out_num_accepted,
+                                                uint32_t* out_row_flags, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma_max, V);
+  if (s != SV_OK) return s;
+  if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
+  s = ragged_checks(cu_draft, n_draft, B, gamma_max, V, eos_id);
+  if (s != SV_OK) return s;
+  float c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (n_draft > 0 &&
+      (draft_logits == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_logits)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma_max, V, dt, prm);
+  const size_t qoff = draft_ws_offset(CALL_SAMPLE, B, gamma_max, V, dt, prm);
+  const size_t need = qoff + make_plan(CALL_DRAFT, B, gamma_max, V, draft_dt, prm).total;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SV_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  QSrc q = q_src_none(V);
+  const Cand* qkept = nullptr;
+  if (n_draft > 0) {
+    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma_max, V, prm, c,
+                       static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, cu_draft, n_draft);
+    if (s != SV_OK) return s;
+  }
+  return verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma_max, V, prm, c,
+                            out_tokens, out_num_accepted, out_row_flags, workspace, st, cu_draft, n_draft,
+                            eos_id < 0 ? -1 : eos_id);
 }
 
 sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,

@@ -26,7 +26,7 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def oracle_ragged(r, eos=-1, requests=None, greedy=False, cu_override=None):
+def oracle_ragged(r, eos=-1, requests=None, greedy=False, cu_override=None, draft_logits=False):
     c = r.cfg
     B = r.cu.shape[0] - 1
     req = np.arange(B) if requests is None else np.asarray(requests)
@@ -39,6 +39,11 @@ def oracle_ragged(r, eos=-1, requests=None, greedy=False, cu_override=None):
         ids = _np(r.ids).astype(np.int64)
         if greedy:
             return oracle.verify_greedy_ragged(lg, ids, cu, r.gamma_max, eos, requests=req)
+        if draft_logits:
+            dz = widen(r.draft_logits).reshape(-1, V)
+            return oracle.verify_sample_ragged_draft_logits(lg, dz, ids, cu, _np(r.u_accept), _np(r.u_resample),
+                                                            r.gamma_max, c.temperature, c.top_k, c.top_p, eos,
+                                                            requests=req)
         q = _np(r.q).reshape(-1, V)
         return oracle.verify_sample_ragged(lg, q, ids, cu, _np(r.u_accept), _np(r.u_resample), r.gamma_max,
                                            c.temperature, c.top_k, c.top_p, eos, requests=req)
@@ -63,6 +68,12 @@ def oracle_ragged(r, eos=-1, requests=None, greedy=False, cu_override=None):
         cu1 = np.array([0, hi - lo])
         if greedy:
             o1 = oracle.verify_greedy_ragged(lg, ids, cu1, r.gamma_max, eos)
+        elif draft_logits:
+            dz = widen(r.draft_logits.index_select(0, di)).reshape(-1, V)
+            ua = _np(r.u_accept.index_select(0, di))
+            ur = _np(r.u_resample.index_select(0, ri))
+            o1 = oracle.verify_sample_ragged_draft_logits(lg, dz, ids, cu1, ua, ur, r.gamma_max, c.temperature,
+                                                           c.top_k, c.top_p, eos)
         else:
             q = _np(r.q.index_select(0, di)).reshape(-1, V)
             ua = _np(r.u_accept.index_select(0, di))
@@ -74,10 +85,14 @@ def oracle_ragged(r, eos=-1, requests=None, greedy=False, cu_override=None):
     return {k: np.concatenate([o[k] for o in out]) for k in keys}
 
 
-def gpu_ragged(r, eos=-1, greedy=False, cu=None):
+def gpu_ragged(r, eos=-1, greedy=False, cu=None, draft_logits=False):
     c = r.cfg
     cu = r.cu if cu is None else cu
-    if greedy:
+    if draft_logits:
+        tok, nacc, fl = sv.verify_sample_ragged_draft_logits(r.logits, r.draft_logits, r.ids, cu, r.u_accept,
+                                                             r.u_resample, r.gamma_max, c.temperature, c.top_k,
+                                                             c.top_p, eos_id=eos)
+    elif greedy:
         tok, nacc, fl = sv.verify_greedy_ragged(r.logits, r.ids, cu, r.gamma_max, eos_id=eos)
     else:
         tok, nacc, fl = sv.verify_sample_ragged(r.logits, r.q, r.ids, cu, r.u_accept, r.u_resample, r.gamma_max,
@@ -86,11 +101,11 @@ def gpu_ragged(r, eos=-1, greedy=False, cu=None):
     return _np(tok), _np(nacc), _np(fl).astype(np.uint32)
 
 
-def compare_ragged(r, eos=-1, requests=None, label="", greedy=False, cu=None):
-    tok, nacc, fl = gpu_ragged(r, eos, greedy, cu)
+def compare_ragged(r, eos=-1, requests=None, label="", greedy=False, cu=None, draft_logits=False):
+    tok, nacc, fl = gpu_ragged(r, eos, greedy, cu, draft_logits)
     B = r.cu.shape[0] - 1
     req = np.arange(B) if requests is None else np.asarray(requests)
-    o = oracle_ragged(r, eos, req, greedy, cu)
+    o = oracle_ragged(r, eos, req, greedy, cu, draft_logits)
     g_tok, g_nacc, g_fl = tok[req], nacc[req], fl[req]
     mism = (g_tok != o["tokens"]).any(axis=1) | (g_nacc != o["n_accepted"]) | (g_fl != o["flags"])
     boundary = o["accept_boundary"] | o["cdf_boundary"] | o["top_p_boundary"]
@@ -255,3 +270,40 @@ def test_greedy_full_size():
     del w
     req = np.sort(np.random.default_rng(1).choice(r.cu.shape[0] - 1, 16, replace=False))
     compare_ragged(r, requests=req, label="ragged c4 full", greedy=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("c2", dict(B=7)),
+    ("c3", dict(B=6)),
+    ("c5", dict(B=5)),
+    ("c3", dict(B=5, gamma=3, V=30011)),
+    ("c5", dict(B=4, gamma=2, V=50001)),
+])
+def test_draft_logits(name, kw):
+    """q formed from the packed draft logits; spans from gamma down to 0 drafts."""
+    w = generate(name, DEV, **kw)
+    G = w.ids.shape[1]
+    r = pack_ragged(w, [G - (b % (G + 1)) for b in range(w.cfg.B)])
+    compare_ragged(r, label=f"ragged dl {name} {kw} gammas={r.gammas.tolist()}", draft_logits=True)
+    E = int(_np(r.ids)[0]) if r.ids.shape[0] else 0
+    compare_ragged(r, eos=E, label=f"ragged dl eos {name}", draft_logits=True)
+
+
+def test_draft_logits_all_zero_and_bad_span():
+    _, r = _ragged("c3", gammas=[0] * 4, B=4, V=9000)
+    compare_ragged(r, label="ragged dl all-zero", draft_logits=True)
+    _, r = _ragged("c5", gammas=[2, 3, 1, 2], B=4, V=20000)
+    cu = _np(r.cu).astype(np.int32)
+    bad = cu.copy()
+    bad[2] = cu[3] + 1  # request 1 ends past request 2's start; request 2 runs backwards
+    o, (tok, nacc, fl) = compare_ragged(r, cu=torch.as_tensor(bad, device=DEV), label="ragged dl bad span",
+                                        draft_logits=True)
+    assert fl[2] == oracle.FLAG_BAD_SPAN
+
+
+def test_draft_logits_full_size():
+    w = generate("c5", DEV)
+    r = pack_ragged(w, ragged_gammas(w.cfg.B, w.ids.shape[1], 13))
+    del w
+    req = np.sort(np.random.default_rng(2).choice(r.cu.shape[0] - 1, 8, replace=False))
+    compare_ragged(r, requests=req, label="ragged dl c5 full", draft_logits=True)

@@ -195,6 +195,7 @@ class RaggedWorkload:
     ids: torch.Tensor               # [N] int32
     u_accept: torch.Tensor          # [N] float32
     u_resample: torch.Tensor        # [N + B] float32
+    draft_logits: Optional[torch.Tensor] = None  # [N, V] (when the workload has them)
 
 
 def ragged_gammas(B: int, gamma_max: int, seed: int) -> np.ndarray:
@@ -223,4 +224,5 @@ def pack_ragged(w: Workload, gammas) -> RaggedWorkload:
         w.ids.reshape(-1).index_select(0, di).contiguous(),
         w.u_accept.reshape(-1).index_select(0, di).contiguous(),
         w.u_resample.reshape(-1).index_select(0, ri).contiguous(),
+        None if w.draft_logits is None else w.draft_logits.reshape(B * G, V).index_select(0, di).contiguous(),
     )
