@@ -135,8 +135,6 @@ def main():
     torch.cuda.synchronize()
     G, B, V = cfg.gamma, cfg.B, cfg.V
     rg = args.ragged
-    if rg and args.draft_logits:
-        raise SystemExit("--ragged and --draft-logits are separate calls")
     lenient = args.lenience is not None
     if lenient and (rg or args.draft_logits or cfg.mode == "greedy"):
         raise SystemExit("--lenience applies to the uniform sampling call with a dense q")
@@ -187,7 +185,10 @@ def main():
         w = copies[i % R]
         if timer is not None:
             lib.spec_set_rowpass_timer(timer[0], timer[1])
-        if rg and greedy:
+        if rg and dl:
+            sv.verify_sample_ragged_draft_logits(w.logits, w.draft_logits, w.ids, w.cu, w.u_accept, w.u_resample, G,
+                                                 cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs)
+        elif rg and greedy:
             sv.verify_greedy_ragged(w.logits, w.ids, w.cu, G, workspace=ws, out=outs)
         elif rg:
             sv.verify_sample_ragged(w.logits, w.q, w.ids, w.cu, w.u_accept, w.u_resample, G, cfg.temperature,
@@ -299,7 +300,7 @@ def main():
         q_rows = rejected * V * qb if untrunc else 0
         step_bytes = rows * row_bytes + q_rows + n_draft * 12 + rows * 4 + B * (G + 1) * 4 + B * 4
         if dl:
-            step_bytes += B * G * V * qb
+            step_bytes += n_draft * V * qb
         if stats and not fused:
             # the separate statistics call: the target's gamma rows and q
             step_bytes += B * G * V * (cfg.logit_bytes + qb)
@@ -339,6 +340,9 @@ def main():
                 g = int(gammas[b])
                 if greedy:
                     oracle.greedy_request(lg[b, : g + 1], ids[b, :g])
+                elif dl:
+                    oracle.verify_request_draft_logits(lg[b, : g + 1], dz[b, :g], ids[b, :g], ua[b, :g],
+                                                       ur[b, : g + 1], cfg.temperature, cfg.top_k, cfg.top_p)
                 else:
                     oracle.verify_request(lg[b, : g + 1], q[b, :g], ids[b, :g], ua[b, :g], ur[b, : g + 1],
                                           cfg.temperature, cfg.top_k, cfg.top_p)
