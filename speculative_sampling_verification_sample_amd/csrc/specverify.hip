@@ -27,7 +27,7 @@ namespace {
 
 using namespace sv;
 
-constexpr int kTargetWG = 2048;   // workgroups a streaming launch aims for (8 per CU)
+constexpr int64_t kChunkBytes = 28672;  // bytes of one row a streaming row-pass workgroup reads
 constexpr int kKMax = 2048;       // longest kept set stored as a list
 constexpr int kFastTopK = 256;    // top-k above this always takes the exact path
 constexpr int kNwTopP = 128;      // chunk elements a top-p candidate threshold certifies
@@ -98,14 +98,12 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
       if (p.nu == 4 || p.rows * nch >= kTruncMinWG) break;
     }
   } else {
-    // Short workgroups in several waves of residency keep the launch tail
-    // short; short launches (few rows) take chunks of at least 6400 elements,
-    // which measured a few per cent faster than 4096 on 64 x 5 rows of 32000.
-    const int64_t minchunk = 6400;
-    const int64_t target = kTargetWG * 4;
-    const int64_t want = p.rows > 0 ? (target + p.rows - 1) / p.rows : 1;
-    const int64_t lim = std::max<int64_t>(1, (V + minchunk - 1) / minchunk);
-    nch = std::max<int64_t>(1, std::min(want, lim));
+    // Chunks of about kChunkBytes: shorter ones pay a workgroup's fixed cost
+    // (launch, the first loads' latency, the reductions) on too few bytes,
+    // longer ones leave a long launch tail.  Measured on 64 x 5 rows of 32000
+    // fp32 and 512 x 9 rows of 152064 bf16.
+    const int64_t esz = (dt == SV_BF16) ? 2 : 4;
+    nch = std::max<int64_t>(1, (V * esz + kChunkBytes - 1) / kChunkBytes);
   }
   chunk = (V + nch - 1) / nch;
   chunk = (chunk + 7) / 8 * 8;

@@ -1145,28 +1145,44 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
   const int G = sp.g;
   const int64_t lo = sp.lo;
   if (P1 <= kWave) {
-    // lane j <= gamma_b: row j's argmax from its chunk results (the loads of
-    // all rows in flight together), then the first mismatch by ballot; the
-    // (max, lowest id) merge does not depend on the order of the chunks
+    // Row j's argmax from its chunk results: L lanes per row (L a power of
+    // two, L * (gamma + 1) <= 64) take every L-th chunk, all loads in flight
+    // together, and meet by xor shuffles inside their group; the (max, lowest
+    // id) merge does not depend on the order of the chunks.  Lane j then
+    // holds row j, and the first mismatch comes by ballot.
+    int L = 1;
+    while (L * 2 * P1 <= kWave) L *= 2;
+    const int jr = lane / L, t = lane & (L - 1);
     float v = kNegInf;
     int i = 0x7fffffff, d = -1;
     uint32_t fl = 0;
-    if (lane <= G) {
-      const ChunkOut* co = a.cout + (lo + b + lane) * a.nchunks;
-      if (lane < G) d = a.ids[lo + lane];
-      for (int c0 = 0; c0 < a.nchunks; c0 += 8) {
+    if (lane < G) d = a.ids[lo + lane];
+    if (jr <= G) {
+      const ChunkOut* co = a.cout + (lo + b + jr) * a.nchunks;
+      for (int c0 = t; c0 < a.nchunks; c0 += 8 * L) {
         ChunkOut o[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (c0 + k < a.nchunks) o[k] = co[c0 + k];
+          if (c0 + k * L < a.nchunks) o[k] = co[c0 + k * L];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          if (c0 + k >= a.nchunks) break;
+          if (c0 + k * L >= a.nchunks) break;
           argmax_merge(v, i, o[k].xmax, o[k].argmax);
           fl |= o[k].flags;
         }
       }
     }
+    for (int o = 1; o < L; o <<= 1) {
+      const float v2 = __shfl_xor(v, o, kWave);
+      const int i2 = __shfl_xor(i, o, kWave);
+      fl |= (uint32_t)__shfl_xor((int)fl, o, kWave);
+      argmax_merge(v, i, v2, i2);
+    }
+    const int src = (lane < P1 ? lane : 0) * L;
+    v = __shfl(v, src, kWave);
+    i = __shfl(i, src, kWave);
+    fl = (uint32_t)__shfl((int)fl, src, kWave);
+    if (lane > G) fl = 0;
     if (ballot(lane <= G && (fl & CF_NAN)) != 0) {
       if (lane < P1) out[lane] = -1;
       if (lane == 0) {
