@@ -52,6 +52,8 @@ def parse():
                          "sampling or greedy call only)")
     ap.add_argument("--lenience", type=float, default=None,
                     help="lenient acceptance factor in (0, 1] for the sampling call (dense q, uniform batch)")
+    ap.add_argument("--no-z-qp", action="store_true",
+                    help="statistics without Z' = sum (q - p)_+ (alpha, Z and accept_prob only)")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -177,7 +179,9 @@ def main():
     # sampling and statistics in one call (one pass over the logits), except
     # with lenience, whose call has no statistics: then the separate call
     fused = stats and not lenient
-    sout = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4)) if stats else None
+    zqp = not args.no_z_qp
+    sout = tuple(None if (k == 2 and not zqp) else torch.empty((B, G), dtype=torch.float32, device=dev)
+                 for k in range(4)) if stats else None
 
     def step(i, timer=None):
         """One verify step; `timer` = (start, stop) hipEvents around the row
@@ -306,9 +310,9 @@ def main():
             step_bytes += B * G * V * (cfg.logit_bytes + qb)
         elif stats:
             # the combined call's statistics: untruncated rows stream logits
-            # and q again; truncated rows read sum(q) of a dense q, nothing
-            # more when q comes from the draft's logits
-            step_bytes += B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl else B * G * V * 4)
+            # and q again; truncated rows read sum(q) of a dense q for Z',
+            # nothing more without Z' or when q comes from the draft's logits
+            step_bytes += B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl or not zqp else B * G * V * 4)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     # ---- CPU oracle baseline on a bounded sample ----
@@ -400,7 +404,8 @@ def main():
                    "q": "formed from the draft's logits" if dl else "dense float32 input",
                    "acceptance": f"lenient, beta = {args.lenience}" if lenient else "lossless",
                    "statistics": ("none" if not stats else
-                                  "combined sampling + statistics call" if fused else "separate statistics call"),
+                                  ("combined sampling + statistics call" if fused else "separate statistics call")
+                                  + ("" if zqp else ", without Z'")),
                    "batch": (f"ragged: gamma_b uniform on 0..{G}, {n_draft} drafts, packed; sampling / greedy "
                              f"call only" if rg else "uniform"),
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,

@@ -125,9 +125,13 @@ sv_status spec_verify_greedy(const void* target_logits, sv_dtype dt, const int32
  *   out_z_pq        = sum_x (p_j - q_j)_+  (residual mass Z)     ([RL] §2)
  *   out_z_qp        = sum_x (q_j - p_j)_+                        ([BS] §五)
  *   out_accept_prob = min(1, p_j(d_j) / q_j(d_j))  ([WR] §6)
- * each [B, gamma] float32.  q is used as given.  q_j(d_j) = 0 gives
- * accept_prob 1 if p_j(d_j) > 0 else 0; an id outside [0, V) gives NaN; a
- * non-finite logits row gives NaN in all four outputs of that position. */
+ * each [B, gamma] float32, or NULL (not computed).  q is used as given.
+ * q_j(d_j) = 0 gives accept_prob 1 if p_j(d_j) > 0 else 0; an id outside
+ * [0, V) gives NaN; a non-finite logits row gives NaN in all four outputs of
+ * that position.  Cost: out_z_qp needs sum_x q_j(x) over the whole row, a
+ * pass over q; without it, a position whose p_j is truncated to a kept set
+ * reads q only at that set's ids (p_j is 0 elsewhere, so alpha and z_pq are
+ * sums over the set). */
 sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,
                             const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V,
                             sv_sampling_params prm, float* out_alpha, float* out_z_pq,
@@ -138,8 +142,8 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
  * spec_verify_sample and of spec_accept_stats for the same inputs, from one
  * pass over the target logits (the statistics reuse the sampling call's row
  * results for rows 0..gamma-1 instead of recomputing them).  Arguments are
- * those of the two calls; the statistics outputs may be NULL only when
- * gamma = 0.  Workspace: spec_verify_workspace_size (which covers this
+ * those of the two calls; each statistics output may be NULL, as in
+ * spec_accept_stats.  Workspace: spec_verify_workspace_size (which covers this
  * call).  [WR] §4.2 and §6; [RL] §2; [MN] §三 (acceptance rate, monitored per
  * round to adapt gamma: [MN] §九, point 3). */
 sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,

@@ -162,9 +162,24 @@ def verify_greedy(logits, ids, workspace: Optional[torch.Tensor] = None, out=Non
     return tokens, nacc, flags
 
 
+def _stats_outs(stats_out, B, G, dev, z_qp):
+    """(alpha, Z, Z', accept_prob) buffers; an entry may be None (not
+    computed).  Without Z' (z_qp=False) a position whose p is truncated to a
+    kept set reads q only at that set's ids."""
+    if stats_out is None:
+        stats_out = tuple(None if (k == 2 and not z_qp) else torch.empty((B, G), dtype=torch.float32, device=dev)
+                          for k in range(4))
+    return stats_out
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
 def accept_stats(logits, q, ids, temperature=1.0, top_k=0, top_p=1.0,
-                 workspace: Optional[torch.Tensor] = None, out=None):
-    """Per-position (alpha, Z, Z', accept_prob), each [B, gamma] float32."""
+                 workspace: Optional[torch.Tensor] = None, out=None, z_qp: bool = True):
+    """Per-position (alpha, Z, Z', accept_prob), each [B, gamma] float32 (Z'
+    None when z_qp is False)."""
     if logits.dim() != 3:
         raise ValueError("logits must be [B, gamma+1, V]")
     B, G1, V = logits.shape
@@ -175,14 +190,12 @@ def accept_stats(logits, q, ids, temperature=1.0, top_k=0, top_p=1.0,
     dev = logits.device
     _check(q, "q", torch.float32, (B, G, V))
     _check(ids, "ids", torch.int32, (B, G))
-    if out is None:
-        out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
-    alpha, zpq, zqp, acc = out
+    alpha, zpq, zqp, acc = _stats_outs(out, B, G, dev, z_qp)
     need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
     ws = _workspace(workspace, need, dev)
     code = load_library().spec_accept_stats(
         logits.data_ptr(), _DT[logits.dtype], q.data_ptr(), ids.data_ptr(), B, G, V,
-        _params(temperature, top_k, top_p), alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        _params(temperature, top_k, top_p), _ptr(alpha), _ptr(zpq), _ptr(zqp), _ptr(acc),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_accept_stats")
     return alpha, zpq, zqp, acc
@@ -237,8 +250,9 @@ def verify_sample_draft_logits(logits, draft_logits, ids, u_accept, u_resample, 
 
 
 def accept_stats_draft_logits(logits, draft_logits, ids, temperature=1.0, top_k=0, top_p=1.0,
-                              workspace: Optional[torch.Tensor] = None, out=None):
-    """Per-position (alpha, Z, Z', accept_prob) with q formed from the draft's logits."""
+                              workspace: Optional[torch.Tensor] = None, out=None, z_qp: bool = True):
+    """Per-position (alpha, Z, Z', accept_prob) with q formed from the draft's
+    logits (Z' None when z_qp is False)."""
     if logits.dim() != 3:
         raise ValueError("logits must be [B, gamma+1, V]")
     B, G1, V = logits.shape
@@ -251,15 +265,13 @@ def accept_stats_draft_logits(logits, draft_logits, ids, temperature=1.0, top_k=
     if draft_logits.dtype not in _DT:
         raise ValueError("draft_logits must be float32 or bfloat16")
     _check(ids, "ids", torch.int32, (B, G))
-    if out is None:
-        out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
-    alpha, zpq, zqp, acc = out
+    alpha, zpq, zqp, acc = _stats_outs(out, B, G, dev, z_qp)
     need = draft_logits_workspace_size(B, G, V, logits.dtype, draft_logits.dtype, temperature, top_k, top_p)
     ws = _workspace(workspace, need, dev)
     code = load_library().spec_accept_stats_draft_logits(
         logits.data_ptr(), _DT[logits.dtype], draft_logits.data_ptr(), _DT[draft_logits.dtype], ids.data_ptr(),
-        B, G, V, _params(temperature, top_k, top_p), alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(),
-        acc.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+        B, G, V, _params(temperature, top_k, top_p), _ptr(alpha), _ptr(zpq), _ptr(zqp),
+        _ptr(acc), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_accept_stats_draft_logits")
     return alpha, zpq, zqp, acc
 
@@ -330,20 +342,19 @@ def verify_greedy_ragged(logits, ids, cu_draft, gamma_max: int, eos_id: int = -1
     return tokens, nacc, flags
 
 
-def _sample_stats_outs(out, stats_out, B, G, dev):
+def _sample_stats_outs(out, stats_out, B, G, dev, z_qp):
     if out is None:
         out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev),
                torch.empty((B,), dtype=torch.int32, device=dev),
                torch.empty((B,), dtype=torch.int32, device=dev))
-    if stats_out is None:
-        stats_out = tuple(torch.empty((B, G), dtype=torch.float32, device=dev) for _ in range(4))
-    return out, stats_out
+    return out, _stats_outs(stats_out, B, G, dev, z_qp)
 
 
 def verify_sample_stats(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0,
-                        workspace: Optional[torch.Tensor] = None, out=None, stats_out=None):
+                        workspace: Optional[torch.Tensor] = None, out=None, stats_out=None, z_qp: bool = True):
     """verify_sample and accept_stats of the same inputs from one pass over the
-    logits; returns (tokens, n_accepted, flags, alpha, z_pq, z_qp, accept_prob)."""
+    logits; returns (tokens, n_accepted, flags, alpha, z_pq, z_qp, accept_prob)
+    (z_qp None when not asked for)."""
     if logits.dim() != 3:
         raise ValueError("logits must be [B, gamma+1, V]")
     B, G1, V = logits.shape
@@ -357,7 +368,7 @@ def verify_sample_stats(logits, q, ids, u_accept, u_resample, temperature=1.0, t
         _check(ids, "ids", torch.int32, (B, G))
         _check(u_accept, "u_accept", torch.float32, (B, G))
     _check(u_resample, "u_resample", torch.float32, (B, G1))
-    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev)
+    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev, z_qp)
     need = workspace_size(B, G, V, logits.dtype, temperature, top_k, top_p)
     ws = _workspace(workspace, need, dev)
     code = load_library().spec_verify_sample_stats(
@@ -366,14 +377,15 @@ def verify_sample_stats(logits, q, ids, u_accept, u_resample, temperature=1.0, t
         u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
         B, G, V, _params(temperature, top_k, top_p),
         tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
-        alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        _ptr(alpha), _ptr(zpq), _ptr(zqp), _ptr(acc),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_verify_sample_stats")
     return tokens, nacc, flags, alpha, zpq, zqp, acc
 
 
 def verify_sample_stats_draft_logits(logits, draft_logits, ids, u_accept, u_resample, temperature=1.0, top_k=0,
-                                     top_p=1.0, workspace: Optional[torch.Tensor] = None, out=None, stats_out=None):
+                                     top_p=1.0, workspace: Optional[torch.Tensor] = None, out=None, stats_out=None,
+                                     z_qp: bool = True):
     """verify_sample_draft_logits and accept_stats_draft_logits of the same
     inputs from one pass over each logits tensor."""
     if logits.dim() != 3:
@@ -393,7 +405,7 @@ def verify_sample_stats_draft_logits(logits, draft_logits, ids, u_accept, u_resa
         _check(ids, "ids", torch.int32, (B, G))
         _check(u_accept, "u_accept", torch.float32, (B, G))
     _check(u_resample, "u_resample", torch.float32, (B, G1))
-    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev)
+    (tokens, nacc, flags), (alpha, zpq, zqp, acc) = _sample_stats_outs(out, stats_out, B, G, dev, z_qp)
     need = draft_logits_workspace_size(B, G, V, logits.dtype, ddt, temperature, top_k, top_p)
     ws = _workspace(workspace, need, dev)
     code = load_library().spec_verify_sample_stats_draft_logits(
@@ -402,7 +414,7 @@ def verify_sample_stats_draft_logits(logits, draft_logits, ids, u_accept, u_resa
         u_accept.data_ptr() if G > 0 else None, u_resample.data_ptr(),
         B, G, V, _params(temperature, top_k, top_p),
         tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(),
-        alpha.data_ptr(), zpq.data_ptr(), zqp.data_ptr(), acc.data_ptr(),
+        _ptr(alpha), _ptr(zpq), _ptr(zqp), _ptr(acc),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _raise(code, "spec_verify_sample_stats_draft_logits")
     return tokens, nacc, flags, alpha, zpq, zqp, acc

@@ -621,8 +621,7 @@ sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
   if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
-  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs) ||
-                    out_alpha == nullptr || out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr))
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
     return SV_ERR_INVALID_ARG;
   const Plan p = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
@@ -655,9 +654,7 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0 || gamma == 0) return SV_OK;
-  if (draft_probs == nullptr || draft_ids == nullptr || !aligned16(draft_probs) || out_alpha == nullptr ||
-      out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr)
-    return SV_ERR_INVALID_ARG;
+  if (draft_probs == nullptr || draft_ids == nullptr || !aligned16(draft_probs)) return SV_ERR_INVALID_ARG;
   const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -722,9 +719,7 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0 || gamma == 0) return SV_OK;
-  if (draft_logits == nullptr || draft_ids == nullptr || !aligned16(draft_logits) || out_alpha == nullptr ||
-      out_z_pq == nullptr || out_z_qp == nullptr || out_accept_prob == nullptr)
-    return SV_ERR_INVALID_ARG;
+  if (draft_logits == nullptr || draft_ids == nullptr || !aligned16(draft_logits)) return SV_ERR_INVALID_ARG;
   const Plan p = make_plan(CALL_STATS, B, gamma, V, dt, prm);
   const size_t qoff = draft_ws_offset(CALL_STATS, B, gamma, V, dt, prm);
   const size_t need = qoff + make_plan(CALL_DRAFT, B, gamma, V, draft_dt, prm).total;
@@ -754,9 +749,7 @@ sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dt
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
   if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
-  if (gamma > 0 && (draft_logits == nullptr || draft_ids == nullptr || u_accept == nullptr ||
-                    !aligned16(draft_logits) || out_alpha == nullptr || out_z_pq == nullptr || out_z_qp == nullptr ||
-                    out_accept_prob == nullptr))
+  if (gamma > 0 && (draft_logits == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_logits)))
     return SV_ERR_INVALID_ARG;
   const Plan p = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);
   const size_t qoff = draft_ws_offset(CALL_SAMPLE_STATS, B, gamma, V, dt, prm);

@@ -1276,8 +1276,9 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
 // Statistics ([WR] §4.2, [RL] §2): per (row, chunk) partial sums, then a
 // per-row finish.
 //   dense q: rows with a stored kept list need only sum(q) from the chunk
-//     pass; the min / positive-part sums over the kept set come from the
-//     list.  Other rows stream logits and q together.
+//     pass, and only for Z' (out_zqp); the min / positive-part sums over the
+//     kept set come from the list.  Other rows stream logits and q together.
+// Each output may be null (not written).
 //   q from the draft's logits: q is 0 off the draft's kept set, so when both
 //     rows have stored lists alpha and Z come from p's list and Z' from q's
 //     list (p evaluated at its ids), with no chunk pass; otherwise the row is
@@ -1334,8 +1335,8 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   double mn = 0.0, pq = 0.0, qp = 0.0, sq = 0.0;
   __shared__ double s_p[4][4];
   const bool big = stats_streamed(a, ri, r);
-  // with q from logits, rows finished from their lists skip the pass
-  if (!(ri.flags & RF_NONFINITE) && (big || !QLOG)) {
+  // rows finished from their lists skip the pass, unless Z' needs sum(q)
+  if (!(ri.flags & RF_NONFINITE) && (big || (!QLOG && a.out_zqp != nullptr))) {
     const QRow qr = q_row(a.q, r);
     const double invS = 1.0 / ri.S;
     // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
@@ -1415,16 +1416,16 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   const bool qbad = a.q.dense == nullptr && (a.q.info[r].flags & RF_NONFINITE);
   if ((ri.flags & RF_NONFINITE) || qbad) {
     if (lane == 0) {
-      a.out_alpha[r] = qnan;
-      a.out_zpq[r] = qnan;
-      a.out_zqp[r] = qnan;
-      a.out_acc[r] = qnan;
+      if (a.out_alpha) a.out_alpha[r] = qnan;
+      if (a.out_zpq) a.out_zpq[r] = qnan;
+      if (a.out_zqp) a.out_zqp[r] = qnan;
+      if (a.out_acc) a.out_acc[r] = qnan;
     }
     return;
   }
   const double invS = 1.0 / ri.S;
   const QRow qr = q_row(a.q, r);
-  double alpha, zpq, zqp;
+  double alpha, zpq, zqp = 0.0;
   if (stats_streamed(a, ri, r)) {
     double acc4[3];
     for (int k = 0; k < 3; ++k) {
@@ -1452,7 +1453,9 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     zpq = wave_sum_d(pq);
     qp = wave_sum_d(qp);
     sqk = wave_sum_d(sqk);
-    if (a.q.dense != nullptr) {
+    if (a.out_zqp == nullptr) {
+      // Z' not asked for: neither sum(q) nor q's list is read
+    } else if (a.q.dense != nullptr) {
       double sq = 0.0;
       for (int c = lane; c < a.nchunks; c += kWave) sq += a.partials[(r * a.nchunks + c) * 4 + 3];
       zqp = (wave_sum_d(sq) - sqk) + qp;
@@ -1475,14 +1478,14 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     }
   }
   if (lane == 0) {
-    a.out_alpha[r] = (float)alpha;
-    a.out_zpq[r] = (float)zpq;
-    a.out_zqp[r] = (float)zqp;
+    if (a.out_alpha) a.out_alpha[r] = (float)alpha;
+    if (a.out_zpq) a.out_zpq[r] = (float)zpq;
+    if (a.out_zqp) a.out_zqp[r] = (float)zqp;
     float ap;
     if (ri.d < 0) ap = qnan;
     else if (ri.qd == 0.0f) ap = ri.ed > 0.0f ? 1.0f : 0.0f;
     else ap = (float)fmin(1.0, ((double)ri.ed * invS) / (double)ri.qd);
-    a.out_acc[r] = ap;
+    if (a.out_acc) a.out_acc[r] = ap;
   }
 }
 

@@ -248,7 +248,7 @@ def test_sample_stats_argument_errors():
                                                          a["wsb"], None)
 
     assert f() == WORKSPACE
-    assert f(al=None) == INVALID
+    assert f(al=None) == WORKSPACE  # a statistics output left out is not computed
     assert f(q=None) == INVALID
     assert f(G=0, q=None, al=None) == WORKSPACE  # no drafts: no statistics outputs needed
     assert f(B=0) == 0
@@ -257,7 +257,7 @@ def test_sample_stats_argument_errors():
     assert f(ws=FAKE, wsb=wsb - 256) == WORKSPACE
     assert g() == WORKSPACE
     assert g(ddt=5) == INVALID
-    assert g(al=None) == INVALID
+    assert g(al=None) == WORKSPACE
     assert g(dz=FAKE + 2) == INVALID
 
 

@@ -113,3 +113,35 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(outs + souts, ref):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dl", [False, True])
+@pytest.mark.parametrize("name,kw", [
+    ("c2", dict(B=4)),
+    ("c3", dict(B=4)),
+    ("c5", dict(B=4)),
+    ("c5", dict(B=3, gamma=3, V=70001)),
+])
+def test_without_z_qp(name, kw, dl):
+    """Leaving Z' out (a null output) changes no other output, bit for bit,
+    in the combined call and in the statistics-only call."""
+    w = generate(name, DEV, **kw)
+    c = w.cfg
+    full = _fused(w, dl)
+    if dl:
+        part = sv.verify_sample_stats_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                                   c.temperature, c.top_k, c.top_p, z_qp=False)
+        st_full = sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, c.temperature, c.top_k, c.top_p)
+        st_part = sv.accept_stats_draft_logits(w.logits, w.draft_logits, w.ids, c.temperature, c.top_k, c.top_p,
+                                               z_qp=False)
+    else:
+        part = sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature, c.top_k,
+                                      c.top_p, z_qp=False)
+        st_full = sv.accept_stats(w.logits, w.q, w.ids, c.temperature, c.top_k, c.top_p)
+        st_part = sv.accept_stats(w.logits, w.q, w.ids, c.temperature, c.top_k, c.top_p, z_qp=False)
+    torch.cuda.synchronize()
+    assert part[5] is None and st_part[2] is None
+    for k in (0, 1, 2, 3, 4, 6):
+        np.testing.assert_array_equal(part[k].cpu().numpy(), full[k].cpu().numpy(), err_msg=f"output {k}")
+    for k in (0, 1, 3):
+        np.testing.assert_array_equal(st_part[k].cpu().numpy(), st_full[k].cpu().numpy(), err_msg=f"stats {k}")
