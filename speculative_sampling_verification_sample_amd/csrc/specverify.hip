@@ -434,8 +434,12 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.ids = draft_ids;
   a.V = V;
   a.gamma = gamma;
-  a.nchunks = p.nchunks;
-  a.chunk = p.chunk;
+  // Truncated rows whose statistics come from their kept lists need no
+  // pass; only rows without a list (rare) stream, one workgroup per row, so
+  // the launch is B * gamma workgroups that mostly return at once.
+  const bool lists = p.trunc && (q.dense == nullptr || so.z_qp == nullptr);
+  a.nchunks = lists ? 1 : p.nchunks;
+  a.chunk = lists ? (int64_t)V : p.chunk;
   a.c = c;
   a.info = ws_at<RowInfo>(workspace, p.off_info);
   a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
@@ -448,7 +452,7 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.out_acc = so.accept_prob;
   a.rows = (int64_t)B * gamma;
   if (a.rows == 0) return SV_OK;
-  dim3 grid((unsigned)(a.rows * p.nchunks));
+  dim3 grid((unsigned)(a.rows * a.nchunks));
   const bool qlog = q.dense == nullptr;
   if (bf) {
     if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<true, true>), grid, dim3(256), 0, st, a);

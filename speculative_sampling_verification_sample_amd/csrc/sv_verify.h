@@ -1335,8 +1335,11 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   double mn = 0.0, pq = 0.0, qp = 0.0, sq = 0.0;
   __shared__ double s_p[4][4];
   const bool big = stats_streamed(a, ri, r);
-  // rows finished from their lists skip the pass, unless Z' needs sum(q)
-  if (!(ri.flags & RF_NONFINITE) && (big || (!QLOG && a.out_zqp != nullptr))) {
+  // Rows finished from their lists skip the pass, unless Z' needs sum(q);
+  // nothing reads their partials then (the test is the same for the whole
+  // workgroup).
+  if ((ri.flags & RF_NONFINITE) || !(big || (!QLOG && a.out_zqp != nullptr))) return;
+  {
     const QRow qr = q_row(a.q, r);
     const double invS = 1.0 / ri.S;
     // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
