@@ -15,6 +15,7 @@ import torch
 import oracle
 from parity import compare_greedy, compare_sample, compare_stats, gpu_sample, widen
 from workloads import generate
+import speculative_sampling_verification_sample_amd as sv
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +163,23 @@ def test_wide_nucleus_exact_path():
     """Flat-ish rows whose nucleus exceeds the fast path's candidate set."""
     w = generate("c5", DEV, B=3, gamma=2, V=30000, temperature=50.0, top_p=0.9)
     compare_sample(w, label="wide nucleus")
+
+
+def test_wide_nucleus_stats_streamed_rows():
+    """Rows without a stored kept list stream whole in the statistics pass,
+    one workgroup per row, when Z' is left out or q comes from the draft's
+    logits: the oracle's statistics to the statistics bar."""
+    w = generate("c5", DEV, B=3, gamma=2, V=30000, temperature=50.0, top_p=0.9)
+    c = w.cfg
+    al, zpq, zqp, acc = sv.accept_stats(w.logits, w.q, w.ids, c.temperature, c.top_k, c.top_p, z_qp=False)
+    assert zqp is None
+    compare_stats(w, label="wide nucleus stats without Z'", gpu=(al, zpq, None, acc))
+    compare_stats(w, label="wide nucleus stats, draft logits", draft_logits=True)
+    out = sv.verify_sample_stats_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                              c.temperature, c.top_k, c.top_p, z_qp=False)
+    torch.cuda.synchronize()
+    compare_stats(w, label="wide nucleus sample+stats, draft logits, without Z'", draft_logits=True,
+                  gpu=(out[3], out[4], None, out[6]))
 
 
 def test_flags():
