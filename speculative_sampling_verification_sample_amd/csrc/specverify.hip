@@ -89,13 +89,21 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   if (p.trunc) {
     // A chunk is held in registers: at most nu * kTruncBS units of 16 bytes,
     // two of them possibly straddling the chunk ends.  Shorter chunks (fewer
-    // units per thread) only when the rows alone do not fill the GPU.
+    // units per thread) only when the rows alone do not fill the GPU, and
+    // only while the chunks' candidates (about nw each) stay well inside the
+    // row finisher's union: past it a row takes the exact path, which on a
+    // few rows costs far more than the idle CUs (2 x 5 rows of 256000 bf16,
+    // top-p: 16 chunks per row put the finisher at 315 us, 8 chunks keep
+    // the whole step at 46 us).
     const int64_t epv = (dt == SV_BF16) ? 8 : 4;
-    int64_t cap = 0;
+    auto chunks_at = [&](int nu) {
+      const int64_t cap = ((int64_t)nu * kTruncBS - 2) * epv / 8 * 8;
+      return (V + cap - 1) / cap;
+    };
     for (p.nu = 16;; p.nu /= 2) {
-      cap = ((int64_t)p.nu * kTruncBS - 2) * epv / 8 * 8;
-      nch = (V + cap - 1) / cap;
+      nch = chunks_at(p.nu);
       if (p.nu == 4 || p.rows * nch >= kTruncMinWG) break;
+      if (chunks_at(p.nu / 2) * p.nw > kUnionMax / 2) break;
     }
   } else {
     // Chunks of about kChunkBytes: shorter ones pay a workgroup's fixed cost
