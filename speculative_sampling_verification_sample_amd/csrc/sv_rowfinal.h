@@ -298,14 +298,16 @@ __device__ __forceinline__ double block_sum_d(double v, double* s_tmp) {
 }
 
 template <bool BF16>
-__device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int64_t dpos, int64_t rowoff, RowInfo ri) {
+__device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int64_t dpos, int64_t rowoff, RowInfo ri,
+                                          uint32_t* hist, unsigned long long* mhist) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t V = a.V;
   const float c = a.c;
   const float R = ri.R;
 
-  __shared__ uint32_t hist[256];
-  __shared__ unsigned long long mhist[256];
+  // hist and mhist are the caller's selection histograms (LDS), free again
+  // once every thread is here
+  __syncthreads();
   __shared__ double s_tmp[4];
   __shared__ int s_digit, s_need, s_cnt[4];
   __shared__ unsigned long long s_above;
@@ -589,7 +591,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
+__global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArgs a) {
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const RowAt at = row_at(a.cu, a.n_live, a.rows_per_req, a.G1, a.gamma, a.V, r);
@@ -703,7 +705,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
     return;
   }
   if ((fl & CF_OVERFLOW) || !a.fast) {
-    exact_row<BF16>(a, r, dpos, rowoff, ri);
+    exact_row<BF16>(a, r, dpos, rowoff, ri, hist, mh);
     return;
   }
 
@@ -759,7 +761,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
   __syncthreads();
   const int nu = s_n;
   if (nu > a.um) {
-    exact_row<BF16>(a, r, dpos, rowoff, ri);
+    exact_row<BF16>(a, r, dpos, rowoff, ri, hist, mh);
     return;
   }
 
@@ -784,7 +786,7 @@ __global__ void __launch_bounds__(256) rowfinal_kernel(RowFinalArgs a) {
       kfinal = kp;
     } else if (!(topk || theta == kLowest)) {
       // the crossing lies below the certified candidates: exact path
-      exact_row<BF16>(a, r, dpos, rowoff, ri);
+      exact_row<BF16>(a, r, dpos, rowoff, ri, hist, mh);
       return;
     }  // else rounding: keep the whole base set
   }
