@@ -1442,15 +1442,29 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   } else {
     const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
-    for (int i = lane; i < ri.nkept; i += kWave) {
-      Cand e = L[i];
-      double p = (double)e.v * invS;
-      double qv = (double)qr.at(e.idx);
-      double d = p - qv;
-      mn += fmin(p, qv);
-      if (d > 0.0) pq += d;
-      if (d < 0.0) qp -= d;
-      sqk += qv;
+    // kStatBlk list steps per round: their entry loads, then their q loads,
+    // are in flight together; each lane still adds its entries in list order
+    constexpr int kStatBlk = 4;
+    const int nk = ri.nkept;
+    for (int i0 = lane; i0 < nk; i0 += kStatBlk * kWave) {
+      Cand e[kStatBlk];
+      float qf[kStatBlk];
+#pragma unroll
+      for (int u = 0; u < kStatBlk; ++u)
+        if (i0 + u * kWave < nk) e[u] = L[i0 + u * kWave];
+#pragma unroll
+      for (int u = 0; u < kStatBlk; ++u) qf[u] = (i0 + u * kWave < nk) ? qr.at(e[u].idx) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kStatBlk; ++u) {
+        if (i0 + u * kWave >= nk) break;
+        double p = (double)e[u].v * invS;
+        double qv = (double)qf[u];
+        double d = p - qv;
+        mn += fmin(p, qv);
+        if (d > 0.0) pq += d;
+        if (d < 0.0) qp -= d;
+        sqk += qv;
+      }
     }
     alpha = wave_sum_d(mn);
     zpq = wave_sum_d(pq);
@@ -1470,12 +1484,24 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
       const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
       double zq = 0.0;
-      for (int i = lane; i < qi.nkept; i += kWave) {
-        Cand e = Lq[i];
-        const double qv = (double)e.v * qinvS;
-        const float z = load_logit<BF16>(a.logits, lrow + e.idx);
-        const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
-        if (qv > p) zq += qv - p;
+      const int nq = qi.nkept;
+      for (int i0 = lane; i0 < nq; i0 += kStatBlk * kWave) {
+        Cand e[kStatBlk];
+        float zf[kStatBlk];
+#pragma unroll
+        for (int u = 0; u < kStatBlk; ++u)
+          if (i0 + u * kWave < nq) e[u] = Lq[i0 + u * kWave];
+#pragma unroll
+        for (int u = 0; u < kStatBlk; ++u)
+          zf[u] = (i0 + u * kWave < nq) ? load_logit<BF16>(a.logits, lrow + e[u].idx) : kNegInf;
+#pragma unroll
+        for (int u = 0; u < kStatBlk; ++u) {
+          if (i0 + u * kWave >= nq) break;
+          const double qv = (double)e[u].v * qinvS;
+          const float z = zf[u];
+          const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
+          if (qv > p) zq += qv - p;
+        }
       }
       zqp = wave_sum_d(zq);
     }
