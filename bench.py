@@ -52,6 +52,8 @@ def parse():
                          "sampling or greedy call only)")
     ap.add_argument("--lenience", type=float, default=None,
                     help="lenient acceptance factor in (0, 1] for the sampling call (dense q, uniform batch)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="requests per step (default: the workload's B); the recipe is otherwise unchanged")
     ap.add_argument("--no-z-qp", action="store_true",
                     help="statistics without Z' = sum (q - p)_+ (alpha, Z and accept_prob only)")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
@@ -129,6 +131,12 @@ def main():
     from workloads import CONFIGS, generate, pack_ragged, ragged_gammas
 
     cfg = CONFIGS[args.config]
+    if args.batch is not None:
+        import dataclasses
+
+        if args.batch < 1:
+            raise SystemExit("--batch must be at least 1")
+        cfg = dataclasses.replace(cfg, B=args.batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = sv.load_library()
@@ -289,7 +297,8 @@ def main():
     row_bytes = V * cfg.logit_bytes
     alg_launch = rows * row_bytes  # the row pass reads every logit of the batch once
     achieved = alg_launch / (k_ms * 1e-3) / 1e9
-    traffic = None if rg else read_traffic(cfg.name)  # counters are taken on the uniform batches
+    # counters are taken on the uniform batches at the workload's own B
+    traffic = None if (rg or args.batch is not None) else read_traffic(cfg.name)
 
     # ---- whole-step algorithmic bytes ----
     nacc = ref[1].cpu().numpy()
