@@ -1442,9 +1442,10 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   } else {
     const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
-    // kStatBlk list steps per round: their entry loads, then their q loads,
-    // are in flight together; each lane still adds its entries in list order
-    constexpr int kStatBlk = 4;
+    // kStatBlk list steps per round (a nucleus of a few hundred tokens in
+    // one): their entry loads, then their q loads, are in flight together;
+    // each lane still adds its entries in list order
+    constexpr int kStatBlk = 8;
     const int nk = ri.nkept;
     for (int i0 = lane; i0 < nk; i0 += kStatBlk * kWave) {
       Cand e[kStatBlk];
