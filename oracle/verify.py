@@ -350,7 +350,7 @@ def verify_greedy(logits, ids, requests=None):
     return _batch_result(res, ids.shape[1])
 
 
-def stats_request(z_rows, q_rows, ids, T, top_k=0, top_p=1.0):
+def stats_request(z_rows, q_rows, ids, T, top_k=0, top_p=1.0, boundary_out=None):
     """Per-position acceptance statistics of one request (positions j < gamma).
 
     alpha_j = sum_x min(p_j, q_j) ([WR] §4.2; [MN] §三, alpha = 1 - TV),
@@ -359,12 +359,16 @@ def stats_request(z_rows, q_rows, ids, T, top_k=0, top_p=1.0):
     a_j = min(1, p_j(d_j) / q_j(d_j)) ([WR] §6).  q is used as given (not
     renormalised).  q_j(d_j) = 0 gives a_j = 1 if p_j(d_j) > 0 else 0; an id
     outside [0, V) gives a_j = NaN; a non-finite logits row gives NaN in all
-    four outputs of that position.
+    four outputs of that position.  ``boundary_out`` (a bool array of length
+    gamma), when given, receives each position's top-p boundary diagnostic
+    (``process_row``): a kept set decided within 1e-6 of top_p.
     """
     gamma = len(ids)
     out = np.full((4, gamma), np.nan)
     for j in range(gamma):
         r = process_row(z_rows[j], T, top_k, top_p)
+        if boundary_out is not None:
+            boundary_out[j] = r.top_p_boundary
         if r.nonfinite:
             continue
         p = r.p
@@ -382,15 +386,20 @@ def stats_request(z_rows, q_rows, ids, T, top_k=0, top_p=1.0):
     return out
 
 
-def accept_stats(logits, q, ids, T, top_k=0, top_p=1.0, requests=None):
-    """Batched ``stats_request``; returns (alpha, z_pq, z_qp, accept_prob), each [B', gamma]."""
-    req = range(logits.shape[0]) if requests is None else requests
-    res = [stats_request(logits[b], q[b], ids[b], T, top_k, top_p) for b in req]
+def accept_stats(logits, q, ids, T, top_k=0, top_p=1.0, requests=None, with_boundary=False):
+    """Batched ``stats_request``; returns (alpha, z_pq, z_qp, accept_prob), each [B', gamma],
+    and with ``with_boundary`` a fifth [B', gamma] bool array: the top-p boundary
+    diagnostic of each position."""
+    req = list(range(logits.shape[0]) if requests is None else requests)
     gamma = ids.shape[1]
+    bnd = np.zeros((len(req), gamma), bool)
+    res = [stats_request(logits[b], q[b], ids[b], T, top_k, top_p, boundary_out=bnd[i]) for i, b in enumerate(req)]
     if not res:
-        return tuple(np.zeros((0, gamma)) for _ in range(4))
-    arr = np.stack(res)  # [B', 4, gamma]
-    return arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3]
+        out = tuple(np.zeros((0, gamma)) for _ in range(4))
+    else:
+        arr = np.stack(res)  # [B', 4, gamma]
+        out = (arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3])
+    return out + (bnd,) if with_boundary else out
 
 
 # --------------------------------------------------------------------------
@@ -436,26 +445,40 @@ def verify_sample_draft_logits(logits, draft_logits, ids, u_accept, u_resample, 
     return _batch_result(res, gamma)
 
 
-def stats_request_draft_logits(z_rows, dz_rows, ids, T, top_k=0, top_p=1.0):
+def stats_request_draft_logits(z_rows, dz_rows, ids, T, top_k=0, top_p=1.0, boundary_out=None):
     """``stats_request`` with q_j = the processed draft logits row j; a
-    position whose draft row has no q gives NaN in all four outputs."""
-    q_rows, _ = draft_q_rows(dz_rows, T, top_k, top_p)
-    out = stats_request(z_rows, q_rows, ids, T, top_k, top_p)
+    position whose draft row has no q gives NaN in all four outputs.
+    ``boundary_out`` receives each position's top-p boundary diagnostic, of
+    the target's or the draft's row."""
+    q_rows = []
+    qb = np.zeros(len(ids), bool)
+    for j in range(len(ids)):
+        rows, qb[j] = draft_q_rows(dz_rows[j:j + 1], T, top_k, top_p)
+        q_rows.append(rows[0])
+    out = stats_request(z_rows, q_rows, ids, T, top_k, top_p, boundary_out=boundary_out)
+    if boundary_out is not None:
+        boundary_out |= qb
     for j, q in enumerate(q_rows):
         if np.isnan(q).all():
             out[:, j] = np.nan
     return out
 
 
-def accept_stats_draft_logits(logits, draft_logits, ids, T, top_k=0, top_p=1.0, requests=None):
-    """Batched ``stats_request_draft_logits``; returns (alpha, z_pq, z_qp, accept_prob)."""
-    req = range(logits.shape[0]) if requests is None else requests
-    res = [stats_request_draft_logits(logits[b], draft_logits[b], ids[b], T, top_k, top_p) for b in req]
+def accept_stats_draft_logits(logits, draft_logits, ids, T, top_k=0, top_p=1.0, requests=None,
+                              with_boundary=False):
+    """Batched ``stats_request_draft_logits``; returns (alpha, z_pq, z_qp, accept_prob)
+    (plus the per-position top-p boundary diagnostic with ``with_boundary``)."""
+    req = list(range(logits.shape[0]) if requests is None else requests)
     gamma = ids.shape[1]
+    bnd = np.zeros((len(req), gamma), bool)
+    res = [stats_request_draft_logits(logits[b], draft_logits[b], ids[b], T, top_k, top_p, boundary_out=bnd[i])
+           for i, b in enumerate(req)]
     if not res:
-        return tuple(np.zeros((0, gamma)) for _ in range(4))
-    arr = np.stack(res)
-    return arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3]
+        out = tuple(np.zeros((0, gamma)) for _ in range(4))
+    else:
+        arr = np.stack(res)
+        out = (arr[:, 0], arr[:, 1], arr[:, 2], arr[:, 3])
+    return out + (bnd,) if with_boundary else out
 
 
 # --------------------------------------------------------------------------

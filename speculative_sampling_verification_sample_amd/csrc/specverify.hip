@@ -64,7 +64,7 @@ struct Plan {
   int nch4 = 1;
   int scale_bits = 40;
   size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
-  size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][4] (CALL_STATS, CALL_SAMPLE_STATS)
+  size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][kStatSums] (CALL_STATS, CALL_SAMPLE_STATS)
   size_t total = 0;
 };
 
@@ -144,10 +144,10 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.off_gath = off;
   if (sampling) off = align_up(off + rows * sizeof(float2), 256);
   p.off_part = off;
-  if (sampling) off = align_up(off + (size_t)B * p.nch4 * sizeof(double), 256);
+  if (sampling) off = align_up(off + (size_t)B * p.nch4 * 4 * sizeof(double), 256);
   p.off_spart = off;
   if (kind == CALL_STATS || kind == CALL_SAMPLE_STATS)
-    off = align_up(off + (size_t)B * gamma * nch * 4 * sizeof(double), 256);
+    off = align_up(off + (size_t)B * gamma * nch * kStatSums * sizeof(double), 256);
   p.total = std::max<size_t>(off, 256);
   return p;
 }
@@ -163,14 +163,24 @@ sv_status check_sizes(int32_t B, int32_t gamma, int32_t V, sv_dtype dt) {
   return SV_OK;
 }
 
-sv_status check_params(sv_sampling_params prm, float* c_out) {
+// log2(e) / T in the three forms the kernels use: the double c64 and its
+// two-float split c + cl (c64 - c rounded to float).
+struct Expo {
+  float c, cl;
+  double c64;
+};
+constexpr Expo kExpoGreedy = {1.0f, 0.0f, 1.0};  // greedy passes take no exponentials
+
+sv_status check_params(sv_sampling_params prm, Expo* c_out) {
   const float T = prm.temperature;
   if (!(T > 0.0f) || !std::isfinite(T)) return SV_ERR_INVALID_ARG;
   if (prm.top_k < 0) return SV_ERR_INVALID_ARG;
   if (!(prm.top_p > 0.0f && prm.top_p <= 1.0f)) return SV_ERR_INVALID_ARG;
   const double c = 1.4426950408889634 / (double)T;
   if (!std::isfinite(c) || c > 1e30) return SV_ERR_INVALID_ARG;
-  *c_out = (float)c;
+  c_out->c64 = c;
+  c_out->c = (float)c;
+  c_out->cl = (float)(c - (double)c_out->c);
   return SV_OK;
 }
 
@@ -215,6 +225,8 @@ QSrc q_src_dense(const float* q, int64_t V) {
   s.info = nullptr;
   s.V = V;
   s.c = 0.0f;
+  s.cl = 0.0f;
+  s.c64 = 0.0;
   s.zbf16 = 0;
   return s;
 }
@@ -226,7 +238,7 @@ QSrc q_src_none(int64_t V) { return q_src_dense(nullptr, V); }
 // `cu`, `n_live`: a ragged batch's draft offsets and its packed rows
 // (n_draft + B); cu = null: uniform.
 template <bool BF16>
-sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, float c, void* ws, hipStream_t st,
+sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, const Expo& c, void* ws, hipStream_t st,
                       const int32_t* ids = nullptr, QSrc q = QSrc{}, int gamma = 0, float2* gath = nullptr,
                       bool timed = true, const int32_t* cu = nullptr, int32_t n_live = 0) {
   RowPassArgs a;
@@ -242,7 +254,8 @@ sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, floa
   a.rows_per_req = p.rows_per_req;
   a.G1 = G1;
   a.nchunks = p.nchunks;
-  a.c = c;
+  a.c = c.c;
+  a.cl = c.cl;
   a.nw = p.nw;
   a.cap_out = p.cap_out;
   a.out = ws_at<ChunkOut>(ws, p.off_cout);
@@ -276,7 +289,7 @@ void set_kernel_attrs() {
 
 template <bool BF16>
 sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int G1,
-                       int gamma, float c, sv_sampling_params prm, void* ws, hipStream_t st,
+                       int gamma, const Expo& c, sv_sampling_params prm, void* ws, hipStream_t st,
                        const int32_t* cu = nullptr, int32_t n_live = 0) {
   RowFinalArgs a;
   a.cu = cu;
@@ -294,7 +307,9 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const i
   a.fast = p.fast ? 1 : 0;
   a.top_k = prm.top_k;
   a.top_p = prm.top_p;
-  a.c = c;
+  a.c = c.c;
+  a.cl = c.cl;
+  a.c64 = c.c64;
   a.um = p.um;
   a.kmax = kKMax;
   a.scale_bits = p.scale_bits;
@@ -322,7 +337,7 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
 // lenient acceptance (the draft compared as beta * q).
 sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
                              const int32_t* draft_ids, const float* u_accept, const float* u_resample, int32_t B,
-                             int32_t gamma, int32_t V, sv_sampling_params prm, float c, int32_t* out_tokens,
+                             int32_t gamma, int32_t V, sv_sampling_params prm, const Expo& c, int32_t* out_tokens,
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
                              const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
                              double beta = 1.0, bool force_rowfinal = false) {
@@ -347,7 +362,9 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   ac.cout = ws_at<ChunkOut>(workspace, p.off_cout);
   ac.nchunks = p.nchunks;
   ac.logits = target_logits;
-  ac.c = c;
+  ac.c = c.c;
+  ac.cl = c.cl;
+  ac.c64 = c.c64;
   ac.gath = gath;
   ac.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
   ac.kmax = kKMax;
@@ -381,7 +398,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   bg.V = V;
   bg.G1 = G1;
   bg.nch4 = p.nch4;
-  bg.c = c;
+  bg.c64 = c.c64;
   bg.jobs = ac.jobs;
   bg.partials = ws_at<double>(workspace, p.off_part);
   bg.out_tokens = out_tokens;
@@ -433,7 +450,7 @@ struct StatsOut {
 // The statistics kernels over target rows 0..gamma-1 whose row results sit
 // in plan p's info / kept regions at rows b * info_rpr + j.
 sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const QSrc& q, const StatsOut& so,
-                       const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, float c, int info_rpr,
+                       const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, const Expo& c, int info_rpr,
                        void* workspace, hipStream_t st) {
   StatsArgs a;
   a.logits = target_logits;
@@ -448,7 +465,7 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   const bool lists = p.trunc && (q.dense == nullptr || so.z_qp == nullptr);
   a.nchunks = lists ? 1 : p.nchunks;
   a.chunk = lists ? (int64_t)V : p.chunk;
-  a.c = c;
+  a.c64 = c.c64;
   a.info = ws_at<RowInfo>(workspace, p.off_info);
   a.kept = p.trunc ? ws_at<Cand>(workspace, p.off_kept) : nullptr;
   a.info_rpr = info_rpr;
@@ -480,7 +497,7 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
 // target's rows 0..gamma-1, plan CALL_STATS).
 sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q, const StatsOut& so,
                             const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
-                            float c, void* workspace, hipStream_t st) {
+                            const Expo& c, void* workspace, hipStream_t st) {
   const bool bf = dt == SV_BF16;
   const int G1 = gamma + 1;
   sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
@@ -498,7 +515,7 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
 // A ragged batch (cu != null) packs its n_draft draft rows: plan row r is
 // packed row r, the draft position the target's kernels read q at.
 sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* draft_ids, int32_t B, int32_t gamma,
-                         int32_t V, sv_sampling_params prm, float c, void* ws, hipStream_t st, QSrc* q_out,
+                         int32_t V, sv_sampling_params prm, const Expo& c, void* ws, hipStream_t st, QSrc* q_out,
                          const Cand** qkept_out, const int32_t* cu = nullptr, int32_t n_draft = 0) {
   const Plan pq = make_plan(CALL_DRAFT, B, gamma, V, ddt, prm);
   const bool bf = ddt == SV_BF16;
@@ -517,7 +534,9 @@ sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* 
   q.z = draft_logits;
   q.info = ws_at<RowInfo>(ws, pq.off_info);
   q.V = V;
-  q.c = c;
+  q.c = c.c;
+  q.cl = c.cl;
+  q.c64 = c.c64;
   q.zbf16 = bf ? 1 : 0;
   *q_out = q;
   *qkept_out = pq.trunc ? ws_at<Cand>(ws, pq.off_kept) : nullptr;
@@ -536,7 +555,7 @@ size_t draft_ws_offset(CallKind kind, int32_t B, int32_t gamma, int32_t V, sv_dt
 sv_status verify_sample_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q,
                                    const StatsOut& so, const int32_t* draft_ids, const float* u_accept,
                                    const float* u_resample, int32_t B, int32_t gamma, int32_t V,
-                                   sv_sampling_params prm, float c, int32_t* out_tokens, int32_t* out_num_accepted,
+                                   sv_sampling_params prm, const Expo& c, int32_t* out_tokens, int32_t* out_num_accepted,
                                    uint32_t* out_row_flags, void* workspace, hipStream_t st) {
   sv_status s = verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
                                    out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0,
@@ -555,10 +574,10 @@ sv_status verify_greedy_impl(const void* target_logits, sv_dtype dt, const int32
   if (workspace == nullptr || workspace_bytes < p.total || !aligned16(workspace)) return SV_ERR_WORKSPACE;
   const bool bf = dt == SV_BF16;
   sv_status s =
-      bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
-                             true, cu, n_draft + B)
-         : run_rowpass<false>(p, target_logits, V, gamma + 1, 1.0f, workspace, st, nullptr, QSrc{}, gamma, nullptr,
-                              true, cu, n_draft + B);
+      bf ? run_rowpass<true>(p, target_logits, V, gamma + 1, kExpoGreedy, workspace, st, nullptr, QSrc{}, gamma,
+                             nullptr, true, cu, n_draft + B)
+         : run_rowpass<false>(p, target_logits, V, gamma + 1, kExpoGreedy, workspace, st, nullptr, QSrc{}, gamma,
+                              nullptr, true, cu, n_draft + B);
   if (s != SV_OK) return s;
   GreedyArgs g;
   g.cout = ws_at<ChunkOut>(workspace, p.off_cout);
@@ -591,7 +610,7 @@ sv_status ragged_checks(const int32_t* cu, int32_t n_draft, int32_t B, int32_t g
 extern "C" {
 
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
-  float c;
+  Expo c;
   if (check_sizes(B, gamma, V, dt) != SV_OK || check_params(prm, &c) != SV_OK) return 0;
   size_t a = make_plan(CALL_SAMPLE_STATS, B, gamma, V, dt, prm).total;  // covers CALL_SAMPLE
   size_t g = make_plan(CALL_GREEDY, B, gamma, V, dt, prm).total;
@@ -606,7 +625,7 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
                              size_t workspace_bytes, void* stream) {
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -628,7 +647,7 @@ sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const
                                    size_t workspace_bytes, void* stream) {
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -662,7 +681,7 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
                             float* out_accept_prob, void* workspace, size_t workspace_bytes, void* stream) {
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0 || gamma == 0) return SV_OK;
@@ -677,7 +696,7 @@ sv_status spec_accept_stats(const void* target_logits, sv_dtype dt, const float*
 
 size_t spec_verify_draft_logits_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_dtype draft_dt,
                                                sv_sampling_params prm) {
-  float c;
+  Expo c;
   if (check_sizes(B, gamma, V, dt) != SV_OK || check_sizes(B, gamma, V, draft_dt) != SV_OK ||
       check_params(prm, &c) != SV_OK)
     return 0;
@@ -696,7 +715,7 @@ sv_status spec_verify_sample_draft_logits(const void* target_logits, sv_dtype dt
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
   if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -727,7 +746,7 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
   if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0 || gamma == 0) return SV_OK;
@@ -756,7 +775,7 @@ sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dt
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
   if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -788,7 +807,7 @@ sv_status spec_verify_sample_lenient(const void* target_logits, sv_dtype dt, con
   if (!(lenience > 0.0f && lenience <= 1.0f)) return SV_ERR_INVALID_ARG;
   sv_status s = common_checks(target_logits, dt, B, gamma, V);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -813,7 +832,7 @@ sv_status spec_verify_sample_ragged(const void* target_logits, sv_dtype dt, cons
   if (s != SV_OK) return s;
   s = ragged_checks(cu_draft, n_draft, B, gamma_max, V, eos_id);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;
@@ -841,7 +860,7 @@ sv_status spec_verify_sample_ragged_draft_logits(const void* target_logits, sv_d
   if (draft_dt != SV_F32 && draft_dt != SV_BF16) return SV_ERR_INVALID_ARG;
   s = ragged_checks(cu_draft, n_draft, B, gamma_max, V, eos_id);
   if (s != SV_OK) return s;
-  float c;
+  Expo c;
   s = check_params(prm, &c);
   if (s != SV_OK) return s;
   if (B == 0) return SV_OK;

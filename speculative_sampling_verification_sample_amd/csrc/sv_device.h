@@ -1,15 +1,26 @@
 // Device-side building blocks of the verify-step kernels (gfx950, wave64).
 //
-// Arithmetic shared by every kernel (so that a value computed in two kernels
-// is bit-identical):
-//   c      = log2(e) / T                     (float, computed once on the host)
-//   R      = ceilf(xmax * c)                 (integral float, per row)
-//   e(x)   = exp2(fma(x, c, -R))             (float; p(x) = e(x) / S)
-//   S      = sum of e over the kept set      (double)
-// p(x) = exp((x - xmax) / T) / sum(...) is the temperature softmax of
-// [WR] §7.2; any reference R >= max(x * c) gives the same p, and an integral R
-// lets partial sums taken against different references be merged exactly
-// with ldexp.
+// Exponentials.  p(x) = exp((x - xmax) / T) / sum(...) is the temperature
+// softmax of [WR] §7.2; any reference R >= max(x * log2(e) / T) gives the
+// same p, and an integral R lets partial sums taken against different
+// references be merged exactly with ldexp.  Three forms of one exponential
+// are used, each where its accuracy is enough (so that a value computed in
+// two kernels is bit-identical, a kernel always uses the form its
+// consumers use):
+//   c, cl  = log2(e) / T as a float and the float of the remainder
+//            (computed once on the host from the double c64)
+//   R      = ceilf(xmax * c)                     (integral float, per row)
+//   e(x)   = exp2(fma(x, c, -R))                 (float: the truncated rows'
+//            streaming pass, top-p masses)
+//   e2(x)  = exp2(fma(x, cl, fma(x, c, -R)))     (float with the two-part c:
+//            the untruncated rows' sums S and their acceptance test)
+//   e64(x) = exp2(x * c64 - R)                   (double: the kept sets' sums
+//            S64, every draw and every statistic)
+// The float forms carry a relative error of a few 1e-7 per term, which is
+// harmless to decisions compared against a uniform (acceptance, top-p
+// cut) but not to a residual (p - q)+ whose total may be small, nor to
+// statistics asked for to 1e-5 relative; those use e64 against S64, the
+// double sum of e64 over the kept set.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,20 +59,24 @@ struct alignas(8) Cand {
 
 // Per row result of the finalisation (kept set and draft gather).
 struct alignas(16) RowInfo {
-  double S;        // normaliser of p over the kept set, reference R
+  double S;        // normaliser of the float exponentials over the kept set
+                   // (e2 on untruncated rows, e on truncated ones), reference R
+  double S64;      // sum of e64 over the kept set; 0 when not known (untruncated
+                   // rows: the passes that need it sum it themselves)
   float R;         // integral reference
   float tau;       // kept set = {x : z(x) >= tau}; kLowest keeps every finite x
   int32_t nkept;   // length of the stored kept list, -1 for RF_BIG rows
   uint32_t flags;  // RF_*
-  float ed;        // e(d) of this row's draft (0 if not kept / bad id / no draft)
+  float ed;        // e2(d) of this row's draft (0 if not kept / bad id / no draft)
   float qd;        // q(d) of this row's draft
   int32_t d;       // draft id; -1 for the bonus row; -2 for an id outside [0, V)
-  int32_t pad;
+  float zd;        // the draft's logit z(d) (when d >= 0)
 };
 
 // A request whose token must be drawn by the full-row sampler.
 struct alignas(16) BigJob {
-  double S;
+  double S;          // normaliser of the float exponentials (classification only)
+  double S64;        // sum of e64 over the kept set, 0 when not known
   float R;
   float tau;
   float u;
@@ -152,8 +167,40 @@ __device__ __forceinline__ void widen(const uint4& w, float* x) {
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// e(x) relative to the integral reference R.
+// The three exponentials against the integral reference R (see the top of
+// this file).
 __device__ __forceinline__ float e_of(float x, float c, float R) { return ex2(__builtin_fmaf(x, c, -R)); }
+__device__ __forceinline__ float e2_of(float x, float c, float cl, float R) {
+  return ex2(__builtin_fmaf(x, cl, __builtin_fmaf(x, c, -R)));
+}
+// 2^t in double for t <= ~2: 2^n e^g with n = rint(t), g = (t - n) ln 2,
+// |g| <= 0.347, and e^g by its Taylor series through g^13 (the first term
+// left out is below 1e-17), evaluated by Horner's rule with the
+// coefficients as scalar operands (no vector registers held for them).
+// Below t = -1074 the result is 0.
+__device__ __forceinline__ double exp2_d(double t) {
+  const double n = __builtin_rint(t);
+  const double g = (t - n) * 0.6931471805599453094;
+  double p = 1.0 / 6227020800.0;              // 1/13!
+  p = __builtin_fma(p, g, 1.0 / 479001600.0);  // 1/12!
+  p = __builtin_fma(p, g, 1.0 / 39916800.0);
+  p = __builtin_fma(p, g, 1.0 / 3628800.0);
+  p = __builtin_fma(p, g, 1.0 / 362880.0);
+  p = __builtin_fma(p, g, 1.0 / 40320.0);
+  p = __builtin_fma(p, g, 1.0 / 5040.0);
+  p = __builtin_fma(p, g, 1.0 / 720.0);
+  p = __builtin_fma(p, g, 1.0 / 120.0);
+  p = __builtin_fma(p, g, 1.0 / 24.0);
+  p = __builtin_fma(p, g, 1.0 / 6.0);
+  p = __builtin_fma(p, g, 0.5);
+  p = __builtin_fma(p, g, 1.0);
+  p = __builtin_fma(p, g, 1.0);
+  const double nc = __builtin_fmax(n, -2000.0);  // keeps the int conversion in range
+  return __builtin_ldexp(p, (int)nc);
+}
+__device__ __forceinline__ double e64_of(float x, double c64, float R) {
+  return exp2_d(__builtin_fma((double)x, c64, -(double)R));
+}
 
 template <bool BF16>
 __device__ __forceinline__ float load_logit(const void* p, int64_t i) {
@@ -170,7 +217,7 @@ __device__ __forceinline__ float load_logit(const void* p, int64_t i) {
 // or the draft's logits [B * gamma][V] processed by the same rules as the
 // target's ([WR] §2.3: p and q are both the distributions after the decoding
 // rules): q_j(x) = e_j(z(x)) / S_j on the draft row's kept set {z >= tau_j},
-// 0 elsewhere, from that row's statistics (S, R, tau) found by the same
+// 0 elsewhere, from that row's statistics (S, S64, R, tau) found by the same
 // row passes.  A draft row without usable statistics (NaN / +Inf logits, or
 // all -Inf) gives q = NaN.
 struct QSrc {
@@ -178,92 +225,125 @@ struct QSrc {
   const void* z;        // draft logits when dense is null; both null: no q (reads give 0)
   const RowInfo* info;  // statistics of the draft rows (with z)
   int64_t V;
-  float c;              // log2(e) / T, shared with the target
+  float c, cl;          // log2(e) / T in two floats, shared with the target
+  double c64;           // log2(e) / T
   int32_t zbf16;        // the draft logits are bfloat16
 };
 
-// One q row.
+// One q row.  Values are read "raw" (the dense q, or the draft's logit) and
+// turned into q by the accessor the caller's precision asks for.
 struct QRow {
   const float* dense;  // start of the dense row, or null
   const void* z;
   int64_t zoff;        // element offset of the row in z
-  double invS;
-  float R, tau, c;
+  double invS;         // 1 / S (float exponentials)
+  double invS64;       // 1 / S64, 0 when S64 is not known (untruncated draft rows)
+  double c64;
+  float R, tau, c, cl;
   int32_t zbf16;
   int32_t bad;         // unusable draft row: q is NaN
 
+  __device__ __forceinline__ bool logits_src() const { return dense == nullptr && z != nullptr; }
+
+  // q of a draft logit as a float (the acceptance test's q(d)): e64 / S64
+  // where S64 is known, else the float exponential that S sums.
   __device__ __forceinline__ float from_logit(float zz) const {
     if (bad) return __builtin_nanf("");
-    return zz >= tau ? (float)((double)e_of(zz, c, R) * invS) : 0.0f;
+    if (!(zz >= tau)) return 0.0f;
+    if (invS64 > 0.0) return (float)(e64_of(zz, c64, R) * invS64);
+    return (float)((double)e2_of(zz, c, cl, R) * invS);
+  }
+  // q in double from a raw value (needs S64 for draft logits).
+  __device__ __forceinline__ double q64(float v) const {
+    if (dense) return (double)v;
+    if (z == nullptr) return 0.0;
+    if (bad) return __builtin_nan("");
+    return v >= tau ? e64_of(v, c64, R) * invS64 : 0.0;
+  }
+  // The unnormalised double weight of a raw value: q itself for a dense
+  // row, e64 of the logit for draft logits (whose normaliser the caller
+  // sums itself).
+  __device__ __forceinline__ double e64raw(float v) const {
+    if (dense) return (double)v;
+    if (z == nullptr) return 0.0;
+    if (bad) return __builtin_nan("");
+    return v >= tau ? e64_of(v, c64, R) : 0.0;
+  }
+  // An approximation of q from e64raw(v), good to a few 1e-7: enough to
+  // tell on which side of p a term lies (the exact sums come from e64raw).
+  __device__ __forceinline__ double approx(double e64r) const { return logits_src() ? e64r * invS : e64r; }
+
+  __device__ __forceinline__ float raw_at(int64_t x) const {
+    if (dense) return dense[x];
+    if (z == nullptr) return 0.0f;
+    return zbf16 ? load_logit<true>(z, zoff + x) : load_logit<false>(z, zoff + x);
   }
   __device__ __forceinline__ float at(int64_t x) const {
     if (dense) return dense[x];
     if (z == nullptr) return 0.0f;
-    return from_logit(zbf16 ? load_logit<true>(z, zoff + x) : load_logit<false>(z, zoff + x));
+    return from_logit(raw_at(x));
   }
-  // q at x0 .. x0+7 of a whole segment whose 16-byte loads the caller knows
-  // to be aligned (dense rows: row * V + x0 a multiple of 4; logits: of 8
-  // for bf16, 4 for fp32).  Straight-line code, so that a caller's unrolled
-  // loop keeps several segments' loads in flight.
-  __device__ __forceinline__ void dense8(int64_t x0, float* qv) const {
-    const uint4* p = reinterpret_cast<const uint4*>(dense + x0);
-    widen<false>(p[0], qv);
-    widen<false>(p[1], qv + 4);
-  }
-  __device__ __forceinline__ void logits8(int64_t x0, float* qv) const {
+  __device__ __forceinline__ double at64(int64_t x) const { return q64(raw_at(x)); }
+
+  // Raw values at x0 .. x0+7 of a whole segment whose 16-byte loads the
+  // caller knows to be aligned (dense rows: row * V + x0 a multiple of 4;
+  // logits: of 8 for bf16, 4 for fp32).  Straight-line code, so that a
+  // caller's unrolled loop keeps several segments' loads in flight.
+  __device__ __forceinline__ void raw8_whole(int64_t x0, float* v) const {
+    if (dense) {
+      const uint4* p = reinterpret_cast<const uint4*>(dense + x0);
+      widen<false>(p[0], v);
+      widen<false>(p[1], v + 4);
+      return;
+    }
     const int64_t o = zoff + x0;
-    float zz[8];
     if (zbf16) {
-      widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], zz);
+      widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], v);
     } else {
       const uint4* p = reinterpret_cast<const uint4*>(z) + (o >> 2);
-      widen<false>(p[0], zz);
-      widen<false>(p[1], zz + 4);
+      widen<false>(p[0], v);
+      widen<false>(p[1], v + 4);
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = from_logit(zz[k]);
   }
-  // q at x0 .. x0+7 (0 past V); 16-byte loads where the segment is whole and
-  // aligned.
-  __device__ __forceinline__ void seg8(int64_t x0, int64_t V, float* qv) const {
+  // Raw values at x0 .. x0+7 past which (>= V) a dense row reads 0 and draft
+  // logits -inf (both: q = 0); 16-byte loads where the segment is whole and
+  // aligned.  A row view without q reads 0.
+  __device__ __forceinline__ void raw8(int64_t x0, int64_t V, float* v) const {
     const bool full = x0 + 8 <= V;
     if (dense) {
       const float* p = dense + x0;
       if (full && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-        widen<false>(reinterpret_cast<const uint4*>(p)[0], qv);
-        widen<false>(reinterpret_cast<const uint4*>(p)[1], qv + 4);
+        widen<false>(reinterpret_cast<const uint4*>(p)[0], v);
+        widen<false>(reinterpret_cast<const uint4*>(p)[1], v + 4);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qv[k] = (x0 + k < V) ? p[k] : 0.0f;
+        for (int k = 0; k < 8; ++k) v[k] = (x0 + k < V) ? p[k] : 0.0f;
       }
       return;
     }
     if (z == nullptr) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) qv[k] = 0.0f;
+      for (int k = 0; k < 8; ++k) v[k] = 0.0f;
       return;
     }
     const int64_t o = zoff + x0;
-    float zz[8];
     if (zbf16) {
       if (full && (o & 7) == 0) {
-        widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], zz);
+        widen<true>(reinterpret_cast<const uint4*>(z)[o >> 3], v);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) zz[k] = (x0 + k < V) ? load_logit<true>(z, o + k) : kNegInf;
+        for (int k = 0; k < 8; ++k) v[k] = (x0 + k < V) ? load_logit<true>(z, o + k) : kNegInf;
       }
     } else {
       if (full && (o & 3) == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(z) + (o >> 2);
-        widen<false>(p[0], zz);
-        widen<false>(p[1], zz + 4);
+        widen<false>(p[0], v);
+        widen<false>(p[1], v + 4);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) zz[k] = (x0 + k < V) ? load_logit<false>(z, o + k) : kNegInf;
+        for (int k = 0; k < 8; ++k) v[k] = (x0 + k < V) ? load_logit<false>(z, o + k) : kNegInf;
       }
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = (x0 + k < V) ? from_logit(zz[k]) : 0.0f;
   }
 };
 
@@ -273,8 +353,11 @@ __device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
   r.z = s.dense ? nullptr : s.z;
   r.zoff = row * s.V;
   r.c = s.c;
+  r.cl = s.cl;
+  r.c64 = s.c64;
   r.zbf16 = s.zbf16;
   r.invS = 0.0;
+  r.invS64 = 0.0;
   r.R = 0.0f;
   r.tau = kLowest;
   r.bad = 0;
@@ -282,6 +365,7 @@ __device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
     const RowInfo ri = s.info[row];
     r.bad = (ri.flags & RF_NONFINITE) ? 1 : 0;
     r.invS = 1.0 / ri.S;
+    r.invS64 = ri.S64 > 0.0 ? 1.0 / ri.S64 : 0.0;
     r.R = ri.R;
     r.tau = ri.tau;
   }
@@ -295,9 +379,12 @@ __device__ __forceinline__ QRow q_none() {
   r.z = nullptr;
   r.zoff = 0;
   r.invS = 0.0;
+  r.invS64 = 0.0;
+  r.c64 = 0.0;
   r.R = 0.0f;
   r.tau = kLowest;
   r.c = 0.0f;
+  r.cl = 0.0f;
   r.zbf16 = 0;
   r.bad = 0;
   return r;

@@ -10,8 +10,9 @@
 //   top-p : keep the most probable tokens until their mass reaches
 //           top_p * S (on the top-k set when both are active), plus ties
 //           (masses as 2^40 fixed point, so sums are exact and order-free).
-// The kept set is stored as a list in token-id order (for the inverse CDF)
-// together with S over it.  It also reads this row's draft logit and q(d) so
+// The kept set is stored as a list of (logit, id) in token-id order (for the
+// inverse CDF) together with S over it and S64, the double sum of its e64
+// (the normaliser of the draws and the statistics).  It also reads this row's draft logit and q(d) so
 // the acceptance test needs no further pass ([WR] §6).
 #pragma once
 
@@ -38,24 +39,29 @@ struct RowFinalArgs {
   int32_t top_k;        // active when 0 < top_k < V
   float top_p;          // active when < 1
   float c;
+  float cl;             // low part of log2(e) / T (untruncated rows' e2)
+  double c64;           // log2(e) / T (e64)
   int32_t um;           // LDS capacity (power of two) for the candidate union
   int32_t kmax;         // capacity of a stored kept list
   int32_t scale_bits;   // fixed-point bits of the exact path's mass histogram
   const ChunkOut* cout;
   const Cand* cand;
   RowInfo* info;        // [rows]
-  Cand* kept;           // [rows][kmax]  (v = e(x), idx = token id), id order
+  Cand* kept;           // [rows][kmax]  (v = z(x), the logit; idx = token id), id order
 };
 
 // Draft gather for a row whose kept set and normaliser are final: the
-// draft's logit and q(d) (acceptance needs e(d), q(d) and S only).  dpos is
-// the row's draft position, < 0 for a row without a draft (the bonus row).
+// draft's logit, its float exponential and q(d) (the acceptance test needs
+// them with S, or with S64).  dpos is the row's draft position, < 0 for a
+// row without a draft (the bonus row).  cl: the low part of c on
+// untruncated rows (their S sums e2), 0 on truncated ones (S sums e).
 template <bool BF16>
 __device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V,
-                                                float c, int64_t dpos, int64_t rowoff, RowInfo& ri) {
+                                                float c, float cl, int64_t dpos, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
+  ri.zd = 0.0f;
   if (dpos < 0) return;
   int d = ids[dpos];
   if (d < 0 || (int64_t)d >= V) {
@@ -64,13 +70,14 @@ __device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& 
   }
   ri.d = d;
   float z = load_logit<BF16>(logits, rowoff + d);
-  ri.ed = (z >= ri.tau) ? e_of(z, c, ri.R) : 0.0f;
+  ri.zd = z;
+  ri.ed = (z >= ri.tau) ? e2_of(z, c, cl, ri.R) : 0.0f;
   ri.qd = q_at(q, dpos, d);
 }
 
 template <bool BF16>
 __device__ __forceinline__ void gather_draft(const RowFinalArgs& a, int64_t dpos, int64_t rowoff, RowInfo& ri) {
-  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, dpos, rowoff, ri);
+  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.trunc ? 0.0f : a.cl, dpos, rowoff, ri);
 }
 
 
@@ -114,8 +121,8 @@ __device__ inline bool merge_nonfinite(const RowMerge& m) {
 // draft's logit and q(d) come from the row pass's gather (gath[grow], the
 // plan row) when `gath` is set.
 template <bool BF16>
-__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, const void* logits, const QSrc& q,
-                                    const int32_t* ids, int64_t V, int64_t dpos, int64_t rowoff,
+__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, float cl, const void* logits,
+                                    const QSrc& q, const int32_t* ids, int64_t V, int64_t dpos, int64_t rowoff,
                                     const float2* gath = nullptr, int64_t grow = 0) {
   // the draft's id and gathered (z(d), q(d)) do not depend on the merge:
   // their loads go out first, with the chunk results'
@@ -128,6 +135,7 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
   RowMerge m = merge_chunks(co, nchunks, c);
   RowInfo ri;
   ri.S = m.S;
+  ri.S64 = 0.0;
   ri.R = m.R;
   ri.tau = kLowest;
   ri.nkept = -1;
@@ -135,7 +143,7 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
-  ri.pad = 0;
+  ri.zd = 0.0f;
   if (merge_nonfinite(m)) {
     ri.flags = RF_NONFINITE;
     return ri;
@@ -147,13 +155,14 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, co
         ri.d = -2;
       } else {
         ri.d = d;
-        ri.ed = (g.x >= ri.tau) ? e_of(g.x, c, ri.R) : 0.0f;
+        ri.zd = g.x;
+        ri.ed = (g.x >= ri.tau) ? e2_of(g.x, c, cl, ri.R) : 0.0f;
         ri.qd = g.y;
       }
     }
     return ri;
   }
-  gather_draft_at<BF16>(logits, q, ids, V, c, dpos, rowoff, ri);
+  gather_draft_at<BF16>(logits, q, ids, V, c, cl, dpos, rowoff, ri);
   return ri;
 }
 
@@ -552,7 +561,19 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
     }
     part += (double)f;
   });
-  const double S = block_sum_d<BF16>(part, s_tmp);  // fixed segments and order: deterministic
+  // S64 in a pass of its own, one token at a time (its double exponentials
+  // would otherwise raise the register count of the whole row finisher)
+  double part64 = 0.0;
+  if (cntp > 0) {
+    const double c64 = a.c64;
+    for (int64_t x = sx0; x < sx1; ++x) {
+      const float zx = load_logit<BF16>(lg, rowoff + x);
+      if (zx >= tau) part64 += e64_of(zx, c64, R);
+    }
+  }
+  // fixed segments and order: deterministic
+  const double S = block_sum_d<BF16>(part, s_tmp);
+  const double S64 = block_sum_d<BF16>(part64, s_tmp);
   const int incl = wave_incl_scan_i(cntp);
   if (lane == kWave - 1) s_cnt[wid] = incl;
   __syncthreads();
@@ -562,6 +583,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
   __syncthreads();
   ri.tau = tau;
   ri.S = S;
+  ri.S64 = S64;
   ri.flags = 0;
   if (nkept > a.kmax) {
     ri.flags = RF_BIG;
@@ -576,7 +598,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
           if (zs[e] >= tau) {
             Cand ce;
             ce.idx = (int32_t)(x + e);
-            ce.v = e_of(zs[e], c, R);
+            ce.v = zs[e];
             out[pos++] = ce;
           }
         }
@@ -591,7 +613,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArgs a) {
+__global__ void __launch_bounds__(256, BF16 ? 6 : 1) rowfinal_kernel(RowFinalArgs a) {
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const RowAt at = row_at(a.cu, a.n_live, a.rows_per_req, a.G1, a.gamma, a.V, r);
@@ -680,6 +702,7 @@ __global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArg
   __syncthreads();
   RowInfo ri;
   ri.S = s_S;
+  ri.S64 = 0.0;
   ri.R = s_R;
   ri.tau = kLowest;
   ri.nkept = -1;
@@ -687,7 +710,7 @@ __global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArg
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
-  ri.pad = 0;
+  ri.zd = 0.0f;
   const uint32_t fl = s_fl;
   if ((fl & (CF_NAN | CF_POSINF)) || !(s_xm > kNegInf) || !(fabsf(s_R) < kPosInf) || (s_S != s_S)) {
     if (tid == 0) {
@@ -795,10 +818,13 @@ __global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArg
   ri.tau = key2f(kfinal);
   if (kfinal == 0) ri.tau = kLowest;
   // ---- kept list in token-id order: compact the kept entries (in any
-  //      order) in place over the union (ids over the keys, e over the
-  //      ids), then store each at its rank by id (ids are unique within a
-  //      row).  Each block of 256 entries is read before any of its slots is
-  //      written; earlier blocks only write slots below the current one. ----
+  //      order) in place over the union (ids over the keys, logits over
+  //      the ids), then store each at its rank by id (ids are unique within
+  //      a row).  Each block of 256 entries is read before any of its slots
+  //      is written; earlier blocks only write slots below the current one.
+  //      S64 sums the entries' e64 as 2^51 fixed point (the union holds at
+  //      most 2048 entries, each e64 <= ~1), so the sum does not depend on
+  //      the order of the additions. ----
   if (tid == 0) s_n = 0;
   __syncthreads();
   int32_t* kid = reinterpret_cast<int32_t*>(keys);
@@ -812,11 +838,15 @@ __global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArg
     const int pos = wave_append_slot(keep, &s_n);
     if (keep) {
       kid[pos] = id;
-      kev[pos] = e_of(key2f(k), a.c, R);
+      kev[pos] = key2f(k);
     }
   }
   __syncthreads();
   const int nkept = s_n;
+  unsigned long long s64fx = 0ull;
+  for (int i = tid; i < nkept; i += 256)
+    s64fx += (unsigned long long)rint(e64_of(kev[i], a.c64, R) * 2251799813685248.0);  // 2^51
+  const double S64 = (double)block_sum_u64(s64fx, s_u64) * (1.0 / 2251799813685248.0);
   if (nkept <= a.kmax) {
     Cand* out = a.kept + r * (int64_t)a.kmax;
     // kid sits at the start of the dynamic LDS (16-byte aligned): ids are
@@ -879,10 +909,12 @@ __global__ void __launch_bounds__(256, BF16 ? 8 : 1) rowfinal_kernel(RowFinalArg
         ri.d = -2;
       } else {
         ri.d = d;
+        ri.zd = s_gz;
         ri.ed = (s_gz >= ri.tau) ? e_of(s_gz, a.c, ri.R) : 0.0f;
         ri.qd = s_gq;
       }
     }
+    ri.S64 = S64;
     a.info[r] = ri;
   }
 }

@@ -42,6 +42,7 @@ struct RowPassArgs {
   int32_t G1;
   int32_t nchunks;
   float c;
+  float cl;            // low part of log2(e) / T (untruncated rows' sums)
   int32_t nw;          // chunk elements the candidate threshold must certify
   int32_t cap_out;     // capacity of one chunk's list
   ChunkOut* out;  // [rows][nchunks]
@@ -102,7 +103,8 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const RowPassArgs& a) {
 // in xmax before finish_flags()).
 constexpr float kRefLag = 16.0f;
 
-template <bool BF16, bool DO_S, bool TRACK_MAX = true>
+// TWO_PART: the sums take e2 (the two-part c, cl set by the caller), else e.
+template <bool BF16, bool DO_S, bool TRACK_MAX = true, bool TWO_PART = false>
 struct UnitAcc {
   static constexpr int EPV = BF16 ? 8 : 4;
   float xmax = kNegInf;
@@ -118,6 +120,7 @@ struct UnitAcc {
   float vt = kNegInf;
   uint32_t nan_words = 0;  // max of |bits| over whole units (per 16-bit half for bf16)
   uint32_t flags = 0;
+  float cl = 0.0f;  // low part of c (TWO_PART)
 
   // Widens a unit into x and returns its max.  rel is the chunk-relative
   // index of the unit's first element; with EDGE, elements outside [0, n)
@@ -162,7 +165,10 @@ struct UnitAcc {
       // a NaN logit turns s into NaN, which the row merge reports
       float ev[EPV];
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) ev[i] = e_of(x[i], c, Re);
+      for (int i = 0; i < EPV; ++i) {
+        if constexpr (TWO_PART) ev[i] = e2_of(x[i], c, cl, Re);
+        else ev[i] = e_of(x[i], c, Re);
+      }
       float t;
       if constexpr (EPV == 8) t = ((ev[0] + ev[1]) + (ev[2] + ev[3])) + ((ev[4] + ev[5]) + (ev[6] + ev[7]));
       else t = (ev[0] + ev[1]) + (ev[2] + ev[3]);
@@ -235,7 +241,10 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     }
   }
 
-  UnitAcc<BF16, DO_S, MODE != M_ARGMAX> acc;
+  // untruncated sums take the two-part c: the acceptance test compares
+  // against them directly
+  UnitAcc<BF16, DO_S, MODE != M_ARGMAX, true> acc;
+  acc.cl = a.cl;
   float bestv = kNegInf;  // running max (argmax mode)
   int aidx = 0x7fffffff;  // row index of this thread's first maximum
 

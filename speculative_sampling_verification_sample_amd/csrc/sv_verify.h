@@ -28,6 +28,8 @@ struct AcceptArgs {
   int32_t nchunks;
   const void* logits;
   float c;
+  float cl;             // low part of log2(e) / T (untruncated rows' e2)
+  double c64;           // log2(e) / T (e64)
   const Cand* kept;     // [rows][kmax]
   int32_t kmax;
   QSrc q;
@@ -47,17 +49,18 @@ struct AcceptArgs {
   double beta;          // lenience: the draft is compared as beta * q (1: lossless)
 };
 
-// Draw from the kept list of one row, stored in token-id order (called by a
-// whole wave).
-// residual: weights (e/S - qs q)_+ on the list (qs = beta); otherwise e/S.
+// Draw from the kept list of one row, stored in token-id order as (logit,
+// id) (called by a whole wave).
+// residual: weights (p - qs q)_+ on the list (qs = beta), with p = e64 / S64
+// and q in double; otherwise p.
 // The list is walked 64 entries at a time in id order (prefix sums by wave
 // scans, carried between steps); the loads of kDrawBlk steps (list entries,
 // then q at their ids) are issued together before their scans.
 constexpr int kDrawBlk = 4;
-__device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bool& residual, float u,
-                              uint32_t& fl, double qs) {
+__device__ int draw_from_list(const Cand* L, int n, double S64, float R, double c64, const QRow& qr,
+                              bool& residual, float u, uint32_t& fl, double qs) {
   const int lane = lane_id();
-  const double invS = 1.0 / S;
+  const double invS = 1.0 / S64;
   // weights of entries i0 + 64 k + lane, k < kDrawBlk (0 past the end)
   auto weights = [&](int i0, bool res, double (&w)[kDrawBlk], int (&id)[kDrawBlk]) {
     Cand e[kDrawBlk];
@@ -70,18 +73,20 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
     }
     float qv[kDrawBlk];
 #pragma unroll
-    for (int k = 0; k < kDrawBlk; ++k) qv[k] = (res && e[k].idx >= 0) ? qr.at(e[k].idx) : 0.0f;
+    for (int k = 0; k < kDrawBlk; ++k) qv[k] = (res && e[k].idx >= 0) ? qr.raw_at(e[k].idx) : 0.0f;
 #pragma unroll
     for (int k = 0; k < kDrawBlk; ++k) {
       id[k] = e[k].idx;
-      const double p = (double)e[k].v * invS;
       if (e[k].idx < 0) {
         w[k] = 0.0;
-      } else if (!res) {
-        w[k] = p;
       } else {
-        const double d = p - qs * (double)qv[k];
-        w[k] = d > 0.0 ? d : 0.0;
+        const double p = e64_of(e[k].v, c64, R) * invS;
+        if (!res) {
+          w[k] = p;
+        } else {
+          const double d = p - qs * qr.q64(qv[k]);
+          w[k] = d > 0.0 ? d : 0.0;
+        }
       }
     }
   };
@@ -133,7 +138,8 @@ __device__ int draw_from_list(const Cand* L, int n, double S, const QRow& qr, bo
   return token >= 0 ? token : lastpos;
 }
 
-// Logits (and q when residual) of tokens x .. x+7 of a row (-inf / 0 past V).
+// Logits (and q's raw values when residual) of tokens x .. x+7 of a row
+// (-inf / q = 0 past V).
 template <bool BF16>
 __device__ __forceinline__ void full_row_seg(const void* logits, const QRow& qr, int64_t rowoff, int64_t V, bool vec,
                                              int64_t x, bool res, float* z, float* qv) {
@@ -157,17 +163,18 @@ __device__ __forceinline__ void full_row_seg(const void* logits, const QRow& qr,
 #pragma unroll
     for (int k = 0; k < 8; ++k) z[k] = (x + k < V) ? load_logit<BF16>(logits, rowoff + x + k) : kNegInf;
   }
-  if (res) qr.seg8(x, V, qv);
+  if (res) qr.raw8(x, V, qv);
 }
 
-// Weight of one token: e(z) on the kept set {z >= tau}, or the residual
-// (e - qs q S)_+ there.
-__device__ __forceinline__ double full_row_weight(float z, float q, bool res, float c, float R, float tau, double S,
-                                                  double qs) {
+// Weight of one token of a row whose S64 is known: e64(z) on the kept set
+// {z >= tau}, or the residual (e64 / S64 - qs q)_+ there (q from its raw
+// value qraw, in double).
+__device__ __forceinline__ double full_row_weight(float z, float qraw, bool res, const QRow& qr, double c64, float R,
+                                                  float tau, double invS64, double qs) {
   if (!(z >= tau)) return 0.0;
-  const double e = (double)e_of(z, c, R);
+  const double e = e64_of(z, c64, R);
   if (!res) return e;
-  const double d = e - (qs * (double)q) * S;
+  const double d = e * invS64 - qs * qr.q64(qraw);
   return d > 0.0 ? d : 0.0;
 }
 
@@ -206,6 +213,7 @@ __device__ int block_first_or_last(int found, int lp, int* s_f, int* s_l) {
 __device__ __forceinline__ RowInfo shfl_info(const RowInfo& r, int src) {
   RowInfo o;
   o.S = __shfl(r.S, src, kWave);
+  o.S64 = __shfl(r.S64, src, kWave);
   o.R = __shfl(r.R, src, kWave);
   o.tau = __shfl(r.tau, src, kWave);
   o.nkept = __shfl(r.nkept, src, kWave);
@@ -213,8 +221,25 @@ __device__ __forceinline__ RowInfo shfl_info(const RowInfo& r, int src) {
   o.ed = __shfl(r.ed, src, kWave);
   o.qd = __shfl(r.qd, src, kWave);
   o.d = __shfl(r.d, src, kWave);
-  o.pad = 0;
+  o.zd = __shfl(r.zd, src, kWave);
   return o;
+}
+
+// Acceptance test of one draft ([WR] §4.1: accept iff u < p(d) / q(d); here
+// u < p(d) / (beta q(d)) with the lenience factor beta, 1 when lossless),
+// without a division.  Rows with a known S64 (truncated rows) compare
+// e64(d) with u beta q(d) S64 in double; untruncated rows compare e2(d)
+// with u beta q(d) S, both from the float exponentials of the row pass
+// (a relative error of a few 1e-7 on p(d) / q(d)).  q(d) = 0 accepts iff
+// p(d) > 0.
+__device__ __forceinline__ bool accept_test(const RowInfo& ri, float ua, double beta, double c64) {
+  if (ri.d < 0) return false;
+  if (ri.qd == 0.0f) return ri.zd >= ri.tau && e64_of(ri.zd, c64, ri.R) > 0.0;
+  if (ri.S64 > 0.0) {
+    const double e = ri.zd >= ri.tau ? e64_of(ri.zd, c64, ri.R) : 0.0;
+    return (double)ua * (beta * (double)ri.qd) * ri.S64 < e;
+  }
+  return (double)ua * (beta * (double)ri.qd) * ri.S < (double)ri.ed;
 }
 
 // Acceptance decision of one request (whole wave): the first rejection,
@@ -259,6 +284,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     if (lane == 0) {
       BigJob jb;
       jb.S = rs.S;
+      jb.S64 = rs.S64;
       jb.R = rs.R;
       jb.tau = rs.tau;
       jb.u = u;
@@ -274,7 +300,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     }
     return;
   }
-  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S, qr, residual, u, fl, a.beta);
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S64, rs.R, a.c64, qr, residual, u, fl, a.beta);
   if (lane == 0) {
     if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
     out[nacc] = token;
@@ -308,10 +334,11 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   ri.qd = 0.0f;
   ri.ed = 0.0f;
   ri.S = 1.0;
+  ri.S64 = 0.0;
   ri.R = 0.0f;
   ri.tau = kLowest;
   ri.nkept = -1;
-  ri.pad = 0;
+  ri.zd = 0.0f;
   Decision dc;
   dc.lo = sp.lo;
   dc.G = G;
@@ -331,12 +358,12 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
     const int64_t dpos = lane < G ? (int64_t)sp.lo + lane : -1;
     if constexpr (FROM_CHUNKS) {
       // ragged rows were not gathered by the row pass: gather here
-      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V, dpos,
+      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.cl, a.logits, a.q, a.ids, a.V, dpos,
                                   prow * a.V, a.cu != nullptr ? nullptr : a.gath, prow);
     } else {
       ri = a.info[prow];
       if (a.cu != nullptr && !(ri.flags & RF_NONFINITE))
-        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, dpos, prow * a.V, ri);
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.kept != nullptr ? 0.0f : a.cl, dpos, prow * a.V, ri);
     }
   }
   bool bad = (lane <= G) && ((ri.flags & RF_NONFINITE) ||
@@ -344,11 +371,7 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   dc.bad = ballot(bad) != 0;
   dc.badfl = 8u;  // SV_ROW_NONFINITE
   bool acc = true;
-  if (lane < G) {
-    if (ri.d < 0) acc = false;
-    else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
-    else acc = (double)ua * (a.beta * (double)ri.qd) * ri.S < (double)ri.ed;  // u < p / (beta q)
-  }
+  if (lane < G) acc = accept_test(ri, ua, a.beta, a.c64);
   uint64_t rej = ballot(!acc);
   dc.nacc = rej ? (int)__builtin_ctzll(rej) : G;
   if (a.eos >= 0) {
@@ -395,7 +418,7 @@ __device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
   if constexpr (FROM_CHUNKS) {
     for (int jj = lane; jj <= G; jj += kWave) {
       const int64_t prow = lo + b + jj;
-      inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.logits, a.q, a.ids, a.V,
+      inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.cl, a.logits, a.q, a.ids, a.V,
                                        jj < G ? lo + jj : -1, prow * a.V);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -405,7 +428,8 @@ __device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
     for (int jj = lane; jj <= G; jj += kWave) {
       RowInfo ri = inf[jj];
       if (!(ri.flags & RF_NONFINITE))
-        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, jj < G ? lo + jj : -1, (lo + b + jj) * a.V, ri);
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.kept != nullptr ? 0.0f : a.cl, jj < G ? lo + jj : -1,
+                              (lo + b + jj) * a.V, ri);
       inf[jj] = ri;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -425,12 +449,7 @@ __device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
   for (int j0 = 0; j0 < G; j0 += kWave) {
     const int jj = j0 + lane;
     bool acc = true;
-    if (jj < G) {
-      RowInfo ri = inf[jj];
-      if (ri.d < 0) acc = false;
-      else if (ri.qd == 0.0f) acc = ri.ed > 0.0f;
-      else acc = (double)a.ua[lo + jj] * (a.beta * (double)ri.qd) * ri.S < (double)ri.ed;
-    }
+    if (jj < G) acc = accept_test(inf[jj], a.ua[lo + jj], a.beta, a.c64);
     uint64_t rej = ballot(!acc);
     if (rej) {
       nacc = j0 + (int)__builtin_ctzll(rej);
@@ -483,7 +502,7 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
 // wave: each wave totals its quarter, and the wave whose quarter holds the
 // crossing of t = u * W finds the token (sums in a fixed order).
 template <bool BF16>
-__global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
+__global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.x;
   __shared__ double s_tot[4];
@@ -500,7 +519,7 @@ __global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
   constexpr int64_t kStep = 8 * kWave;
   const int64_t Lq = (V + 4 * kStep - 1) / (4 * kStep) * kStep;  // a quarter, whole steps
   const int64_t q0 = min((int64_t)wid * Lq, V), q1 = min(q0 + Lq, V);
-  const double S = jb.S;
+  const double invS64 = 1.0 / jb.S64;  // truncated rows always carry S64
   // this wave's quarter: its total (t < 0), or the search from `carry`
   struct QOut {
     double carry;
@@ -517,7 +536,7 @@ __global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
       int lastk = -1;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const double wk = full_row_weight(z[k], qv[k], res, a.c, jb.R, jb.tau, S, a.beta);
+        const double wk = full_row_weight(z[k], qv[k], res, qr, a.c64, jb.R, jb.tau, invS64, a.beta);
         seg += wk;
         if (wk > 0.0) lastk = k;
       }
@@ -534,7 +553,7 @@ __global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
             double run = ex;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              run = run + full_row_weight(z[k], qv[k], res, a.c, jb.R, jb.tau, S, a.beta);
+              run = run + full_row_weight(z[k], qv[k], res, qr, a.c64, jb.R, jb.tau, invS64, a.beta);
               if (found < 0 && run > t) found = x + k;
             }
             if (found < 0) found = x + lastk;  // rounding: the lane's last positive token
@@ -599,16 +618,29 @@ __global__ void __launch_bounds__(256) accept_trunc_kernel(AcceptArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K4: full-row draw, two launches.  big_partial_kernel (grid nch4 * B):
-// workgroup ci of request b weighs the 2048 tokens [2048 ci, 2048 ci + 2048)
-// of the sampled row (thread t owns 8 consecutive tokens, read with 16-byte
-// loads) and writes their total, reduced in a fixed order.
-// big_finish_kernel (grid B) walks the chunk totals, picks the chunk where
-// the running total first exceeds t = u * W, and recomputes that chunk with
-// the same arithmetic to find the token.  Workgroups never wait on or signal
-// each other inside a launch.
+// K4: full-row draws of untruncated rows.  Their S64 is not known (the row
+// pass sums float exponentials only), so one pass over the sampled row takes
+// four double sums per chunk:
+//   ea = sum of e64_p(x)                     (summed over chunks: S64 of p)
+//   eg = sum of e64_p(x) over x in G
+//   qa = sum of q's unnormalised weight w_q(x): e64_q(x) for q formed from
+//        the draft's logits (summed over chunks: S64 of q, Sq), the dense q
+//        itself otherwise (used as given, Sq = 1)
+//   qg = sum of w_q(x) over x in G
+// where G = {x : p(x) > beta q(x)} is told apart with the float
+// approximations of p and q (a term they could misplace differs from the
+// cut by a few 1e-7 of its p, so its residual weight is of that order).
+// A chunk's residual weight ([WR] §5: (p - q)_+) is eg / S64 - beta qg / Sq,
+// its weight under p is ea; the token is then located by a rescan of the
+// chunk holding the crossing of t = u * W, token by token with the same
+// arithmetic.
+// Two launches: big_partial_kernel (grid nch4 * B), workgroup ci of request
+// b sums the tokens [2048 ci, 2048 ci + 2048) (thread t owns 8 consecutive
+// tokens, 16-byte loads) in a fixed order; big_finish_kernel (grid B) forms
+// the chunk weights, walks them and rescans.  Workgroups never wait on or
+// signal each other inside a launch.
 // ---------------------------------------------------------------------------
-constexpr int kSeg = 8;  // tokens per thread segment (QRow::seg8)
+constexpr int kSeg = 8;  // tokens per thread segment
 constexpr int kChunk4 = 256 * kSeg;
 
 struct BigArgs {
@@ -617,23 +649,23 @@ struct BigArgs {
   int64_t V;
   int32_t G1;
   int32_t nch4;
-  float c;
+  double c64;
   const BigJob* jobs;
-  double* partials;  // [B][nch4]
+  double* partials;  // [B][nch4][4]: ea, eg, qa, qg
   int32_t* out_tokens;
   uint32_t* out_flags;
   int32_t eos;       // end-of-sequence id, < 0: none
   double beta;       // lenience (the residual is (p - beta q)_+)
 };
 
-// Weights of tokens x0 .. x0+7 of the job's row (0 past the end).
+// Raw logits and q values of tokens x0 .. x0+7 of the job's rows (-inf / q
+// = 0 past V; 16-byte loads when aligned).
 template <bool BF16>
-__device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0,
-                                            double* w) {
+__device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, const QRow& qr, bool residual, int64_t x0,
+                                         float* z, float* qv) {
   const int64_t V = a.V;
   const int64_t zo = (int64_t)jb.row * V + x0;
   const bool full = x0 + kSeg <= V;
-  float z[kSeg];
   if constexpr (BF16) {
     if (full && (zo & 7) == 0) {
       widen<true>(reinterpret_cast<const uint4*>(a.logits)[zo >> 3], z);
@@ -651,41 +683,53 @@ __device__ __forceinline__ void seg_weights(const BigArgs& a, const BigJob& jb, 
       for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
     }
   }
-  float qv[kSeg];
-  if (residual) {
-    if (a.q.dense != nullptr) {
-      const int64_t qo = (int64_t)jb.qrow * V + x0;
-      if (full && (qo & 3) == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.q.dense) + (qo >> 2);
-        widen<false>(p[0], qv);
-        widen<false>(p[1], qv + 4);
-      } else {
-#pragma unroll
-        for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q.dense[qo + k] : 0.0f;
-      }
-    } else {
-      q_row(a.q, jb.qrow).seg8(x0, V, qv);
-    }
-  }
+  if (residual) qr.raw8(x0, V, qv);
+}
+
+// Per token of a segment: ep = e64_p, eq = w_q (residual only) and whether
+// the token is in G.
+__device__ __forceinline__ void seg_terms(const BigJob& jb, const QRow& qr, bool residual, double c64, double beta,
+                                          const float* z, const float* qv, double* ep, double* eq, bool* gt) {
+  const double invS = 1.0 / jb.S;
 #pragma unroll
   for (int k = 0; k < kSeg; ++k) {
-    double wk = 0.0;
-    if (z[k] >= jb.tau) {
-      double e = (double)e_of(z[k], a.c, jb.R);
-      if (residual) {
-        double d = e - (a.beta * (double)qv[k]) * jb.S;
-        wk = d > 0.0 ? d : 0.0;
-      } else {
-        wk = e;
-      }
+    ep[k] = (z[k] >= jb.tau) ? e64_of(z[k], c64, jb.R) : 0.0;
+    eq[k] = 0.0;
+    gt[k] = false;
+    if (residual) {
+      eq[k] = qr.e64raw(qv[k]);
+      gt[k] = ep[k] * invS > beta * qr.approx(eq[k]);
     }
-    w[k] = wk;
   }
 }
 
-// Chunk total (thread segments summed left to right, then a fixed-order
-// block reduction); also returns this thread's exclusive prefix.
-__device__ __forceinline__ double chunk_reduce(double seg, double& excl, double* s_w) {
+// Weight of one token once the normalisers are known: the residual
+// p - beta q on G (0 elsewhere), else e64_p.
+__device__ __forceinline__ double term_weight(bool residual, double ep, double eq, bool gt, double invSp, double invSq,
+                                              double beta) {
+  if (!residual) return ep;
+  return gt ? ep * invSp - beta * (eq * invSq) : 0.0;
+}
+
+// Sum of four values over a 256-thread workgroup in a fixed order; the
+// totals land in s_out[0..3] (visible after the call's last barrier).
+__device__ __forceinline__ void block_sum4(const double (&v)[4], double (*s_w)[4], double* s_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = wave_sum_d(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_w[wid][i] = r[i];
+  }
+  __syncthreads();
+  if (tid < 4) s_out[tid] = ((s_w[0][tid] + s_w[1][tid]) + s_w[2][tid]) + s_w[3][tid];
+  __syncthreads();
+}
+
+// Exclusive prefix of this thread's segment total within the chunk (threads
+// in order), fixed order.
+__device__ __forceinline__ double chunk_excl(double seg, double* s_w) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double incl = wave_incl_scan_d(seg);
   double ex = __shfl_up(incl, 1, kWave);
@@ -695,30 +739,19 @@ __device__ __forceinline__ double chunk_reduce(double seg, double& excl, double*
   __syncthreads();
   double off = 0.0;
   for (int k = 0; k < wid; ++k) off += s_w[k];
-  excl = off + ex;
-  return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
-}
-
-template <bool BF16>
-__device__ __forceinline__ double chunk_weights(const BigArgs& a, const BigJob& jb, bool residual, int ci,
-                                                double* w, double& seg, double& excl, double* s_w) {
-  const int64_t x0 = (int64_t)ci * kChunk4 + (int64_t)threadIdx.x * kSeg;
-  seg_weights<BF16>(a, jb, residual, x0, w);
-  seg = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSeg; ++k) seg += w[k];
-  return chunk_reduce(seg, excl, s_w);
+  return off + ex;
 }
 
 // FUSED (untruncated rows, gamma + 1 <= 64): every workgroup of request b
 // first takes the acceptance decision itself (wave 0; it is a few hundred
 // bytes of reads, so repeating it per chunk is cheaper than a launch), chunk
-// 0 writes the request's outputs and the job, then all weigh their chunk.
+// 0 writes the request's outputs and the job, then all sum their chunk.
 template <bool BF16, bool FUSED>
 __global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs ac) {
   const int64_t blk = blockIdx.x;
   const int b = (int)(blk / a.nch4), ci = (int)(blk - (int64_t)b * a.nch4);
-  __shared__ double s_w[4];
+  __shared__ double s_w[4][4];
+  __shared__ double s_tot[4];
   __shared__ BigJob s_job;
   BigJob jb;
   if constexpr (FUSED) {
@@ -738,6 +771,7 @@ __global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs 
         if (lane == 0) {
           BigJob j;
           j.S = dc.rs.S;
+          j.S64 = 0.0;
           j.R = dc.rs.R;
           j.tau = dc.rs.tau;
           j.u = ac.ur[(int64_t)dc.lo + b + dc.nacc];
@@ -765,13 +799,31 @@ __global__ void __launch_bounds__(256) big_partial_kernel(BigArgs a, AcceptArgs 
     jb = a.jobs[b];
   }
   if (!jb.active) return;
-  double w[kSeg], seg, excl;
-  double W = chunk_weights<BF16>(a, jb, jb.qrow >= 0, ci, w, seg, excl, s_w);
-  if (threadIdx.x == 0) a.partials[(int64_t)b * a.nch4 + ci] = W;
+  const bool res = jb.qrow >= 0;
+  const QRow qr = res ? q_row(a.q, jb.qrow) : q_none();
+  const int64_t x0 = (int64_t)ci * kChunk4 + (int64_t)threadIdx.x * kSeg;
+  float z[kSeg], qv[kSeg];
+  seg_load<BF16>(a, jb, qr, res, x0, z, qv);
+  double ep[kSeg], eq[kSeg];
+  bool gt[kSeg];
+  seg_terms(jb, qr, res, a.c64, a.beta, z, qv, ep, eq, gt);
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) {
+    v[0] += ep[k];
+    v[2] += eq[k];
+    if (gt[k]) {
+      v[1] += ep[k];
+      v[3] += eq[k];
+    }
+  }
+  block_sum4(v, s_w, s_tot);
+  if (threadIdx.x < 4) a.partials[((int64_t)b * a.nch4 + ci) * 4 + threadIdx.x] = s_tot[threadIdx.x];
 }
 
-// One workgroup per request: walk the chunk totals (written by the previous
-// launch) and rescan the chunk that holds the token.
+// One workgroup per request: the normalisers and chunk weights from the
+// chunk sums (written by the previous launch), the walk to the chunk that
+// holds the token, and its rescan.
 template <bool BF16>
 __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -780,57 +832,58 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
   if (!jb.active) return;
   __shared__ double s_w[4];
   __shared__ int s_cstar, s_wf[4], s_wl[4];
-  __shared__ double s_carry, s_t;
-  double* P = a.partials + (int64_t)b * a.nch4;
+  __shared__ double s_carry, s_t, s_inv[2];
+  __shared__ int s_res;
+  const double* P = a.partials + (int64_t)b * a.nch4 * 4;
   bool residual = jb.qrow >= 0;
-  double w[kSeg], seg, excl;
+  const bool qlog = residual && a.q.dense == nullptr && a.q.z != nullptr;
   uint32_t extra = 0;
-  // Walk the chunk totals with wave scans (fixed order: identical sums in
-  // both walks).  Wave 0 decides; the result goes through LDS.
-  auto walk_total = [&]() {
-    if (wid == 0) {
+  if (wid == 0) {
+    // normalisers: chunk sums in a fixed order (lanes over chunks, then the
+    // butterfly)
+    double sp = 0.0, sq = 0.0;
+    for (int k = lane; k < a.nch4; k += kWave) {
+      sp += P[k * 4 + 0];
+      sq += P[k * 4 + 2];
+    }
+    sp = wave_sum_d(sp);
+    sq = wave_sum_d(sq);
+    const double invSp = 1.0 / sp, invSq = qlog ? 1.0 / sq : 1.0;
+    auto wchunk = [&](int k, bool res) -> double {
+      if (k >= a.nch4) return 0.0;
+      return res ? P[k * 4 + 1] * invSp - a.beta * (P[k * 4 + 3] * invSq) : P[k * 4 + 0];
+    };
+    // total weight (the same scans as the walk below: identical sums)
+    auto walk_total = [&](bool res) {
       double carry = 0.0;
       for (int k0 = 0; k0 < a.nch4; k0 += kWave) {
-        const int k = k0 + lane;
-        double pk = k < a.nch4 ? P[k] : 0.0;
-        double incl = wave_incl_scan_d(pk);
+        const double incl = wave_incl_scan_d(wchunk(k0 + lane, res));
         carry = carry + __shfl(incl, kWave - 1, kWave);
       }
-      if (lane == 0) s_carry = carry;
+      return carry;
+    };
+    double tot = walk_total(residual);
+    if (residual && !(tot > 0.0)) {
+      extra |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
+      residual = false;
+      tot = walk_total(false);
     }
-    __syncthreads();
-    double tot = s_carry;
-    __syncthreads();
-    return tot;
-  };
-  double tot = walk_total();
-  if (residual && !(tot > 0.0)) {
-    extra |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
-    residual = false;
-    for (int k = 0; k < a.nch4; ++k) {
-      double wk = chunk_weights<BF16>(a, jb, false, k, w, seg, excl, s_w);
-      if (tid == 0) P[k] = wk;
-      __syncthreads();
-    }
-    tot = walk_total();
-  }
-  if (wid == 0) {
     const double t = (double)jb.u * tot;
     double carry = 0.0;
     int cstar = -1, lastc = -1;
     double cex = 0.0;
     for (int k0 = 0; k0 < a.nch4; k0 += kWave) {
       const int k = k0 + lane;
-      double pk = k < a.nch4 ? P[k] : 0.0;
-      double incl = wave_incl_scan_d(pk);
-      double C = carry + incl;
+      const double pk = wchunk(k, residual);
+      const double incl = wave_incl_scan_d(pk);
+      const double C = carry + incl;
       double ex = __shfl_up(C, 1, kWave);
       if (lane == 0) ex = carry;
-      uint64_t pos = ballot(k < a.nch4 && pk > 0.0);
+      const uint64_t pos = ballot(k < a.nch4 && pk > 0.0);
       if (pos) lastc = k0 + 63 - (int)__builtin_clzll(pos);
-      uint64_t hit = ballot(k < a.nch4 && C > t);
+      const uint64_t hit = ballot(k < a.nch4 && C > t);
       if (hit) {
-        int src = (int)__builtin_ctzll(hit);
+        const int src = (int)__builtin_ctzll(hit);
         cstar = k0 + src;
         cex = __shfl(ex, src, kWave);
         break;
@@ -847,16 +900,31 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
       s_cstar = cstar;
       s_carry = cex;
       s_t = t;
+      s_inv[0] = invSp;
+      s_inv[1] = invSq;
+      s_res = residual ? 1 : 0;
     }
   }
   __syncthreads();
   const int cstar = s_cstar;
+  residual = s_res != 0;
   int token = -1;
   if (cstar >= 0) {
-    const double t = s_t;
-    chunk_weights<BF16>(a, jb, residual, cstar, w, seg, excl, s_w);
+    const double t = s_t, invSp = s_inv[0], invSq = s_inv[1];
+    const QRow qr = residual ? q_row(a.q, jb.qrow) : q_none();
     const int64_t x0 = (int64_t)cstar * kChunk4 + (int64_t)tid * kSeg;
-    double run = s_carry + excl;
+    float z[kSeg], qv[kSeg];
+    seg_load<BF16>(a, jb, qr, residual, x0, z, qv);
+    double ep[kSeg], eq[kSeg], w[kSeg];
+    bool gt[kSeg];
+    seg_terms(jb, qr, residual, a.c64, a.beta, z, qv, ep, eq, gt);
+    double seg = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      w[k] = term_weight(residual, ep[k], eq[k], gt[k], invSp, invSq, a.beta);
+      seg += w[k];
+    }
+    double run = s_carry + chunk_excl(seg, s_w);
     int found = 0x7fffffff, lp = -1;
 #pragma unroll
     for (int k = 0; k < kSeg; ++k) {
@@ -875,13 +943,13 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
 
 // ---------------------------------------------------------------------------
 // Untruncated requests with gamma + 1 <= 64, in one launch: one workgroup
-// of BS threads per request takes the acceptance decision (wave 0), weighs
-// the sampled row in tiles of BS * 8 tokens (each thread 8 consecutive
-// tokens, 16-byte loads; tile totals reduced in a fixed order and kept in
-// LDS), then re-weighs only the tile holding t = u * W (now in L2) to find
-// the token.
+// of BS threads per request takes the acceptance decision (wave 0), sums the
+// sampled row in tiles of BS * 8 tokens (each thread 8 consecutive tokens,
+// 16-byte loads; the four sums of K4 per tile, reduced in a fixed order and
+// kept in LDS), then re-weighs only the tile holding t = u * W (now in L2)
+// to find the token.
 // ---------------------------------------------------------------------------
-constexpr int kMaxTiles = 256;  // rows up to 256 * 8192 tokens (BS = 1024)
+constexpr int kMaxTiles = 64;  // rows up to 64 * 8192 tokens (BS = 1024)
 
 template <int BS>
 __device__ __forceinline__ double block_excl_scan(double v, double& total, double* s_wt) {
@@ -901,77 +969,18 @@ __device__ __forceinline__ double block_excl_scan(double v, double& total, doubl
   return off + ex;
 }
 
-// Raw logits / q of tokens x0 .. x0+7 (16-byte loads when aligned).
-template <bool BF16>
-__device__ __forceinline__ void seg_load(const BigArgs& a, const BigJob& jb, bool residual, int64_t x0, float* z,
-                                         float* qv) {
-  const int64_t V = a.V;
-  const int64_t zo = (int64_t)jb.row * V + x0;
-  const bool full = x0 + kSeg <= V;
-  if constexpr (BF16) {
-    if (full && (zo & 7) == 0) {
-      widen<true>(reinterpret_cast<const uint4*>(a.logits)[zo >> 3], z);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<true>(a.logits, zo + k) : kNegInf;
-    }
-  } else {
-    if (full && (zo & 3) == 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.logits) + (zo >> 2);
-      widen<false>(p[0], z);
-      widen<false>(p[1], z + 4);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) z[k] = (x0 + k < V) ? load_logit<false>(a.logits, zo + k) : kNegInf;
-    }
-  }
-  if (residual) {
-    if (a.q.dense != nullptr) {
-      const int64_t qo = (int64_t)jb.qrow * V + x0;
-      if (full && (qo & 3) == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.q.dense) + (qo >> 2);
-        widen<false>(p[0], qv);
-        widen<false>(p[1], qv + 4);
-      } else {
-#pragma unroll
-        for (int k = 0; k < kSeg; ++k) qv[k] = (x0 + k < V) ? a.q.dense[qo + k] : 0.0f;
-      }
-    } else {
-      q_row(a.q, jb.qrow).seg8(x0, V, qv);
-    }
-  }
-}
-
-__device__ __forceinline__ void seg_weigh(const BigJob& jb, float c, bool residual, const float* z, const float* qv,
-                                          double* w, double qs) {
-#pragma unroll
-  for (int k = 0; k < kSeg; ++k) {
-    double wk = 0.0;
-    if (z[k] >= jb.tau) {
-      double e = (double)e_of(z[k], c, jb.R);
-      if (residual) {
-        double d = e - (qs * (double)qv[k]) * jb.S;
-        wk = d > 0.0 ? d : 0.0;
-      } else {
-        wk = e;
-      }
-    }
-    w[k] = wk;
-  }
-}
-
 template <bool BF16, int BS>
 __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs ac) {
   constexpr int NW = BS / kWave;
-  constexpr int kU = 4;  // tiles whose loads are in flight together
+  constexpr int kU = BS >= 1024 ? 2 : 4;  // tiles whose loads are in flight together (128 VGPRs at 1024 threads)
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
   __shared__ BigJob s_job;
   __shared__ double s_wt[NW];
-  __shared__ double s_part[kMaxTiles * NW];  // per-wave tile partial sums
-  __shared__ double s_tile[kMaxTiles];
-  __shared__ int s_kstar, s_wf[NW], s_wl[NW];
-  __shared__ double s_cex, s_t, s_W;
+  __shared__ double s_part[4][kMaxTiles * NW];  // per-wave tile sums (ea, eg, qa, qg)
+  __shared__ double s_tile[4][kMaxTiles];
+  __shared__ int s_kstar, s_wf[NW], s_wl[NW], s_res;
+  __shared__ double s_cex, s_t, s_inv[2];
   const int P1 = ac.gamma + 1;
   int32_t* out = ac.out_tokens + (int64_t)b * P1;
   if (tid < kWave) {
@@ -989,6 +998,7 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
       if (lane == 0) {
         BigJob j;
         j.S = dc.rs.S;
+        j.S64 = 0.0;
         j.R = dc.rs.R;
         j.tau = dc.rs.tau;
         j.u = ac.ur[(int64_t)dc.lo + b + dc.nacc];
@@ -1007,58 +1017,73 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
   if (!jb.active) return;
   uint32_t fl = (uint32_t)jb.pad;
   bool residual = jb.qrow >= 0;
+  const bool qlog = residual && a.q.dense == nullptr && a.q.z != nullptr;
+  const QRow qr = residual ? q_row(a.q, jb.qrow) : q_none();
   constexpr int64_t kTileN = (int64_t)BS * kSeg;
   const int ntiles = (int)((a.V + kTileN - 1) / kTileN);
 
-  // Pass 1: tile totals.  Loads of kU tiles are issued together; each wave
+  // Pass 1: tile sums.  Loads of kU tiles are issued together; each wave
   // reduces its share of a tile and parks it in LDS (no barrier in the loop).
-  auto weigh_row = [&](bool res) {
-    for (int k0 = 0; k0 < ntiles; k0 += kU) {
-      float z[kU][kSeg], qv[kU][kSeg];
+  for (int k0 = 0; k0 < ntiles; k0 += kU) {
+    float z[kU][kSeg], qv[kU][kSeg];
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (k0 + u < ntiles) seg_load<BF16>(a, jb, res, (int64_t)(k0 + u) * kTileN + (int64_t)tid * kSeg, z[u], qv[u]);
+    for (int u = 0; u < kU; ++u)
+      if (k0 + u < ntiles)
+        seg_load<BF16>(a, jb, qr, residual, (int64_t)(k0 + u) * kTileN + (int64_t)tid * kSeg, z[u], qv[u]);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (k0 + u >= ntiles) break;
-        double w[kSeg];
-        seg_weigh(jb, a.c, res, z[u], qv[u], w, a.beta);
-        double seg = 0.0;
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + u >= ntiles) break;
+      double ep[kSeg], eq[kSeg];
+      bool gt[kSeg];
+      seg_terms(jb, qr, residual, a.c64, a.beta, z[u], qv[u], ep, eq, gt);
+      double v[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int i = 0; i < kSeg; ++i) seg += w[i];
-        double ws = wave_sum_d(seg);
-        if (lane == 0) s_part[(k0 + u) * NW + wid] = ws;
+      for (int i = 0; i < kSeg; ++i) {
+        v[0] += ep[i];
+        v[2] += eq[i];
+        if (gt[i]) {
+          v[1] += ep[i];
+          v[3] += eq[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double ws = wave_sum_d(v[i]);
+        if (lane == 0) s_part[i][(k0 + u) * NW + wid] = ws;
       }
     }
-    __syncthreads();
-    for (int k = tid; k < ntiles; k += BS) {
-      double t = 0.0;
-      for (int w2 = 0; w2 < NW; ++w2) t += s_part[k * NW + w2];
-      s_tile[k] = t;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double W = 0.0;
-      for (int k = 0; k < ntiles; ++k) W = W + s_tile[k];
-      s_W = W;
-    }
-    __syncthreads();
-    double W = s_W;
-    __syncthreads();
-    return W;
-  };
-  double W = weigh_row(residual);
-  if (residual && !(W > 0.0)) {
-    fl |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
-    residual = false;
-    W = weigh_row(false);
   }
+  __syncthreads();
+  for (int k = tid; k < 4 * ntiles; k += BS) {
+    const int i = k / ntiles, kt = k - i * ntiles;
+    double t = 0.0;
+    for (int w2 = 0; w2 < NW; ++w2) t += s_part[i][kt * NW + w2];
+    s_tile[i][kt] = t;
+  }
+  __syncthreads();
   if (tid == 0) {
+    double sp = 0.0, sq = 0.0;
+    for (int k = 0; k < ntiles; ++k) {
+      sp += s_tile[0][k];
+      sq += s_tile[2][k];
+    }
+    const double invSp = 1.0 / sp, invSq = qlog ? 1.0 / sq : 1.0;
+    auto wtile = [&](int k, bool res) {
+      return res ? s_tile[1][k] * invSp - a.beta * (s_tile[3][k] * invSq) : s_tile[0][k];
+    };
+    double W = 0.0;
+    for (int k = 0; k < ntiles; ++k) W = W + wtile(k, residual);
+    if (residual && !(W > 0.0)) {
+      fl |= 4u;  // SV_ROW_Z_DEGENERATE: draw from p instead
+      residual = false;
+      W = 0.0;
+      for (int k = 0; k < ntiles; ++k) W = W + wtile(k, false);
+    }
     const double t = (double)jb.u * W;
     double carry = 0.0;
     int kstar = -1, lastk = -1;
     for (int k = 0; k < ntiles; ++k) {
-      const double tk = s_tile[k];
+      const double tk = wtile(k, residual);
       if (tk > 0.0) lastk = k;
       if (carry + tk > t) {
         kstar = k;
@@ -1075,19 +1100,28 @@ __global__ void __launch_bounds__(BS) sample_full_kernel(BigArgs a, AcceptArgs a
     s_kstar = kstar;
     s_cex = carry;
     s_t = t;
+    s_inv[0] = invSp;
+    s_inv[1] = invSq;
+    s_res = residual ? 1 : 0;
   }
   __syncthreads();
   const int kstar = s_kstar;
+  residual = s_res != 0;
   int token = -1;
   if (kstar >= 0) {
+    const double invSp = s_inv[0], invSq = s_inv[1];
     const int64_t x0 = (int64_t)kstar * kTileN + (int64_t)tid * kSeg;
     float z[kSeg], qv[kSeg];
-    double w[kSeg];
-    seg_load<BF16>(a, jb, residual, x0, z, qv);
-    seg_weigh(jb, a.c, residual, z, qv, w, a.beta);
+    seg_load<BF16>(a, jb, qr, residual, x0, z, qv);
+    double ep[kSeg], eq[kSeg], w[kSeg];
+    bool gt[kSeg];
+    seg_terms(jb, qr, residual, a.c64, a.beta, z, qv, ep, eq, gt);
     double seg = 0.0;
 #pragma unroll
-    for (int i = 0; i < kSeg; ++i) seg += w[i];
+    for (int i = 0; i < kSeg; ++i) {
+      w[i] = term_weight(residual, ep[i], eq[i], gt[i], invSp, invSq, a.beta);
+      seg += w[i];
+    }
     double tot;
     const double ex = block_excl_scan<BS>(seg, tot, s_wt);
     const double t = s_t;
@@ -1273,16 +1307,23 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Statistics ([WR] §4.2, [RL] §2): per (row, chunk) partial sums, then a
-// per-row finish.
-//   dense q: rows with a stored kept list need only sum(q) from the chunk
-//     pass, and only for Z' (out_zqp); the min / positive-part sums over the
-//     kept set come from the list.  Other rows stream logits and q together.
+// Statistics ([WR] §4.2, [RL] §2, [BS] §五): alpha = sum min(p, q),
+// Z = sum (p - q)_+, Z' = sum (q - p)_+ and a = min(1, p(d) / q(d)) per
+// position, every p (and a q formed from the draft's logits) in double:
+// p = e64 / S64.
+//   Rows whose kept set is a stored list (truncated rows): p is 0 off the
+//     list, so alpha and Z are sums over the list; Z' adds, for a dense q,
+//     sum(q) over the row minus its sum over the list (the chunk pass sums q,
+//     and only when Z' is asked for), and for q formed from the draft's
+//     logits it is the sum over q's own list with p evaluated at its ids.
+//   Other rows stream the logits and q together, chunk by chunk, into six
+//     double sums: of e64_p and of q's unnormalised weight w_q (the dense q,
+//     or e64 of the draft's logit), each over the whole row and over the
+//     terms where p < q and where p > q (told apart by the float
+//     approximations of p and q).  With S64 = sum e64_p and Sq = sum w_q
+//     (1 for a dense q): alpha = sum_{p<q} p + sum_{p>=q} q,
+//     Z = sum_{p>q} (p - q) and Z' = sum_{p<q} (q - p).
 // Each output may be null (not written).
-//   q from the draft's logits: q is 0 off the draft's kept set, so when both
-//     rows have stored lists alpha and Z come from p's list and Z' from q's
-//     list (p evaluated at its ids), with no chunk pass; otherwise the row is
-//     streamed like an untruncated one.
 // ---------------------------------------------------------------------------
 struct StatsArgs {
   const void* logits;
@@ -1293,7 +1334,7 @@ struct StatsArgs {
   int32_t gamma;
   int32_t nchunks;
   int64_t chunk;
-  float c;
+  double c64;
   // Row results of the target's rows 0..gamma-1: info and kept lists of
   // position j of request b at row b * info_rpr + j (info_rpr = gamma for
   // the statistics call's own row passes, gamma + 1 when they are the
@@ -1302,13 +1343,17 @@ struct StatsArgs {
   const Cand* kept;
   int32_t info_rpr;
   int32_t kmax;
-  double* partials;     // [rows][nchunks][4]
+  double* partials;     // [rows][nchunks][kStatSums]
   float* out_alpha;
   float* out_zpq;
   float* out_zqp;
   float* out_acc;
   int64_t rows;
 };
+
+// The sums of a streamed row: e64_p and w_q over the row, over p < q and
+// over p > q.
+enum { ST_EP = 0, ST_EP_LT = 1, ST_EP_GT = 2, ST_WQ = 3, ST_WQ_LT = 4, ST_WQ_GT = 5, kStatSums = 6 };
 
 __device__ __forceinline__ int64_t info_row(const StatsArgs& a, int64_t r) {
   const int64_t b = r / a.gamma;
@@ -1332,43 +1377,64 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
   const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
   const int64_t x0 = (int64_t)ci * a.chunk, x1 = min(x0 + a.chunk, a.V);
-  double mn = 0.0, pq = 0.0, qp = 0.0, sq = 0.0;
-  __shared__ double s_p[4][4];
+  double sm[kStatSums];
+#pragma unroll
+  for (int i = 0; i < kStatSums; ++i) sm[i] = 0.0;
+  __shared__ double s_p[4][kStatSums];
   const bool big = stats_streamed(a, ri, r);
   // Rows finished from their lists skip the pass, unless Z' needs sum(q);
   // nothing reads their partials then (the test is the same for the whole
   // workgroup).
   if ((ri.flags & RF_NONFINITE) || !(big || (!QLOG && a.out_zqp != nullptr))) return;
-  {
-    const QRow qr = q_row(a.q, r);
-    const double invS = 1.0 / ri.S;
-    // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
-    const bool vec = (a.V & 7) == 0;
-    constexpr int kU = 4;
-    const int64_t ngroups = (x1 - x0 + 7) / 8;
+  const QRow qr = q_row(a.q, r);
+  // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
+  const bool vec = (a.V & 7) == 0;
+  const int64_t ngroups = (x1 - x0 + 7) / 8;
+  if (!big) {
+    // a dense q's sum only (Z' of a row finished from its list): q alone is
+    // streamed, kQ segments of 32 bytes in flight per thread
+    constexpr int kQ = 8;
+    for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kQ * 256) {
+      float qv[kQ][8];
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+        const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
+        if (vec && x + 8 <= x1) {
+          qr.raw8_whole(x, qv[u]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) qv[u][k] = x + k < x1 ? qr.raw_at(x + k) : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sm[ST_WQ] += (double)qv[u][k];
+      }
+    }
+  } else {
+    const double invS = 1.0 / ri.S;  // float exponentials: only to tell p < q from p > q
+    constexpr int kU = 2;
     for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kU * 256) {
       float qv[kU][8], zv[kU][8];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
         if (vec && x + 8 <= x1) {
-          if constexpr (QLOG) qr.logits8(x, qv[u]);
-          else qr.dense8(x, qv[u]);
-          if (big) {
-            if constexpr (BF16) {
-              widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
-            } else {
-              const uint4* zp4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + x);
-              widen<false>(zp4[0], zv[u]);
-              widen<false>(zp4[1], zv[u] + 4);
-            }
+          qr.raw8_whole(x, qv[u]);
+          if constexpr (BF16) {
+            widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
+          } else {
+            const uint4* zp4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + x);
+            widen<false>(zp4[0], zv[u]);
+            widen<false>(zp4[1], zv[u] + 4);
           }
         } else {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const bool in = x + k < x1;
-            qv[u][k] = in ? qr.at(x + k) : 0.0f;
-            zv[u][k] = (in && big) ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
+            qv[u][k] = in ? qr.raw_at(x + k) : (QLOG ? kNegInf : 0.0f);
+            zv[u][k] = in ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
           }
         }
       }
@@ -1376,35 +1442,32 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
       for (int u = 0; u < kU; ++u) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const double qd = (double)qv[u][k];
-          if (big) {
-            const float z = zv[u][k];
-            const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
-            const double d = p - qd;
-            mn += fmin(p, qd);
-            if (d > 0.0) pq += d;
-            if (d < 0.0) qp -= d;
-          } else {
-            sq += qd;
+          const double wq = qr.e64raw(qv[u][k]);
+          const float z = zv[u][k];
+          const double ep = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) : 0.0;
+          const double pa = ep * invS, qa = qr.approx(wq);
+          sm[ST_WQ] += wq;
+          sm[ST_EP] += ep;
+          if (pa < qa) {
+            sm[ST_EP_LT] += ep;
+            sm[ST_WQ_LT] += wq;
+          } else if (pa > qa) {
+            sm[ST_EP_GT] += ep;
+            sm[ST_WQ_GT] += wq;
           }
         }
       }
     }
   }
-  mn = wave_sum_d(mn);
-  pq = wave_sum_d(pq);
-  qp = wave_sum_d(qp);
-  sq = wave_sum_d(sq);
-  if (lane == 0) {
-    s_p[wid][0] = mn;
-    s_p[wid][1] = pq;
-    s_p[wid][2] = qp;
-    s_p[wid][3] = sq;
+#pragma unroll
+  for (int i = 0; i < kStatSums; ++i) {
+    const double v = wave_sum_d(sm[i]);
+    if (lane == 0) s_p[wid][i] = v;
   }
   __syncthreads();
-  if (tid < 4) {
+  if (tid < kStatSums) {
     double v = ((s_p[0][tid] + s_p[1][tid]) + s_p[2][tid]) + s_p[3][tid];
-    a.partials[(r * a.nchunks + ci) * 4 + tid] = v;
+    a.partials[(r * a.nchunks + ci) * kStatSums + tid] = v;
   }
 }
 
@@ -1416,7 +1479,8 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   const int64_t ir = info_row(a, r);
   const RowInfo ri = a.info[ir];
   const float qnan = __builtin_nanf("");
-  const bool qbad = a.q.dense == nullptr && (a.q.info[r].flags & RF_NONFINITE);
+  const bool qlog = a.q.dense == nullptr;
+  const bool qbad = qlog && (a.q.info[r].flags & RF_NONFINITE);
   if ((ri.flags & RF_NONFINITE) || qbad) {
     if (lane == 0) {
       if (a.out_alpha) a.out_alpha[r] = qnan;
@@ -1426,20 +1490,31 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     }
     return;
   }
-  const double invS = 1.0 / ri.S;
   const QRow qr = q_row(a.q, r);
-  double alpha, zpq, zqp = 0.0;
+  const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
+  const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
+  double alpha, zpq, zqp = 0.0, pd = 0.0, qd = 0.0;
+  const bool has_d = ri.d >= 0;
+  // the draft's q(d) in double: a dense q as given, else from the draft's logit
+  const float qraw_d = (has_d && qlog) ? qr.raw_at(ri.d) : 0.0f;
   if (stats_streamed(a, ri, r)) {
-    double acc4[3];
-    for (int k = 0; k < 3; ++k) {
+    double sm[kStatSums];
+#pragma unroll
+    for (int i = 0; i < kStatSums; ++i) {
       double v = 0.0;
-      for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * 4 + k];
-      acc4[k] = wave_sum_d(v);
+      for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * kStatSums + i];
+      sm[i] = wave_sum_d(v);
     }
-    alpha = acc4[0];
-    zpq = acc4[1];
-    zqp = acc4[2];
+    const double invSp = 1.0 / sm[ST_EP], invSq = qlog ? 1.0 / sm[ST_WQ] : 1.0;
+    alpha = sm[ST_EP_LT] * invSp + (sm[ST_WQ] - sm[ST_WQ_LT]) * invSq;
+    zpq = sm[ST_EP_GT] * invSp - sm[ST_WQ_GT] * invSq;
+    zqp = sm[ST_WQ_LT] * invSq - sm[ST_EP_LT] * invSp;
+    if (has_d) {
+      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) * invSp : 0.0;
+      qd = qlog ? qr.e64raw(qraw_d) * invSq : (double)ri.qd;
+    }
   } else {
+    const double invS = 1.0 / ri.S64;
     const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     // kStatBlk list steps per round (a nucleus of a few hundred tokens in
@@ -1454,14 +1529,14 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       for (int u = 0; u < kStatBlk; ++u)
         if (i0 + u * kWave < nk) e[u] = L[i0 + u * kWave];
 #pragma unroll
-      for (int u = 0; u < kStatBlk; ++u) qf[u] = (i0 + u * kWave < nk) ? qr.at(e[u].idx) : 0.0f;
+      for (int u = 0; u < kStatBlk; ++u) qf[u] = (i0 + u * kWave < nk) ? qr.raw_at(e[u].idx) : 0.0f;
 #pragma unroll
       for (int u = 0; u < kStatBlk; ++u) {
         if (i0 + u * kWave >= nk) break;
-        double p = (double)e[u].v * invS;
-        double qv = (double)qf[u];
-        double d = p - qv;
-        mn += fmin(p, qv);
+        const double p = e64_of(e[u].v, a.c64, ri.R) * invS;
+        const double qv = qr.q64(qf[u]);
+        const double d = p - qv;
+        mn += (p < qv) ? p : qv;
         if (d > 0.0) pq += d;
         if (d < 0.0) qp -= d;
         sqk += qv;
@@ -1473,17 +1548,15 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     sqk = wave_sum_d(sqk);
     if (a.out_zqp == nullptr) {
       // Z' not asked for: neither sum(q) nor q's list is read
-    } else if (a.q.dense != nullptr) {
+    } else if (!qlog) {
       double sq = 0.0;
-      for (int c = lane; c < a.nchunks; c += kWave) sq += a.partials[(r * a.nchunks + c) * 4 + 3];
+      for (int c = lane; c < a.nchunks; c += kWave) sq += a.partials[(r * a.nchunks + c) * kStatSums + ST_WQ];
       zqp = (wave_sum_d(sq) - sqk) + qp;
     } else {
       // Z' = sum over q's kept set of (q - p)_+, with p read at its ids
       const RowInfo qi = a.q.info[r];
-      const double qinvS = 1.0 / qi.S;
+      const double qinvS = 1.0 / qi.S64;
       const Cand* Lq = a.qkept + r * a.kmax;
-      const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
-      const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
       double zq = 0.0;
       const int nq = qi.nkept;
       for (int i0 = lane; i0 < nq; i0 += kStatBlk * kWave) {
@@ -1498,13 +1571,17 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
 #pragma unroll
         for (int u = 0; u < kStatBlk; ++u) {
           if (i0 + u * kWave >= nq) break;
-          const double qv = (double)e[u].v * qinvS;
+          const double qv = e64_of(e[u].v, a.c64, qi.R) * qinvS;
           const float z = zf[u];
-          const double p = (z >= ri.tau) ? (double)e_of(z, a.c, ri.R) * invS : 0.0;
+          const double p = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) * invS : 0.0;
           if (qv > p) zq += qv - p;
         }
       }
       zqp = wave_sum_d(zq);
+    }
+    if (has_d) {
+      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) * invS : 0.0;
+      qd = qlog ? qr.q64(qraw_d) : (double)ri.qd;
     }
   }
   if (lane == 0) {
@@ -1512,9 +1589,9 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     if (a.out_zpq) a.out_zpq[r] = (float)zpq;
     if (a.out_zqp) a.out_zqp[r] = (float)zqp;
     float ap;
-    if (ri.d < 0) ap = qnan;
-    else if (ri.qd == 0.0f) ap = ri.ed > 0.0f ? 1.0f : 0.0f;
-    else ap = (float)fmin(1.0, ((double)ri.ed * invS) / (double)ri.qd);
+    if (!has_d) ap = qnan;
+    else if (qd == 0.0) ap = pd > 0.0 ? 1.0f : 0.0f;
+    else ap = (float)fmin(1.0, pd / qd);
     if (a.out_acc) a.out_acc[r] = ap;
   }
 }

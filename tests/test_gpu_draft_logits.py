@@ -1,7 +1,7 @@
 """GPU parity of the draft-logits calls (q formed in the library from the
 draft's logits) against the CPU oracle's draft-logits functions, with the
 same bar as the q-input calls: exact tokens / lengths / flags outside the
-boundary band, statistics within 1e-5 relative (plus 2e-7 absolute)."""
+boundary band, statistics within 1e-5 relative (no absolute term)."""
 
 import numpy as np
 import pytest
@@ -21,11 +21,6 @@ DEV = "cuda"
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-
-
-def _sampled(B, n=16, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(B, size=min(n, B), replace=False))
 
 
 @pytest.mark.parametrize("name,kw", [
@@ -122,7 +117,7 @@ def test_fp32_draft_with_bf16_target():
 def test_full_size(name):
     w = generate(name, DEV)
     gpu = gpu_sample(w, draft_logits=True)
-    compare_sample(w, requests=_sampled(w.cfg.B), label=f"dl {name} full", gpu=gpu, draft_logits=True)
+    compare_sample(w, label=f"dl {name} full", gpu=gpu, draft_logits=True, pool=True)
     tok, nacc, fl = gpu
     pos = np.arange(w.cfg.gamma + 1)[None, :]
     assert ((tok >= 0) == (pos <= nacc[:, None])).all()
@@ -131,7 +126,7 @@ def test_full_size(name):
 
 def test_full_size_stats():
     w = generate("c5", DEV)
-    compare_stats(w, requests=_sampled(w.cfg.B, 8), label="dl c5 full stats", draft_logits=True)
+    compare_stats(w, label="dl c5 full stats", draft_logits=True, pool=True)
 
 
 def test_graph_replay_matches_eager():

@@ -4,8 +4,10 @@ Sampling: token ids, accepted lengths and flags must match exactly for every
 request outside the boundary band (a uniform within 1e-6 of an acceptance or
 CDF boundary, or a top-p cut within 1e-6 of top_p, as the oracle reports);
 boundary rows are counted and printed.  Greedy: bit-exact for every request.
-Statistics: within 1e-5 relative (plus 2e-7 absolute, the float32 resolution
-of the per-token probabilities).
+Statistics: within 1e-5 relative, with no absolute term (positions whose
+top-p cut lies within 1e-6 of top_p are counted and printed instead).  At
+full sizes every request is compared, the oracle spread over the host's
+cores.
 """
 
 import numpy as np
@@ -264,6 +266,31 @@ def test_stats_small():
     compare_stats(generate("c2", DEV, B=4, gamma=3, V=4001), label="stats c2 V=4001")
 
 
+@pytest.mark.parametrize("name,kw", [("c3", dict(B=4)), ("c5", dict(B=3, V=60000)), ("c2", dict(B=4))])
+@pytest.mark.parametrize("delta", [1e-2, 1e-4])
+def test_small_residual(name, kw, delta):
+    """A draft q within a relative delta of p (q = p (1 + delta N(0, 1)),
+    renormalised, float32), so Z = sum (p - q)+ is about delta / 3: the
+    statistics keep 1e-5 relative, and a rejection's residual draw stays
+    exact, at small Z."""
+    w = generate(name, DEV, **kw)
+    c = w.cfg
+    lg = widen(w.logits)
+    rng = np.random.default_rng(11)
+    q = np.zeros((c.B, c.gamma, c.V), np.float32)
+    for b in range(c.B):
+        for j in range(c.gamma):
+            p = oracle.process_row(lg[b, j], c.temperature, c.top_k, c.top_p).p
+            x = np.maximum(p * (1.0 + delta * rng.standard_normal(p.size)), 0.0)
+            q[b, j] = (x / x.sum()).astype(np.float32)
+    w.q = torch.from_numpy(q).to(DEV)
+    # every draft rejected at position 0 half the time: u just below / above a
+    ua = torch.full_like(w.u_accept, 0.999999)
+    w.u_accept = ua
+    compare_stats(w, label=f"small Z {name} delta={delta}")
+    compare_sample(w, label=f"small Z {name} delta={delta}")
+
+
 def test_stats_flags_and_flat():
     w = generate("c5", DEV, B=3, gamma=2, V=5000)
     w.logits = torch.zeros_like(w.logits)
@@ -277,18 +304,13 @@ def test_stats_flags_and_flat():
     compare_stats(w, label="stats flags")
 
 
-# ---- full sizes, sampled requests -------------------------------------------
-
-def _sampled(B, n=16, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(B, size=min(n, B), replace=False))
-
+# ---- full sizes, every request ----------------------------------------------
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c5"])
 def test_full_size_sample(name):
     w = generate(name, DEV)
     gpu = gpu_sample(w)
-    compare_sample(w, requests=_sampled(w.cfg.B), label=f"{name} full", gpu=gpu)
+    compare_sample(w, label=f"{name} full", gpu=gpu, pool=True)
     # properties that hold for every request
     tok, nacc, fl = gpu
     G1 = w.cfg.gamma + 1
@@ -311,11 +333,11 @@ def test_full_size_sample(name):
 ])
 def test_row_pass_shapes(name, kw):
     """Batch and vocabulary sizes that give the truncated row pass its other
-    chunk shapes (units per thread, dtype); sampled requests against the
-    oracle, every request checked for well-formed outputs."""
+    chunk shapes (units per thread, dtype); every request against the
+    oracle and checked for well-formed outputs."""
     w = generate(name, DEV, **kw)
     gpu = gpu_sample(w)
-    compare_sample(w, requests=_sampled(w.cfg.B, n=8, seed=3), label=f"{name} {kw}", gpu=gpu)
+    compare_sample(w, label=f"{name} {kw}", gpu=gpu, pool=True)
     tok, nacc, fl = gpu
     pos = np.arange(w.cfg.gamma + 1)[None, :]
     assert ((tok >= 0) == (pos <= nacc[:, None])).all()
@@ -324,12 +346,18 @@ def test_row_pass_shapes(name, kw):
 
 def test_full_size_greedy():
     w = generate("c4", DEV)
-    compare_greedy(w, requests=_sampled(w.cfg.B), label="c4 full")
+    compare_greedy(w, label="c4 full", pool=True)
 
 
 def test_full_size_stats():
     w = generate("c5", DEV)
-    compare_stats(w, requests=_sampled(w.cfg.B, 8), label="c5 full stats")
+    compare_stats(w, label="c5 full stats", pool=True)
+
+
+def test_toy_million_rounds_every_request():
+    """The toy workload's 10^6 rounds, every round against the oracle."""
+    w = generate("toy", DEV)
+    compare_sample(w, label="toy 1e6", pool=True)
 
 
 # ---- graph capture (the benchmark replays captured steps) ---------------------
