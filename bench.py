@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the speculative-sampling verify step on one MI355X.
 
-One step = one whole verify call over one batch of synthetic input (for the
-default workload ``c2``: the sampling verify of 64 requests x 5 positions x
-32000 fp32 logits).  Inputs are resident in HBM before timing starts; the
-batch is rotated over enough copies (>= 600 MB in total) that every step
-reads HBM rather than the 256 MB Infinity Cache.  Steps are replayed from HIP
-graphs (one per copy) so the host's launch cost does not pace the GPU;
-``--no-graph`` times plain stream launches instead.
+One step = one whole verify call over one batch of synthetic input.  The
+default workload is ``c5``, the largest: 1024 requests x 5 positions x
+256000 bf16 logits, T = 0.7, top-p = 0.95, sampled and with the acceptance
+statistics (alpha, Z, Z', accept_prob) of the same call.  Inputs are
+resident in HBM before timing starts; the batch is rotated over enough
+copies (>= 600 MB in total) that every step reads HBM rather than the 256 MB
+Infinity Cache.  Steps are replayed from HIP graphs (one per copy) so the
+host's launch cost does not pace the GPU; ``--no-graph`` times plain stream
+launches instead.
 
-Printed: one JSON line with verify rows/s (value), the row-pass kernel's
-achieved algorithmic HBM bandwidth against the 8 TB/s peak (``roofline``,
-its duration measured with HIP events recorded by the library around that
-kernel), and the CPU oracle's rows/s on a bounded sample (``cpu_baseline``).
-Progress goes to stderr.
+Printed: one JSON line with verify rows/s (value); ``roofline`` for the
+step's dominant kernel (the stage with the longest mean duration, measured
+with HIP events that the library attaches to each kernel dispatch), with
+every stage's duration and algorithmic bandwidth beside it and the step's
+own fraction of the 8 TB/s peak; and the CPU oracle's rows/s on a bounded
+sample (``cpu_baseline``: one process, then a process pool over the host's
+cores).  Progress goes to stderr.
 """
 
 import argparse
@@ -31,7 +35,20 @@ if ROOT not in sys.path:
 
 METRIC = "verify rows/sec and achieved HBM GB/s (% of peak) at B×(γ+1)×V"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
-KERNEL_SOURCES = ["sv_device.h", "sv_rowpass.h"]
+
+# Kernel stages the library can time (sv_stage in include/specverify.h):
+# name, the tag of its counter summaries under profiles/, and the sources
+# its kernels are built from (a summary taken on other sources is stale).
+STAGES = {
+    0: ("row pass", "rowpass", ["sv_device.h", "sv_rowpass.h"]),
+    1: ("row finisher", "rowfinal", ["sv_device.h", "sv_rowfinal.h"]),
+    2: ("acceptance and draws", "accept", ["sv_device.h", "sv_rowfinal.h", "sv_verify.h"]),
+    3: ("full-row draw sums", "draw_partial", ["sv_device.h", "sv_verify.h"]),
+    4: ("full-row draw finish", "draw_finish", ["sv_device.h", "sv_verify.h"]),
+    5: ("statistics pass", "stats_pass", ["sv_device.h", "sv_verify.h"]),
+    6: ("statistics finish", "stats_finish", ["sv_device.h", "sv_verify.h"]),
+    7: ("greedy decision", "greedy", ["sv_device.h", "sv_verify.h"]),
+}
 
 
 def log(*a):
@@ -43,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["toy", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c5", choices=["toy", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--draft-logits", action="store_true",
                     help="hand the draft's logits instead of q (the library forms q); sampling workloads only")
@@ -57,24 +74,26 @@ def parse():
     ap.add_argument("--no-z-qp", action="store_true",
                     help="statistics without Z' = sum (q - p)_+ (alpha, Z and accept_prob only)")
     ap.add_argument("--rotate-mb", type=float, default=600.0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle time budget of each of its two legs (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run one plain device copy of this size (for counter calibration)")
     return ap.parse_args()
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources):
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
+    for n in sources:
         with open(os.path.join(ROOT, "speculative_sampling_verification_sample_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(config):
-    """HBM bytes per row-pass launch from the committed counter summary,
-    or None when it is missing or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"rowpass_{config}_counters.txt")
+def read_traffic(stage, config):
+    """HBM bytes per launch of a stage's kernel from the committed counter
+    summary, or None when it is missing or was taken on other sources."""
+    _, tag, sources = STAGES[stage]
+    path = os.path.join(ROOT, "profiles", f"{tag}_{config}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -82,12 +101,22 @@ def read_traffic(config):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != kernel_source_hash():
+    if kv.get("source_hash") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class HipEvents:
@@ -98,6 +127,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipGetLastError.restype = ctypes.c_int
 
     def create(self):
         e = ctypes.c_void_p()
@@ -106,8 +136,11 @@ class HipEvents:
         return e
 
     def elapsed_ms(self, a, b):
+        """Milliseconds between two recorded events; RuntimeError (with the
+        runtime's error state cleared) when they were never recorded."""
         ms = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            self.hip.hipGetLastError()
             raise RuntimeError("hipEventElapsedTime failed")
         return float(ms.value)
 
@@ -191,12 +224,12 @@ def main():
     sout = tuple(None if (k == 2 and not zqp) else torch.empty((B, G), dtype=torch.float32, device=dev)
                  for k in range(4)) if stats else None
 
-    def step(i, timer=None):
-        """One verify step; `timer` = (start, stop) hipEvents around the row
-        pass of the sampling / greedy call."""
+    def step(i, timers=None):
+        """One verify step; `timers` = {stage: (start, stop)} hipEvents the
+        library attaches to that stage's kernel dispatch."""
         w = copies[i % R]
-        if timer is not None:
-            lib.spec_set_rowpass_timer(timer[0], timer[1])
+        for st, (ta, tb) in (timers or {}).items():
+            lib.spec_set_stage_timer(st, ta, tb)
         if rg and dl:
             sv.verify_sample_ragged_draft_logits(w.logits, w.draft_logits, w.ids, w.cu, w.u_accept, w.u_resample, G,
                                                  cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws, out=outs)
@@ -223,8 +256,8 @@ def main():
         else:
             sv.verify_sample(w.logits, w.q, w.ids, w.u_accept, w.u_resample, cfg.temperature, cfg.top_k,
                              cfg.top_p, workspace=ws, out=outs)
-        if timer is not None:
-            lib.spec_set_rowpass_timer(None, None)
+        for st in (timers or {}):
+            lib.spec_set_stage_timer(st, None, None)
         if stats and not fused:
             sv.accept_stats(w.logits, w.q, w.ids, cfg.temperature, cfg.top_k, cfg.top_p, workspace=ws,
                             out=sout)
@@ -278,58 +311,88 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     value = rows / (ms_step * 1e-3)
 
-    # ---- row-pass kernel duration (HIP events recorded by the library) ----
-    log("row-pass kernel timing")
+    # ---- per-stage kernel durations (HIP events the library attaches to
+    #      each stage's kernel dispatch; the separate statistics call of the
+    #      lenient workload runs untimed) ----
+    log("stage timing")
     hev = HipEvents()
-    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    nk = min(args.steps, 100)
+    pairs = [{st: (hev.create(), hev.create()) for st in STAGES} for _ in range(nk)]
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(pairs):
-        step(i, timer=(a, b))
+    for i, tm in enumerate(pairs):
+        step(i, timers=tm)
     torch.cuda.synchronize()
-    durs = [hev.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
-        hev.destroy(a)
-        hev.destroy(b)
+    stage_ms = {}
+    for st in STAGES:
+        try:
+            hev.elapsed_ms(pairs[0][st][0], pairs[0][st][1])
+        except RuntimeError:  # events never recorded: no such stage in this call
+            continue
+        stage_ms[st] = float(np.mean([hev.elapsed_ms(tm[st][0], tm[st][1]) for tm in pairs]))
+    for tm in pairs:
+        for a, b in tm.values():
+            hev.destroy(a)
+            hev.destroy(b)
     for a, b in zip(outs, ref):
         if R == 1 and not torch.equal(a, b):
             raise RuntimeError("outputs changed between steps")
-    k_ms = float(np.mean(durs))
-    row_bytes = V * cfg.logit_bytes
-    alg_launch = rows * row_bytes  # the row pass reads every logit of the batch once
-    achieved = alg_launch / (k_ms * 1e-3) / 1e9
-    # counters are taken on the uniform batches at the workload's own B
-    traffic = None if (rg or args.batch is not None) else read_traffic(cfg.name)
 
-    # ---- whole-step algorithmic bytes ----
+    # ---- algorithmic bytes: per stage and per step ----
     nacc = ref[1].cpu().numpy()
+    untrunc = cfg.top_k == 0 and cfg.top_p >= 1.0
+    row_bytes = V * cfg.logit_bytes
+    # q bytes per token: dense float32, or the draft's logits
+    qb = (w0.draft_logits.element_size() if dl else 4) if not greedy else 0
+    rejected = 0 if greedy else int((nacc < (gammas if rg else G)).sum())
+    stage_bytes = {0: rows * row_bytes}
     if greedy:
         step_bytes = rows * row_bytes + n_draft * 4 + B * (G + 2) * 4
     else:
-        rejected = int((nacc < (gammas if rg else G)).sum())
-        untrunc = cfg.top_k == 0 and cfg.top_p >= 1.0
-        # q bytes per token: dense float32, or the draft's logits (read once
-        # per call for their statistics, again on a rejected untruncated row)
-        qb = w0.draft_logits.element_size() if dl else 4
-        q_rows = rejected * V * qb if untrunc else 0
-        step_bytes = rows * row_bytes + q_rows + n_draft * 12 + rows * 4 + B * (G + 1) * 4 + B * 4
+        # a full-row draw reads the drawn row, and q's row on a rejection
+        draw_bytes = (B * row_bytes + rejected * V * qb) if untrunc else 0
+        stage_bytes[2 if G + 1 <= 64 else 3] = draw_bytes
+        step_bytes = rows * row_bytes + draw_bytes + n_draft * 12 + rows * 4 + B * (G + 1) * 4 + B * 4
         if dl:
-            step_bytes += n_draft * V * qb
-        if stats and not fused:
-            # the separate statistics call: the target's gamma rows and q
-            step_bytes += B * G * V * (cfg.logit_bytes + qb)
-        elif stats:
-            # the combined call's statistics: untruncated rows stream logits
-            # and q again; truncated rows read sum(q) of a dense q for Z',
-            # nothing more without Z' or when q comes from the draft's logits
-            step_bytes += B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl or not zqp else B * G * V * 4)
+            step_bytes += n_draft * V * qb  # the draft rows' own pass
+        if stats:
+            # statistics: untruncated rows stream logits and q again;
+            # truncated rows read sum(q) of a dense q for Z', nothing more
+            # without Z' or when q comes from the draft's logits
+            sb = B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl or not zqp else B * G * V * 4)
+            stage_bytes[5] = sb
+            step_bytes += sb
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # ---- CPU oracle baseline on a bounded sample ----
+    def stage_line(st):
+        ms = stage_ms[st]
+        by = stage_bytes.get(st, 0)
+        gbps = by / (ms * 1e-3) / 1e9 if by else None
+        return {"us": ms * 1e3, "alg_bytes": by, "GBps": gbps, "frac": gbps / PEAK_GBPS if by else None}
+
+    stages = {STAGES[st][0]: stage_line(st) for st in sorted(stage_ms)}
+    dom = max(stage_ms, key=lambda st: stage_ms[st])
+    # the dominant kernel again, with only its own events attached
+    solo = [(hev.create(), hev.create()) for _ in range(nk)]
+    torch.cuda.synchronize()
+    for i, tm in enumerate(solo):
+        step(i, timers={dom: tm})
+    torch.cuda.synchronize()
+    stage_ms[dom] = float(np.mean([hev.elapsed_ms(a, b) for a, b in solo]))
+    for a, b in solo:
+        hev.destroy(a)
+        hev.destroy(b)
+    dom_line = stage_line(dom)
+    # counters are taken on uniform batches at the workload's own B
+    traffic = None if (rg or args.batch is not None or dl or lenient) else read_traffic(dom, cfg.name)
+    log(" ".join(f"{n}={v['us']:.1f}us" for n, v in stages.items()))
+
+    # ---- CPU oracle baseline on a bounded sample: one process, then a pool
+    #      over the host's cores (at most 16) ----
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
+        from oracle import pool as opool
 
-        log(f"cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
         nsamp = min(B, 64)
         lg = wu.logits[:nsamp].detach().cpu()
         lg = oracle.bf16_bits_to_f64(lg.view(torch.int16).numpy()) if lg.dtype == torch.bfloat16 \
@@ -343,6 +406,8 @@ def main():
             dz = wu.draft_logits[:nsamp].detach().cpu()
             dz = oracle.bf16_bits_to_f64(dz.view(torch.int16).numpy()) if dz.dtype == torch.bfloat16 \
                 else dz.double().numpy()
+        beta = float(np.float32(args.lenience)) if lenient else 1.0
+        log(f"cpu oracle baseline, one process (~{args.cpu_seconds:.0f} s)")
         done = 0
         nrows = 0
         t0 = time.perf_counter()
@@ -368,18 +433,59 @@ def main():
             elif dl:
                 oracle.verify_request_draft_logits(lg[b], dz[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k,
                                                    cfg.top_p)
-                if cfg.stats:
+                if stats:
                     oracle.stats_request_draft_logits(lg[b], dz[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             else:
                 oracle.verify_request(lg[b], q[b], ids[b], ua[b], ur[b], cfg.temperature, cfg.top_k, cfg.top_p,
-                                      beta=float(np.float32(args.lenience)) if lenient else 1.0)
-                if cfg.stats:
+                                      beta=beta)
+                if stats:
                     oracle.stats_request(lg[b], q[b], ids[b], cfg.temperature, cfg.top_k, cfg.top_p)
             done += 1
-        el = time.perf_counter() - t0
-        cpu = {"value": nrows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} requests ({nrows} rows) cycled over the first {nsamp} requests of the "
-                         f"same {cfg.name} batch, one process, one thread, {el:.1f} s"}
+        el1 = time.perf_counter() - t0
+        single = nrows / el1
+        cpu = {"value": single, "unit": "rows/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
+               "single_process_rows_per_s": single,
+               "sample": f"one process: {done} requests ({nrows} rows) cycled over the first {nsamp} requests of "
+                         f"the same {cfg.name} batch, {el1:.1f} s"}
+        if not rg:
+            # the pool: the first n requests of the batch, n sized from the
+            # single-process rate to about --cpu-seconds of work per core
+            # (a batch smaller than that is run `rep` times over)
+            workers = opool.default_workers()
+            want = max(workers, math.ceil(done / el1 * workers * args.cpu_seconds))
+            n = int(min(B, want))
+            rep = max(1, want // n)
+            arrays = dict(logits=(wu.logits[:n].view(torch.int16) if wu.logits.dtype == torch.bfloat16
+                                  else wu.logits[:n]).cpu().numpy(), ids=wu.ids[:n].cpu().numpy())
+            prm = dict(T=cfg.temperature, top_k=cfg.top_k, top_p=cfg.top_p, beta=beta)
+            if greedy:
+                kinds = ["greedy"]
+            else:
+                arrays.update(u_accept=wu.u_accept[:n].cpu().numpy(), u_resample=wu.u_resample[:n].cpu().numpy())
+                if dl:
+                    d = wu.draft_logits[:n]
+                    arrays["draft_logits"] = (d.view(torch.int16) if d.dtype == torch.bfloat16 else d).cpu().numpy()
+                    kinds = ["sample_draft_logits"] + (["stats_draft_logits"] if stats else [])
+                else:
+                    arrays["q"] = wu.q[:n].cpu().numpy()
+                    kinds = ["sample"] + (["stats"] if stats else [])
+            log(f"cpu oracle baseline, {workers} processes over {n} requests")
+            with opool.make_pool(workers) as pl:
+                opool.run("greedy", dict(logits=arrays["logits"][:workers], ids=arrays["ids"][:workers]), {},
+                          min(workers, n), pool=pl)  # workers started and warm
+                t0 = time.perf_counter()
+                for k in kinds:
+                    need = {"greedy": ("logits", "ids"),
+                            "sample": ("logits", "q", "ids", "u_accept", "u_resample"),
+                            "stats": ("logits", "q", "ids"),
+                            "sample_draft_logits": ("logits", "draft_logits", "ids", "u_accept", "u_resample"),
+                            "stats_draft_logits": ("logits", "draft_logits", "ids")}[k]
+                    opool.run(k, {a: arrays[a] for a in need}, prm, n, pool=pl, repeat=rep)
+                el2 = time.perf_counter() - t0
+            cpu.update(value=rep * n * (G + 1) / el2, cores=workers,
+                       sample=cpu["sample"] + f"; pool: the first {n} requests"
+                                              f"{f' {rep} times over' if rep > 1 else ''}, {workers} worker "
+                                              f"processes, {el2:.1f} s (value and cores are the pool's)")
 
     if args.copy_calibration_mb > 0:
         n = int(args.copy_calibration_mb * 1e6) // 4
@@ -406,7 +512,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if w0.logits.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {desc}", "B": B, "gamma": G, "V": V,
                    "logits": cfg.dtype, "temperature": cfg.temperature, "top_k": cfg.top_k, "top_p": cfg.top_p,
@@ -419,9 +525,10 @@ def main():
                              f"call only" if rg else "uniform"),
                    "rows_per_step": rows, "rotated_copies": R, "graph_replay": graphs is not None,
                    "wall_s_timed": wall, "step_alg_bytes": step_bytes, "step_alg_GBps": step_gbps},
-        "roofline": {"bound": "hbm", "kernel": "rowpass (K1)", "achieved": achieved, "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg_launch, "launch_us": k_ms * 1e3},
+        "roofline": {"bound": "hbm", "kernel": STAGES[dom][0], "achieved": dom_line["GBps"], "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": dom_line["frac"], "traffic": traffic,
+                     "alg_bytes_per_launch": dom_line["alg_bytes"], "launch_us": dom_line["us"],
+                     "step_frac": step_gbps / PEAK_GBPS, "stages": stages},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -13,7 +13,7 @@
  * - Every tensor argument is a DEVICE pointer owned by the caller.  The
  *   library never allocates, frees or retains caller memory and keeps no
  *   state between calls (apart from the optional profiling hook
- *   spec_set_rowpass_timer).  All scratch lives in the caller's `workspace`
+ *   spec_set_stage_timer).  All scratch lives in the caller's `workspace`
  *   (device memory of at least the reported workspace size, 16-byte
  *   aligned, contents need not be initialised).
  * - Layout is contiguous row-major.  `target_logits` is [B, gamma+1, V]
@@ -269,14 +269,30 @@ sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dt
                                                float* out_z_qp, float* out_accept_prob, void* workspace,
                                                size_t workspace_bytes, void* stream);
 
+/* Kernel stages of a call, for the profiling hook below. */
+typedef enum {
+  SV_STAGE_ROWPASS = 0,       /* the streaming pass over the target logits (not the draft rows') */
+  SV_STAGE_ROWFINAL = 1,      /* the target rows' finisher (kept sets, normalisers, draft gather) */
+  SV_STAGE_ACCEPT = 2,        /* the acceptance decision launch (with the draws it takes itself) */
+  SV_STAGE_DRAW_PARTIAL = 3,  /* untruncated draws, long drafts: the chunk sums after the decision */
+  SV_STAGE_DRAW_FINISH = 4,   /* untruncated draws: the walk and rescan launch */
+  SV_STAGE_STATS_PASS = 5,    /* statistics: the pass over streamed rows and a dense q's sum */
+  SV_STAGE_STATS_FINISH = 6,  /* statistics: the per-position finish */
+  SV_STAGE_GREEDY = 7,        /* greedy decision */
+  SV_STAGE_COUNT = 8
+} sv_stage;
+
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both
- * arguments are non-NULL, every later spec_verify_sample /
- * spec_verify_greedy / spec_accept_stats call attaches the two events to the
- * dispatch of its streaming row-pass kernel (the HBM-bound pass over the
- * target logits; not the draft rows' pass of the draft-logits calls) on the
- * call's stream: `start_event` takes the kernel's start time and
- * `stop_event` its end time.  Both are hipEvent_t handles owned by the
- * caller.  Passing NULL for either turns it off.  Nothing else changes. */
+ * events are non-NULL, every later call attaches them to the dispatch of
+ * its kernel of stage `stage` (an sv_stage) on the call's stream:
+ * `start_event` takes the kernel's start time and `stop_event` its end
+ * time.  Both are hipEvent_t handles owned by the caller.  Passing NULL for
+ * either turns that stage's hook off.  A stage absent from a call leaves
+ * its events untouched.  Nothing else changes.  Returns
+ * SV_ERR_INVALID_ARG for an unknown stage. */
+sv_status spec_set_stage_timer(int32_t stage, void* start_event, void* stop_event);
+
+/* spec_set_stage_timer(SV_STAGE_ROWPASS, start_event, stop_event). */
 sv_status spec_set_rowpass_timer(void* start_event, void* stop_event);
 
 /* Static description of a status code. */

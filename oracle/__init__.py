@@ -5,7 +5,9 @@ execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
 library (no kernels, headers, helpers or tables); the only module both sides
 use is the seeded input generator in ``workloads/``, which holds none of the
-method's arithmetic.
+verify step's arithmetic: it builds what a caller hands over, among it the
+draft's q, which it forms with its own softmax and truncation code (the
+draft side's decoding rules); both sides take that q as an input.
 
 It is a plain, slow, float64 NumPy implementation, one request and one row at
 a time, written from the pages listed below.  Citations name the page and the

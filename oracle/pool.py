@@ -15,7 +15,7 @@ from multiprocessing import shared_memory
 
 import numpy as np
 
-import oracle
+from . import verify as oracle
 
 
 def default_workers() -> int:
@@ -63,11 +63,23 @@ def _job(args):
     return lo, o
 
 
-def run(kind: str, arrays: dict, params: dict, B: int, workers: int | None = None):
+def make_pool(workers: int | None = None):
+    """A pool of oracle workers (spawned: fresh interpreters that import
+    numpy and the oracle only), for several ``run`` calls."""
+    return mp.get_context("spawn").Pool(workers or default_workers())
+
+
+def run(kind: str, arrays: dict, params: dict, B: int, workers: int | None = None, pool=None, repeat: int = 1):
     """The oracle call `kind` over requests 0..B-1 of `arrays` (host numpy
-    arrays, first axis = request), split over `workers` processes.  Returns
-    what the oracle call returns for the whole batch."""
-    workers = workers or default_workers()
+    arrays, first axis = request), split over `workers` processes (or the
+    processes of `pool`, from ``make_pool``).  Returns what the oracle call
+    returns for the whole batch.  ``repeat`` > 1 runs the whole batch that
+    many times (for timing; the results of the first run are returned)."""
+    own = pool is None
+    if own:
+        workers = workers or default_workers()
+    else:
+        workers = pool._processes
     shms, specs = [], {}
     try:
         for k, a in arrays.items():
@@ -78,8 +90,13 @@ def run(kind: str, arrays: dict, params: dict, B: int, workers: int | None = Non
             specs[k] = (shm.name, a.shape, a.dtype.str)
         chunk = max(1, -(-B // (workers * 4)))
         jobs = [(kind, specs, params, lo, min(lo + chunk, B)) for lo in range(0, B, chunk)]
-        with mp.get_context("spawn").Pool(workers) as pool:
-            parts = sorted(pool.imap_unordered(_job, jobs), key=lambda t: t[0])
+        nj = len(jobs)
+        jobs = jobs * max(1, int(repeat))
+        if own:
+            with make_pool(workers) as p:
+                parts = list(p.imap(_job, jobs))[:nj]
+        else:
+            parts = list(pool.imap(_job, jobs))[:nj]
     finally:
         for shm in shms:
             shm.close()

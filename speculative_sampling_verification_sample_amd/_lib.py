@@ -83,6 +83,7 @@ SIGNATURES = {
     ),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "spec_set_rowpass_timer": (ctypes.c_int, [_ptr, _ptr]),
+    "spec_set_stage_timer": (ctypes.c_int, [_c_int32, _ptr, _ptr]),
 }
 
 _LIB = None

@@ -191,17 +191,25 @@ T* ws_at(void* ws, size_t off) {
 
 sv_status launched() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
-hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;  // profiling hook
+// Profiling hook: per stage, two caller events attached to that stage's
+// kernel dispatch (spec_set_stage_timer).
+hipEvent_t g_timer_start[SV_STAGE_COUNT] = {}, g_timer_stop[SV_STAGE_COUNT] = {};
 
-// Launches a row pass.  With the profiling hook set, the two events are
-// attached to the kernel's own dispatch, so they take its start and end
-// times.
+// Launches a kernel of stage `stage` (< 0: never timed).  With the stage's
+// events set, they are attached to the kernel's own dispatch, so they take
+// its start and end times.
+template <typename... KArgs, typename... Args>
+void launch_stage(int stage, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                  Args... args) {
+  if (stage >= 0 && g_timer_start[stage] && g_timer_stop[stage])
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, g_timer_start[stage], g_timer_stop[stage], 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+}
+
 void launch_row_kernel(void (*kernel)(RowPassArgs), dim3 grid, dim3 block, hipStream_t st, const RowPassArgs& a,
                        bool timed) {
-  if (timed && g_timer_start && g_timer_stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timer_start, g_timer_stop, 0, a);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+  launch_stage(timed ? SV_STAGE_ROWPASS : -1, kernel, grid, block, 0, st, a);
 }
 
 template <int MODE, bool BF16>
@@ -290,7 +298,7 @@ void set_kernel_attrs() {
 template <bool BF16>
 sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const int32_t* ids, int64_t V, int G1,
                        int gamma, const Expo& c, sv_sampling_params prm, void* ws, hipStream_t st,
-                       const int32_t* cu = nullptr, int32_t n_live = 0) {
+                       const int32_t* cu = nullptr, int32_t n_live = 0, bool timed = true) {
   RowFinalArgs a;
   a.cu = cu;
   a.n_live = n_live;
@@ -319,7 +327,7 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const i
   a.kept = p.trunc ? ws_at<Cand>(ws, p.off_kept) : nullptr;
   set_kernel_attrs();
   size_t dyn = p.trunc ? (size_t)p.um * 8 : 0;  // key and token id per union entry
-  hipLaunchKernelGGL((rowfinal_kernel<BF16>), dim3((unsigned)p.rows), dim3(256), dyn, st, a);
+  launch_stage(timed ? SV_STAGE_ROWFINAL : -1, rowfinal_kernel<BF16>, dim3((unsigned)p.rows), dim3(256), dyn, st, a);
   return launched();
 }
 
@@ -387,8 +395,8 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   if (p.trunc) {
     // kept lists (stored in token-id order) and oversized kept sets are
     // drawn inside K3, one workgroup per request
-    if (bf) hipLaunchKernelGGL((accept_trunc_kernel<true>), dim3((unsigned)B), dim3(256), 0, st, ac);
-    else hipLaunchKernelGGL((accept_trunc_kernel<false>), dim3((unsigned)B), dim3(256), 0, st, ac);
+    if (bf) launch_stage(SV_STAGE_ACCEPT, accept_trunc_kernel<true>, dim3((unsigned)B), dim3(256), 0, st, ac);
+    else launch_stage(SV_STAGE_ACCEPT, accept_trunc_kernel<false>, dim3((unsigned)B), dim3(256), 0, st, ac);
     return launched();
   }
 
@@ -409,31 +417,31 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   if (G1 <= kWave && tiles_big <= kMaxTiles && B >= kOneLaunchMinB) {
     // one workgroup per request: decision, row weights and the draw
     if (V >= 16384) {
-      if (bf) hipLaunchKernelGGL((sample_full_kernel<true, 1024>), dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
-      else hipLaunchKernelGGL((sample_full_kernel<false, 1024>), dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
+      if (bf) launch_stage(SV_STAGE_ACCEPT, sample_full_kernel<true, 1024>, dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
+      else launch_stage(SV_STAGE_ACCEPT, sample_full_kernel<false, 1024>, dim3((unsigned)B), dim3(1024), 0, st, bg, ac);
     } else {
-      if (bf) hipLaunchKernelGGL((sample_full_kernel<true, 256>), dim3((unsigned)B), dim3(256), 0, st, bg, ac);
-      else hipLaunchKernelGGL((sample_full_kernel<false, 256>), dim3((unsigned)B), dim3(256), 0, st, bg, ac);
+      if (bf) launch_stage(SV_STAGE_ACCEPT, sample_full_kernel<true, 256>, dim3((unsigned)B), dim3(256), 0, st, bg, ac);
+      else launch_stage(SV_STAGE_ACCEPT, sample_full_kernel<false, 256>, dim3((unsigned)B), dim3(256), 0, st, bg, ac);
     }
     return launched();
   }
   dim3 grid((unsigned)((int64_t)p.nch4 * B));
   if (G1 <= kWave) {
     // acceptance fused into the chunk weighing
-    if (bf) hipLaunchKernelGGL((big_partial_kernel<true, true>), grid, dim3(256), 0, st, bg, ac);
-    else hipLaunchKernelGGL((big_partial_kernel<false, true>), grid, dim3(256), 0, st, bg, ac);
+    if (bf) launch_stage(SV_STAGE_ACCEPT, big_partial_kernel<true, true>, grid, dim3(256), 0, st, bg, ac);
+    else launch_stage(SV_STAGE_ACCEPT, big_partial_kernel<false, true>, grid, dim3(256), 0, st, bg, ac);
   } else {
-    if (bf) hipLaunchKernelGGL((accept_kernel<true>), agrid, dim3(256), 0, st, ac);
-    else hipLaunchKernelGGL((accept_kernel<false>), agrid, dim3(256), 0, st, ac);
+    if (bf) launch_stage(SV_STAGE_ACCEPT, accept_kernel<true>, agrid, dim3(256), 0, st, ac);
+    else launch_stage(SV_STAGE_ACCEPT, accept_kernel<false>, agrid, dim3(256), 0, st, ac);
     s = launched();
     if (s != SV_OK) return s;
-    if (bf) hipLaunchKernelGGL((big_partial_kernel<true, false>), grid, dim3(256), 0, st, bg, ac);
-    else hipLaunchKernelGGL((big_partial_kernel<false, false>), grid, dim3(256), 0, st, bg, ac);
+    if (bf) launch_stage(SV_STAGE_DRAW_PARTIAL, big_partial_kernel<true, false>, grid, dim3(256), 0, st, bg, ac);
+    else launch_stage(SV_STAGE_DRAW_PARTIAL, big_partial_kernel<false, false>, grid, dim3(256), 0, st, bg, ac);
   }
   s = launched();
   if (s != SV_OK) return s;
-  if (bf) hipLaunchKernelGGL((big_finish_kernel<true>), dim3((unsigned)B), dim3(256), 0, st, bg);
-  else hipLaunchKernelGGL((big_finish_kernel<false>), dim3((unsigned)B), dim3(256), 0, st, bg);
+  if (bf) launch_stage(SV_STAGE_DRAW_FINISH, big_finish_kernel<true>, dim3((unsigned)B), dim3(256), 0, st, bg);
+  else launch_stage(SV_STAGE_DRAW_FINISH, big_finish_kernel<false>, dim3((unsigned)B), dim3(256), 0, st, bg);
   return launched();
 }
 
@@ -480,16 +488,16 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   dim3 grid((unsigned)(a.rows * a.nchunks));
   const bool qlog = q.dense == nullptr;
   if (bf) {
-    if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<true, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((stats_chunk_kernel<true, false>), grid, dim3(256), 0, st, a);
+    if (qlog) launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<true, true>, grid, dim3(256), 0, st, a);
+    else launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<true, false>, grid, dim3(256), 0, st, a);
   } else {
-    if (qlog) hipLaunchKernelGGL((stats_chunk_kernel<false, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((stats_chunk_kernel<false, false>), grid, dim3(256), 0, st, a);
+    if (qlog) launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<false, true>, grid, dim3(256), 0, st, a);
+    else launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<false, false>, grid, dim3(256), 0, st, a);
   }
   sv_status s = launched();
   if (s != SV_OK) return s;
-  if (bf) hipLaunchKernelGGL((stats_final_kernel<true>), dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((stats_final_kernel<false>), dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+  if (bf) launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<true>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+  else launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<false>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
   return launched();
 }
 
@@ -525,9 +533,10 @@ sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* 
          : run_rowpass<false>(pq, draft_logits, V, gamma, c, ws, st, nullptr, q_src_none(V), 0, nullptr, false, cu,
                               n_draft);
   if (s != SV_OK) return s;
-  s = bf ? run_rowfinal<true>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st, cu, n_draft)
+  s = bf ? run_rowfinal<true>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st, cu, n_draft,
+                              false)
          : run_rowfinal<false>(pq, draft_logits, q_src_none(V), draft_ids, V, gamma, gamma, c, prm, ws, st, cu,
-                               n_draft);
+                               n_draft, false);
   if (s != SV_OK) return s;
   QSrc q;
   q.dense = nullptr;
@@ -592,7 +601,7 @@ sv_status verify_greedy_impl(const void* target_logits, sv_dtype dt, const int32
   g.cu = cu;
   g.n_draft = n_draft;
   g.eos = eos;
-  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, g);
+  launch_stage(SV_STAGE_GREEDY, greedy_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, g);
   return launched();
 }
 
@@ -901,15 +910,20 @@ sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, cons
                             cu_draft, n_draft, eos_id < 0 ? -1 : eos_id);
 }
 
-sv_status spec_set_rowpass_timer(void* start_event, void* stop_event) {
+sv_status spec_set_stage_timer(int32_t stage, void* start_event, void* stop_event) {
+  if (stage < 0 || stage >= SV_STAGE_COUNT) return SV_ERR_INVALID_ARG;
   if (start_event == nullptr || stop_event == nullptr) {
-    g_timer_start = nullptr;
-    g_timer_stop = nullptr;
+    g_timer_start[stage] = nullptr;
+    g_timer_stop[stage] = nullptr;
   } else {
-    g_timer_start = reinterpret_cast<hipEvent_t>(start_event);
-    g_timer_stop = reinterpret_cast<hipEvent_t>(stop_event);
+    g_timer_start[stage] = reinterpret_cast<hipEvent_t>(start_event);
+    g_timer_stop[stage] = reinterpret_cast<hipEvent_t>(stop_event);
   }
   return SV_OK;
+}
+
+sv_status spec_set_rowpass_timer(void* start_event, void* stop_event) {
+  return spec_set_stage_timer(SV_STAGE_ROWPASS, start_event, stop_event);
 }
 
 const char* spec_status_string(sv_status status) {

@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 import oracle
-import oracle_pool
+from oracle import pool as oracle_pool
 import speculative_sampling_verification_sample_amd as sv
 
 

@@ -5,7 +5,7 @@ import numpy as np
 import torch
 
 import oracle
-import oracle_pool
+from oracle import pool as oracle_pool
 from workloads import generate
 
 

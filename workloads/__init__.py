@@ -1,8 +1,12 @@
 """Seeded synthetic inputs for the speculative-sampling verify step.
 
 This module is the only code the CPU oracle and the HIP library's callers
-share.  It holds none of the verify method's arithmetic: it draws random
-numbers and builds what a *caller* of the verify step hands over --
+share.  It holds none of the verify step's arithmetic (acceptance, residual,
+draws, statistics): it draws random numbers and builds what a *caller* of
+the verify step hands over.  One piece of that is the draft side's own
+decoding rules: q is formed from the draft logits by this module's own
+softmax with temperature, top-k and top-p (written apart from the oracle's
+processing of p), and both sides then take that q as an input --
 
 * target logits for gamma+1 positions,
 * the draft's own sampling distribution q for gamma positions, built by the
