@@ -110,6 +110,24 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
                              int32_t* out_num_accepted, uint32_t* out_row_flags,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* spec_verify_sample without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing.  Its
+ * scratch is a static device array of SV_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its address
+ * is looked up on the first call on each device).  Sizes whose workspace
+ * (spec_verify_workspace_size) exceeds it return SV_ERR_UNSUPPORTED and
+ * launch nothing; SV_ERR_HIP when the array's address cannot be obtained.
+ * Every call on one GPU shares that array, so calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Arguments, outputs and results are those of spec_verify_sample. */
+#define SV_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+sv_status spec_verify_sample_noalloc(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                     const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                     int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
+                                     int32_t* out_tokens, int32_t* out_num_accepted, uint32_t* out_row_flags,
+                                     void* stream);
+
 /* Greedy verify ([WR] §7.1; [RL] §2 last paragraph; [BS] §二 example):
  * g_j = argmax of row j (lowest id on ties), j = 0..gamma;
  * n = first j < gamma with d_j != g_j (else gamma); emit d_0..d_{n-1}, g_n.

@@ -21,6 +21,7 @@ from .api import (  # noqa: F401
     verify_sample,
     verify_sample_draft_logits,
     verify_sample_lenient,
+    verify_sample_noalloc,
     verify_sample_ragged,
     verify_sample_ragged_draft_logits,
     verify_sample_stats,

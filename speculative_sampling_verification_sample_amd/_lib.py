@@ -30,6 +30,11 @@ SIGNATURES = {
         [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
          _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     ),
+    "spec_verify_sample_noalloc": (
+        ctypes.c_int,
+        [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _c_int32, _c_int32, _c_int32, SamplingParamsC,
+         _ptr, _ptr, _ptr, _ptr],
+    ),
     "spec_verify_greedy": (
         ctypes.c_int,
         [_ptr, ctypes.c_int, _ptr, _c_int32, _c_int32, _c_int32, _ptr, _ptr, _ptr, _ptr, _size, _ptr],

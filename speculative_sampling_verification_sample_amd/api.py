@@ -170,6 +170,23 @@ def verify_sample(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0
     return tokens, nacc, flags
 
 
+def verify_sample_noalloc(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0, out=None):
+    """verify_sample through the allocation-free entry point: the library's
+    static per-GPU scratch replaces the workspace (sizes whose workspace
+    exceeds it are refused), and calls on one GPU must not overlap.  Pass
+    `out` to allocate nothing here either."""
+    B, G1, V = _logits3(logits)
+    G, dev = G1 - 1, logits.device
+    _sample_inputs(logits, "q", q, ids, u_accept, u_resample, B, G, V, torch.float32)
+    tokens, nacc, flags = _outs(out, B, G1, dev)
+    code = load_library().spec_verify_sample_noalloc(
+        logits.data_ptr(), _DT[logits.dtype], _if(G > 0, q), _if(G > 0, ids), _if(G > 0, u_accept),
+        u_resample.data_ptr(), B, G, V, _params(temperature, top_k, top_p),
+        tokens.data_ptr(), nacc.data_ptr(), flags.data_ptr(), _stream(dev))
+    _raise(code, "spec_verify_sample_noalloc")
+    return tokens, nacc, flags
+
+
 def verify_sample_lenient(logits, q, ids, u_accept, u_resample, temperature=1.0, top_k=0, top_p=1.0,
                           lenience=1.0, workspace: Optional[torch.Tensor] = None, out=None):
     """Sampling verify step with lenient acceptance u < p / (lenience * q),

@@ -616,6 +616,37 @@ sv_status ragged_checks(const int32_t* cu, int32_t n_draft, int32_t B, int32_t g
 
 }  // namespace
 
+// ---- the allocation-free variant's scratch ------------------------------------
+// One file-scope device array per GPU, used as the workspace of
+// spec_verify_sample_noalloc.  Host code never passes the array's name to a
+// kernel: its device address, per device, comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device), or
+// null when the device cannot be queried.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
@@ -646,6 +677,29 @@ sv_status spec_verify_sample(const void* target_logits, sv_dtype dt, const float
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
                             gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags, workspace, st);
+}
+
+sv_status spec_verify_sample_noalloc(const void* target_logits, sv_dtype dt, const float* draft_probs,
+                                     const int32_t* draft_ids, const float* u_accept, const float* u_resample,
+                                     int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
+                                     int32_t* out_tokens, int32_t* out_num_accepted, uint32_t* out_row_flags,
+                                     void* stream) {
+  sv_status s = common_checks(target_logits, dt, B, gamma, V);
+  if (s != SV_OK) return s;
+  Expo c;
+  s = check_params(prm, &c);
+  if (s != SV_OK) return s;
+  if (B == 0) return SV_OK;
+  if (u_resample == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARG;
+  if (gamma > 0 && (draft_probs == nullptr || draft_ids == nullptr || u_accept == nullptr || !aligned16(draft_probs)))
+    return SV_ERR_INVALID_ARG;
+  const Plan p = make_plan(CALL_SAMPLE, B, gamma, V, dt, prm);
+  if (p.total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_UNSUPPORTED;  // beyond the static scratch
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return SV_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return verify_sample_impl(p, target_logits, dt, q_src_dense(draft_probs, V), draft_ids, u_accept, u_resample, B,
+                            gamma, V, prm, c, out_tokens, out_num_accepted, out_row_flags, ws, st);
 }
 
 sv_status spec_verify_sample_stats(const void* target_logits, sv_dtype dt, const float* draft_probs,

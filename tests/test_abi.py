@@ -271,3 +271,19 @@ def test_product_path_fails_loudly_without_library(tmp_path):
             L.load_library(str(tmp_path / "missing.so"))
         finally:
             L._LIB = saved
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch():
+    """The allocation-free call refuses, before any launch, sizes whose
+    workspace exceeds its static scratch (here 1024 x 5 x 256000 bf16 top-p)."""
+    lib = _lib()
+    prm = _P(0.7, 0, 0.95)
+    assert lib.spec_verify_workspace_size(1024, 4, 256000, 1, prm) > 64 * 1024 * 1024
+    code = lib.spec_verify_sample_noalloc(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1024, 4, 256000, prm,
+                                          FAKE, FAKE, FAKE, None)
+    assert code == 2  # SV_ERR_UNSUPPORTED
+    # argument errors come first, as in spec_verify_sample
+    assert lib.spec_verify_sample_noalloc(None, 1, FAKE, FAKE, FAKE, FAKE, 2, 3, 100, prm, FAKE, FAKE, FAKE,
+                                          None) == 1
+    assert lib.spec_verify_sample_noalloc(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 3, 100, _P(T=0.0), FAKE, FAKE,
+                                          FAKE, None) == 1
