@@ -48,6 +48,7 @@ STAGES = {
     5: ("statistics pass", "stats_pass", ["sv_device.h", "sv_verify.h"]),
     6: ("statistics finish", "stats_finish", ["sv_device.h", "sv_verify.h"]),
     7: ("greedy decision", "greedy", ["sv_device.h", "sv_verify.h"]),
+    8: ("dense q row sums", "qsum", ["sv_device.h", "sv_verify.h"]),
 }
 
 
@@ -356,11 +357,14 @@ def main():
             step_bytes += n_draft * V * qb  # the draft rows' own pass
         if stats:
             # statistics: untruncated rows stream logits and q again;
-            # truncated rows read sum(q) of a dense q for Z', nothing more
-            # without Z' or when q comes from the draft's logits
-            sb = B * G * V * (cfg.logit_bytes + qb) if untrunc else (0 if dl or not zqp else B * G * V * 4)
-            stage_bytes[5] = sb
-            step_bytes += sb
+            # truncated rows read sum(q) of a dense q for Z' (the row sums
+            # beside the target's passes), nothing more without Z' or when q
+            # comes from the draft's logits
+            if untrunc:
+                stage_bytes[5] = B * G * V * (cfg.logit_bytes + qb)
+            elif zqp and not dl:
+                stage_bytes[8] = B * G * V * 4
+            step_bytes += stage_bytes.get(5, 0) + stage_bytes.get(8, 0)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     def stage_line(st):

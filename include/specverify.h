@@ -12,8 +12,10 @@
  * ---------------------------------------
  * - Every tensor argument is a DEVICE pointer owned by the caller.  The
  *   library never allocates, frees or retains caller memory and keeps no
- *   state between calls (apart from the optional profiling hook
- *   spec_set_stage_timer).  All scratch lives in the caller's `workspace`
+ *   state between calls, apart from the optional profiling hook
+ *   (spec_set_stage_timer), the allocation-free call's per-GPU scratch, and
+ *   for the statistics calls with a dense q and Z' a side stream with two
+ *   events per (device, caller stream), made on the first such call.  All scratch lives in the caller's `workspace`
  *   (device memory of at least the reported workspace size, 16-byte
  *   aligned, contents need not be initialised).
  * - Layout is contiguous row-major.  `target_logits` is [B, gamma+1, V]
@@ -297,7 +299,8 @@ typedef enum {
   SV_STAGE_STATS_PASS = 5,    /* statistics: the pass over streamed rows and a dense q's sum */
   SV_STAGE_STATS_FINISH = 6,  /* statistics: the per-position finish */
   SV_STAGE_GREEDY = 7,        /* greedy decision */
-  SV_STAGE_COUNT = 8
+  SV_STAGE_QSUM = 8,          /* statistics: a dense q's row sums for Z' (on the library's side stream) */
+  SV_STAGE_COUNT = 9
 } sv_stage;
 
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both

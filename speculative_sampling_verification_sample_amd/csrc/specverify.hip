@@ -15,7 +15,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "specverify.h"
 #include "sv_device.h"
@@ -65,6 +67,8 @@ struct Plan {
   int scale_bits = 40;
   size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
   size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][kStatSums] (CALL_STATS, CALL_SAMPLE_STATS)
+  size_t off_qsum = 0;   // a dense q's row sums by chunk [B * gamma][nchq] (the same calls)
+  int nchq = 1;
   size_t total = 0;
 };
 
@@ -148,6 +152,10 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.off_spart = off;
   if (kind == CALL_STATS || kind == CALL_SAMPLE_STATS)
     off = align_up(off + (size_t)B * gamma * nch * kStatSums * sizeof(double), 256);
+  p.nchq = (int)((V + kQSumChunk - 1) / kQSumChunk);
+  p.off_qsum = off;
+  if (kind == CALL_STATS || kind == CALL_SAMPLE_STATS)
+    off = align_up(off + (size_t)B * gamma * p.nchq * sizeof(double), 256);
   p.total = std::max<size_t>(off, 256);
   return p;
 }
@@ -338,6 +346,82 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
   return SV_OK;
 }
 
+// ---- a second stream for work that does not depend on the target's passes
+// A call's dense-q row sums (only Z' needs them) read nothing the row passes
+// write, so they run on a stream of the library's beside the caller's: the
+// call records `fork` on its stream, the side stream waits for it, runs the
+// sums and records `join`, and the caller's stream waits for `join` before
+// the statistics finish.  One side stream (non-blocking, default priority)
+// and its two events per (device, caller stream), made on first use; under
+// graph capture the fork and join make the side work part of the graph.
+// Without them (creation failed) the sums run on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::map<std::pair<int, hipStream_t>, SideStream> g_side;
+
+const SideStream* side_stream(hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  auto it = g_side.find({dev, st});
+  if (it != g_side.end()) return it->second.s ? &it->second : nullptr;
+  SideStream ss;
+  bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    if (ss.join) (void)hipEventDestroy(ss.join);
+    if (ss.s) (void)hipStreamDestroy(ss.s);
+    ss = SideStream{};
+  }
+  auto& slot = g_side[{dev, st}];
+  slot = ss;
+  return slot.s ? &slot : nullptr;
+}
+
+// Starts a dense q's row sums (rows b * gamma + j, j < gamma) for Z' beside
+// the caller's stream; returns the event the statistics finish must wait
+// for (null: nothing to wait for, the sums went on the caller's stream or
+// are not needed).
+hipEvent_t fork_qsum(const Plan& p, const float* q, int32_t B, int32_t gamma, int32_t V, void* ws, hipStream_t st,
+                     sv_status* status) {
+  *status = SV_OK;
+  QSumArgs a;
+  a.q = q;
+  a.V = V;
+  a.rows = (int64_t)B * gamma;
+  a.nchq = p.nchq;
+  a.out = ws_at<double>(ws, p.off_qsum);
+  if (a.rows == 0) return nullptr;
+  const dim3 grid((unsigned)(a.rows * p.nchq));
+  const SideStream* ss = side_stream(st);
+  if (ss == nullptr) {
+    launch_stage(SV_STAGE_QSUM, qsum_kernel, grid, dim3(256), 0, st, a);
+    *status = launched();
+    return nullptr;
+  }
+  if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+    *status = SV_ERR_HIP;
+    return nullptr;
+  }
+  launch_stage(SV_STAGE_QSUM, qsum_kernel, grid, dim3(256), 0, ss->s, a);
+  *status = launched();
+  if (*status != SV_OK) return nullptr;
+  if (hipEventRecord(ss->join, ss->s) != hipSuccess) {
+    *status = SV_ERR_HIP;
+    return nullptr;
+  }
+  return ss->join;
+}
+
 // The sampling verify once q's source is known (dense, or the draft's
 // logits after their row passes).  `workspace` holds plan p's regions.
 // Ragged batches pass their draft offsets `cu` (gamma is then the maximum
@@ -348,7 +432,8 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
                              int32_t gamma, int32_t V, sv_sampling_params prm, const Expo& c, int32_t* out_tokens,
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
                              const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
-                             double beta = 1.0, bool force_rowfinal = false) {
+                             double beta = 1.0, bool force_rowfinal = false, const float* qsum_of = nullptr,
+                             hipEvent_t* qsum_join = nullptr) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
@@ -359,6 +444,12 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
       bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live)
          : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live);
   if (s != SV_OK) return s;
+  if (qsum_of != nullptr) {
+    // the statistics' dense-q row sums, beside the latency-bound kernels
+    // that follow the row pass
+    *qsum_join = fork_qsum(p, qsum_of, B, gamma, V, workspace, st, &s);
+    if (s != SV_OK) return s;
+  }
   if (p.trunc || force_rowfinal) {
     s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live)
            : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live);
@@ -459,7 +550,7 @@ struct StatsOut {
 // in plan p's info / kept regions at rows b * info_rpr + j.
 sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const QSrc& q, const StatsOut& so,
                        const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, const Expo& c, int info_rpr,
-                       void* workspace, hipStream_t st) {
+                       void* workspace, hipStream_t st, hipEvent_t qsum_join) {
   StatsArgs a;
   a.logits = target_logits;
   a.q = q;
@@ -468,9 +559,10 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.V = V;
   a.gamma = gamma;
   // Truncated rows whose statistics come from their kept lists need no
-  // pass; only rows without a list (rare) stream, one workgroup per row, so
-  // the launch is B * gamma workgroups that mostly return at once.
-  const bool lists = p.trunc && (q.dense == nullptr || so.z_qp == nullptr);
+  // pass (a dense q's sum for Z' comes from qsum_kernel); only rows without
+  // a list (rare) stream, one workgroup per row, so the launch is B * gamma
+  // workgroups that mostly return at once.
+  const bool lists = p.trunc;
   a.nchunks = lists ? 1 : p.nchunks;
   a.chunk = lists ? (int64_t)V : p.chunk;
   a.c64 = c.c64;
@@ -479,6 +571,8 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.info_rpr = info_rpr;
   a.kmax = kKMax;
   a.partials = ws_at<double>(workspace, p.off_spart);
+  a.qsum = ws_at<double>(workspace, p.off_qsum);
+  a.nchq = p.nchq;
   a.out_alpha = so.alpha;
   a.out_zpq = so.z_pq;
   a.out_zqp = so.z_qp;
@@ -496,6 +590,7 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   }
   sv_status s = launched();
   if (s != SV_OK) return s;
+  if (qsum_join != nullptr && hipStreamWaitEvent(st, qsum_join, 0) != hipSuccess) return SV_ERR_HIP;
   if (bf) launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<true>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
   else launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<false>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
   return launched();
@@ -508,13 +603,19 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
                             const Expo& c, void* workspace, hipStream_t st) {
   const bool bf = dt == SV_BF16;
   const int G1 = gamma + 1;
+  hipEvent_t join = nullptr;
   sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
                    : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
   if (s != SV_OK) return s;
+  if (q.dense != nullptr && so.z_qp != nullptr && p.trunc) {
+    // the dense-q row sums, beside the row finisher and the statistics pass
+    join = fork_qsum(p, q.dense, B, gamma, V, workspace, st, &s);
+    if (s != SV_OK) return s;
+  }
   s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
          : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
   if (s != SV_OK) return s;
-  return launch_stats(p, target_logits, bf, q, so, draft_ids, B, gamma, V, c, gamma, workspace, st);
+  return launch_stats(p, target_logits, bf, q, so, draft_ids, B, gamma, V, c, gamma, workspace, st, join);
 }
 
 // Row passes over the draft's logits [B, gamma, V] (plan CALL_DRAFT, in its
@@ -566,11 +667,14 @@ sv_status verify_sample_stats_impl(const Plan& p, const void* target_logits, sv_
                                    const float* u_resample, int32_t B, int32_t gamma, int32_t V,
                                    sv_sampling_params prm, const Expo& c, int32_t* out_tokens, int32_t* out_num_accepted,
                                    uint32_t* out_row_flags, void* workspace, hipStream_t st) {
+  hipEvent_t join = nullptr;
+  const bool qsum = q.dense != nullptr && so.z_qp != nullptr && p.trunc;
   sv_status s = verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
                                    out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0,
-                                   /*force_rowfinal=*/true);
+                                   /*force_rowfinal=*/true, qsum ? q.dense : nullptr, &join);
   if (s != SV_OK) return s;
-  return launch_stats(p, target_logits, dt == SV_BF16, q, so, draft_ids, B, gamma, V, c, gamma + 1, workspace, st);
+  return launch_stats(p, target_logits, dt == SV_BF16, q, so, draft_ids, B, gamma, V, c, gamma + 1, workspace, st,
+                      join);
 }
 
 // Greedy verify (uniform, or ragged with draft offsets `cu`).

@@ -1344,6 +1344,8 @@ struct StatsArgs {
   int32_t info_rpr;
   int32_t kmax;
   double* partials;     // [rows][nchunks][kStatSums]
+  const double* qsum;   // dense q's row sums by chunk [rows][nchq] (qsum_kernel), for Z'
+  int32_t nchq;
   float* out_alpha;
   float* out_zpq;
   float* out_zqp;
@@ -1366,6 +1368,59 @@ __device__ __forceinline__ bool stats_streamed(const StatsArgs& a, const RowInfo
   return ((ri.flags | a.q.info[r].flags) & RF_BIG) != 0 || a.qkept == nullptr;
 }
 
+// Sum of a dense q over each of its rows, for Z' of rows whose p is a kept
+// list (Z' = sum q - sum over the list of q + sum over the list of
+// (q - p)+).  It reads nothing but q, so it runs beside the target's passes
+// (the statistics finish waits for it).  Workgroup c of row r sums the
+// kQSumChunk floats [c * kQSumChunk, ...) of the row: each thread eight
+// 16-byte segments, all in flight at once, added in double in a fixed order.
+constexpr int kQSumChunk = 256 * 32;  // floats per workgroup (32 KB)
+
+struct QSumArgs {
+  const float* q;   // [rows][V]
+  int64_t V;
+  int64_t rows;
+  int32_t nchq;     // chunks per row
+  double* out;      // [rows][nchq]
+};
+
+__global__ void __launch_bounds__(256) qsum_kernel(QSumArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t blk = blockIdx.x;
+  const int64_t r = blk / a.nchq;
+  const int c = (int)(blk - r * a.nchq);
+  __shared__ double s_w[4];
+  const int64_t x0 = (int64_t)c * kQSumChunk, x1 = min(x0 + (int64_t)kQSumChunk, a.V);
+  const float* row = a.q + r * a.V;
+  const bool vec = (a.V & 3) == 0;  // rows (and so segments of 4) 16-byte aligned
+  constexpr int kSegs = kQSumChunk / (256 * 4);  // 16-byte segments per thread
+  double acc = 0.0;
+  uint4 w[kSegs];
+#pragma unroll
+  for (int k = 0; k < kSegs; ++k) {
+    const int64_t x = x0 + ((int64_t)k * 256 + tid) * 4;
+    if (vec && x + 4 <= x1) {
+      w[k] = *reinterpret_cast<const uint4*>(row + x);
+    } else {
+      float f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = x + i < x1 ? row[x + i] : 0.0f;
+      w[k] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kSegs; ++k) {
+    acc += (double)__uint_as_float(w[k].x);
+    acc += (double)__uint_as_float(w[k].y);
+    acc += (double)__uint_as_float(w[k].z);
+    acc += (double)__uint_as_float(w[k].w);
+  }
+  acc = wave_sum_d(acc);
+  if (lane == 0) s_w[wid] = acc;
+  __syncthreads();
+  if (tid == 0) a.out[r * a.nchq + c] = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
 // QLOG: q comes from the draft's logits (else dense).
 template <bool BF16, bool QLOG>
 __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
@@ -1382,37 +1437,15 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   for (int i = 0; i < kStatSums; ++i) sm[i] = 0.0;
   __shared__ double s_p[4][kStatSums];
   const bool big = stats_streamed(a, ri, r);
-  // Rows finished from their lists skip the pass, unless Z' needs sum(q);
-  // nothing reads their partials then (the test is the same for the whole
-  // workgroup).
-  if ((ri.flags & RF_NONFINITE) || !(big || (!QLOG && a.out_zqp != nullptr))) return;
+  // Rows finished from their lists skip the pass (a dense q's sum comes
+  // from qsum_kernel); nothing reads their partials (the test is the same
+  // for the whole workgroup).
+  if ((ri.flags & RF_NONFINITE) || !big) return;
   const QRow qr = q_row(a.q, r);
   // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
   const bool vec = (a.V & 7) == 0;
   const int64_t ngroups = (x1 - x0 + 7) / 8;
-  if (!big) {
-    // a dense q's sum only (Z' of a row finished from its list): q alone is
-    // streamed, kQ segments of 32 bytes in flight per thread
-    constexpr int kQ = 8;
-    for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kQ * 256) {
-      float qv[kQ][8];
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-        const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
-        if (vec && x + 8 <= x1) {
-          qr.raw8_whole(x, qv[u]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) qv[u][k] = x + k < x1 ? qr.raw_at(x + k) : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sm[ST_WQ] += (double)qv[u][k];
-      }
-    }
-  } else {
+  {
     const double invS = 1.0 / ri.S;  // float exponentials: only to tell p < q from p > q
     constexpr int kU = 2;
     for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kU * 256) {
@@ -1550,7 +1583,7 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       // Z' not asked for: neither sum(q) nor q's list is read
     } else if (!qlog) {
       double sq = 0.0;
-      for (int c = lane; c < a.nchunks; c += kWave) sq += a.partials[(r * a.nchunks + c) * kStatSums + ST_WQ];
+      for (int c = lane; c < a.nchq; c += kWave) sq += a.qsum[r * a.nchq + c];
       zqp = (wave_sum_d(sq) - sqk) + qp;
     } else {
       // Z' = sum over q's kept set of (q - p)_+, with p read at its ids
