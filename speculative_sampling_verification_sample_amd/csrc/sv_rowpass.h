@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     for (int i = 0; i < kUnroll; ++i) {
       const int64_t u = g.U0 + (k0 + i) * BS + tid;
       wv[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (k0 + i < nsteps && u < g.U1) wv[i] = base[u];
+      if (k0 + i < nsteps && u < g.U1) wv[i] = ld_stream(base + u);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   for (int k0 = 0; k0 < NU; k0 += kUnroll) {
     uint4 wv[kUnroll];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) wv[i] = base[g.U0 + min((k0 + i) * BS + tid, nunits - 1)];
+    for (int i = 0; i < kUnroll; ++i) wv[i] = ld_stream(base + g.U0 + min((k0 + i) * BS + tid, nunits - 1));
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const int k = k0 + i;

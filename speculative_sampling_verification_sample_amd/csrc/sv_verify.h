@@ -1373,7 +1373,8 @@ __device__ __forceinline__ bool stats_streamed(const StatsArgs& a, const RowInfo
 // (q - p)+).  It reads nothing but q, so it runs beside the target's passes
 // (the statistics finish waits for it).  Workgroup c of row r sums the
 // kQSumChunk floats [c * kQSumChunk, ...) of the row: each thread eight
-// 16-byte segments, all in flight at once, added in double in a fixed order.
+// 16-byte segments (non-temporal loads), all in flight at once, added in
+// double in a fixed order.
 constexpr int kQSumChunk = 256 * 32;  // floats per workgroup (32 KB)
 
 struct QSumArgs {
@@ -1400,7 +1401,7 @@ __global__ void __launch_bounds__(256) qsum_kernel(QSumArgs a) {
   for (int k = 0; k < kSegs; ++k) {
     const int64_t x = x0 + ((int64_t)k * 256 + tid) * 4;
     if (vec && x + 4 <= x1) {
-      w[k] = *reinterpret_cast<const uint4*>(row + x);
+      w[k] = ld_stream(reinterpret_cast<const uint4*>(row + x));
     } else {
       float f[4];
 #pragma unroll
