@@ -428,51 +428,131 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---- wave reductions / scans (fixed butterfly order: deterministic) -------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// ---- wave reductions / scans over DPP (fixed order: deterministic) --------
+// Cross-lane moves use the data-parallel primitives of the VALU (DPP: the
+// source lane is picked by a fixed pattern inside the instruction), not the
+// LDS crossbar, so one step costs a move and an add instead of an LDS round
+// trip.  Patterns used (CDNA encodings): quad_perm within groups of 4 lanes,
+// row_shr:n (lane l of a 16-lane row reads lane l - n of that row),
+// row_half_mirror and row_mirror (lane l reads 7 - l / 15 - l within its
+// half-row / row), row_bcast:15 and row_bcast:31 (the last lane of row r,
+// resp. of rows 0-1, is read by the rows the row mask selects), and wave_shr:1
+// (lane l reads lane l - 1 of the whole wave).  Lanes whose source lies
+// outside the pattern's range, or whose row the mask leaves out, keep `old`.
+// Every caller runs these with all 64 lanes active.
+enum : int {
+  kDppQuadSwap1 = 0xB1,  // quad_perm [1,0,3,2]: lane l reads l ^ 1
+  kDppQuadSwap2 = 0x4E,  // quad_perm [2,3,0,1]: lane l reads l ^ 2
+  kDppRowShr = 0x110,    // + n: row_shr:n
+  kDppRowMirror = 0x140,
+  kDppRowHalfMirror = 0x141,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143,
+  kDppWaveShr1 = 0x138,
+};
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
 }
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+// 64-bit values move as two 32-bit halves under the same pattern.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long old, unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)old, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  return __longlong_as_double(
+      (long long)dpp_u64<CTRL, ROW_MASK>((unsigned long long)__double_as_longlong(old),
+                                         (unsigned long long)__double_as_longlong(v)));
+}
+
+// Lane 63's value, uniform over the wave.
+__device__ __forceinline__ int wave_last_i(int v) { return __builtin_amdgcn_readlane(v, kWave - 1); }
+__device__ __forceinline__ uint32_t wave_last_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+__device__ __forceinline__ float wave_last_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+__device__ __forceinline__ unsigned long long wave_last_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ double wave_last_d(double v) {
+  return __longlong_as_double((long long)wave_last_u64((unsigned long long)__double_as_longlong(v)));
+}
+
+// Lane l - 1's value (lane 0: `first`).
+__device__ __forceinline__ double wave_prev_d(double v, double first) { return dpp_f64<kDppWaveShr1>(first, v); }
+__device__ __forceinline__ int wave_prev_i(int v, int first) { return dpp_i32<kDppWaveShr1>(first, v); }
+
+// Reduction: quad swaps and the two mirrors leave every lane of a 16-lane
+// row with its row's result; the broadcasts fold row 0 into row 1, row 2
+// into row 3, then rows 0-1 into rows 2-3, so lane 63 ends with
+// (r3 . r2) . (r1 . r0), which is read back to all lanes.  OP(a, b) must be
+// commutative (every lane then holds bit-identical row results); ID is its
+// identity.
+#define SV_WAVE_REDUCE(T, DPP, LAST, OP, ID)            \
+  do {                                                   \
+    v = OP(v, DPP<kDppQuadSwap1>(ID, v));                \
+    v = OP(v, DPP<kDppQuadSwap2>(ID, v));                \
+    v = OP(v, DPP<kDppRowHalfMirror>(ID, v));            \
+    v = OP(v, DPP<kDppRowMirror>(ID, v));                \
+    v = OP(v, DPP<kDppRowBcast15, 0xa>(ID, v));          \
+    v = OP(v, DPP<kDppRowBcast31, 0xc>(ID, v));          \
+    return LAST(v);                                      \
+  } while (0)
+
+__device__ __forceinline__ float op_fmax(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ uint32_t op_or(uint32_t a, uint32_t b) { return a | b; }
+__device__ __forceinline__ uint32_t op_umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ int op_addi(int a, int b) { return a + b; }
+__device__ __forceinline__ double op_addd(double a, double b) { return a + b; }
+__device__ __forceinline__ unsigned long long op_addu64(unsigned long long a, unsigned long long b) { return a + b; }
+
+__device__ __forceinline__ float wave_max(float v) { SV_WAVE_REDUCE(float, dpp_f32, wave_last_f, op_fmax, kNegInf); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) { SV_WAVE_REDUCE(uint32_t, dpp_u32, wave_last_u32, op_or, 0u); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, kWave));
-  return v;
+  SV_WAVE_REDUCE(uint32_t, dpp_u32, wave_last_u32, op_umax, 0u);
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ int wave_sum_i(int v) { SV_WAVE_REDUCE(int, dpp_i32, wave_last_i, op_addi, 0); }
+__device__ __forceinline__ double wave_sum_d(double v) { SV_WAVE_REDUCE(double, dpp_f64, wave_last_d, op_addd, 0.0); }
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  SV_WAVE_REDUCE(unsigned long long, dpp_u64, wave_last_u64, op_addu64, 0ull);
 }
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-// Inclusive prefix sum across lanes (lane 0 first).
-__device__ __forceinline__ double wave_incl_scan_d(double v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan_i(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
-  return v;
-}
+
+// Inclusive prefix sum across lanes (lane 0 first): row_shr 1, 2, 4, 8 scan
+// each 16-lane row, then the broadcasts carry rows 0, 0-1 and 2 forward.
+#define SV_WAVE_SCAN(DPP, ZERO)                     \
+  do {                                              \
+    v = v + DPP<kDppRowShr + 1>(ZERO, v);           \
+    v = v + DPP<kDppRowShr + 2>(ZERO, v);           \
+    v = v + DPP<kDppRowShr + 4>(ZERO, v);           \
+    v = v + DPP<kDppRowShr + 8>(ZERO, v);           \
+    v = v + DPP<kDppRowBcast15, 0xa>(ZERO, v);      \
+    v = v + DPP<kDppRowBcast31, 0xc>(ZERO, v);      \
+    return v;                                       \
+  } while (0)
+
+__device__ __forceinline__ double wave_incl_scan_d(double v) { SV_WAVE_SCAN(dpp_f64, 0.0); }
+__device__ __forceinline__ int wave_incl_scan_i(int v) { SV_WAVE_SCAN(dpp_i32, 0); }
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) { SV_WAVE_SCAN(dpp_u64, 0ull); }
+
+#undef SV_WAVE_SCAN
+#undef SV_WAVE_REDUCE
+
 // (value, index) argmax: larger value wins, equal values keep the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
@@ -480,13 +560,24 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
     i = i2;
   }
 }
+// Argmax over the wave with the same pattern as the reductions (the merge
+// is commutative on (value, index) pairs of distinct indices).
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float v2 = __shfl_xor(v, o, kWave);
-    int i2 = __shfl_xor(i, o, kWave);
-    argmax_merge(v, i, v2, i2);
+#define SV_ARGMAX_STEP(CTRL, RM)                                                   \
+  {                                                                                \
+    const float v2 = dpp_f32<CTRL, RM>(kNegInf, v);                                \
+    const int i2 = dpp_i32<CTRL, RM>(0x7fffffff, i);                               \
+    argmax_merge(v, i, v2, i2);                                                    \
   }
+  SV_ARGMAX_STEP(kDppQuadSwap1, 0xf)
+  SV_ARGMAX_STEP(kDppQuadSwap2, 0xf)
+  SV_ARGMAX_STEP(kDppRowHalfMirror, 0xf)
+  SV_ARGMAX_STEP(kDppRowMirror, 0xf)
+  SV_ARGMAX_STEP(kDppRowBcast15, 0xa)
+  SV_ARGMAX_STEP(kDppRowBcast31, 0xc)
+#undef SV_ARGMAX_STEP
+  v = wave_last_f(v);
+  i = wave_last_i(i);
 }
 
 // Exact merge of (s, R) pairs: s * 2^R summed onto the larger reference.

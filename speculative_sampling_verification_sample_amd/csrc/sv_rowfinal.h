@@ -177,8 +177,7 @@ __device__ __forceinline__ unsigned long long to_fixed(float e) {
 
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s_tmp /*[4]*/) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+v = wave_sum_u64(v);
   __syncthreads();
   if (lane == 0) s_tmp[wid] = v;
   __syncthreads();
@@ -242,12 +241,7 @@ __device__ __forceinline__ bool block_select_mass(const uint32_t* keys, float c,
     if (wid == 0) {
       unsigned long long c0 = mh[255 - 4 * lane], c1 = mh[254 - 4 * lane], c2 = mh[253 - 4 * lane],
                          c3 = mh[252 - 4 * lane];
-      unsigned long long ls = c0 + c1 + c2 + c3, incl = ls;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        unsigned long long t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
+      const unsigned long long ls = c0 + c1 + c2 + c3, incl = wave_incl_scan_u64(ls);
       const unsigned long long above = *s_above;
       uint64_t hit = ballot((double)(above + incl) >= target);
       if (!hit) {
@@ -508,11 +502,7 @@ __device__ __forceinline__ void exact_row(const RowFinalArgs& a, int64_t r, int6
         unsigned long long c0 = mhist[255 - 4 * lane], c1 = mhist[254 - 4 * lane], c2 = mhist[253 - 4 * lane],
                            c3 = mhist[252 - 4 * lane];
         unsigned long long ls = c0 + c1 + c2 + c3;
-        unsigned long long incl = ls;
-        for (int o = 1; o < 64; o <<= 1) {
-          unsigned long long t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
+        const unsigned long long incl = wave_incl_scan_u64(ls);
         unsigned long long above = s_above;
         uint64_t hit = ballot((double)(above + incl) >= target);
         int src = hit ? (int)__builtin_ctzll(hit) : -1;

@@ -508,7 +508,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   for (int r = 0; r < 3; ++r)
     if (lon[r]) nc += count_unit(lw[r], lrel[r]);
   const int incl = wave_incl_scan_i(nc);
-  const int wtot = __shfl(incl, kWave - 1, kWave);
+  const int wtot = wave_last_i(incl);
   int wbase = 0;
   if (lane == kWave - 1 && wtot > 0) wbase = atomicAdd(&s_out, wtot);
   wbase = __shfl(wbase, kWave - 1, kWave);

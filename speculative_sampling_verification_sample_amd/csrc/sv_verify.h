@@ -100,7 +100,7 @@ __device__ int draw_from_list(const Cand* L, int n, double S64, float R, double 
       for (int k = 0; k < kDrawBlk; ++k) {
         if (i0 + k * kWave >= n) break;
         const double incl = wave_incl_scan_d(w[k]);
-        carry = carry + __shfl(incl, kWave - 1, kWave);
+        carry = carry + wave_last_d(incl);
       }
     }
     return carry;
@@ -132,7 +132,7 @@ __device__ int draw_from_list(const Cand* L, int n, double S64, float R, double 
       }
       const uint64_t pos = ballot(i < n && w[k] > 0.0);
       if (pos) lastpos = __shfl(id[k], 63 - (int)__builtin_clzll(pos), kWave);
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+      carry = carry + wave_last_d(incl);
     }
   }
   return token >= 0 ? token : lastpos;
@@ -543,8 +543,7 @@ __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
       const double incl = wave_incl_scan_d(seg);
       if (t >= 0.0) {
         const double C = carry + incl;
-        double ex = __shfl_up(C, 1, kWave);
-        if (lane == 0) ex = carry;
+        const double ex = wave_prev_d(C, carry);
         const uint64_t hit = ballot(in && C > t);
         if (hit) {
           const int src = (int)__builtin_ctzll(hit);
@@ -564,7 +563,7 @@ __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
         const uint64_t pos = ballot(in && lastk >= 0);
         if (pos) lastpos = __shfl(x + lastk, 63 - (int)__builtin_clzll(pos), kWave);
       }
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+      carry = carry + wave_last_d(incl);
     }
     return QOut{carry, token, lastpos};
   };
@@ -732,8 +731,7 @@ __device__ __forceinline__ void block_sum4(const double (&v)[4], double (*s_w)[4
 __device__ __forceinline__ double chunk_excl(double seg, double* s_w) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double incl = wave_incl_scan_d(seg);
-  double ex = __shfl_up(incl, 1, kWave);
-  if (lane == 0) ex = 0.0;
+  const double ex = wave_prev_d(incl, 0.0);
   __syncthreads();
   if (lane == 63) s_w[wid] = incl;
   __syncthreads();
@@ -858,7 +856,7 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
       double carry = 0.0;
       for (int k0 = 0; k0 < a.nch4; k0 += kWave) {
         const double incl = wave_incl_scan_d(wchunk(k0 + lane, res));
-        carry = carry + __shfl(incl, kWave - 1, kWave);
+        carry = carry + wave_last_d(incl);
       }
       return carry;
     };
@@ -877,8 +875,7 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
       const double pk = wchunk(k, residual);
       const double incl = wave_incl_scan_d(pk);
       const double C = carry + incl;
-      double ex = __shfl_up(C, 1, kWave);
-      if (lane == 0) ex = carry;
+      const double ex = wave_prev_d(C, carry);
       const uint64_t pos = ballot(k < a.nch4 && pk > 0.0);
       if (pos) lastc = k0 + 63 - (int)__builtin_clzll(pos);
       const uint64_t hit = ballot(k < a.nch4 && C > t);
@@ -888,7 +885,7 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
         cex = __shfl(ex, src, kWave);
         break;
       }
-      carry = carry + __shfl(incl, kWave - 1, kWave);
+      carry = carry + wave_last_d(incl);
     }
     if (cstar < 0) {
       // rounding left no chunk above t: the last positive token of the last
@@ -956,8 +953,7 @@ __device__ __forceinline__ double block_excl_scan(double v, double& total, doubl
   constexpr int NW = BS / kWave;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   double incl = wave_incl_scan_d(v);
-  double ex = __shfl_up(incl, 1, kWave);
-  if (lane == 0) ex = 0.0;
+  const double ex = wave_prev_d(incl, 0.0);
   __syncthreads();
   if (lane == 63) s_wt[wid] = incl;
   __syncthreads();
