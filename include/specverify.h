@@ -42,7 +42,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations have int as their underlying type in C++ too, so every
+ * int a caller passes for one is a value of that type; the library checks
+ * the value and returns SV_ERR_INVALID_ARG for one it does not know. */
+#ifdef __cplusplus
+#define SV_ENUM_INT : int
+#else
+#define SV_ENUM_INT
+#endif
+
+typedef enum SV_ENUM_INT {
   SV_OK = 0,
   SV_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or parameter */
   SV_ERR_UNSUPPORTED = 2, /* a size the kernels do not handle (e.g. V >= 2^31) */
@@ -50,7 +59,7 @@ typedef enum {
   SV_ERR_HIP = 4          /* a kernel launch failed                           */
 } sv_status;
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+typedef enum SV_ENUM_INT { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 /* Decoding rules that turn target logits into the processed distribution p
  * ([WR] §2.3: p is the distribution after the production decoding rules;
@@ -290,7 +299,7 @@ sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dt
                                                size_t workspace_bytes, void* stream);
 
 /* Kernel stages of a call, for the profiling hook below. */
-typedef enum {
+typedef enum SV_ENUM_INT {
   SV_STAGE_ROWPASS = 0,       /* the streaming pass over the target logits (not the draft rows') */
   SV_STAGE_ROWFINAL = 1,      /* the target rows' finisher (kept sets, normalisers, draft gather) */
   SV_STAGE_ACCEPT = 2,        /* the acceptance decision launch (with the draws it takes itself) */

@@ -7,7 +7,10 @@ fails with an explicit error; there is no fallback implementation.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+# SPECVERIFY_LIB names another build of the same library (the host-sanitized
+# one, for the ABI checks under AddressSanitizer).
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libspecverify.so")
 
 SV_OK = 0
 SV_F32 = 0

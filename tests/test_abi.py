@@ -57,6 +57,8 @@ def test_status_strings():
     for code in range(5):
         assert lib.spec_status_string(code)
     assert lib.spec_status_string(0) == b"ok"
+    assert lib.spec_status_string(99) == b"unknown status"
+    assert lib.spec_status_string(-1) == b"unknown status"
 
 
 def test_workspace_size_validation():
