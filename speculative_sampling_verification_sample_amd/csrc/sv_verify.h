@@ -838,7 +838,7 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
   uint32_t extra = 0;
   if (wid == 0) {
     // normalisers: chunk sums in a fixed order (lanes over chunks, then the
-    // butterfly)
+    // wave reduction)
     double sp = 0.0, sq = 0.0;
     for (int k = lane; k < a.nch4; k += kWave) {
       sp += P[k * 4 + 0];
