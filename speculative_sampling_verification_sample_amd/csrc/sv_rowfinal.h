@@ -186,7 +186,7 @@ v = wave_sum_u64(v);
   return t;
 }
 
-// Key of the `need`-th largest entry (count), entries with key >= floor only.
+// Key of the `need`-th largest entry of the list (counted with multiplicity).
 template <bool BF16>
 __device__ uint32_t block_select_count(const uint32_t* keys, int n, int need, uint32_t* hist, int* s_dn) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
