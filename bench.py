@@ -453,12 +453,12 @@ def main():
                          f"the same {cfg.name} batch, {el1:.1f} s"}
         if not rg:
             # the pool: the first n requests of the batch, n sized from the
-            # single-process rate to about --cpu-seconds of work per core
-            # (a batch smaller than that is run `rep` times over)
+            # single-process rate to about --cpu-seconds of work per core; a
+            # batch smaller than that is passed over again, as many whole
+            # times as fit in that time
             workers = opool.default_workers()
             want = max(workers, math.ceil(done / el1 * workers * args.cpu_seconds))
             n = int(min(B, want))
-            rep = max(1, want // n)
             arrays = dict(logits=(wu.logits[:n].view(torch.int16) if wu.logits.dtype == torch.bfloat16
                                   else wu.logits[:n]).cpu().numpy(), ids=wu.ids[:n].cpu().numpy())
             prm = dict(T=cfg.temperature, top_k=cfg.top_k, top_p=cfg.top_p, beta=beta)
@@ -477,14 +477,22 @@ def main():
             with opool.make_pool(workers) as pl:
                 opool.run("greedy", dict(logits=arrays["logits"][:workers], ids=arrays["ids"][:workers]), {},
                           min(workers, n), pool=pl)  # workers started and warm
+                need = {"greedy": ("logits", "ids"),
+                        "sample": ("logits", "q", "ids", "u_accept", "u_resample"),
+                        "stats": ("logits", "q", "ids"),
+                        "sample_draft_logits": ("logits", "draft_logits", "ids", "u_accept", "u_resample"),
+                        "stats_draft_logits": ("logits", "draft_logits", "ids")}
+                # one pass, then as many more (in one go) as fit the time
+                def passes(r):
+                    for k in kinds:
+                        opool.run(k, {a: arrays[a] for a in need[k]}, prm, n, pool=pl, repeat=r)
                 t0 = time.perf_counter()
-                for k in kinds:
-                    need = {"greedy": ("logits", "ids"),
-                            "sample": ("logits", "q", "ids", "u_accept", "u_resample"),
-                            "stats": ("logits", "q", "ids"),
-                            "sample_draft_logits": ("logits", "draft_logits", "ids", "u_accept", "u_resample"),
-                            "stats_draft_logits": ("logits", "draft_logits", "ids")}[k]
-                    opool.run(k, {a: arrays[a] for a in need}, prm, n, pool=pl, repeat=rep)
+                passes(1)
+                el_one = time.perf_counter() - t0
+                more = int((args.cpu_seconds - el_one) // el_one) if el_one > 0 else 0
+                if more > 0:
+                    passes(more)
+                rep = 1 + max(0, more)
                 el2 = time.perf_counter() - t0
             cpu.update(value=rep * n * (G + 1) / el2, cores=workers,
                        sample=cpu["sample"] + f"; pool: the first {n} requests"
