@@ -388,6 +388,7 @@ def main():
     dom_line = stage_line(dom)
     # counters are taken on uniform batches at the workload's own B
     traffic = None if (rg or args.batch is not None or dl or lenient) else read_traffic(dom, cfg.name)
+    k1_traffic = None if (rg or args.batch is not None or dl or lenient) else read_traffic(0, cfg.name)
     log(" ".join(f"{n}={v['us']:.1f}us" for n, v in stages.items()))
 
     # ---- CPU oracle baseline on a bounded sample: one process, then a pool
@@ -540,7 +541,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": STAGES[dom][0], "achieved": dom_line["GBps"], "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": dom_line["frac"], "traffic": traffic,
                      "alg_bytes_per_launch": dom_line["alg_bytes"], "launch_us": dom_line["us"],
-                     "step_frac": step_gbps / PEAK_GBPS, "stages": stages},
+                     "step_frac": step_gbps / PEAK_GBPS, "stages": stages,
+                     # the target logits' row pass (K1), with its own measured traffic
+                     "row_pass": (dict(stages[STAGES[0][0]], traffic=k1_traffic)
+                                  if STAGES[0][0] in stages else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
