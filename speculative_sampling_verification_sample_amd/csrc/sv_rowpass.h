@@ -472,34 +472,47 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
       lrel[r] = rel0 + k * BS * EPV;
     }
   }
-  auto count_unit = [&](const uint4& w, int rel) {
+  // Bit e of a unit's mask: element e reaches t0 and lies inside the chunk
+  // (elements [max(0, -rel), min(EPV, n - rel)) of the unit do).  The count
+  // is the mask's population; the elements are then taken out of the raw
+  // 16 bytes by their index, only for the set bits.
+  auto unit_mask = [&](const uint4& w, int rel) -> uint32_t {
     float x[EPV];
     widen<BF16>(w, x);
-    int cnt = 0;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) cnt += (x[e] >= t0 && (unsigned)(rel + e) < (unsigned)n) ? 1 : 0;
-    return cnt;
+    for (int e = 0; e < EPV; ++e) m |= (x[e] >= t0) ? (1u << e) : 0u;
+    const int lo = max(0, -rel), hi = min(EPV, n - rel);
+    return hi > lo ? m & ((1u << hi) - (1u << lo)) : 0u;
   };
-  auto emit_unit = [&](const uint4& w, int rel, int& pos) {
-    float x[EPV];
-    widen<BF16>(w, x);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      if (x[e] >= t0 && (unsigned)(rel + e) < (unsigned)n) {
-        if (pos < a.cap_out) {
-          Cand ce;
-          ce.v = x[e];
-          ce.idx = id0 + rel + e;
-          dst[pos] = ce;
-        }
-        ++pos;
+  // (selects on 64-bit halves, so that the unit stays in registers)
+  auto element = [&](uint4 w, int e) -> float {
+    const int q = BF16 ? e >> 1 : e;  // 32-bit word of the element
+    const uint64_t h = (q & 2) ? (((uint64_t)w.w << 32) | w.z) : (((uint64_t)w.y << 32) | w.x);
+    const uint32_t v = (q & 1) ? (uint32_t)(h >> 32) : (uint32_t)h;
+    if constexpr (BF16) return __uint_as_float((e & 1) ? (v & 0xffff0000u) : (v << 16));
+    else return __uint_as_float(v);
+  };
+  auto emit_unit = [&](const uint4& w, int rel, uint32_t m, int& pos) {
+    while (m != 0u) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if (pos < a.cap_out) {
+        Cand ce;
+        ce.v = element(w, e);
+        ce.idx = id0 + rel + e;
+        dst[pos] = ce;
       }
+      ++pos;
     }
   };
+  uint32_t lm[3];
   int nc = 0;
 #pragma unroll
-  for (int r = 0; r < 3; ++r)
-    if (lon[r]) nc += count_unit(lw[r], lrel[r]);
+  for (int r = 0; r < 3; ++r) {
+    lm[r] = lon[r] ? unit_mask(lw[r], lrel[r]) : 0u;
+    nc += __builtin_popcount(lm[r]);
+  }
   const int incl = wave_incl_scan_i(nc);
   const int wtot = wave_last_i(incl);
   int wbase = 0;
@@ -507,18 +520,17 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   wbase = __shfl(wbase, kWave - 1, kWave);
   int pos = wbase + incl - nc;
 #pragma unroll
-  for (int r = 0; r < 3; ++r)
-    if (lon[r]) emit_unit(lw[r], lrel[r], pos);
+  for (int r = 0; r < 3; ++r) emit_unit(lw[r], lrel[r], lm[r], pos);
   // lanes with more than two further units (ties, flat rows): one at a time
   while (more != 0) {
     const int k = __builtin_ctz(more);
     more &= more - 1;
     const uint4 w = base[g.U0 + k * BS + tid];
     const int rel = rel0 + k * BS * EPV;
-    const int cnt = count_unit(w, rel);
-    if (cnt > 0) {
-      int p2 = atomicAdd(&s_out, cnt);
-      emit_unit(w, rel, p2);
+    const uint32_t m = unit_mask(w, rel);
+    if (m != 0u) {
+      int p2 = atomicAdd(&s_out, __builtin_popcount(m));
+      emit_unit(w, rel, m, p2);
     }
   }
   __syncthreads();
