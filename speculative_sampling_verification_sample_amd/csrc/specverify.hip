@@ -354,13 +354,17 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
 // the statistics finish.  One side stream (non-blocking, default priority)
 // and its two events per (device, caller stream), made on first use; under
 // graph capture the fork and join make the side work part of the graph.
-// Without them (creation failed) the sums run on the caller's stream.
+// Without them (creation failed, or kMaxSideStreams pairs already made:
+// the library keeps what it makes until the process ends, so a caller that
+// cycles through many streams cannot make it grow without bound) the sums
+// run on the caller's stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
 std::map<std::pair<int, hipStream_t>, SideStream> g_side;
+constexpr size_t kMaxSideStreams = 64;
 
 const SideStream* side_stream(hipStream_t st) {
   int dev = -1;
@@ -371,6 +375,7 @@ const SideStream* side_stream(hipStream_t st) {
   std::lock_guard<std::mutex> lock(g_side_mu);
   auto it = g_side.find({dev, st});
   if (it != g_side.end()) return it->second.s ? &it->second : nullptr;
+  if (g_side.size() >= kMaxSideStreams) return nullptr;
   SideStream ss;
   bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
