@@ -114,6 +114,30 @@ def test_graph_replay_matches_eager():
             assert torch.equal(a, b)
 
 
+def test_calls_on_several_streams():
+    """The dense-q sums run on a side stream of the caller's stream: calls
+    enqueued on three caller streams at once, each with its own workspace
+    and outputs, give the default stream's results bit for bit."""
+    w = generate("c5", DEV, B=4, V=50000)
+    c = w.cfg
+    ref = [t.clone() for t in sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample,
+                                                     c.temperature, c.top_k, c.top_p)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    res = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            res.append(sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature,
+                                              c.top_k, c.top_p))
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for r in res:
+        for a, b in zip(r, ref):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("dl", [False, True])
 @pytest.mark.parametrize("name,kw", [
     ("c2", dict(B=4)),
