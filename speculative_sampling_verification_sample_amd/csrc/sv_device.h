@@ -170,15 +170,21 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // The three exponentials against the integral reference R (see the top of
 // this file).
 __device__ __forceinline__ float e_of(float x, float c, float R) { return ex2(__builtin_fmaf(x, c, -R)); }
+// x = -inf is taken as the lowest finite float: then x * cl stays finite
+// whatever cl's sign, the exponent is -inf and the result 0 (-inf * cl
+// would be +inf for a negative cl, and +inf - inf a NaN); NaN still
+// propagates (the NaN-keeping maximum).
 __device__ __forceinline__ float e2_of(float x, float c, float cl, float R) {
-  return ex2(__builtin_fmaf(x, cl, __builtin_fmaf(x, c, -R)));
+  const float xs = __builtin_elementwise_maximum(x, -3.40282347e38f);
+  return ex2(__builtin_fmaf(xs, cl, __builtin_fmaf(xs, c, -R)));
 }
 // 2^t in double for t <= ~2: 2^n e^g with n = rint(t), g = (t - n) ln 2,
 // |g| <= 0.347, and e^g by its Taylor series through g^13 (the first term
 // left out is below 1e-17), evaluated by Horner's rule with the
 // coefficients as scalar operands (no vector registers held for them).
-// Below t = -1074 the result is 0.
+// Below t = -1100 (-inf included) the result is 0; NaN stays NaN.
 __device__ __forceinline__ double exp2_d(double t) {
+  if (t < -1100.0) return 0.0;
   const double n = __builtin_rint(t);
   const double g = (t - n) * 0.6931471805599453094;
   double p = 1.0 / 6227020800.0;              // 1/13!
@@ -247,6 +253,7 @@ struct QRow {
   int64_t zoff;        // element offset of the row in z
   double invS;         // 1 / S (float exponentials)
   double invS64;       // 1 / S64, 0 when S64 is not known (untruncated draft rows)
+  double S64;          // S64 itself (0 when not known)
   double c64;
   float R, tau, c, cl;
   int32_t zbf16;
@@ -268,6 +275,14 @@ struct QRow {
     if (z == nullptr) return 0.0;
     if (bad) return __builtin_nan("");
     return v >= tau ? e64_of(v, c64, R) * invS64 : 0.0;
+  }
+  // The same by a true division e64 / S64 (the statistics: a one-token
+  // distribution is then exactly 1, as in the plain definition).
+  __device__ __forceinline__ double q64_div(float v) const {
+    if (dense) return (double)v;
+    if (z == nullptr) return 0.0;
+    if (bad) return __builtin_nan("");
+    return v >= tau ? e64_of(v, c64, R) / S64 : 0.0;
   }
   // The unnormalised double weight of a raw value: q itself for a dense
   // row, e64 of the logit for draft logits (whose normaliser the caller
@@ -367,6 +382,7 @@ __device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
   r.zbf16 = s.zbf16;
   r.invS = 0.0;
   r.invS64 = 0.0;
+  r.S64 = 0.0;
   r.R = 0.0f;
   r.tau = kLowest;
   r.bad = 0;
@@ -375,6 +391,7 @@ __device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
     r.bad = (ri.flags & RF_NONFINITE) ? 1 : 0;
     r.invS = 1.0 / ri.S;
     r.invS64 = ri.S64 > 0.0 ? 1.0 / ri.S64 : 0.0;
+    r.S64 = ri.S64;
     r.R = ri.R;
     r.tau = ri.tau;
   }
@@ -389,6 +406,7 @@ __device__ __forceinline__ QRow q_none() {
   r.zoff = 0;
   r.invS = 0.0;
   r.invS64 = 0.0;
+  r.S64 = 0.0;
   r.c64 = 0.0;
   r.R = 0.0f;
   r.tau = kLowest;

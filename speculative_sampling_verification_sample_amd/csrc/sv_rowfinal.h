@@ -812,9 +812,12 @@ __global__ void __launch_bounds__(256, BF16 ? 6 : 1) rowfinal_kernel(RowFinalArg
   //      the ids), then store each at its rank by id (ids are unique within
   //      a row).  Each block of 256 entries is read before any of its slots
   //      is written; earlier blocks only write slots below the current one.
-  //      S64 sums the entries' e64 as 2^51 fixed point (the union holds at
-  //      most 2048 entries, each e64 <= ~1), so the sum does not depend on
-  //      the order of the additions. ----
+  //      S64 sums the entries' e64 as 2^53 fixed point, in 32-bit halves
+  //      (the union holds at most 2048 entries, each e64 < 2, so neither
+  //      half can overflow): integer sums, so S64 does not depend on the
+  //      order of the additions, and a term of at least 1/2 (the row's
+  //      largest is one) is taken exactly, so a kept set of one token has
+  //      S64 = its e64 and p = 1 exactly, as in the plain definition. ----
   if (tid == 0) s_n = 0;
   __syncthreads();
   int32_t* kid = reinterpret_cast<int32_t*>(keys);
@@ -833,10 +836,15 @@ __global__ void __launch_bounds__(256, BF16 ? 6 : 1) rowfinal_kernel(RowFinalArg
   }
   __syncthreads();
   const int nkept = s_n;
-  unsigned long long s64fx = 0ull;
-  for (int i = tid; i < nkept; i += 256)
-    s64fx += (unsigned long long)rint(e64_of(kev[i], a.c64, R) * 2251799813685248.0);  // 2^51
-  const double S64 = (double)block_sum_u64(s64fx, s_u64) * (1.0 / 2251799813685248.0);
+  unsigned long long s64hi = 0ull, s64lo = 0ull;
+  for (int i = tid; i < nkept; i += 256) {
+    const unsigned long long v = (unsigned long long)rint(e64_of(kev[i], a.c64, R) * 9007199254740992.0);  // 2^53
+    s64hi += v >> 32;
+    s64lo += v & 0xffffffffull;
+  }
+  s64hi = block_sum_u64(s64hi, s_u64);
+  s64lo = block_sum_u64(s64lo, s_u64);
+  const double S64 = ((double)s64hi * 4294967296.0 + (double)s64lo) * (1.0 / 9007199254740992.0);
   if (nkept <= a.kmax) {
     Cand* out = a.kept + r * (int64_t)a.kmax;
     // kid sits at the start of the dynamic LDS (16-byte aligned): ids are

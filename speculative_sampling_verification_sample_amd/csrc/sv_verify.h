@@ -1535,16 +1535,18 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * kStatSums + i];
       sm[i] = wave_sum_d(v);
     }
-    const double invSp = 1.0 / sm[ST_EP], invSq = qlog ? 1.0 / sm[ST_WQ] : 1.0;
-    alpha = sm[ST_EP_LT] * invSp + (sm[ST_WQ] - sm[ST_WQ_LT]) * invSq;
-    zpq = sm[ST_EP_GT] * invSp - sm[ST_WQ_GT] * invSq;
-    zqp = sm[ST_WQ_LT] * invSq - sm[ST_EP_LT] * invSp;
+    // normalised by true divisions, as the plain definition is (a product
+    // with a reciprocal can leave a one-token distribution at 1 - 2^-53)
+    const double Sp = sm[ST_EP], Sq = qlog ? sm[ST_WQ] : 1.0;
+    alpha = sm[ST_EP_LT] / Sp + (sm[ST_WQ] - sm[ST_WQ_LT]) / Sq;
+    zpq = sm[ST_EP_GT] / Sp - sm[ST_WQ_GT] / Sq;
+    zqp = sm[ST_WQ_LT] / Sq - sm[ST_EP_LT] / Sp;
     if (has_d) {
-      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) * invSp : 0.0;
-      qd = qlog ? qr.e64raw(qraw_d) * invSq : (double)ri.qd;
+      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / Sp : 0.0;
+      qd = qlog ? qr.e64raw(qraw_d) / Sq : (double)ri.qd;
     }
   } else {
-    const double invS = 1.0 / ri.S64;
+    const double S64 = ri.S64;  // p = e64 / S64 by true division (see above)
     const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     // kStatBlk list steps per round (a nucleus of a few hundred tokens in
@@ -1563,8 +1565,8 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
 #pragma unroll
       for (int u = 0; u < kStatBlk; ++u) {
         if (i0 + u * kWave >= nk) break;
-        const double p = e64_of(e[u].v, a.c64, ri.R) * invS;
-        const double qv = qr.q64(qf[u]);
+        const double p = e64_of(e[u].v, a.c64, ri.R) / S64;
+        const double qv = qr.q64_div(qf[u]);
         const double d = p - qv;
         mn += (p < qv) ? p : qv;
         if (d > 0.0) pq += d;
@@ -1585,7 +1587,7 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     } else {
       // Z' = sum over q's kept set of (q - p)_+, with p read at its ids
       const RowInfo qi = a.q.info[r];
-      const double qinvS = 1.0 / qi.S64;
+      const double qS64 = qi.S64;
       const Cand* Lq = a.qkept + r * a.kmax;
       double zq = 0.0;
       const int nq = qi.nkept;
@@ -1601,17 +1603,17 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
 #pragma unroll
         for (int u = 0; u < kStatBlk; ++u) {
           if (i0 + u * kWave >= nq) break;
-          const double qv = e64_of(e[u].v, a.c64, qi.R) * qinvS;
+          const double qv = e64_of(e[u].v, a.c64, qi.R) / qS64;
           const float z = zf[u];
-          const double p = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) * invS : 0.0;
+          const double p = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) / S64 : 0.0;
           if (qv > p) zq += qv - p;
         }
       }
       zqp = wave_sum_d(zq);
     }
     if (has_d) {
-      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) * invS : 0.0;
-      qd = qlog ? qr.q64(qraw_d) : (double)ri.qd;
+      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / S64 : 0.0;
+      qd = qlog ? qr.q64_div(qraw_d) : (double)ri.qd;
     }
   }
   if (lane == 0) {

@@ -248,6 +248,27 @@ def test_nonfinite_rows(name):
     compare_stats(w, label=f"stats nonfinite {name}")
 
 
+@pytest.mark.parametrize("T", [0.7, 0.3, 1.3])
+@pytest.mark.parametrize("name,V", [("c2", 1001), ("c2", 32000), ("c5", 4099)])
+def test_untruncated_minus_inf_logits(name, V, T):
+    """Untruncated rows at temperatures whose log2(e)/T has a negative low
+    float part (0.7, 0.3) or a positive one (1.3), with -inf logits in the
+    data (a masked tail, scattered ids, the first and last elements) and
+    vocabularies that leave partial 16-byte units: -inf adds 0 to every
+    exponential sum, and no request is flagged."""
+    w = generate(name, DEV, B=5, gamma=3, V=V, temperature=T, top_k=0, top_p=1.0)
+    lg = w.logits.clone()
+    ninf = float("-inf")
+    lg[0, :, V // 2:] = ninf  # masked tail on every row of request 0
+    lg[1, 1, ::7] = ninf      # scattered
+    lg[2, 0, 0] = ninf        # first element
+    lg[3, 3, -1] = ninf       # last element of the bonus row
+    w.logits = lg.contiguous()
+    o, _ = compare_sample(w, label=f"-inf {name} V={V} T={T}")
+    assert ((o["flags"] & oracle.FLAG_NONFINITE) == 0).all()
+    compare_stats(w, label=f"stats -inf {name} V={V} T={T}")
+
+
 def test_determinism():
     for name, kw in (("c5", dict(B=4)), ("c2", dict(B=8)), ("c3", dict(B=6))):
         w = generate(name, DEV, **kw)
