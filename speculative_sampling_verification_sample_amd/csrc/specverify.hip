@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -171,13 +172,16 @@ sv_status check_sizes(int32_t B, int32_t gamma, int32_t V, sv_dtype dt) {
   return SV_OK;
 }
 
-// log2(e) / T in the three forms the kernels use: the double c64 and its
-// two-float split c + cl (c64 - c rounded to float).
+// log2(e) / T in the forms the kernels use: the double c64; c, c64 rounded
+// to the nearest float (the one-part e); and the two-part split c2 + cl of
+// e2, with c2 the float just below c64 and cl the (positive, at least
+// FLT_MIN) float of the remainder, so that a -inf logit never meets a
+// negative low part (-inf * cl would be +inf, and +inf - inf a NaN).
 struct Expo {
-  float c, cl;
+  float c, c2, cl;
   double c64;
 };
-constexpr Expo kExpoGreedy = {1.0f, 0.0f, 1.0};  // greedy passes take no exponentials
+constexpr Expo kExpoGreedy = {1.0f, 1.0f, 0.0f, 1.0};  // greedy passes take no exponentials
 
 sv_status check_params(sv_sampling_params prm, Expo* c_out) {
   const float T = prm.temperature;
@@ -188,7 +192,10 @@ sv_status check_params(sv_sampling_params prm, Expo* c_out) {
   if (!std::isfinite(c) || c > 1e30) return SV_ERR_INVALID_ARG;
   c_out->c64 = c;
   c_out->c = (float)c;
-  c_out->cl = (float)(c - (double)c_out->c);
+  float c2 = (float)c;
+  if ((double)c2 >= c) c2 = std::nextafter(c2, 0.0f);
+  c_out->c2 = c2;
+  c_out->cl = std::max((float)(c - (double)c2), std::numeric_limits<float>::min());
   return SV_OK;
 }
 
@@ -241,6 +248,7 @@ QSrc q_src_dense(const float* q, int64_t V) {
   s.info = nullptr;
   s.V = V;
   s.c = 0.0f;
+  s.c2 = 0.0f;
   s.cl = 0.0f;
   s.c64 = 0.0;
   s.zbf16 = 0;
@@ -271,6 +279,7 @@ sv_status run_rowpass(const Plan& p, const void* logits, int64_t V, int G1, cons
   a.G1 = G1;
   a.nchunks = p.nchunks;
   a.c = c.c;
+  a.c2 = c.c2;
   a.cl = c.cl;
   a.nw = p.nw;
   a.cap_out = p.cap_out;
@@ -324,6 +333,7 @@ sv_status run_rowfinal(const Plan& p, const void* logits, const QSrc& q, const i
   a.top_k = prm.top_k;
   a.top_p = prm.top_p;
   a.c = c.c;
+  a.c2 = c.c2;
   a.cl = c.cl;
   a.c64 = c.c64;
   a.um = p.um;
@@ -467,6 +477,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
   ac.nchunks = p.nchunks;
   ac.logits = target_logits;
   ac.c = c.c;
+  ac.c2 = c.c2;
   ac.cl = c.cl;
   ac.c64 = c.c64;
   ac.gath = gath;
@@ -650,6 +661,7 @@ sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* 
   q.info = ws_at<RowInfo>(ws, pq.off_info);
   q.V = V;
   q.c = c.c;
+  q.c2 = c.c2;
   q.cl = c.cl;
   q.c64 = c.c64;
   q.zbf16 = bf ? 1 : 0;

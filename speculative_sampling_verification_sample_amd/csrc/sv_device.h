@@ -7,12 +7,13 @@
 // are used, each where its accuracy is enough (so that a value computed in
 // two kernels is bit-identical, a kernel always uses the form its
 // consumers use):
-//   c, cl  = log2(e) / T as a float and the float of the remainder
+//   c      = log2(e) / T rounded to a float; c2 + cl the same as a float
+//            just below it plus the (positive) float of the remainder
 //            (computed once on the host from the double c64)
 //   R      = ceilf(xmax * c)                     (integral float, per row)
 //   e(x)   = exp2(fma(x, c, -R))                 (float: the truncated rows'
 //            streaming pass, top-p masses)
-//   e2(x)  = exp2(fma(x, cl, fma(x, c, -R)))     (float with the two-part c:
+//   e2(x)  = exp2(fma(x, cl, fma(x, c2, -R)))    (float with the two-part c:
 //            the untruncated rows' sums S and their acceptance test)
 //   e64(x) = exp2(x * c64 - R)                   (double: the kept sets' sums
 //            S64, every draw and every statistic)
@@ -170,13 +171,11 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // The three exponentials against the integral reference R (see the top of
 // this file).
 __device__ __forceinline__ float e_of(float x, float c, float R) { return ex2(__builtin_fmaf(x, c, -R)); }
-// x = -inf is taken as the lowest finite float: then x * cl stays finite
-// whatever cl's sign, the exponent is -inf and the result 0 (-inf * cl
-// would be +inf for a negative cl, and +inf - inf a NaN); NaN still
-// propagates (the NaN-keeping maximum).
-__device__ __forceinline__ float e2_of(float x, float c, float cl, float R) {
-  const float xs = __builtin_elementwise_maximum(x, -3.40282347e38f);
-  return ex2(__builtin_fmaf(xs, cl, __builtin_fmaf(xs, c, -R)));
+// e2 takes the split c2 + cl with c2 below c64 and cl > 0 (not c and the
+// signed remainder): then x = -inf gives -inf + -inf and 2^-inf = 0 (with a
+// negative low part -inf * cl would be +inf and +inf - inf a NaN).
+__device__ __forceinline__ float e2_of(float x, float c2, float cl, float R) {
+  return ex2(__builtin_fmaf(x, cl, __builtin_fmaf(x, c2, -R)));
 }
 // 2^t in double for t <= ~2: 2^n e^g with n = rint(t), g = (t - n) ln 2,
 // |g| <= 0.347, and e^g by its Taylor series through g^13 (the first term
@@ -240,7 +239,7 @@ struct QSrc {
   const void* z;        // draft logits when dense is null; both null: no q (reads give 0)
   const RowInfo* info;  // statistics of the draft rows (with z)
   int64_t V;
-  float c, cl;          // log2(e) / T in two floats, shared with the target
+  float c, c2, cl;      // log2(e) / T: c for e; c2 + cl for e2 (shared with the target)
   double c64;           // log2(e) / T
   int32_t zbf16;        // the draft logits are bfloat16
 };
@@ -255,7 +254,7 @@ struct QRow {
   double invS64;       // 1 / S64, 0 when S64 is not known (untruncated draft rows)
   double S64;          // S64 itself (0 when not known)
   double c64;
-  float R, tau, c, cl;
+  float R, tau, c, c2, cl;
   int32_t zbf16;
   int32_t bad;         // unusable draft row: q is NaN
 
@@ -267,7 +266,7 @@ struct QRow {
     if (bad) return __builtin_nanf("");
     if (!(zz >= tau)) return 0.0f;
     if (invS64 > 0.0) return (float)(e64_of(zz, c64, R) * invS64);
-    return (float)((double)e2_of(zz, c, cl, R) * invS);
+    return (float)((double)e2_of(zz, c2, cl, R) * invS);
   }
   // q in double from a raw value (needs S64 for draft logits).
   __device__ __forceinline__ double q64(float v) const {
@@ -377,6 +376,7 @@ __device__ __forceinline__ QRow q_row(const QSrc& s, int64_t row) {
   r.z = s.dense ? nullptr : s.z;
   r.zoff = row * s.V;
   r.c = s.c;
+  r.c2 = s.c2;
   r.cl = s.cl;
   r.c64 = s.c64;
   r.zbf16 = s.zbf16;
@@ -411,6 +411,7 @@ __device__ __forceinline__ QRow q_none() {
   r.R = 0.0f;
   r.tau = kLowest;
   r.c = 0.0f;
+  r.c2 = 0.0f;
   r.cl = 0.0f;
   r.zbf16 = 0;
   r.bad = 0;

@@ -39,7 +39,7 @@ struct RowFinalArgs {
   int32_t top_k;        // active when 0 < top_k < V
   float top_p;          // active when < 1
   float c;
-  float cl;             // low part of log2(e) / T (untruncated rows' e2)
+  float c2, cl;         // two-part log2(e) / T (untruncated rows' e2)
   double c64;           // log2(e) / T (e64)
   int32_t um;           // LDS capacity (power of two) for the candidate union
   int32_t kmax;         // capacity of a stored kept list
@@ -53,11 +53,11 @@ struct RowFinalArgs {
 // Draft gather for a row whose kept set and normaliser are final: the
 // draft's logit, its float exponential and q(d) (the acceptance test needs
 // them with S, or with S64).  dpos is the row's draft position, < 0 for a
-// row without a draft (the bonus row).  cl: the low part of c on
-// untruncated rows (their S sums e2), 0 on truncated ones (S sums e).
+// row without a draft (the bonus row).  (ch, cl): e2's two-part c on
+// untruncated rows (their S sums e2), (c, 0) on truncated ones (S sums e).
 template <bool BF16>
 __device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& q, const int32_t* ids, int64_t V,
-                                                float c, float cl, int64_t dpos, int64_t rowoff, RowInfo& ri) {
+                                                float ch, float cl, int64_t dpos, int64_t rowoff, RowInfo& ri) {
   ri.ed = 0.0f;
   ri.qd = 0.0f;
   ri.d = -1;
@@ -71,13 +71,13 @@ __device__ __forceinline__ void gather_draft_at(const void* logits, const QSrc& 
   ri.d = d;
   float z = load_logit<BF16>(logits, rowoff + d);
   ri.zd = z;
-  ri.ed = (z >= ri.tau) ? e2_of(z, c, cl, ri.R) : 0.0f;
+  ri.ed = (z >= ri.tau) ? e2_of(z, ch, cl, ri.R) : 0.0f;
   ri.qd = q_at(q, dpos, d);
 }
 
 template <bool BF16>
 __device__ __forceinline__ void gather_draft(const RowFinalArgs& a, int64_t dpos, int64_t rowoff, RowInfo& ri) {
-  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.trunc ? 0.0f : a.cl, dpos, rowoff, ri);
+  gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.trunc ? a.c : a.c2, a.trunc ? 0.0f : a.cl, dpos, rowoff, ri);
 }
 
 
@@ -121,7 +121,7 @@ __device__ inline bool merge_nonfinite(const RowMerge& m) {
 // draft's logit and q(d) come from the row pass's gather (gath[grow], the
 // plan row) when `gath` is set.
 template <bool BF16>
-__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, float cl, const void* logits,
+__device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, float c2, float cl, const void* logits,
                                     const QSrc& q, const int32_t* ids, int64_t V, int64_t dpos, int64_t rowoff,
                                     const float2* gath = nullptr, int64_t grow = 0) {
   // the draft's id and gathered (z(d), q(d)) do not depend on the merge:
@@ -156,13 +156,13 @@ __device__ RowInfo untrunc_row_info(const ChunkOut* co, int nchunks, float c, fl
       } else {
         ri.d = d;
         ri.zd = g.x;
-        ri.ed = (g.x >= ri.tau) ? e2_of(g.x, c, cl, ri.R) : 0.0f;
+        ri.ed = (g.x >= ri.tau) ? e2_of(g.x, c2, cl, ri.R) : 0.0f;
         ri.qd = g.y;
       }
     }
     return ri;
   }
-  gather_draft_at<BF16>(logits, q, ids, V, c, cl, dpos, rowoff, ri);
+  gather_draft_at<BF16>(logits, q, ids, V, c2, cl, dpos, rowoff, ri);
   return ri;
 }
 

@@ -42,7 +42,7 @@ struct RowPassArgs {
   int32_t G1;
   int32_t nchunks;
   float c;
-  float cl;            // low part of log2(e) / T (untruncated rows' sums)
+  float c2, cl;        // two-part log2(e) / T (untruncated rows' e2 sums)
   int32_t nw;          // chunk elements the candidate threshold must certify
   int32_t cap_out;     // capacity of one chunk's list
   ChunkOut* out;  // [rows][nchunks]
@@ -120,7 +120,7 @@ struct UnitAcc {
   float vt = kNegInf;
   uint32_t nan_words = 0;  // max of |bits| over whole units (per 16-bit half for bf16)
   uint32_t flags = 0;
-  float cl = 0.0f;  // low part of c (TWO_PART)
+  float c2 = 0.0f, cl = 0.0f;  // the two-part c (TWO_PART)
 
   // Widens a unit into x and returns its max.  rel is the chunk-relative
   // index of the unit's first element; with EDGE, elements outside [0, n)
@@ -166,7 +166,7 @@ struct UnitAcc {
       float ev[EPV];
 #pragma unroll
       for (int i = 0; i < EPV; ++i) {
-        if constexpr (TWO_PART) ev[i] = e2_of(x[i], c, cl, Re);
+        if constexpr (TWO_PART) ev[i] = e2_of(x[i], c2, cl, Re);
         else ev[i] = e_of(x[i], c, Re);
       }
       float t;
@@ -244,6 +244,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   // untruncated sums take the two-part c: the acceptance test compares
   // against them directly
   UnitAcc<BF16, DO_S, MODE != M_ARGMAX, true> acc;
+  acc.c2 = a.c2;
   acc.cl = a.cl;
   float bestv = kNegInf;  // running max (argmax mode)
   int aidx = 0x7fffffff;  // row index of this thread's first maximum

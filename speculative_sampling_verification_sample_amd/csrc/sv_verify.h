@@ -28,7 +28,7 @@ struct AcceptArgs {
   int32_t nchunks;
   const void* logits;
   float c;
-  float cl;             // low part of log2(e) / T (untruncated rows' e2)
+  float c2, cl;         // two-part log2(e) / T (untruncated rows' e2)
   double c64;           // log2(e) / T (e64)
   const Cand* kept;     // [rows][kmax]
   int32_t kmax;
@@ -358,12 +358,13 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
     const int64_t dpos = lane < G ? (int64_t)sp.lo + lane : -1;
     if constexpr (FROM_CHUNKS) {
       // ragged rows were not gathered by the row pass: gather here
-      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.cl, a.logits, a.q, a.ids, a.V, dpos,
+      ri = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.c2, a.cl, a.logits, a.q, a.ids, a.V, dpos,
                                   prow * a.V, a.cu != nullptr ? nullptr : a.gath, prow);
     } else {
       ri = a.info[prow];
       if (a.cu != nullptr && !(ri.flags & RF_NONFINITE))
-        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.kept != nullptr ? 0.0f : a.cl, dpos, prow * a.V, ri);
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.kept != nullptr ? a.c : a.c2, a.kept != nullptr ? 0.0f : a.cl,
+                              dpos, prow * a.V, ri);
     }
   }
   bool bad = (lane <= G) && ((ri.flags & RF_NONFINITE) ||
@@ -418,7 +419,7 @@ __device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
   if constexpr (FROM_CHUNKS) {
     for (int jj = lane; jj <= G; jj += kWave) {
       const int64_t prow = lo + b + jj;
-      inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.cl, a.logits, a.q, a.ids, a.V,
+      inf[jj] = untrunc_row_info<BF16>(a.cout + prow * a.nchunks, a.nchunks, a.c, a.c2, a.cl, a.logits, a.q, a.ids, a.V,
                                        jj < G ? lo + jj : -1, prow * a.V);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -428,7 +429,8 @@ __device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
     for (int jj = lane; jj <= G; jj += kWave) {
       RowInfo ri = inf[jj];
       if (!(ri.flags & RF_NONFINITE))
-        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.c, a.kept != nullptr ? 0.0f : a.cl, jj < G ? lo + jj : -1,
+        gather_draft_at<BF16>(a.logits, a.q, a.ids, a.V, a.kept != nullptr ? a.c : a.c2, a.kept != nullptr ? 0.0f : a.cl,
+                              jj < G ? lo + jj : -1,
                               (lo + b + jj) * a.V, ri);
       inf[jj] = ri;
     }
