@@ -133,3 +133,17 @@ def test_random_extreme_scales(shape, T, scale):
     label = f"extreme {shape} T={T} scale={scale}"
     compare_sample(w, label=label)
     compare_stats(w, label=label)
+
+
+@pytest.mark.parametrize("shape,factor", [("c2", 0.5), ("c3", 0.9), ("c5", 1.1), ("c2", 3.0), ("c5", 0.25),
+                                          ("c3", 2.0)])
+def test_random_unnormalised_q(shape, factor):
+    """q as given, not summing to one (R11): the acceptance ratio, the
+    residual (p - q)+ (which may vanish: Z_DEGENERATE) and the statistics
+    all take it as it is."""
+    w = generate(shape, DEV, B=5, gamma=4, V=7001, seed=74000 + int(factor * 100))
+    w.q = (w.q * factor).contiguous()
+    label = f"unnormalised q x{factor} {shape}"
+    compare_sample(w, label=label)
+    compare_sample(w, label=label + " lenient 0.7", lenience=0.7)
+    compare_stats(w, label=label)
