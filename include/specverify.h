@@ -308,7 +308,7 @@ typedef enum SV_ENUM_INT {
   SV_STAGE_ACCEPT = 2,        /* the acceptance decision launch (with the draws it takes itself) */
   SV_STAGE_DRAW_PARTIAL = 3,  /* untruncated draws, long drafts: the chunk sums after the decision */
   SV_STAGE_DRAW_FINISH = 4,   /* untruncated draws: the walk and rescan launch */
-  SV_STAGE_STATS_PASS = 5,    /* statistics: the pass over streamed rows and a dense q's sum */
+  SV_STAGE_STATS_PASS = 5,    /* statistics: the pass over streamed rows (not the untruncated rows' S64 pass before it) */
   SV_STAGE_STATS_FINISH = 6,  /* statistics: the per-position finish */
   SV_STAGE_GREEDY = 7,        /* greedy decision */
   SV_STAGE_QSUM = 8,          /* statistics: a dense q's row sums for Z' (on the library's side stream) */

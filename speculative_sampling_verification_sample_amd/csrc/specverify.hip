@@ -69,6 +69,7 @@ struct Plan {
   size_t off_cout = 0, off_cand = 0, off_info = 0, off_kept = 0, off_jobs = 0, off_part = 0, off_gath = 0;
   size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][kStatSums] (CALL_STATS, CALL_SAMPLE_STATS)
   size_t off_qsum = 0;   // a dense q's row sums by chunk [B * gamma][nchq] (the same calls)
+  size_t off_s64 = 0;    // untruncated rows' S64 by chunk [2][B * gamma][nchunks]: the target's, the draft's (the same calls)
   int nchq = 1;
   size_t total = 0;
 };
@@ -157,6 +158,9 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.off_qsum = off;
   if (kind == CALL_STATS || kind == CALL_SAMPLE_STATS)
     off = align_up(off + (size_t)B * gamma * p.nchq * sizeof(double), 256);
+  p.off_s64 = off;
+  if (!p.trunc && (kind == CALL_STATS || kind == CALL_SAMPLE_STATS))
+    off = align_up(off + 2 * (size_t)B * gamma * nch * sizeof(double), 256);
   p.total = std::max<size_t>(off, 256);
   return p;
 }
@@ -587,6 +591,9 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.info_rpr = info_rpr;
   a.kmax = kKMax;
   a.partials = ws_at<double>(workspace, p.off_spart);
+  a.p_s64 = nullptr;
+  a.q_s64 = nullptr;
+  a.s64_nch = p.nchunks;
   a.qsum = ws_at<double>(workspace, p.off_qsum);
   a.nchq = p.nchq;
   a.out_alpha = so.alpha;
@@ -597,6 +604,40 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   if (a.rows == 0) return SV_OK;
   dim3 grid((unsigned)(a.rows * a.nchunks));
   const bool qlog = q.dense == nullptr;
+  if (!p.trunc) {
+    // untruncated rows: their S64 first (the target's, then the draft's
+    // when q comes from its logits), chunk by chunk
+    double* s64 = ws_at<double>(workspace, p.off_s64);
+    S64Args sa;
+    sa.logits = target_logits;
+    sa.info = a.info;
+    sa.V = V;
+    sa.gamma = gamma;
+    sa.lrpr = gamma + 1;
+    sa.info_rpr = info_rpr;
+    sa.nchunks = p.nchunks;
+    sa.chunk = p.chunk;
+    sa.c64 = c.c64;
+    sa.out = s64;
+    const dim3 sgrid((unsigned)(a.rows * p.nchunks));
+    if (bf) launch_stage(-1, s64_chunk_kernel<true>, sgrid, dim3(256), 0, st, sa);
+    else launch_stage(-1, s64_chunk_kernel<false>, sgrid, dim3(256), 0, st, sa);
+    sv_status s = launched();
+    if (s != SV_OK) return s;
+    a.p_s64 = s64;
+    if (qlog) {
+      sa.logits = q.z;
+      sa.info = q.info;
+      sa.lrpr = gamma;
+      sa.info_rpr = gamma;
+      sa.out = s64 + (size_t)a.rows * p.nchunks;
+      if (q.zbf16) launch_stage(-1, s64_chunk_kernel<true>, sgrid, dim3(256), 0, st, sa);
+      else launch_stage(-1, s64_chunk_kernel<false>, sgrid, dim3(256), 0, st, sa);
+      s = launched();
+      if (s != SV_OK) return s;
+      a.q_s64 = sa.out;
+    }
+  }
   if (bf) {
     if (qlog) launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<true, true>, grid, dim3(256), 0, st, a);
     else launch_stage(SV_STAGE_STATS_PASS, stats_chunk_kernel<true, false>, grid, dim3(256), 0, st, a);

@@ -1314,13 +1314,15 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
 //     sum(q) over the row minus its sum over the list (the chunk pass sums q,
 //     and only when Z' is asked for), and for q formed from the draft's
 //     logits it is the sum over q's own list with p evaluated at its ids.
-//   Other rows stream the logits and q together, chunk by chunk, into six
-//     double sums: of e64_p and of q's unnormalised weight w_q (the dense q,
-//     or e64 of the draft's logit), each over the whole row and over the
-//     terms where p < q and where p > q (told apart by the float
-//     approximations of p and q).  With S64 = sum e64_p and Sq = sum w_q
-//     (1 for a dense q): alpha = sum_{p<q} p + sum_{p>=q} q,
-//     Z = sum_{p>q} (p - q) and Z' = sum_{p<q} (q - p).
+//   Other rows stream the logits and q together, chunk by chunk, into the
+//     three sums of the plain definitions, term by term: min(p, q),
+//     (p - q)_+ and (q - p)_+, each p (and a q formed from the draft's
+//     logits) a true division e64 / S64.  A truncated row carries its S64;
+//     an untruncated row's S64 is summed first, by s64_chunk_kernel, so
+//     that every term is classified by its p and q in double, as the
+//     definitions do: a sign taken from float approximations misplaces the
+//     terms where p and q agree to a few 1e-7, which moves a small Z by as
+//     much.
 // Each output may be null (not written).
 // ---------------------------------------------------------------------------
 struct StatsArgs {
@@ -1341,6 +1343,10 @@ struct StatsArgs {
   const Cand* kept;
   int32_t info_rpr;
   int32_t kmax;
+  // Untruncated rows' S64 as chunk sums [B * gamma][s64_nch] (s64_chunk_kernel):
+  const double* p_s64;  // the target's rows (else null)
+  const double* q_s64;  // the draft's rows, q from the draft's logits (else null)
+  int32_t s64_nch;
   double* partials;     // [rows][nchunks][kStatSums]
   const double* qsum;   // dense q's row sums by chunk [rows][nchq] (qsum_kernel), for Z'
   int32_t nchq;
@@ -1351,9 +1357,93 @@ struct StatsArgs {
   int64_t rows;
 };
 
-// The sums of a streamed row: e64_p and w_q over the row, over p < q and
-// over p > q.
-enum { ST_EP = 0, ST_EP_LT = 1, ST_EP_GT = 2, ST_WQ = 3, ST_WQ_LT = 4, ST_WQ_GT = 5, kStatSums = 6 };
+// The sums of a streamed row: min(p, q), (p - q)_+ and (q - p)_+.
+enum { ST_MIN = 0, ST_PQ = 1, ST_QP = 2, kStatSums = 3 };
+
+// S64 of an untruncated row from its chunk sums, added in one fixed order
+// (lane-strided, then the wave reduction), so that every wave that asks
+// gets the same double.  Called by whole waves.
+__device__ __forceinline__ double row_s64(const double* part, int64_t r, int nch) {
+  double v = 0.0;
+  for (int c = threadIdx.x & 63; c < nch; c += kWave) v += part[r * nch + c];
+  return wave_sum_d(v);
+}
+
+// S64 of the target's row r: its own where the row carries one (truncated
+// rows), else the sum of its chunk sums.
+__device__ __forceinline__ double stats_s64_p(const StatsArgs& a, const RowInfo& ri, int64_t r) {
+  return (ri.S64 > 0.0 || a.p_s64 == nullptr) ? ri.S64 : row_s64(a.p_s64, r, a.s64_nch);
+}
+
+// q's row r, with the S64 of an untruncated draft row filled in.
+__device__ __forceinline__ QRow stats_q_row(const StatsArgs& a, int64_t r) {
+  QRow qr = q_row(a.q, r);
+  if (qr.logits_src() && !(qr.S64 > 0.0) && a.q_s64 != nullptr) qr.S64 = row_s64(a.q_s64, r, a.s64_nch);
+  return qr;
+}
+
+// S64 of untruncated rows, by chunks: workgroup c of statistics row r sums
+// e64 over [c * chunk, (c + 1) * chunk) of the row, each thread its 8-token
+// segments in order, then a fixed-order workgroup sum.  The rows are the
+// target's (logits [B][gamma + 1][V], row results at info rows
+// b * info_rpr + j) or the draft's (logits [B][gamma][V], info_rpr = gamma).
+struct S64Args {
+  const void* logits;
+  const RowInfo* info;
+  int64_t V;
+  int32_t gamma;
+  int32_t lrpr;      // logits rows per request
+  int32_t info_rpr;  // row results per request
+  int32_t nchunks;
+  int64_t chunk;
+  double c64;
+  double* out;       // [B * gamma][nchunks]
+};
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) s64_chunk_kernel(S64Args a) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t blk = blockIdx.x;
+  const int64_t r = blk / a.nchunks;
+  const int ci = (int)(blk - r * a.nchunks);
+  const int64_t b = r / a.gamma, j = r - b * a.gamma;
+  const RowInfo ri = a.info[b * a.info_rpr + j];
+  const int64_t lrow = (b * a.lrpr + j) * a.V;
+  const int64_t x0 = (int64_t)ci * a.chunk, x1 = min(x0 + a.chunk, a.V);
+  __shared__ double s_w[4];
+  // rows whose statistics are NaN (non-finite logits) are not read
+  if (ri.flags & RF_NONFINITE) return;
+  const bool vec = (a.V & 7) == 0;  // rows (and chunks) 16-byte aligned
+  double acc = 0.0;
+  constexpr int kU = 2;
+  for (int64_t x = x0 + (int64_t)tid * 8; x < x1; x += (int64_t)kU * 256 * 8) {
+    float z[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t xu = x + (int64_t)u * 256 * 8;
+      if (vec && xu + 8 <= x1) {
+        if constexpr (BF16) {
+          widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + xu), z[u]);
+        } else {
+          const uint4* p4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + xu);
+          widen<false>(p4[0], z[u]);
+          widen<false>(p4[1], z[u] + 4);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[u][k] = xu + k < x1 ? load_logit<BF16>(a.logits, lrow + xu + k) : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += e64_of(z[u][k], a.c64, ri.R);
+  }
+  acc = wave_sum_d(acc);
+  if (lane == 0) s_w[wid] = acc;
+  __syncthreads();
+  if (tid == 0) a.out[r * a.nchunks + ci] = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
 
 __device__ __forceinline__ int64_t info_row(const StatsArgs& a, int64_t r) {
   const int64_t b = r / a.gamma;
@@ -1440,54 +1530,46 @@ __global__ void __launch_bounds__(256) stats_chunk_kernel(StatsArgs a) {
   // from qsum_kernel); nothing reads their partials (the test is the same
   // for the whole workgroup).
   if ((ri.flags & RF_NONFINITE) || !big) return;
-  const QRow qr = q_row(a.q, r);
+  const QRow qr = stats_q_row(a, r);
+  const double S64 = stats_s64_p(a, ri, r);
   // rows are 16-byte aligned when V is a multiple of 8 (chunks are too)
   const bool vec = (a.V & 7) == 0;
   const int64_t ngroups = (x1 - x0 + 7) / 8;
-  {
-    const double invS = 1.0 / ri.S;  // float exponentials: only to tell p < q from p > q
-    constexpr int kU = 2;
-    for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kU * 256) {
-      float qv[kU][8], zv[kU][8];
+  constexpr int kU = 2;
+  for (int64_t g0 = 0; g0 < ngroups; g0 += (int64_t)kU * 256) {
+    float qv[kU][8], zv[kU][8];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
-        if (vec && x + 8 <= x1) {
-          qr.raw8_whole(x, qv[u]);
-          if constexpr (BF16) {
-            widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
-          } else {
-            const uint4* zp4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + x);
-            widen<false>(zp4[0], zv[u]);
-            widen<false>(zp4[1], zv[u] + 4);
-          }
+    for (int u = 0; u < kU; ++u) {
+      const int64_t x = x0 + (g0 + (int64_t)u * 256 + tid) * 8;
+      if (vec && x + 8 <= x1) {
+        qr.raw8_whole(x, qv[u]);
+        if constexpr (BF16) {
+          widen<true>(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.logits) + lrow + x), zv[u]);
         } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const bool in = x + k < x1;
-            qv[u][k] = in ? qr.raw_at(x + k) : (QLOG ? kNegInf : 0.0f);
-            zv[u][k] = in ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
-          }
+          const uint4* zp4 = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.logits) + lrow + x);
+          widen<false>(zp4[0], zv[u]);
+          widen<false>(zp4[1], zv[u] + 4);
         }
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const double wq = qr.e64raw(qv[u][k]);
-          const float z = zv[u][k];
-          const double ep = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) : 0.0;
-          const double pa = ep * invS, qa = qr.approx(wq);
-          sm[ST_WQ] += wq;
-          sm[ST_EP] += ep;
-          if (pa < qa) {
-            sm[ST_EP_LT] += ep;
-            sm[ST_WQ_LT] += wq;
-          } else if (pa > qa) {
-            sm[ST_EP_GT] += ep;
-            sm[ST_WQ_GT] += wq;
-          }
+          const bool in = x + k < x1;
+          qv[u][k] = in ? qr.raw_at(x + k) : (QLOG ? kNegInf : 0.0f);
+          zv[u][k] = in ? load_logit<BF16>(a.logits, lrow + x + k) : kNegInf;
         }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float z = zv[u][k];
+        const double p = (z >= ri.tau) ? e64_of(z, a.c64, ri.R) / S64 : 0.0;
+        const double q = qr.q64_div(qv[u][k]);
+        const double d = p - q;
+        sm[ST_MIN] += (p < q) ? p : q;
+        if (d > 0.0) sm[ST_PQ] += d;
+        if (d < 0.0) sm[ST_QP] -= d;
       }
     }
   }
@@ -1522,10 +1604,11 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     }
     return;
   }
-  const QRow qr = q_row(a.q, r);
+  const QRow qr = stats_q_row(a, r);
+  const double S64 = stats_s64_p(a, ri, r);  // p = e64 / S64 by true division (see above)
   const int b = (int)(r / a.gamma), j = (int)(r - (int64_t)b * a.gamma);
   const int64_t lrow = ((int64_t)b * (a.gamma + 1) + j) * a.V;
-  double alpha, zpq, zqp = 0.0, pd = 0.0, qd = 0.0;
+  double alpha, zpq, zqp = 0.0;
   const bool has_d = ri.d >= 0;
   // the draft's q(d) in double: a dense q as given, else from the draft's logit
   const float qraw_d = (has_d && qlog) ? qr.raw_at(ri.d) : 0.0f;
@@ -1537,18 +1620,10 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       for (int c = lane; c < a.nchunks; c += kWave) v += a.partials[(r * a.nchunks + c) * kStatSums + i];
       sm[i] = wave_sum_d(v);
     }
-    // normalised by true divisions, as the plain definition is (a product
-    // with a reciprocal can leave a one-token distribution at 1 - 2^-53)
-    const double Sp = sm[ST_EP], Sq = qlog ? sm[ST_WQ] : 1.0;
-    alpha = sm[ST_EP_LT] / Sp + (sm[ST_WQ] - sm[ST_WQ_LT]) / Sq;
-    zpq = sm[ST_EP_GT] / Sp - sm[ST_WQ_GT] / Sq;
-    zqp = sm[ST_WQ_LT] / Sq - sm[ST_EP_LT] / Sp;
-    if (has_d) {
-      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / Sp : 0.0;
-      qd = qlog ? qr.e64raw(qraw_d) / Sq : (double)ri.qd;
-    }
+    alpha = sm[ST_MIN];
+    zpq = sm[ST_PQ];
+    zqp = sm[ST_QP];
   } else {
-    const double S64 = ri.S64;  // p = e64 / S64 by true division (see above)
     const Cand* L = a.kept + ir * a.kmax;  // token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     // kStatBlk list steps per round (a nucleus of a few hundred tokens in
@@ -1613,10 +1688,11 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       }
       zqp = wave_sum_d(zq);
     }
-    if (has_d) {
-      pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / S64 : 0.0;
-      qd = qlog ? qr.q64_div(qraw_d) : (double)ri.qd;
-    }
+  }
+  double pd = 0.0, qd = 0.0;
+  if (has_d) {
+    pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / S64 : 0.0;
+    qd = qlog ? qr.q64_div(qraw_d) : (double)ri.qd;
   }
   if (lane == 0) {
     if (a.out_alpha) a.out_alpha[r] = (float)alpha;
