@@ -406,12 +406,26 @@ const SideStream* side_stream(hipStream_t st) {
   return slot.s ? &slot : nullptr;
 }
 
-// Starts a dense q's row sums (rows b * gamma + j, j < gamma) for Z' beside
-// the caller's stream; returns the event the statistics finish must wait
-// for (null: nothing to wait for, the sums went on the caller's stream or
-// are not needed).
-hipEvent_t fork_qsum(const Plan& p, const float* q, int32_t B, int32_t gamma, int32_t V, void* ws, hipStream_t st,
-                     sv_status* status) {
+// A dense q's row sums (rows b * gamma + j, j < gamma) for Z', in two
+// steps.  qsum_fork_point records `fork` on the caller's stream right after
+// the target's row pass (running beside that pass, the sums slow it more
+// than they gain).  launch_qsum, called once the kernels that follow on the
+// caller's stream are launched, starts the sums on the side stream behind
+// `fork`: launched in that order (also as graph nodes), the latency-bound
+// row finisher and acceptance kernels are dispatched before the sums' many
+// short workgroups, which would otherwise take every free CU slot and hold
+// them back until the sums are done.  launch_qsum returns the event the
+// statistics finish must wait for (null: nothing to wait for, the sums went
+// on the caller's stream).
+const SideStream* qsum_fork_point(hipStream_t st, sv_status* status) {
+  *status = SV_OK;
+  const SideStream* ss = side_stream(st);
+  if (ss != nullptr && hipEventRecord(ss->fork, st) != hipSuccess) *status = SV_ERR_HIP;
+  return ss;
+}
+
+hipEvent_t launch_qsum(const SideStream* ss, const Plan& p, const float* q, int32_t B, int32_t gamma, int32_t V,
+                       void* ws, hipStream_t st, sv_status* status) {
   *status = SV_OK;
   QSumArgs a;
   a.q = q;
@@ -421,13 +435,12 @@ hipEvent_t fork_qsum(const Plan& p, const float* q, int32_t B, int32_t gamma, in
   a.out = ws_at<double>(ws, p.off_qsum);
   if (a.rows == 0) return nullptr;
   const dim3 grid((unsigned)(a.rows * p.nchq));
-  const SideStream* ss = side_stream(st);
   if (ss == nullptr) {
     launch_stage(SV_STAGE_QSUM, qsum_kernel, grid, dim3(256), 0, st, a);
     *status = launched();
     return nullptr;
   }
-  if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+  if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
     *status = SV_ERR_HIP;
     return nullptr;
   }
@@ -451,8 +464,8 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
                              int32_t gamma, int32_t V, sv_sampling_params prm, const Expo& c, int32_t* out_tokens,
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
                              const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
-                             double beta = 1.0, bool force_rowfinal = false, const float* qsum_of = nullptr,
-                             hipEvent_t* qsum_join = nullptr) {
+                             double beta = 1.0, bool force_rowfinal = false,
+                             const SideStream** qsum_fork = nullptr) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
@@ -463,10 +476,10 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
       bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live)
          : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st, draft_ids, q, gamma, gath, true, cu, n_live);
   if (s != SV_OK) return s;
-  if (qsum_of != nullptr) {
-    // the statistics' dense-q row sums, beside the latency-bound kernels
-    // that follow the row pass
-    *qsum_join = fork_qsum(p, qsum_of, B, gamma, V, workspace, st, &s);
+  if (qsum_fork != nullptr) {
+    // the statistics' dense-q row sums may start here (the caller launches
+    // them after this call's kernels)
+    *qsum_fork = qsum_fork_point(st, &s);
     if (s != SV_OK) return s;
   }
   if (p.trunc || force_rowfinal) {
@@ -661,17 +674,23 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
   const bool bf = dt == SV_BF16;
   const int G1 = gamma + 1;
   hipEvent_t join = nullptr;
+  const SideStream* fork = nullptr;
+  const bool qsum = q.dense != nullptr && so.z_qp != nullptr && p.trunc;
   sv_status s = bf ? run_rowpass<true>(p, target_logits, V, G1, c, workspace, st)
                    : run_rowpass<false>(p, target_logits, V, G1, c, workspace, st);
   if (s != SV_OK) return s;
-  if (q.dense != nullptr && so.z_qp != nullptr && p.trunc) {
+  if (qsum) {
     // the dense-q row sums, beside the row finisher and the statistics pass
-    join = fork_qsum(p, q.dense, B, gamma, V, workspace, st, &s);
+    fork = qsum_fork_point(st, &s);
     if (s != SV_OK) return s;
   }
   s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
          : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
   if (s != SV_OK) return s;
+  if (qsum) {
+    join = launch_qsum(fork, p, q.dense, B, gamma, V, workspace, st, &s);
+    if (s != SV_OK) return s;
+  }
   return launch_stats(p, target_logits, bf, q, so, draft_ids, B, gamma, V, c, gamma, workspace, st, join);
 }
 
@@ -726,11 +745,17 @@ sv_status verify_sample_stats_impl(const Plan& p, const void* target_logits, sv_
                                    sv_sampling_params prm, const Expo& c, int32_t* out_tokens, int32_t* out_num_accepted,
                                    uint32_t* out_row_flags, void* workspace, hipStream_t st) {
   hipEvent_t join = nullptr;
+  const SideStream* fork = nullptr;
   const bool qsum = q.dense != nullptr && so.z_qp != nullptr && p.trunc;
   sv_status s = verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
                                    out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0,
-                                   /*force_rowfinal=*/true, qsum ? q.dense : nullptr, &join);
+                                   /*force_rowfinal=*/true, qsum ? &fork : nullptr);
   if (s != SV_OK) return s;
+  if (qsum) {
+    // the dense-q row sums, behind the fork point after the row pass
+    join = launch_qsum(fork, p, q.dense, B, gamma, V, workspace, st, &s);
+    if (s != SV_OK) return s;
+  }
   return launch_stats(p, target_logits, dt == SV_BF16, q, so, draft_ids, B, gamma, V, c, gamma + 1, workspace, st,
                       join);
 }
