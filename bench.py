@@ -49,6 +49,7 @@ STAGES = {
     6: ("statistics finish", "stats_finish", ["sv_device.h", "sv_verify.h"]),
     7: ("greedy decision", "greedy", ["sv_device.h", "sv_verify.h"]),
     8: ("dense q row sums", "qsum", ["sv_device.h", "sv_verify.h"]),
+    9: ("Z' completion", "stats_zqp", ["sv_device.h", "sv_verify.h"]),
 }
 
 

@@ -312,7 +312,8 @@ typedef enum SV_ENUM_INT {
   SV_STAGE_STATS_FINISH = 6,  /* statistics: the per-position finish */
   SV_STAGE_GREEDY = 7,        /* greedy decision */
   SV_STAGE_QSUM = 8,          /* statistics: a dense q's row sums for Z' (on the library's side stream) */
-  SV_STAGE_COUNT = 9
+  SV_STAGE_STATS_ZQP = 9,     /* statistics: Z' of listed rows with a dense q, after the q sums */
+  SV_STAGE_COUNT = 10
 } sv_stage;
 
 /* Profiling hook (for benchmarks; process-wide, not thread-safe).  When both

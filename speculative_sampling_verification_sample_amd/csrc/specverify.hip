@@ -70,6 +70,7 @@ struct Plan {
   size_t off_spart = 0;  // statistics partials [B * gamma][nchunks][kStatSums] (CALL_STATS, CALL_SAMPLE_STATS)
   size_t off_qsum = 0;   // a dense q's row sums by chunk [B * gamma][nchq] (the same calls)
   size_t off_s64 = 0;    // untruncated rows' S64 by chunk [2][B * gamma][nchunks]: the target's, the draft's (the same calls)
+  size_t off_zqp = 0;    // listed rows' two list sums for Z' [B * gamma][2] (the same calls, truncated rows)
   int nchq = 1;
   size_t total = 0;
 };
@@ -161,6 +162,9 @@ Plan make_plan(CallKind kind, int32_t B, int32_t gamma, int64_t V, sv_dtype dt, 
   p.off_s64 = off;
   if (!p.trunc && (kind == CALL_STATS || kind == CALL_SAMPLE_STATS))
     off = align_up(off + 2 * (size_t)B * gamma * nch * sizeof(double), 256);
+  p.off_zqp = off;
+  if (p.trunc && (kind == CALL_STATS || kind == CALL_SAMPLE_STATS))
+    off = align_up(off + 2 * (size_t)B * gamma * sizeof(double), 256);
   p.total = std::max<size_t>(off, 256);
   return p;
 }
@@ -609,6 +613,10 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   a.s64_nch = p.nchunks;
   a.qsum = ws_at<double>(workspace, p.off_qsum);
   a.nchq = p.nchq;
+  // listed rows with a dense q: Z' is completed after the q sums, so that
+  // the rest of the finish runs beside them
+  const bool defer_zqp = p.trunc && q.dense != nullptr && so.z_qp != nullptr;
+  a.zqp_part = defer_zqp ? ws_at<double>(workspace, p.off_zqp) : nullptr;
   a.out_alpha = so.alpha;
   a.out_zpq = so.z_pq;
   a.out_zqp = so.z_qp;
@@ -660,9 +668,20 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
   }
   sv_status s = launched();
   if (s != SV_OK) return s;
+  const dim3 fgrid((unsigned)((a.rows + 3) / 4));
+  if (defer_zqp) {
+    // the finish beside the q sums, then Z' once they are in
+    if (bf) launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<true>, fgrid, dim3(256), 0, st, a);
+    else launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<false>, fgrid, dim3(256), 0, st, a);
+    s = launched();
+    if (s != SV_OK) return s;
+    if (qsum_join != nullptr && hipStreamWaitEvent(st, qsum_join, 0) != hipSuccess) return SV_ERR_HIP;
+    launch_stage(SV_STAGE_STATS_ZQP, stats_zqp_kernel, fgrid, dim3(256), 0, st, a);
+    return launched();
+  }
   if (qsum_join != nullptr && hipStreamWaitEvent(st, qsum_join, 0) != hipSuccess) return SV_ERR_HIP;
-  if (bf) launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<true>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
-  else launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<false>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+  if (bf) launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<true>, fgrid, dim3(256), 0, st, a);
+  else launch_stage(SV_STAGE_STATS_FINISH, stats_final_kernel<false>, fgrid, dim3(256), 0, st, a);
   return launched();
 }
 

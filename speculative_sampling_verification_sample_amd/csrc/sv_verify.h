@@ -1350,6 +1350,11 @@ struct StatsArgs {
   double* partials;     // [rows][nchunks][kStatSums]
   const double* qsum;   // dense q's row sums by chunk [rows][nchq] (qsum_kernel), for Z'
   int32_t nchq;
+  // Listed rows with a dense q, Z' asked for: the finish stores the list's
+  // two sums here [rows][2] (sum of q, sum of (q - p)_+ over the list), and
+  // stats_zqp_kernel completes Z' once the q sums are in; null: the finish
+  // reads the q sums itself.
+  double* zqp_part;
   float* out_alpha;
   float* out_zpq;
   float* out_zqp;
@@ -1657,6 +1662,12 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     sqk = wave_sum_d(sqk);
     if (a.out_zqp == nullptr) {
       // Z' not asked for: neither sum(q) nor q's list is read
+    } else if (!qlog && a.zqp_part != nullptr) {
+      // finished by stats_zqp_kernel after the q sums
+      if (lane == 0) {
+        a.zqp_part[2 * r] = sqk;
+        a.zqp_part[2 * r + 1] = qp;
+      }
     } else if (!qlog) {
       double sq = 0.0;
       for (int c = lane; c < a.nchq; c += kWave) sq += a.qsum[r * a.nchq + c];
@@ -1689,6 +1700,7 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       zqp = wave_sum_d(zq);
     }
   }
+  const bool deferred_zqp = !stats_streamed(a, ri, r) && !qlog && a.zqp_part != nullptr;
   double pd = 0.0, qd = 0.0;
   if (has_d) {
     pd = (ri.zd >= ri.tau) ? e64_of(ri.zd, a.c64, ri.R) / S64 : 0.0;
@@ -1697,13 +1709,30 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   if (lane == 0) {
     if (a.out_alpha) a.out_alpha[r] = (float)alpha;
     if (a.out_zpq) a.out_zpq[r] = (float)zpq;
-    if (a.out_zqp) a.out_zqp[r] = (float)zqp;
+    if (a.out_zqp && !(deferred_zqp)) a.out_zqp[r] = (float)zqp;
     float ap;
     if (!has_d) ap = qnan;
     else if (qd == 0.0) ap = pd > 0.0 ? 1.0f : 0.0f;
     else ap = (float)fmin(1.0, pd / qd);
     if (a.out_acc) a.out_acc[r] = ap;
   }
+}
+
+// Z' of listed rows with a dense q, once the q sums are in:
+// Z' = (sum q - sum over the list of q) + sum over the list of (q - p)_+,
+// the list's two sums from stats_final_kernel.  One wave per position;
+// rows without a usable result (non-finite) or streamed were finished
+// there.
+__global__ void __launch_bounds__(256) stats_zqp_kernel(StatsArgs a) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wid;
+  if (r >= a.rows) return;
+  const RowInfo ri = a.info[info_row(a, r)];
+  if ((ri.flags & RF_NONFINITE) || stats_streamed(a, ri, r)) return;
+  double sq = 0.0;
+  for (int c = lane; c < a.nchq; c += kWave) sq += a.qsum[r * a.nchq + c];
+  const double zqp = (wave_sum_d(sq) - a.zqp_part[2 * r]) + a.zqp_part[2 * r + 1];
+  if (lane == 0) a.out_zqp[r] = (float)zqp;
 }
 
 }  // namespace sv

@@ -289,3 +289,16 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
                                           None) == 1
     assert lib.spec_verify_sample_noalloc(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 3, 100, _P(T=0.0), FAKE, FAKE,
                                           FAKE, None) == 1
+
+
+def test_stage_timer_bounds():
+    """Every stage the header enumerates takes the profiling hook (NULL
+    events turn it off, touching no GPU state); one past the last does not."""
+    lib = _lib()
+    text = open(HEADER).read()
+    count = int(re.search(r"SV_STAGE_COUNT\s*=\s*(\d+)", text).group(1))
+    assert count == len(re.findall(r"\bSV_STAGE_(?!COUNT)\w+\s*=\s*\d+", text))
+    for st in range(count):
+        assert lib.spec_set_stage_timer(st, None, None) == 0
+    assert lib.spec_set_stage_timer(count, None, None) == 1
+    assert lib.spec_set_stage_timer(-1, None, None) == 1
