@@ -241,12 +241,22 @@ void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st, bool ti
   launch_row_kernel(rowpass_kernel<MODE, BF16, 256>, grid, dim3(256), st, a, timed);
 }
 
+template <bool BF16, bool NEED_S, bool ALIGNED>
+void launch_trunc_nu(const Plan& p, const RowPassArgs& a, hipStream_t st, bool timed) {
+  dim3 grid((unsigned)(p.nchunks * p.rows));
+  if (p.nu == 16) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 16, ALIGNED>, grid, dim3(kTruncBS), st, a, timed);
+  else if (p.nu == 8) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 8, ALIGNED>, grid, dim3(kTruncBS), st, a, timed);
+  else launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 4, ALIGNED>, grid, dim3(kTruncBS), st, a, timed);
+}
+
 template <bool BF16, bool NEED_S>
 void launch_trunc(const Plan& p, const RowPassArgs& a, hipStream_t st, bool timed) {
-  dim3 grid((unsigned)(p.nchunks * p.rows));
-  if (p.nu == 16) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 16>, grid, dim3(kTruncBS), st, a, timed);
-  else if (p.nu == 8) launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 8>, grid, dim3(kTruncBS), st, a, timed);
-  else launch_row_kernel(trunc_pass_kernel<BF16, NEED_S, 4>, grid, dim3(kTruncBS), st, a, timed);
+  // rows start at multiples of V and chunks at multiples of 8 elements, so
+  // V a multiple of the elements per 16-byte unit makes every chunk's units
+  // whole (and every unit lies inside the tensor)
+  const int64_t epv = BF16 ? 8 : 4;
+  if (a.V % epv == 0) launch_trunc_nu<BF16, NEED_S, true>(p, a, st, timed);
+  else launch_trunc_nu<BF16, NEED_S, false>(p, a, st, timed);
 }
 
 QSrc q_src_dense(const float* q, int64_t V) {

@@ -348,7 +348,11 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
 // read is an HBM access: without the kept unit they made 8% more traffic
 // than the row on 256 x 6 rows of 128256 bf16 with top-k 50, with it under
 // 1%, and the pass went from 67 to 64 us.)
-template <bool BF16, bool NEED_S, int NU>
+// ALIGNED: the host has checked that V is a multiple of the elements per
+// unit, so every chunk starts and ends on a unit boundary and every unit in
+// range is whole: the unit code then has one copy per unit (about 40% of
+// the code, and fewer registers, against the copy with the edge tests).
+template <bool BF16, bool NEED_S, int NU, bool ALIGNED>
 __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) {
   constexpr int BS = kTruncBS;
   constexpr int EPV = BF16 ? 8 : 4;
@@ -375,7 +379,7 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
   const int nunits = (int)(g.U1 - g.U0);
   const int relu = (int)(g.U0 * EPV - g.F0);  // relative index of unit 0's first element
   const int rel0 = relu + tid * EPV;
-  const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
+  const bool aligned = ALIGNED || ((g.F0 % EPV == 0) && (g.F1 % EPV == 0));
   const int nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
   UnitAcc<BF16, NEED_S, false> acc;  // the running max is bestv
   float um[NU];
@@ -394,7 +398,9 @@ __global__ void __launch_bounds__(kTruncBS, 6) trunc_pass_kernel(RowPassArgs a) 
       const int rel = rel0 + k * BS * EPV;
       float x[EPV];
       um[k] = kNegInf;
-      if (k < nfull) {
+      if constexpr (ALIGNED) {
+        if (k < nfull || ul < nunits) um[k] = acc.template add<false>(wv[i], rel, n, c, x);
+      } else if (k < nfull) {
         um[k] = acc.template add<false>(wv[i], rel, n, c, x);
       } else if (ul < nunits) {
         if (aligned || (ul > 0 && ul + 1 < nunits)) um[k] = acc.template add<false>(wv[i], rel, n, c, x);
