@@ -238,7 +238,10 @@ void launch_row_kernel(void (*kernel)(RowPassArgs), dim3 grid, dim3 block, hipSt
 template <int MODE, bool BF16>
 void launch_rowpass(const Plan& p, const RowPassArgs& a, hipStream_t st, bool timed) {
   dim3 grid((unsigned)(p.nchunks * p.rows));
-  launch_row_kernel(rowpass_kernel<MODE, BF16, 256>, grid, dim3(256), st, a, timed);
+  // V a multiple of the unit width: every chunk's units are whole (see
+  // launch_trunc)
+  if (a.V % (BF16 ? 8 : 4) == 0) launch_row_kernel(rowpass_kernel<MODE, BF16, 256, true>, grid, dim3(256), st, a, timed);
+  else launch_row_kernel(rowpass_kernel<MODE, BF16, 256, false>, grid, dim3(256), st, a, timed);
 }
 
 template <bool BF16, bool NEED_S, bool ALIGNED>

@@ -214,7 +214,9 @@ __device__ __forceinline__ void wave_sr_merge(double& s, float& R) {
   R = Rm;
 }
 
-template <int MODE, bool BF16, int BS>
+// ALIGNED: as for the truncated pass, the host has checked that every unit
+// in range is whole, so the edge variant of the unit code is left out.
+template <int MODE, bool BF16, int BS, bool ALIGNED>
 __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NWV = BS / kWave;
@@ -273,7 +275,7 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
   // Step k gives thread tid the unit U0 + k*BS + tid; up to kUnroll units'
   // loads are issued before any is processed.
   constexpr int kUnroll = 8;
-  const bool aligned = (g.F0 % EPV == 0) && (g.F1 % EPV == 0);
+  const bool aligned = ALIGNED || ((g.F0 % EPV == 0) && (g.F1 % EPV == 0));
   const int64_t nunits = g.U1 - g.U0;
   const int64_t nsteps = (nunits + BS - 1) / BS;
   const int64_t nfull = aligned ? nunits / BS : 0;  // steps whose units are all whole and in range
@@ -289,8 +291,13 @@ __global__ void __launch_bounds__(BS) rowpass_kernel(RowPassArgs a) {
     for (int i = 0; i < kUnroll; ++i) {
       if (k0 + i >= nsteps) break;
       const int64_t u = g.U0 + (k0 + i) * BS + tid;
-      if (k0 + i < nfull) process(u, wv[i], NoEdge{});
-      else if (u < g.U1) process(u, wv[i], Edge{});
+      if constexpr (ALIGNED) {
+        if (k0 + i < nfull || u < g.U1) process(u, wv[i], NoEdge{});
+      } else if (k0 + i < nfull) {
+        process(u, wv[i], NoEdge{});
+      } else if (u < g.U1) {
+        process(u, wv[i], Edge{});
+      }
     }
     acc.flush();
   }
