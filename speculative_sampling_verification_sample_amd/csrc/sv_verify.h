@@ -1311,9 +1311,11 @@ __global__ void __launch_bounds__(256) greedy_kernel(GreedyArgs a) {
 // p = e64 / S64.
 //   Rows whose kept set is a stored list (truncated rows): p is 0 off the
 //     list, so alpha and Z are sums over the list; Z' adds, for a dense q,
-//     sum(q) over the row minus its sum over the list (the chunk pass sums q,
-//     and only when Z' is asked for), and for q formed from the draft's
-//     logits it is the sum over q's own list with p evaluated at its ids.
+//     sum(q) over the row minus its sum over the list (qsum_kernel sums q
+//     beside the other kernels, only when Z' is asked for, and
+//     stats_zqp_kernel completes Z' once it is in), and for q formed from
+//     the draft's logits it is the sum over q's own list with p evaluated
+//     at its ids.
 //   Other rows stream the logits and q together, chunk by chunk, into the
 //     three sums of the plain definitions, term by term: min(p, q),
 //     (p - q)_+ and (q - p)_+, each p (and a q formed from the draft's
