@@ -14,10 +14,11 @@
  *   library never allocates, frees or retains caller memory and keeps no
  *   state between calls, apart from the optional profiling hook
  *   (spec_set_stage_timer), the allocation-free call's per-GPU scratch, and
- *   for the statistics calls with a dense q and Z' a side stream with two
- *   events per (device, caller stream), made on the first such call and
- *   kept until the process ends (at most 64 such pairs; past that, and
- *   where one cannot be made, the work stays on the caller's stream).  All
+ *   a side stream with two events per (device, caller stream), made on the
+ *   first call that uses one (the statistics with a dense q and Z', and the
+ *   draft-logits calls under top-k or top-p) and kept until the process
+ *   ends (at most 64 such pairs; past that, and where one cannot be made,
+ *   the work stays on the caller's stream).  All
  *   scratch lives in the caller's `workspace`
  *   (device memory of at least the reported workspace size, 16-byte
  *   aligned, contents need not be initialised).

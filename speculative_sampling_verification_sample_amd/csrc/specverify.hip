@@ -379,10 +379,12 @@ sv_status common_checks(const void* logits, sv_dtype dt, int32_t B, int32_t gamm
 
 // ---- a second stream for work that does not depend on the target's passes
 // A call's dense-q row sums (only Z' needs them) read nothing the row passes
-// write, so they run on a stream of the library's beside the caller's: the
-// call records `fork` on its stream, the side stream waits for it, runs the
-// sums and records `join`, and the caller's stream waits for `join` before
-// the statistics finish.  One side stream (non-blocking, default priority)
+// write, and the draft rows' passes of a draft-logits call under top-k or
+// top-p write nothing the target's row pass reads, so they run on a stream
+// of the library's beside the caller's: the call records `fork` on its
+// stream, the side stream waits for it, runs the work and records `join`,
+// and the caller's stream waits for `join` before the first kernel that
+// reads the results (the statistics finish; the target's row finisher).  One side stream (non-blocking, default priority)
 // and its two events per (device, caller stream), made on first use; under
 // graph capture the fork and join make the side work part of the graph.
 // Without them (creation failed, or kMaxSideStreams pairs already made:
@@ -482,7 +484,7 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
                              int32_t* out_num_accepted, uint32_t* out_row_flags, void* workspace, hipStream_t st,
                              const int32_t* cu = nullptr, int32_t n_draft = 0, int32_t eos = -1,
                              double beta = 1.0, bool force_rowfinal = false,
-                             const SideStream** qsum_fork = nullptr) {
+                             const SideStream** qsum_fork = nullptr, hipEvent_t q_ready = nullptr) {
   const int G1 = gamma + 1;
   const bool bf = dt == SV_BF16;
 
@@ -499,6 +501,9 @@ sv_status verify_sample_impl(const Plan& p, const void* target_logits, sv_dtype 
     *qsum_fork = qsum_fork_point(st, &s);
     if (s != SV_OK) return s;
   }
+  // q's row results made on another stream (truncated rows only: their row
+  // pass reads nothing of q); the row finisher is their first reader
+  if (q_ready != nullptr && hipStreamWaitEvent(st, q_ready, 0) != hipSuccess) return SV_ERR_HIP;
   if (p.trunc || force_rowfinal) {
     s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live)
            : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st, cu, n_live);
@@ -702,7 +707,7 @@ sv_status launch_stats(const Plan& p, const void* target_logits, bool bf, const 
 // target's rows 0..gamma-1, plan CALL_STATS).
 sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype dt, const QSrc& q, const StatsOut& so,
                             const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm,
-                            const Expo& c, void* workspace, hipStream_t st) {
+                            const Expo& c, void* workspace, hipStream_t st, hipEvent_t q_ready = nullptr) {
   const bool bf = dt == SV_BF16;
   const int G1 = gamma + 1;
   hipEvent_t join = nullptr;
@@ -716,6 +721,7 @@ sv_status accept_stats_impl(const Plan& p, const void* target_logits, sv_dtype d
     fork = qsum_fork_point(st, &s);
     if (s != SV_OK) return s;
   }
+  if (q_ready != nullptr && hipStreamWaitEvent(st, q_ready, 0) != hipSuccess) return SV_ERR_HIP;
   s = bf ? run_rowfinal<true>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st)
          : run_rowfinal<false>(p, target_logits, q, draft_ids, V, G1, gamma, c, prm, workspace, st);
   if (s != SV_OK) return s;
@@ -762,6 +768,31 @@ sv_status run_draft_rows(const void* draft_logits, sv_dtype ddt, const int32_t* 
   return SV_OK;
 }
 
+// The draft rows' passes for a call whose target plan is p.  With truncated
+// rows the target's row pass reads nothing of q, so the draft's passes run
+// on the library's side stream (after the work already on the caller's
+// stream), beside the target's row pass, and *q_ready is the event the
+// caller's stream waits for before the target's row finisher, the first
+// reader of q.  Otherwise (untruncated rows, whose row pass gathers q(d); no
+// side stream) they run on the caller's stream and *q_ready is null.
+sv_status draft_rows_beside(const Plan& p, const void* draft_logits, sv_dtype ddt, const int32_t* draft_ids,
+                            int32_t B, int32_t gamma, int32_t V, sv_sampling_params prm, const Expo& c, void* ws,
+                            hipStream_t st, QSrc* q_out, const Cand** qkept_out, hipEvent_t* q_ready,
+                            const int32_t* cu = nullptr, int32_t n_draft = 0) {
+  *q_ready = nullptr;
+  const SideStream* ss = p.trunc ? side_stream(st) : nullptr;
+  if (ss == nullptr) return run_draft_rows(draft_logits, ddt, draft_ids, B, gamma, V, prm, c, ws, st, q_out, qkept_out,
+                                           cu, n_draft);
+  if (hipEventRecord(ss->fork, st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return SV_ERR_HIP;
+  sv_status s = run_draft_rows(draft_logits, ddt, draft_ids, B, gamma, V, prm, c, ws, ss->s, q_out, qkept_out, cu,
+                               n_draft);
+  if (s != SV_OK) return s;
+  if (hipEventRecord(ss->join, ss->s) != hipSuccess) return SV_ERR_HIP;
+  *q_ready = ss->join;
+  return SV_OK;
+}
+
 // Workspace of the draft-logits calls: the target call's regions, then the
 // draft rows' (at draft_ws_offset).
 size_t draft_ws_offset(CallKind kind, int32_t B, int32_t gamma, int32_t V, sv_dtype dt, sv_sampling_params prm) {
@@ -775,13 +806,14 @@ sv_status verify_sample_stats_impl(const Plan& p, const void* target_logits, sv_
                                    const StatsOut& so, const int32_t* draft_ids, const float* u_accept,
                                    const float* u_resample, int32_t B, int32_t gamma, int32_t V,
                                    sv_sampling_params prm, const Expo& c, int32_t* out_tokens, int32_t* out_num_accepted,
-                                   uint32_t* out_row_flags, void* workspace, hipStream_t st) {
+                                   uint32_t* out_row_flags, void* workspace, hipStream_t st,
+                                   hipEvent_t q_ready = nullptr) {
   hipEvent_t join = nullptr;
   const SideStream* fork = nullptr;
   const bool qsum = q.dense != nullptr && so.z_qp != nullptr && p.trunc;
   sv_status s = verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
                                    out_tokens, out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0,
-                                   /*force_rowfinal=*/true, qsum ? &fork : nullptr);
+                                   /*force_rowfinal=*/true, qsum ? &fork : nullptr, q_ready);
   if (s != SV_OK) return s;
   if (qsum) {
     // the dense-q row sums, behind the fork point after the row pass
@@ -1011,13 +1043,15 @@ sv_status spec_verify_sample_draft_logits(const void* target_logits, sv_dtype dt
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   QSrc q = q_src_none(V);
   const Cand* qkept = nullptr;
+  hipEvent_t q_ready = nullptr;
   if (gamma > 0) {
-    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c, static_cast<unsigned char*>(workspace) + qoff,
-                       st, &q, &qkept);
+    s = draft_rows_beside(p, draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c,
+                          static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, &q_ready);
     if (s != SV_OK) return s;
   }
   return verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma, V, prm, c, out_tokens,
-                            out_num_accepted, out_row_flags, workspace, st);
+                            out_num_accepted, out_row_flags, workspace, st, nullptr, 0, -1, 1.0, false, nullptr,
+                            q_ready);
 }
 
 sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
@@ -1040,11 +1074,12 @@ sv_status spec_accept_stats_draft_logits(const void* target_logits, sv_dtype dt,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   QSrc q;
   const Cand* qkept = nullptr;
-  s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c, static_cast<unsigned char*>(workspace) + qoff,
-                     st, &q, &qkept);
+  hipEvent_t q_ready = nullptr;
+  s = draft_rows_beside(p, draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c,
+                        static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, &q_ready);
   if (s != SV_OK) return s;
   const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, qkept};
-  return accept_stats_impl(p, target_logits, dt, q, so, draft_ids, B, gamma, V, prm, c, workspace, st);
+  return accept_stats_impl(p, target_logits, dt, q, so, draft_ids, B, gamma, V, prm, c, workspace, st, q_ready);
 }
 
 sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dtype dt, const void* draft_logits,
@@ -1071,14 +1106,15 @@ sv_status spec_verify_sample_stats_draft_logits(const void* target_logits, sv_dt
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   QSrc q = q_src_none(V);
   const Cand* qkept = nullptr;
+  hipEvent_t q_ready = nullptr;
   if (gamma > 0) {
-    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c,
-                       static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept);
+    s = draft_rows_beside(p, draft_logits, draft_dt, draft_ids, B, gamma, V, prm, c,
+                          static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, &q_ready);
     if (s != SV_OK) return s;
   }
   const StatsOut so{out_alpha, out_z_pq, out_z_qp, out_accept_prob, qkept};
   return verify_sample_stats_impl(p, target_logits, dt, q, so, draft_ids, u_accept, u_resample, B, gamma, V, prm, c,
-                                  out_tokens, out_num_accepted, out_row_flags, workspace, st);
+                                  out_tokens, out_num_accepted, out_row_flags, workspace, st, q_ready);
 }
 
 sv_status spec_verify_sample_lenient(const void* target_logits, sv_dtype dt, const float* draft_probs,
@@ -1157,14 +1193,15 @@ sv_status spec_verify_sample_ragged_draft_logits(const void* target_logits, sv_d
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   QSrc q = q_src_none(V);
   const Cand* qkept = nullptr;
+  hipEvent_t q_ready = nullptr;
   if (n_draft > 0) {
-    s = run_draft_rows(draft_logits, draft_dt, draft_ids, B, gamma_max, V, prm, c,
-                       static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, cu_draft, n_draft);
+    s = draft_rows_beside(p, draft_logits, draft_dt, draft_ids, B, gamma_max, V, prm, c,
+                          static_cast<unsigned char*>(workspace) + qoff, st, &q, &qkept, &q_ready, cu_draft, n_draft);
     if (s != SV_OK) return s;
   }
   return verify_sample_impl(p, target_logits, dt, q, draft_ids, u_accept, u_resample, B, gamma_max, V, prm, c,
                             out_tokens, out_num_accepted, out_row_flags, workspace, st, cu_draft, n_draft,
-                            eos_id < 0 ? -1 : eos_id);
+                            eos_id < 0 ? -1 : eos_id, 1.0, false, nullptr, q_ready);
 }
 
 sv_status spec_verify_greedy_ragged(const void* target_logits, sv_dtype dt, const int32_t* draft_ids,
