@@ -8,7 +8,8 @@ from float approximations of p and q would move Z by as much as Z itself.
 - q formed from draft logits equal to the target's: p = q term by term,
   on both sides, so Z = Z' = 0 and alpha = 1 up to the rounding of sum p;
 - sharp rows (T = 0.2) in a large batch of short rows, where a Z of a few
-  1e-12 holds only the double precision floor.
+  1e-12 holds only the double precision floor;
+- the c2 and c3 workloads' full batches, every position.
 """
 
 import numpy as np
@@ -88,3 +89,13 @@ def test_sharp_short_rows(draft_logits):
     1e-14 to 1e-9."""
     w = generate("c3", DEV, B=341, gamma=11, V=255, temperature=0.2, top_k=0, top_p=1.0, seed=200246)
     compare_stats(w, label=f"sharp short rows draft_logits={draft_logits}", draft_logits=draft_logits)
+
+
+@pytest.mark.parametrize("shape,draft_logits", [("c2", False), ("c2", True), ("c3", False), ("c3", True)])
+def test_full_size_every_request(shape, draft_logits):
+    """The workloads' full batches, every position against the oracle (in
+    a pool of host processes): untruncated rows (c2: the S64 pass, streamed
+    sums, for p and for a q formed from the draft's logits) and top-k lists
+    (c3)."""
+    w = generate(shape, DEV)
+    compare_stats(w, label=f"{shape} full stats draft_logits={draft_logits}", draft_logits=draft_logits, pool=True)
