@@ -114,22 +114,30 @@ def test_graph_replay_matches_eager():
             assert torch.equal(a, b)
 
 
-def test_calls_on_several_streams():
-    """The dense-q sums run on a side stream of the caller's stream: calls
-    enqueued on three caller streams at once, each with its own workspace
-    and outputs, give the default stream's results bit for bit."""
+@pytest.mark.parametrize("dl", [False, True])
+def test_calls_on_several_streams(dl):
+    """The dense-q sums (and, with q from the draft's logits under top-p,
+    the draft rows' passes) run on a side stream of the caller's stream:
+    calls enqueued on three caller streams at once, each with its own
+    workspace and outputs, give the default stream's results bit for bit."""
     w = generate("c5", DEV, B=4, V=50000)
     c = w.cfg
-    ref = [t.clone() for t in sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample,
-                                                     c.temperature, c.top_k, c.top_p)]
+
+    def call():
+        if dl:
+            return sv.verify_sample_stats_draft_logits(w.logits, w.draft_logits, w.ids, w.u_accept, w.u_resample,
+                                                       c.temperature, c.top_k, c.top_p)
+        return sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature, c.top_k,
+                                      c.top_p)
+
+    ref = [t.clone() for t in call()]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream() for _ in range(3)]
     res = []
     for st in streams:
         st.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(st):
-            res.append(sv.verify_sample_stats(w.logits, w.q, w.ids, w.u_accept, w.u_resample, c.temperature,
-                                              c.top_k, c.top_p))
+            res.append(call())
     for st in streams:
         torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
