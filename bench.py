@@ -59,10 +59,11 @@ def log(*a):
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c5", choices=["toy", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1: the step is measured on one GPU)")
+    ap.add_argument("--steps", type=int, default=200, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before them")
+    ap.add_argument("--config", default="c5", choices=["toy", "c2", "c3", "c4", "c5"],
+                    help="workload (default c5: sampling plus the acceptance statistics)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--draft-logits", action="store_true",
                     help="hand the draft's logits instead of q (the library forms q); sampling workloads only")
@@ -75,7 +76,9 @@ def parse():
                     help="requests per step (default: the workload's B); the recipe is otherwise unchanged")
     ap.add_argument("--no-z-qp", action="store_true",
                     help="statistics without Z' = sum (q - p)_+ (alpha, Z and accept_prob only)")
-    ap.add_argument("--rotate-mb", type=float, default=600.0)
+    ap.add_argument("--rotate-mb", type=float, default=600.0,
+                    help="workloads smaller than this are copied and the timed loop rotates over the copies, so "
+                         "that the inputs come from HBM rather than the last-level cache")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle time budget of each of its two legs (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
