@@ -55,53 +55,120 @@ struct AcceptArgs {
 // and q in double; otherwise p.
 // The list is walked 64 entries at a time in id order (prefix sums by wave
 // scans, carried between steps); the loads of kDrawBlk steps (list entries,
-// then q at their ids) are issued together before their scans.
+// then q at their ids) are issued together before their scans.  A list of
+// at most kDrawBlk * 64 entries is read once: the total and the search take
+// the same registers.  has_pre: the caller already loaded entry `lane`
+// (pre) of a list of at most 64 entries.
 constexpr int kDrawBlk = 4;
-__device__ int draw_from_list(const Cand* L, int n, double S64, float R, double c64, const QRow& qr,
-                              bool& residual, float u, uint32_t& fl, double qs) {
+struct DrawBlk {
+  Cand e[kDrawBlk];   // entries i0 + 64 k + lane (idx = -1 past the end)
+  float qv[kDrawBlk]; // q's raw values at their ids (residual draws)
+};
+
+__device__ __forceinline__ void draw_load(const Cand* L, int n, int i0, bool res, const QRow& qr, DrawBlk& d) {
   const int lane = lane_id();
-  const double invS = 1.0 / S64;
-  // weights of entries i0 + 64 k + lane, k < kDrawBlk (0 past the end)
-  auto weights = [&](int i0, bool res, double (&w)[kDrawBlk], int (&id)[kDrawBlk]) {
-    Cand e[kDrawBlk];
 #pragma unroll
-    for (int k = 0; k < kDrawBlk; ++k) {
-      const int i = i0 + k * kWave + lane;
-      e[k].v = 0.0f;
-      e[k].idx = -1;
-      if (i < n) e[k] = L[i];
-    }
-    float qv[kDrawBlk];
+  for (int k = 0; k < kDrawBlk; ++k) {
+    const int i = i0 + k * kWave + lane;
+    d.e[k].v = 0.0f;
+    d.e[k].idx = -1;
+    if (i < n) d.e[k] = L[i];
+  }
 #pragma unroll
-    for (int k = 0; k < kDrawBlk; ++k) qv[k] = (res && e[k].idx >= 0) ? qr.raw_at(e[k].idx) : 0.0f;
+  for (int k = 0; k < kDrawBlk; ++k) d.qv[k] = (res && d.e[k].idx >= 0) ? qr.raw_at(d.e[k].idx) : 0.0f;
+}
+
+__device__ __forceinline__ void draw_weights(const DrawBlk& d, bool res, double invS, float R, double c64,
+                                             const QRow& qr, double qs, double (&w)[kDrawBlk]) {
 #pragma unroll
-    for (int k = 0; k < kDrawBlk; ++k) {
-      id[k] = e[k].idx;
-      if (e[k].idx < 0) {
-        w[k] = 0.0;
+  for (int k = 0; k < kDrawBlk; ++k) {
+    if (d.e[k].idx < 0) {
+      w[k] = 0.0;
+    } else {
+      const double p = e64_of(d.e[k].v, c64, R) * invS;
+      if (!res) {
+        w[k] = p;
       } else {
-        const double p = e64_of(e[k].v, c64, R) * invS;
-        if (!res) {
-          w[k] = p;
-        } else {
-          const double d = p - qs * qr.q64(qv[k]);
-          w[k] = d > 0.0 ? d : 0.0;
-        }
+        const double dd = p - qs * qr.q64(d.qv[k]);
+        w[k] = dd > 0.0 ? dd : 0.0;
       }
     }
+  }
+}
+
+__device__ __forceinline__ int draw_from_list(const Cand* L, int n, double S64, float R, double c64, const QRow& qr,
+                              bool& residual, float u, uint32_t& fl, double qs, bool has_pre = false,
+                              Cand pre = Cand{}) {
+  const int lane = lane_id();
+  const double invS = 1.0 / S64;
+  // sum of one block's weights, carried (the scans of the search below)
+  auto blk_total = [&](int i0, const double (&w)[kDrawBlk], double carry) -> double {
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) {
+      if (i0 + k * kWave >= n) break;
+      const double incl = wave_incl_scan_d(w[k]);
+      carry = carry + wave_last_d(incl);
+    }
+    return carry;
   };
+  // search of one block from `carry`: the token at the crossing of t, else
+  // -1 (lastpos: the last positive entry so far)
+  auto blk_search = [&](int i0, const double (&w)[kDrawBlk], const DrawBlk& d, double t, double& carry,
+                        int& lastpos) -> int {
+#pragma unroll
+    for (int k = 0; k < kDrawBlk; ++k) {
+      const int j0 = i0 + k * kWave;
+      if (j0 >= n) break;
+      const int i = j0 + lane;
+      const double incl = wave_incl_scan_d(w[k]);
+      const double C = carry + incl;
+      const uint64_t hit = ballot(i < n && C > t);
+      if (hit) return __shfl(d.e[k].idx, (int)__builtin_ctzll(hit), kWave);
+      const uint64_t pos = ballot(i < n && w[k] > 0.0);
+      if (pos) lastpos = __shfl(d.e[k].idx, 63 - (int)__builtin_clzll(pos), kWave);
+      carry = carry + wave_last_d(incl);
+    }
+    return -1;
+  };
+  if (n <= kDrawBlk * kWave) {
+    DrawBlk d;
+    if (has_pre && n <= kWave) {
+      d.e[0].v = 0.0f;
+      d.e[0].idx = -1;
+      if (lane < n) d.e[0] = pre;
+#pragma unroll
+      for (int k = 1; k < kDrawBlk; ++k) {
+        d.e[k].v = 0.0f;
+        d.e[k].idx = -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kDrawBlk; ++k) d.qv[k] = (residual && d.e[k].idx >= 0) ? qr.raw_at(d.e[k].idx) : 0.0f;
+    } else {
+      draw_load(L, n, 0, residual, qr, d);
+    }
+    double w[kDrawBlk];
+    draw_weights(d, residual, invS, R, c64, qr, qs, w);
+    double W = blk_total(0, w, 0.0);
+    if (residual && !(W > 0.0)) {
+      fl |= 4u;  // SV_ROW_Z_DEGENERATE
+      residual = false;
+      draw_weights(d, false, invS, R, c64, qr, qs, w);
+      W = blk_total(0, w, 0.0);
+    }
+    const double t = (double)u * W;
+    double carry = 0.0;
+    int lastpos = -1;
+    const int token = blk_search(0, w, d, t, carry, lastpos);
+    return token >= 0 ? token : lastpos;
+  }
   auto total = [&](bool res) -> double {
     double carry = 0.0;
     for (int i0 = 0; i0 < n; i0 += kDrawBlk * kWave) {
+      DrawBlk d;
+      draw_load(L, n, i0, res, qr, d);
       double w[kDrawBlk];
-      int id[kDrawBlk];
-      weights(i0, res, w, id);
-#pragma unroll
-      for (int k = 0; k < kDrawBlk; ++k) {
-        if (i0 + k * kWave >= n) break;
-        const double incl = wave_incl_scan_d(w[k]);
-        carry = carry + wave_last_d(incl);
-      }
+      draw_weights(d, res, invS, R, c64, qr, qs, w);
+      carry = blk_total(i0, w, carry);
     }
     return carry;
   };
@@ -115,25 +182,11 @@ __device__ int draw_from_list(const Cand* L, int n, double S64, float R, double 
   double carry = 0.0;
   int token = -1, lastpos = -1;
   for (int i0 = 0; i0 < n && token < 0; i0 += kDrawBlk * kWave) {
+    DrawBlk d;
+    draw_load(L, n, i0, residual, qr, d);
     double w[kDrawBlk];
-    int id[kDrawBlk];
-    weights(i0, residual, w, id);
-#pragma unroll
-    for (int k = 0; k < kDrawBlk; ++k) {
-      const int j0 = i0 + k * kWave;
-      if (j0 >= n) break;
-      const int i = j0 + lane;
-      const double incl = wave_incl_scan_d(w[k]);
-      const double C = carry + incl;
-      const uint64_t hit = ballot(i < n && C > t);
-      if (hit) {
-        token = __shfl(id[k], (int)__builtin_ctzll(hit), kWave);
-        break;
-      }
-      const uint64_t pos = ballot(i < n && w[k] > 0.0);
-      if (pos) lastpos = __shfl(id[k], 63 - (int)__builtin_clzll(pos), kWave);
-      carry = carry + wave_last_d(incl);
-    }
+    draw_weights(d, residual, invS, R, c64, qr, qs, w);
+    token = blk_search(i0, w, d, t, carry, lastpos);
   }
   return token >= 0 ? token : lastpos;
 }
@@ -256,9 +309,17 @@ struct Decision {
   RowInfo rs;      // info of row n_accepted (the row the token is drawn from)
 };
 
+// Entry `lane` of the draw row's kept list and that row's resample uniform,
+// loaded before the decision was known (see accept_trunc_kernel).
+struct ListPick {
+  Cand e;
+  float u;
+};
+
 // Emit the outputs of one request once its decision is known (whole wave).
 template <bool BF16>
-__device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, int32_t* out) {
+__device__ __forceinline__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, int32_t* out,
+                               bool has_pk = false, ListPick pk = ListPick{}) {
   const int lane = lane_id();
   const int nacc = dc.nacc, G = dc.G, P1 = a.gamma + 1;
   const int64_t lo = dc.lo;
@@ -275,7 +336,7 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     return;
   }
   bool residual = nacc < G;
-  const float u = a.ur[lo + b + nacc];
+  const float u = has_pk ? pk.u : a.ur[lo + b + nacc];
   const int64_t trow = lo + b + nacc;  // plan row of the draw (= its logits row)
   const int64_t qrow = residual ? lo + nacc : -1;
   const QRow qr = residual ? q_row(a.q, qrow) : q_none();
@@ -300,7 +361,8 @@ __device__ void finish_request(const AcceptArgs& a, int b, const Decision& dc, i
     }
     return;
   }
-  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S64, rs.R, a.c64, qr, residual, u, fl, a.beta);
+  int token = draw_from_list(a.kept + trow * a.kmax, rs.nkept, rs.S64, rs.R, a.c64, qr, residual, u, fl, a.beta,
+                             has_pk, pk.e);
   if (lane == 0) {
     if (a.eos >= 0 && token == a.eos) fl |= 16u;  // SV_ROW_EOS
     out[nacc] = token;
@@ -389,25 +451,14 @@ __device__ Decision decide_short(const AcceptArgs& a, int b) {
   return dc;
 }
 
-// One request's acceptance and draw, by one wave (a row whose kept set is
+// One request's acceptance and draw with gamma + 1 > 64, by one wave: rows
+// go through the workspace copy of the row infos (a row whose kept set is
 // not a list leaves a BigJob for a full-row draw).
 template <bool BF16, bool FROM_CHUNKS>
-__device__ __forceinline__ void accept_request(const AcceptArgs& a, int b) {
+__device__ __forceinline__ void accept_long(const AcceptArgs& a, int b) {
   const int lane = lane_id();
   const int P1 = a.gamma + 1;
   int32_t* out = a.out_tokens + (int64_t)b * P1;
-
-  if (P1 <= kWave) {
-    Decision dc = decide_short<BF16, FROM_CHUNKS>(a, b);
-    if (dc.bad) {
-      empty_request(a, b, out, dc.badfl);
-      return;
-    }
-    finish_request<BF16>(a, b, dc, out);
-    return;
-  }
-
-  // Long drafts: rows go through the workspace copy of the row infos.
   const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
   if (!sp.ok) {
     empty_request(a, b, out, 32u);  // SV_ROW_BAD_SPAN
@@ -495,7 +546,7 @@ template <bool BF16>
 __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
   const int b = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
   if (b >= a.B) return;
-  accept_request<BF16, true>(a, b);
+  accept_long<BF16, true>(a, b);
 }
 
 // Truncated rows: one request per workgroup.  Wave 0 takes the decision and
@@ -503,13 +554,55 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
 // wide nucleus) is drawn by the whole workgroup, one quarter of the row per
 // wave: each wave totals its quarter, and the wave whose quarter holds the
 // crossing of t = u * W finds the token (sums in a fixed order).
+//
+// Requests of at most kPfRows rows: while wave 0 reads the row infos and
+// takes the decision, waves 1-3 copy the first 64 entries of every row's
+// kept list and every row's resample uniform into LDS, so that once the
+// draw row is known a list of up to 64 entries costs no further round trip
+// but q at its ids (entries past the row's nkept are never used).
+constexpr int kPfRows = 8;
 template <bool BF16>
 __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.x;
   __shared__ double s_tot[4];
   __shared__ long long s_tok;
-  if (wid == 0) accept_request<BF16, false>(a, b);
+  __shared__ Cand s_pre[kPfRows * kWave];
+  __shared__ float s_ur[kPfRows];
+  if (a.gamma + 1 <= kWave) {
+    const bool pf = a.gamma + 1 <= kPfRows;
+    Decision dc;
+    if (wid == 0) {
+      dc = decide_short<BF16, false>(a, b);
+    } else if (pf) {
+      const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
+      if (sp.ok) {
+        const int t = (int)threadIdx.x - kWave;
+        for (int i = t; i < (sp.g + 1) * kWave; i += 3 * kWave)
+          s_pre[i] = a.kept[((int64_t)sp.lo + b + (i >> 6)) * a.kmax + (i & 63)];
+        if (t <= sp.g) s_ur[t] = a.ur[(int64_t)sp.lo + b + t];
+      }
+    }
+    if (pf) __syncthreads();
+    if (wid == 0) {
+      int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
+      if (dc.bad) {
+        empty_request(a, b, out, dc.badfl);
+      } else {
+        ListPick pk;
+        pk.e.v = 0.0f;
+        pk.e.idx = -1;
+        pk.u = 0.0f;
+        if (pf) {
+          pk.e = s_pre[dc.nacc * kWave + lane];
+          pk.u = s_ur[dc.nacc];
+        }
+        finish_request<BF16>(a, b, dc, out, pf, pk);
+      }
+    }
+  } else if (wid == 0) {
+    accept_long<BF16, false>(a, b);
+  }
   __syncthreads();
   const BigJob jb = a.jobs[b];
   if (!jb.active) return;
