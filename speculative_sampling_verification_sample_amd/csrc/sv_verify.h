@@ -1691,9 +1691,26 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
   const int64_t r = (int64_t)blockIdx.x * 4 + wid;
   if (r >= a.rows) return;
   const int64_t ir = info_row(a, r);
+  const bool qlog = a.q.dense == nullptr;
+  // The first kStatPre * 64 entries of p's kept list (and of q's, when its
+  // Z' is asked for) are loaded together with the row info, before nkept
+  // is known (a nucleus of a few hundred tokens then costs no round trip
+  // but q at its ids); entries past nkept are never used.
+  constexpr int kStatBlk = 8;
+  constexpr int kStatPre = 4;
+  const Cand* L = a.kept != nullptr ? a.kept + ir * a.kmax : nullptr;
+  const Cand* Lq = (qlog && a.qkept != nullptr && a.out_zqp != nullptr) ? a.qkept + r * a.kmax : nullptr;
+  Cand pre[kStatPre], qpre[kStatPre];
+#pragma unroll
+  for (int u = 0; u < kStatPre; ++u) {
+    pre[u].v = 0.0f;
+    pre[u].idx = 0;
+    qpre[u] = pre[u];
+    if (L != nullptr) pre[u] = L[lane + u * kWave];
+    if (Lq != nullptr) qpre[u] = Lq[lane + u * kWave];
+  }
   const RowInfo ri = a.info[ir];
   const float qnan = __builtin_nanf("");
-  const bool qlog = a.q.dense == nullptr;
   const bool qbad = qlog && (a.q.info[r].flags & RF_NONFINITE);
   if ((ri.flags & RF_NONFINITE) || qbad) {
     if (lane == 0) {
@@ -1724,19 +1741,26 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
     zpq = sm[ST_PQ];
     zqp = sm[ST_QP];
   } else {
-    const Cand* L = a.kept + ir * a.kmax;  // token-id order
+    // L: token-id order
     double mn = 0.0, pq = 0.0, qp = 0.0, sqk = 0.0;
     // kStatBlk list steps per round (a nucleus of a few hundred tokens in
     // one): their entry loads, then their q loads, are in flight together;
     // each lane still adds its entries in list order
-    constexpr int kStatBlk = 8;
     const int nk = ri.nkept;
     for (int i0 = lane; i0 < nk; i0 += kStatBlk * kWave) {
       Cand e[kStatBlk];
       float qf[kStatBlk];
+      if (i0 == lane) {
 #pragma unroll
-      for (int u = 0; u < kStatBlk; ++u)
-        if (i0 + u * kWave < nk) e[u] = L[i0 + u * kWave];
+        for (int u = 0; u < kStatBlk; ++u) {
+          if (u < kStatPre) e[u] = pre[u];
+          else if (i0 + u * kWave < nk) e[u] = L[i0 + u * kWave];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kStatBlk; ++u)
+          if (i0 + u * kWave < nk) e[u] = L[i0 + u * kWave];
+      }
 #pragma unroll
       for (int u = 0; u < kStatBlk; ++u) qf[u] = (i0 + u * kWave < nk) ? qr.raw_at(e[u].idx) : 0.0f;
 #pragma unroll
@@ -1771,15 +1795,22 @@ __global__ void __launch_bounds__(256) stats_final_kernel(StatsArgs a) {
       // Z' = sum over q's kept set of (q - p)_+, with p read at its ids
       const RowInfo qi = a.q.info[r];
       const double qS64 = qi.S64;
-      const Cand* Lq = a.qkept + r * a.kmax;
       double zq = 0.0;
       const int nq = qi.nkept;
       for (int i0 = lane; i0 < nq; i0 += kStatBlk * kWave) {
         Cand e[kStatBlk];
         float zf[kStatBlk];
+        if (i0 == lane) {
 #pragma unroll
-        for (int u = 0; u < kStatBlk; ++u)
-          if (i0 + u * kWave < nq) e[u] = Lq[i0 + u * kWave];
+          for (int u = 0; u < kStatBlk; ++u) {
+            if (u < kStatPre) e[u] = qpre[u];
+            else if (i0 + u * kWave < nq) e[u] = Lq[i0 + u * kWave];
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < kStatBlk; ++u)
+            if (i0 + u * kWave < nq) e[u] = Lq[i0 + u * kWave];
+        }
 #pragma unroll
         for (int u = 0; u < kStatBlk; ++u)
           zf[u] = (i0 + u * kWave < nq) ? load_logit<BF16>(a.logits, lrow + e[u].idx) : kNegInf;
