@@ -559,7 +559,8 @@ __global__ void __launch_bounds__(256) accept_kernel(AcceptArgs a) {
 // takes the decision, waves 1-3 copy the first 64 entries of every row's
 // kept list and every row's resample uniform into LDS, so that once the
 // draw row is known a list of up to 64 entries costs no further round trip
-// but q at its ids (entries past the row's nkept are never used).
+// but q at its ids (entries past the row's nkept are never used).  Waves 1-3
+// leave as soon as the decision shows that the draw row has a list.
 constexpr int kPfRows = 8;
 template <bool BF16>
 __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
@@ -569,11 +570,14 @@ __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
   __shared__ long long s_tok;
   __shared__ Cand s_pre[kPfRows * kWave];
   __shared__ float s_ur[kPfRows];
+  __shared__ int s_big;
   if (a.gamma + 1 <= kWave) {
     const bool pf = a.gamma + 1 <= kPfRows;
     Decision dc;
     if (wid == 0) {
       dc = decide_short<BF16, false>(a, b);
+      // the draw row's kept set is not a list: the four waves draw it below
+      if (lane == 0) s_big = (!dc.bad && !dc.eos_cut && (dc.rs.flags & RF_BIG)) ? 1 : 0;
     } else if (pf) {
       const Span sp = span_of(Layout{a.cu, a.n_draft, a.gamma}, b);
       if (sp.ok) {
@@ -583,7 +587,9 @@ __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
         if (t <= sp.g) s_ur[t] = a.ur[(int64_t)sp.lo + b + t];
       }
     }
-    if (pf) __syncthreads();
+    __syncthreads();
+    const bool big = s_big != 0;
+    if (wid != 0 && !big) return;  // nothing left for waves 1-3
     if (wid == 0) {
       int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
       if (dc.bad) {
@@ -600,10 +606,12 @@ __global__ void __launch_bounds__(256, 4) accept_trunc_kernel(AcceptArgs a) {
         finish_request<BF16>(a, b, dc, out, pf, pk);
       }
     }
-  } else if (wid == 0) {
-    accept_long<BF16, false>(a, b);
+    if (!big) return;
+    __syncthreads();  // wave 0 has stored the request's BigJob
+  } else {
+    if (wid == 0) accept_long<BF16, false>(a, b);
+    __syncthreads();
   }
-  __syncthreads();
   const BigJob jb = a.jobs[b];
   if (!jb.active) return;
   const int64_t V = a.V;
