@@ -929,13 +929,21 @@ template <bool BF16>
 __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
+  const double* P = a.partials + (int64_t)b * a.nch4 * 4;
+  // rows of at most 64 chunks: wave 0 loads lane k's four chunk sums
+  // together with the job (the address does not depend on it)
+  const bool few = a.nch4 <= kWave;
+  double cs[4] = {0.0, 0.0, 0.0, 0.0};
+  if (few && wid == 0 && lane < a.nch4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cs[i] = P[lane * 4 + i];
+  }
   const BigJob jb = a.jobs[b];
   if (!jb.active) return;
   __shared__ double s_w[4];
   __shared__ int s_cstar, s_wf[4], s_wl[4];
   __shared__ double s_carry, s_t, s_inv[2];
   __shared__ int s_res;
-  const double* P = a.partials + (int64_t)b * a.nch4 * 4;
   bool residual = jb.qrow >= 0;
   const bool qlog = residual && a.q.dense == nullptr && a.q.z != nullptr;
   uint32_t extra = 0;
@@ -943,15 +951,21 @@ __global__ void __launch_bounds__(256) big_finish_kernel(BigArgs a) {
     // normalisers: chunk sums in a fixed order (lanes over chunks, then the
     // wave reduction)
     double sp = 0.0, sq = 0.0;
-    for (int k = lane; k < a.nch4; k += kWave) {
-      sp += P[k * 4 + 0];
-      sq += P[k * 4 + 2];
+    if (few) {
+      sp += cs[0];
+      sq += cs[2];
+    } else {
+      for (int k = lane; k < a.nch4; k += kWave) {
+        sp += P[k * 4 + 0];
+        sq += P[k * 4 + 2];
+      }
     }
     sp = wave_sum_d(sp);
     sq = wave_sum_d(sq);
     const double invSp = 1.0 / sp, invSq = qlog ? 1.0 / sq : 1.0;
     auto wchunk = [&](int k, bool res) -> double {
       if (k >= a.nch4) return 0.0;
+      if (few) return res ? cs[1] * invSp - a.beta * (cs[3] * invSq) : cs[0];  // k == lane
       return res ? P[k * 4 + 1] * invSp - a.beta * (P[k * 4 + 3] * invSq) : P[k * 4 + 0];
     };
     // total weight (the same scans as the walk below: identical sums)
