@@ -6,7 +6,9 @@ statistics finish change how they read them:
 - a list of up to 64 entries is drawn from that copy, up to 256 from one
   read, longer ones in streamed steps of 256;
 - the statistics finish loads the first 256 entries of p's (and q's) list
-  with the row info and reads the rest afterwards.
+  with the row info and reads the rest afterwards;
+- a kept set too long for a list is drawn by all four waves, which stay
+  only in that case.
 
 fp32 logits (no ties) keep exactly top_k tokens; every request is compared
 with the oracle: sampling, lenient sampling and the statistics, with a
@@ -50,3 +52,14 @@ def test_list_sizes_top_p_bf16(top_p):
     compare_sample(w, label=label)
     compare_stats(w, label=label)
     compare_stats(w, label=label + " draft logits", draft_logits=True)
+
+
+@pytest.mark.parametrize("gamma", [7, 9])
+def test_oversized_kept_sets(gamma):
+    """Flat-ish rows (T = 50, top-p 0.9) whose kept sets are too long for a
+    list: the acceptance's four waves draw them from the whole row, with the
+    list copy made during the decision (gamma = 7) and without it (gamma = 9)."""
+    w = generate("c5", DEV, B=3, gamma=gamma, V=30000, temperature=50.0, top_p=0.9, seed=93000 + gamma)
+    label = f"oversized kept sets gamma={gamma}"
+    compare_sample(w, label=label)
+    compare_sample(w, label=label + " draft logits", draft_logits=True)
